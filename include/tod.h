@@ -1,0 +1,232 @@
+/*
+ * tod.h -- C ABI of the MI355X (gfx950) block-scheduled int4 decode library.
+ *
+ * The library runs the throughput-oriented generation loop of FlexGen on one
+ * GPU: greedy decode of an OPT-shaped decoder stack for a block of K GPU
+ * batches, with
+ *   - the zig-zag block schedule: each layer's weights are read once per
+ *     decode step and used for every batch of the block
+ *       (FlexGen guide, "2. The Zig-Zag Block Schedule");
+ *   - group-wise 4-bit weights and a group-wise 4-bit KV cache, dequantized
+ *     on the fly for fp16 compute
+ *       (FlexGen guide, "3. Group-Wise 4-Bit Quantization for Weights and KV Cache");
+ *   - optionally, fp16 weights held in pinned host memory and streamed into
+ *     HBM layer by layer, overlapped with compute
+ *       (FlexGen guide, "1. Three-Tier Storage Hierarchy"; TightLLM abstract,
+ *        on overlapping transfer with computation).
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success, a negative TOD_E* code on error; never abort and
+ *     never throw. last_error() returns a message for the calling thread's
+ *     last failing call.
+ *   - Pointers named d_* are caller-owned device (HBM) memory; h_* are
+ *     caller-owned host memory. Sizes are element counts unless stated.
+ *   - fp16 tensors are passed as uint16_t bit patterns (IEEE binary16).
+ *   - stream is a hipStream_t passed as void*; NULL is the null stream.
+ *     Calls that take a stream are asynchronous on it; init_model,
+ *     set_global_weights, set_layer_weights and free_model synchronize.
+ *   - A kernel fault surfaces as TOD_EHIP at the next synchronizing call.
+ *
+ * Group-wise int4 format (canonical, as exchanged through this ABI): a tensor
+ * of n elements is cut into n/64 contiguous groups. Per group: zero = group
+ * minimum (fp16), scale = fp16(fp32(max - min) / 15), code c in [0, 15] =
+ * nearest grid point zero + c*scale with ties to the larger code; element
+ * value zero + c*scale rounded once to fp16. Codes are packed two per byte,
+ * element 2t in the low nibble of byte t. Weight matrices W[out][in] are
+ * grouped along `in`; K and V vectors along the head dimension.
+ */
+#ifndef TOD_H
+#define TOD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TOD_OK 0
+#define TOD_EINVAL (-1) /* bad argument: null pointer, shape or size mismatch, group != 64 */
+#define TOD_ENOMEM (-2) /* device or pinned host allocation failed */
+#define TOD_EHIP (-3)   /* HIP runtime error; the message carries hipGetErrorString */
+#define TOD_ESTATE (-4) /* call out of order: decode before prefill, context full, block out of range */
+
+#define TOD_GROUP 64
+
+/* Where a model's six decoder matrices per layer live. */
+#define TOD_W_HBM_INT4 0         /* int4 group-64 in HBM, quantized at load */
+#define TOD_W_HOST_FP16_STREAM 1 /* fp16 in pinned host memory, streamed per layer into a 2-slot HBM buffer */
+
+/* Order of the 16 per-layer tensors passed to set_layer_weights. */
+enum {
+    TOD_LN1_G = 0, TOD_LN1_B, TOD_Q_W, TOD_Q_B, TOD_K_W, TOD_K_B, TOD_V_W, TOD_V_B,
+    TOD_O_W, TOD_O_B, TOD_LN2_G, TOD_LN2_B, TOD_FC1_W, TOD_FC1_B, TOD_FC2_W, TOD_FC2_B,
+    TOD_LAYER_TENSORS
+};
+
+/* Matrix ids for export_weight. */
+enum { TOD_MAT_Q = 0, TOD_MAT_K, TOD_MAT_V, TOD_MAT_O, TOD_MAT_FC1, TOD_MAT_FC2 };
+
+typedef struct tod_model tod_model;
+
+/* OPT decoder stack shape. hidden = n_heads * head_dim; head_dim % 64 == 0;
+ * hidden % 64 == 0; ffn % 64 == 0; max_pos = rows of the position table
+ * minus the two offset rows. */
+typedef struct {
+    int32_t n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos;
+} tod_model_config;
+
+/* One block = batches_per_block (K) GPU batches of gpu_batch sequences each;
+ * its K*gpu_batch rows are row k*gpu_batch + i for batch k. Every sequence
+ * has prompt_len prompt tokens and at most gen_len generated tokens, so the
+ * KV cache holds prompt_len + gen_len - 1 positions. n_blocks blocks are
+ * resident at once (each has its own KV cache). group must be 64. */
+typedef struct {
+    int32_t gpu_batch, batches_per_block, prompt_len, gen_len, group, weight_tier, n_blocks;
+} tod_run_config;
+
+/*
+ * init_model: allocate a model (weights store, KV caches, activation buffers).
+ * Weights are supplied afterwards with set_global_weights / set_layer_weights.
+ * FlexGen guide, "2. The Zig-Zag Block Schedule" (a block of K micro-batches
+ * shares each weight load) and "1. Three-Tier Storage Hierarchy" (weight tier).
+ * Errors: TOD_EINVAL on an invalid shape, TOD_ENOMEM if HBM or pinned host
+ * memory runs out, TOD_EHIP otherwise. *out is NULL on error.
+ */
+int init_model(const tod_model_config *cfg, const tod_run_config *run, void *stream, tod_model **out);
+
+/*
+ * set_global_weights: copy the fp16 token embedding h_tok_emb [vocab][hidden]
+ * (also the tied LM head), the position table h_pos_emb [max_pos + 2][hidden]
+ * (OPT's two offset rows first) and the final LayerNorm gain/shift [hidden]
+ * into HBM. Host buffers may be freed on return.
+ */
+int set_global_weights(tod_model *m, const uint16_t *h_tok_emb, const uint16_t *h_pos_emb,
+                       const uint16_t *h_lnf_g, const uint16_t *h_lnf_b);
+
+/*
+ * set_layer_weights: supply layer `layer`'s 16 fp16 host tensors in TOD_*
+ * order (matrices row-major [out][in]: q, k, v, o [hidden][hidden], fc1
+ * [ffn][hidden], fc2 [hidden][ffn]; vectors [out] or [hidden]).
+ * TOD_W_HBM_INT4: the six matrices are copied to HBM and quantized there to
+ * int4 group-64 (FlexGen guide, "3. Group-Wise 4-Bit Quantization"); host
+ * buffers may be freed on return.
+ * TOD_W_HOST_FP16_STREAM: the matrices are copied into the library's pinned
+ * host tier and streamed to HBM on every pass over the layer.
+ */
+int set_layer_weights(tod_model *m, int layer, const uint16_t *const *h_tensors);
+
+/*
+ * prefill: run the prompts of block `block` (d_ids int32 [K*b][prompt_len])
+ * through the stack in the zig-zag order (per layer, batch by batch), storing
+ * every prompt position's K/V into the int4 cache, and write each row's first
+ * generated token to d_next int32 [K*b]. d_logits (nullable) receives the fp16
+ * logits of the last prompt position, [K*b][vocab].
+ * Resets the block's decode position. FlexGen guide, "2. The Zig-Zag Block
+ * Schedule"; FlexLLMGen page, "Key highlights" (generate API).
+ * Errors: TOD_EINVAL, TOD_ESTATE (weights missing, block out of range).
+ */
+int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint16_t *d_logits, void *stream);
+
+/*
+ * decode_block: run n_steps greedy decode steps for all K*b rows of block
+ * `block`. Step t feeds d_ids_in [K*b] (t = 0) or the previous step's picks,
+ * at position prompt_len + (decode steps already run since prefill), appends that
+ * position's quantized K/V, and writes the picks to d_ids_out int32
+ * [n_steps][K*b]; d_logits (nullable) receives fp16 [n_steps][K*b][vocab].
+ * Within a step every layer's weights are read from HBM (or streamed from the
+ * host tier) once for the whole block: the block's rows form the M dimension
+ * of each fused int4 GEMM (FlexGen guide, "2. The Zig-Zag Block Schedule";
+ * comparison table, "Weight Reuse per Load").
+ * Errors: TOD_ESTATE before prefill or when the KV cache would overflow.
+ */
+int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, int32_t *d_ids_out,
+                 uint16_t *d_logits, void *stream);
+
+/*
+ * set_decode_position: set how many decode steps block `block` has completed
+ * since its prefill (0 <= steps <= gen_len - 1); later decode steps overwrite
+ * the cache from that position on. Lets a caller replay decode steps.
+ */
+int set_decode_position(tod_model *m, int block, int steps);
+
+/*
+ * quantize_groupwise: group-wise int4 quantization of d_x fp16 [n] into the
+ * canonical format above: d_codes uint8 [n/2], d_scale fp16 [n/group],
+ * d_zero fp16 [n/group]. n % group == 0, group == 64. Non-finite inputs are
+ * outside the contract (codes undefined, no error).
+ * FlexGen guide, "3. Group-Wise 4-Bit Quantization for Weights and KV Cache".
+ */
+int quantize_groupwise(const uint16_t *d_x, int64_t n, int group, uint8_t *d_codes, uint16_t *d_scale,
+                       uint16_t *d_zero, void *stream);
+
+/* dequantize_groupwise: d_out fp16 [n] = fp16(zero + code * scale) from the canonical format. */
+int dequantize_groupwise(const uint8_t *d_codes, const uint16_t *d_scale, const uint16_t *d_zero, int64_t n,
+                         int group, uint16_t *d_out, void *stream);
+
+/* free_model: synchronize, release every allocation of m. NULL is accepted. */
+int free_model(tod_model *m);
+
+/* last_error: message of the calling thread's last failing call ("" if none). */
+const char *last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Inspection and unit entry points (used by tests and the benchmark).      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * export_weight: copy layer `layer`'s matrix `which` (TOD_MAT_*) back out of
+ * the int4 store in the canonical format (device buffers: codes [out*in/2],
+ * scale and zero [out*in/64]). TOD_ESTATE for the fp16 host tier.
+ */
+int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t *d_scale, uint16_t *d_zero,
+                  void *stream);
+
+/*
+ * export_kv: copy positions [t0, t1) of (layer, block, row, head) out of the
+ * KV cache in the canonical per-position format (device buffers): K codes
+ * [t1-t0][head_dim/2], K scale/zero [t1-t0][head_dim/64], same for V.
+ */
+int export_kv(tod_model *m, int layer, int block, int row, int head, int t0, int t1, uint8_t *d_kc,
+              uint16_t *d_ks, uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream);
+
+/*
+ * linear_w4: y [rows][out] = fp16(a [rows][in] . What^T + bias [+ residual]
+ * [, ReLU]) with W given in the canonical int4 format (device). The library
+ * repacks W into its GEMM layout in scratch memory it owns, then runs the same
+ * fused dequant+MFMA GEMM as the decode path. relu: 0/1. bias and residual
+ * are nullable. Used to test the GEMM at full shapes.
+ */
+int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes, const uint16_t *d_scale,
+              const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
+              void *stream);
+
+/* linear_f16: as linear_w4 with fp16 weights d_w [out][in] (the LM head's and the host tier's path). */
+int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_t *d_w, const uint16_t *d_bias,
+               const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream);
+
+/*
+ * Isolated decode attention over an int4 KV cache (one query per sequence).
+ * attn_cache_create allocates a cache for batch x heads sequences of up to
+ * cap positions with head_dim (multiple of 64) and returns a handle.
+ * attn_cache_fill quantizes and stores fp16 d_k, d_v [n][batch][heads][head_dim]
+ * (position-major) at positions [t0, t0+n). attn_decode_step quantizes and appends the new
+ * d_k_new, d_v_new [batch][heads][head_dim] at position pos, then writes
+ * d_out [batch][heads][head_dim] = attention of d_q [batch][heads][head_dim]
+ * over positions 0..pos (FlexGen guide, "3. Group-Wise 4-Bit Quantization"
+ * for the dynamic KV cache). attn_cache_export reads a position range of one
+ * (sequence, head) back in the canonical format, as export_kv.
+ */
+typedef struct tod_attn_cache tod_attn_cache;
+int attn_cache_create(int batch, int heads, int head_dim, int cap, tod_attn_cache **out);
+int attn_cache_fill(tod_attn_cache *c, const uint16_t *d_k, const uint16_t *d_v, int t0, int n, void *stream);
+int attn_decode_step(tod_attn_cache *c, int pos, const uint16_t *d_q, const uint16_t *d_k_new,
+                     const uint16_t *d_v_new, uint16_t *d_out, void *stream);
+int attn_cache_export(tod_attn_cache *c, int seq, int head, int t0, int t1, uint8_t *d_kc, uint16_t *d_ks,
+                      uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream);
+int attn_cache_free(tod_attn_cache *c);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOD_H */

@@ -59,7 +59,7 @@ def _lib() -> ctypes.CDLL:
         "o_linear_w4": ([vp, i64, i32, i32, vp, vp, vp, i32, vp, vp, i32, vp], i32),
         "o_linear_f16": ([vp, i64, i32, i32, vp, vp, vp, i32, vp], i32),
         "o_attend": ([i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp], None),
-        "o_layer_new": ([vp, vp], vp),
+        "o_layer_new": ([vp, vp, i32], vp),
         "o_layer_free": ([vp], None),
         "o_layer_export": ([vp, i32, vp, vp, vp], i32),
         "o_kv_new": ([vp, i32], vp),
@@ -215,17 +215,19 @@ def head(shape, lnf_g, lnf_b, tok_emb, hidden):
 # ---------------------------------------------------------------------------- layers and cache
 
 class Layer:
-    """One decoder layer built from its 16 fp16 tensors (dict keyed by synth.LAYER_TENSORS)."""
+    """One decoder layer built from its 16 fp16 tensors (dict keyed by synth.LAYER_TENSORS).
+
+    int4_weights=False keeps the six matrices in fp16 (the host-streamed weight tier)."""
 
     ORDER = ("ln1_g", "ln1_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b",
              "o_w", "o_b", "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
 
-    def __init__(self, shape, tensors: dict, group: int = 64):
+    def __init__(self, shape, tensors: dict, group: int = 64, int4_weights: bool = True):
         self.shape = shape
         self.dims = dims_of(shape, group)
         keep = [_h(tensors[n]) for n in self.ORDER]
         ptrs = (ctypes.c_void_p * 16)(*[_p(t) for t in keep])
-        self._ptr = _lib().o_layer_new(ctypes.byref(self.dims), ptrs)
+        self._ptr = _lib().o_layer_new(ctypes.byref(self.dims), ptrs, int(int4_weights))
         if not self._ptr:
             raise ValueError("oracle layer construction failed")
 
@@ -313,7 +315,7 @@ def generate(shape, layers, glob: dict, prompts, gen_len: int, batches_per_block
 
 
 def teacher_forced_logits(shape, layer_source, glob: dict, ids: np.ndarray, first: int,
-                          group: int = 64):
+                          group: int = 64, int4_weights: bool = True, progress=None):
     """Logits of one sequence at positions first..T-1 given all its T input ids.
 
     Runs the whole sequence through one layer at a time (``layer_source(l)``
@@ -325,9 +327,11 @@ def teacher_forced_logits(shape, layer_source, glob: dict, ids: np.ndarray, firs
     T = ids.size
     hid = embed(shape, glob["tok_emb"], glob["pos_emb"], ids, np.arange(T, dtype=np.int32))
     for l in range(shape.n_layers):
-        layer = Layer(shape, layer_source(l), group)
+        layer = Layer(shape, layer_source(l), group, int4_weights)
         cache = KVCache(shape, T, group)
         hid = layer.forward(cache, 0, hid)
         layer.close()
         cache.close()
+        if progress:
+            progress(l)
     return head(shape, glob["lnf_g"], glob["lnf_b"], glob["tok_emb"], hid[first:])

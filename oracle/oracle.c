@@ -346,10 +346,12 @@ void o_layer_free(o_layer *L)
 /*
  * Build one layer from its 16 fp16 tensors, in this order:
  * ln1 gain, ln1 shift, Wq, bq, Wk, bk, Wv, bv, Wo, bo, ln2 gain, ln2 shift,
- * W1, b1, W2, b2 (matrices row-major [out][in]). The six matrices are
- * quantized by this file's quantizer; the rest stays fp16.
+ * W1, b1, W2, b2 (matrices row-major [out][in]). With int4_weights the six
+ * matrices are quantized by this file's quantizer (the weight tier kept in
+ * GPU memory); otherwise they stay fp16 (the tier streamed from host memory,
+ * FlexGen guide, "1. Three-Tier Storage Hierarchy"). The rest stays fp16.
  */
-o_layer *o_layer_new(const o_dims *dm, const uint16_t *const *t)
+o_layer *o_layer_new(const o_dims *dm, const uint16_t *const *t, int int4_weights)
 {
     const int h = dm->hidden, f = dm->ffn, G = dm->group;
     o_layer *L = calloc(1, sizeof(o_layer));
@@ -364,6 +366,19 @@ o_layer *o_layer_new(const o_dims *dm, const uint16_t *const *t)
         L->rows[m] = rows[m];
         L->cols[m] = cols[m];
         L->bias[m] = dup16(t[src[m] + 1], rows[m]);
+        if (!int4_weights) {
+            float *w = malloc(sizeof(float) * (size_t)n);
+            const uint16_t *x = t[src[m]];
+            if (!w) {
+                o_layer_free(L);
+                return NULL;
+            }
+#pragma omp parallel for schedule(static)
+            for (int64_t i = 0; i < n; i++)
+                w[i] = (float)o_half_to_double(x[i]);
+            L->w[m] = w;
+            continue;
+        }
         L->codes[m] = malloc((size_t)n / 2);
         L->scale[m] = malloc(sizeof(uint16_t) * (size_t)(n / G));
         L->zero[m] = malloc(sizeof(uint16_t) * (size_t)(n / G));
@@ -385,7 +400,7 @@ o_layer *o_layer_new(const o_dims *dm, const uint16_t *const *t)
 
 int o_layer_export(const o_layer *L, int which, uint8_t *codes, uint16_t *scale, uint16_t *zero)
 {
-    if (which < 0 || which >= N_MATS)
+    if (which < 0 || which >= N_MATS || !L->codes[which])
         return -1;
     const int64_t n = (int64_t)L->rows[which] * L->cols[which];
     memcpy(codes, L->codes[which], (size_t)n / 2);

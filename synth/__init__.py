@@ -237,12 +237,13 @@ def prompt_ids(n_seq: int, prompt_len: int, vocab: int, seed: int = SEED_PROMPTS
     return uniform_ids(seed, 0, (n_seq, prompt_len), vocab)
 
 
-def attn_tensors(batch: int, heads: int, head_dim: int, context: int):
-    """Query, cached K and cached V of the isolated attention workload, all N(0, 1)."""
-    q = normal_f16(SEED_ATTN, 0, (batch, heads, head_dim), 0.0, 1.0)
-    k = normal_f16(SEED_ATTN, 1, (batch, heads, context, head_dim), 0.0, 1.0)
-    v = normal_f16(SEED_ATTN, 2, (batch, heads, context, head_dim), 0.0, 1.0)
-    return q, k, v
+def attn_cache_chunk(batch: int, heads: int, head_dim: int, t0: int, t1: int):
+    """Cached K and V of positions t0..t1-1 of the isolated attention workload, N(0, 1),
+    position-major [t1-t0][batch][heads][head_dim] (so position chunks are contiguous draws)."""
+    per = batch * heads * head_dim
+    k = normal_f16(SEED_ATTN, 1, (t1 - t0, batch, heads, head_dim), 0.0, 1.0, offset=t0 * per)
+    v = normal_f16(SEED_ATTN, 2, (t1 - t0, batch, heads, head_dim), 0.0, 1.0, offset=t0 * per)
+    return k, v
 
 
 def attn_step_tensors(step: int, batch: int, heads: int, head_dim: int):

@@ -1,0 +1,126 @@
+"""GPU decode attention over the int4 KV cache and the per-step KV quantize+append.
+
+Cache codes, scales and zeros must equal the oracle's quantizer bit for bit;
+attention outputs (fp16) must agree with the oracle's float64 attention over
+the same dequantized cache to within a few fp16 ulps.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import to_dev, to_np16, torch_cuda, ulps
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_cache(kseq, vseq):
+    """kseq, vseq: [T][d] fp16 of one (sequence, head) -> the oracle's int4 cache arrays."""
+    T, d = kseq.shape
+    kc, ks, kz = oracle.quantize_groupwise(np.ascontiguousarray(kseq))
+    vc, vs, vz = oracle.quantize_groupwise(np.ascontiguousarray(vseq))
+    G = d // 64
+    return (kc.reshape(T, d // 2), ks.reshape(T, G), kz.reshape(T, G), vc.reshape(T, d // 2), vs.reshape(T, G),
+            vz.reshape(T, G))
+
+
+def _export(tod, torch, c, b, h, T, d):
+    G = d // 64
+    kc = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+    vc = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+    ks, kz, vs, vz = (torch.empty((T, G), dtype=torch.float16, device="cuda") for _ in range(4))
+    tod.attn_cache_export(c, b, h, 0, T, kc, ks, kz, vc, vs, vz)
+    torch.cuda.synchronize()
+    return (kc.cpu().numpy(), to_np16(ks), to_np16(kz), vc.cpu().numpy(), to_np16(vs), to_np16(vz))
+
+
+@pytest.mark.parametrize("B,H,d,T", [(3, 2, 128, 0), (3, 2, 128, 63), (2, 3, 128, 64), (2, 2, 128, 200),
+                                     (4, 2, 64, 65), (1, 1, 64, 1), (2, 1, 128, 700)])
+def test_decode_step_matches_oracle(B, H, d, T):
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    print(f"attention B={B} H={H} d={d} cached={T}", flush=True)
+    seed = 100 + B * 13 + H * 7 + d + T
+    k = synth.normal_f16(seed, 1, (T, B, H, d), 0.0, 1.0)
+    v = synth.normal_f16(seed, 2, (T, B, H, d), 0.0, 1.0)
+    q = synth.normal_f16(seed, 3, (B, H, d), 0.0, 1.0)
+    kn = synth.normal_f16(seed, 4, (B, H, d), 0.0, 1.0)
+    vn = synth.normal_f16(seed, 5, (B, H, d), 0.0, 1.0)
+    c = tod.attn_cache_create(B, H, d, T + 1)
+    try:
+        if T:
+            tod.attn_cache_fill(c, to_dev(k, torch), to_dev(v, torch), 0)
+        out = torch.empty((B, H, d), dtype=torch.float16, device="cuda")
+        tod.attn_decode_step(c, T, to_dev(q, torch), to_dev(kn, torch), to_dev(vn, torch), out)
+        torch.cuda.synchronize()
+        got = to_np16(out)
+        for b in range(B):
+            for h in range(H):
+                ks = np.concatenate([k[:, b, h, :], kn[None, b, h, :]])
+                vs = np.concatenate([v[:, b, h, :], vn[None, b, h, :]])
+                ref_cache = _oracle_cache(ks, vs)
+                gpu_cache = _export(tod, torch, c, b, h, T + 1, d)
+                for x, y in zip(gpu_cache, ref_cache):
+                    assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+                ref = oracle.attend(q[b, h], *ref_cache)
+                u = ulps(got[b, h], ref)
+                assert u.max() <= 3, f"(b={b}, h={h}) max {u.max()} ulp"
+    finally:
+        tod.attn_cache_free(c)
+
+
+def test_decode_attention_full_size():
+    """Isolated attention workload at full size: batch 256, 96 heads, d 128, 2048 cached
+    positions; 3 decode steps appended; sampled (sequence, head) pairs against the oracle."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    W = synth.ATTN_WORKLOAD
+    B, H, d, T = W["batch"], W["heads"], W["head_dim"], W["context"]
+    steps = 3
+    pairs = [(0, 0), (0, 95), (1, 7), (127, 48), (200, 3), (255, 95)]
+    hist_k = {p: [] for p in pairs}
+    hist_v = {p: [] for p in pairs}
+    c = tod.attn_cache_create(B, H, d, T + steps)
+    try:
+        chunk = 128
+        for t0 in range(0, T, chunk):
+            k, v = synth.attn_cache_chunk(B, H, d, t0, t0 + chunk)
+            for (b, h) in pairs:
+                hist_k[(b, h)].append(k[:, b, h, :].copy())
+                hist_v[(b, h)].append(v[:, b, h, :].copy())
+            tod.attn_cache_fill(c, to_dev(k, torch), to_dev(v, torch), t0)
+            del k, v
+        print("filled 2048 positions", flush=True)
+        out = torch.empty((B, H, d), dtype=torch.float16, device="cuda")
+        for st in range(steps):
+            kn, vn, q = synth.attn_step_tensors(st, B, H, d)
+            tod.attn_decode_step(c, T + st, to_dev(q, torch), to_dev(kn, torch), to_dev(vn, torch), out)
+            for (b, h) in pairs:
+                hist_k[(b, h)].append(kn[None, b, h, :])
+                hist_v[(b, h)].append(vn[None, b, h, :])
+        torch.cuda.synchronize()
+        got = to_np16(out)
+        for (b, h) in pairs:
+            ks = np.concatenate(hist_k[(b, h)])
+            vs = np.concatenate(hist_v[(b, h)])
+            ref_cache = _oracle_cache(ks, vs)
+            gpu_cache = _export(tod, torch, c, b, h, T + steps, d)
+            for x, y in zip(gpu_cache, ref_cache):
+                assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+            ref = oracle.attend(q[b, h], *ref_cache)
+            u = ulps(got[b, h], ref)
+            assert u.max() <= 3, f"(b={b}, h={h}) max {u.max()} ulp"
+    finally:
+        tod.attn_cache_free(c)
+
+
+def test_attention_bad_position_is_an_error():
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    c = tod.attn_cache_create(1, 1, 64, 64)
+    try:
+        x = torch.zeros((1, 1, 64), dtype=torch.float16, device="cuda")
+        with pytest.raises(tod.TodError):
+            tod.attn_decode_step(c, 64, x, x, x, x)
+    finally:
+        tod.attn_cache_free(c)

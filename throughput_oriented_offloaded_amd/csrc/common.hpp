@@ -1,0 +1,152 @@
+// Shared device helpers and internal launcher declarations of libtod (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+
+#define TOD_WAVE 64
+
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(half_t, b); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (half_t)f); }
+
+// Wave-wide reductions over 64 lanes (xor butterfly).
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_min(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// int4 packing inside the GEMM's tiled weight layout: a 32-bit word carries 8
+// consecutive reduction-axis elements e0..e7 with nibble p holding
+// e0 e2 e4 e6 e1 e3 e5 e7 (p = 0..7), so that (w >> 4j) & 0x000F000F yields
+// the ordered pair (e_2j, e_2j+1) in the two 16-bit halves.
+__device__ __forceinline__ uint32_t tiled_word_from_canonical(uint32_t c)
+{
+    // canonical: nibble p holds element p
+    uint32_t r = 0;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const uint32_t v = (c >> (4 * e)) & 15u;
+        const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+        r |= v << (4 * p);
+    }
+    return r;
+}
+__device__ __forceinline__ uint32_t canonical_word_from_tiled(uint32_t t)
+{
+    uint32_t r = 0;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
+        r |= ((t >> (4 * p)) & 15u) << (4 * e);
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// KV cache view (one layer): for each (sequence, head) "slab" of `cap`
+// positions (cap % 64 == 0):
+//   K codes  : [cap/64][d/32][64 positions][16 B]  (16-B piece j of each
+//              position's d/2 code bytes, 64 positions side by side)
+//   K params : [cap][d/64] x uint32 (scale in the low half, zero in the high)
+//   V codes  : [cap][d/2]  canonical bytes
+//   V params : [cap][d/64] x uint32
+// Slab (s, h) starts at index (s * heads + h) in units of the per-slab sizes.
+// ---------------------------------------------------------------------------
+struct KvView {
+    uint8_t *kc;
+    uint32_t *kp;
+    uint8_t *vc;
+    uint32_t *vp;
+    int heads, head_dim, cap;
+};
+
+__device__ __forceinline__ size_t kv_slab(const KvView &v, int seq, int head) { return (size_t)seq * v.heads + head; }
+
+// Rows of activations feeding the KV and attention kernels: row r belongs to
+// sequence seq0 + r / rows_per_seq at position pos0 + r % rows_per_seq.
+struct RowMap {
+    int seq0, rows_per_seq, pos0;
+};
+
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_RES = 1, EPI_BIAS_RELU = 2, EPI_NONE = 3 };
+
+// ---------------------------------------------------------------------------
+// Launchers (host side), defined next to their kernels.
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_groupwise(const uint16_t *x, int64_t n, uint8_t *codes, uint16_t *scale, uint16_t *zero,
+                                     hipStream_t st);
+hipError_t launch_dequantize_groupwise(const uint8_t *codes, const uint16_t *scale, const uint16_t *zero, int64_t n,
+                                       uint16_t *out, hipStream_t st);
+// canonical int4 W[N][K] -> tiled GEMM layout (codes [N/32][K/64][64][16 B], params [N/32][K/64][32] u32)
+hipError_t launch_repack_w4(const uint8_t *codes, const uint16_t *scale, const uint16_t *zero, int N, int K,
+                            uint32_t *tcodes, uint32_t *tparams, hipStream_t st);
+hipError_t launch_unpack_w4(const uint32_t *tcodes, const uint32_t *tparams, int N, int K, uint8_t *codes,
+                            uint16_t *scale, uint16_t *zero, hipStream_t st);
+// Where the K/V vector of (row r, head) starts, in elements:
+//   (r / rows_per_seq) * seq_stride + (r % rows_per_seq) * pos_stride + head * head_stride
+struct SrcMap {
+    int64_t seq_stride, pos_stride, head_stride;
+};
+// quantize + store the K and V vectors of `rows` rows into the cache
+hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, SrcMap src, int rows, RowMap map, KvView kv,
+                            hipStream_t st);
+hipError_t launch_kv_export(KvView kv, int seq, int head, int t0, int t1, uint8_t *kc, uint16_t *ks, uint16_t *kz,
+                            uint8_t *vc, uint16_t *vs, uint16_t *vz, hipStream_t st);
+// decode attention: each of `rows` rows is one sequence (seq0 + r) attending positions 0..ctx-1
+hipError_t launch_attn_decode(const uint16_t *q, int64_t q_stride, uint16_t *out, int64_t out_stride, int rows,
+                              int seq0, int ctx, KvView kv, hipStream_t st);
+// causal prefill attention: `n_seq` sequences starting at seq0, `len` positions each, from position 0
+hipError_t launch_attn_prefill(const uint16_t *q, int64_t q_stride, uint16_t *out, int64_t out_stride, int n_seq,
+                               int seq0, int len, KvView kv, hipStream_t st);
+
+struct GemmArgs {
+    const uint16_t *a;   // [M][lda] fp16
+    int64_t lda;
+    const uint32_t *wc;  // int4 tiled codes (int4 path)
+    const uint32_t *wp;  // int4 tiled params
+    const uint16_t *wf;  // fp16 weights [N][K] (fp16 path)
+    const uint16_t *bias;     // [N] or null
+    const uint16_t *residual; // [M][ldc] or null (may alias y)
+    uint16_t *y;              // [M][ldc]
+    int64_t ldc;
+    int M, N, K;
+    int epi;
+    float *ws;       // split-K workspace (fp32 [splits][M][N]) or null
+    size_t ws_bytes;
+};
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
+size_t gemm_workspace_bytes(int M, int N, int K, bool int4);
+
+hipError_t launch_layernorm(const uint16_t *x, int rows, int h, const uint16_t *g, const uint16_t *b, uint16_t *y,
+                            hipStream_t st);
+// h[r] = fp16(E[ids[r]] + P[pos + 2]), pos = pos0 + r % rows_per_seq
+hipError_t launch_embed(const int32_t *ids, int rows, int rows_per_seq, int pos0, const uint16_t *tok, int vocab,
+                        const uint16_t *posemb, int h, uint16_t *out, hipStream_t st);
+// ids[r] = argmax over fp16 logits [rows][V], lowest index on ties
+hipError_t launch_argmax(const uint16_t *logits, int rows, int V, int32_t *ids, hipStream_t st);
+// dst[r][i] = src[r * src_step + i], i < h (e.g. the last prompt position of each sequence)
+hipError_t launch_gather_rows(const uint16_t *src, int64_t src_step, int rows, int h, uint16_t *dst, hipStream_t st);

@@ -1,0 +1,276 @@
+// Group-wise asymmetric int4 quantization on gfx950: weight quantization at
+// load time, the per-step KV-cache quantize+append, layout repacking and the
+// canonical exports.
+//
+// Quantizer (FlexGen guide, "3. Group-Wise 4-Bit Quantization for Weights and
+// KV Cache": contiguous groups, 16-bit to 4-bit, dequantized on the fly):
+// per group of 64, zero = min, scale = fp16(fp32(max - min) / 15), and the code
+// of x is the nearest grid point zero + c*scale with ties to the larger code.
+// One wavefront handles one group: lane i holds element i, min/max come from
+// xor-butterfly shuffles, each lane estimates its code from a division and
+// settles it with exact threshold comparisons (c + 1/2) * scale, which are
+// exact in fp32, so the codes are independent of how the estimate rounds.
+#include "common.hpp"
+
+namespace {
+
+#pragma clang fp contract(off)
+
+struct QuantLane {
+    uint16_t scale, zero;
+    int code;
+};
+
+__device__ __forceinline__ QuantLane quantize_lane(float x)
+{
+    float mn = wave_min(x), mx = wave_max(x);
+    // -0 and +0 are one value: a zero minimum is stored as +0, a zero range gives scale +0
+    if (mn == 0.0f)
+        mn = fabsf(mn);
+    if (mx == 0.0f)
+        mx = fabsf(mx);
+    const float range = mx - mn;
+    const float s32 = range / 15.0f; // correctly rounded division
+    const half_t s16 = (half_t)s32;  // round to nearest even
+    const float sf = (float)s16;
+    int c = 0;
+    if (sf != 0.0f) {
+        const float d = x - mn;
+        c = (int)(d / sf + 0.5f);
+        c = c < 0 ? 0 : (c > 15 ? 15 : c);
+        // exact settlement: c = #{k in 0..14 : d >= (k + 1/2) * scale}
+        while (c < 15 && d >= ((float)c + 0.5f) * sf)
+            c++;
+        while (c > 0 && d < ((float)c - 0.5f) * sf)
+            c--;
+    }
+    QuantLane q;
+    q.scale = __builtin_bit_cast(uint16_t, s16);
+    q.zero = f2h(mn); // exact: mn is one of the fp16 inputs
+    q.code = c;
+    return q;
+}
+
+// Pack the wave's 64 codes two per byte (even element in the low nibble);
+// returns the byte for even lanes.
+__device__ __forceinline__ uint8_t pack_pair(int code)
+{
+    const int hi = __shfl_down(code, 1, 64);
+    return (uint8_t)(code | (hi << 4));
+}
+
+__global__ void __launch_bounds__(256) k_quantize_groupwise(const uint16_t *__restrict__ x, int64_t ngroups,
+                                                            uint8_t *__restrict__ codes, uint16_t *__restrict__ scale,
+                                                            uint16_t *__restrict__ zero)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= ngroups)
+        return; // whole wave exits together
+    const QuantLane q = quantize_lane(h2f(x[g * 64 + lane]));
+    const uint8_t b = pack_pair(q.code);
+    if ((lane & 1) == 0)
+        codes[g * 32 + (lane >> 1)] = b;
+    if (lane == 0) {
+        scale[g] = q.scale;
+        zero[g] = q.zero;
+    }
+}
+
+__global__ void __launch_bounds__(256) k_dequantize_groupwise(const uint8_t *__restrict__ codes,
+                                                              const uint16_t *__restrict__ scale,
+                                                              const uint16_t *__restrict__ zero, int64_t nbytes,
+                                                              uint16_t *__restrict__ out)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nbytes)
+        return;
+    const uint8_t b = codes[t];
+    const int64_t g = t / 32;
+    const half_t s = __builtin_bit_cast(half_t, scale[g]);
+    const half_t z = __builtin_bit_cast(half_t, zero[g]);
+    // one rounding: fp16 fma of (code, scale, zero)
+    const half_t lo = __builtin_fmaf16((half_t)(float)(b & 15), s, z);
+    const half_t hi = __builtin_fmaf16((half_t)(float)(b >> 4), s, z);
+    out[2 * t] = __builtin_bit_cast(uint16_t, lo);
+    out[2 * t + 1] = __builtin_bit_cast(uint16_t, hi);
+}
+
+// tiled word index w -> (nb, g, lane, t); canonical word = n * (K/8) + g*8 + 2t + hk
+__global__ void __launch_bounds__(256) k_repack_w4(const uint32_t *__restrict__ ccodes,
+                                                   const uint16_t *__restrict__ scale,
+                                                   const uint16_t *__restrict__ zero, int N, int K,
+                                                   uint32_t *__restrict__ tcodes, uint32_t *__restrict__ tparams)
+{
+    const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int KG = K / 64;
+    const int64_t nwords = (int64_t)N * K / 8;
+    if (w >= nwords)
+        return;
+    const int t = (int)(w & 3);
+    const int lane = (int)((w >> 2) & 63);
+    const int64_t blk = w >> 8; // (nb * KG + g)
+    const int g = (int)(blk % KG);
+    const int nb = (int)(blk / KG);
+    const int n = nb * 32 + (lane & 31);
+    const int hk = lane >> 5;
+    tcodes[w] = tiled_word_from_canonical(ccodes[(int64_t)n * (K / 8) + g * 8 + 2 * t + hk]);
+    if (t == 0 && hk == 0)
+        tparams[blk * 32 + (lane & 31)] =
+            (uint32_t)scale[(int64_t)n * KG + g] | ((uint32_t)zero[(int64_t)n * KG + g] << 16);
+}
+
+__global__ void __launch_bounds__(256) k_unpack_w4(const uint32_t *__restrict__ tcodes,
+                                                   const uint32_t *__restrict__ tparams, int N, int K,
+                                                   uint32_t *__restrict__ ccodes, uint16_t *__restrict__ scale,
+                                                   uint16_t *__restrict__ zero)
+{
+    const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int KG = K / 64;
+    const int64_t nwords = (int64_t)N * K / 8;
+    if (w >= nwords)
+        return;
+    const int t = (int)(w & 3);
+    const int lane = (int)((w >> 2) & 63);
+    const int64_t blk = w >> 8;
+    const int g = (int)(blk % KG);
+    const int nb = (int)(blk / KG);
+    const int n = nb * 32 + (lane & 31);
+    const int hk = lane >> 5;
+    ccodes[(int64_t)n * (K / 8) + g * 8 + 2 * t + hk] = canonical_word_from_tiled(tcodes[w]);
+    if (t == 0 && hk == 0) {
+        const uint32_t p = tparams[blk * 32 + (lane & 31)];
+        scale[(int64_t)n * KG + g] = (uint16_t)(p & 0xffff);
+        zero[(int64_t)n * KG + g] = (uint16_t)(p >> 16);
+    }
+}
+
+// One wave per (row, head, group, K-or-V). The new token's K goes to the
+// position-chunked layout, its V to the canonical layout.
+__global__ void __launch_bounds__(256) k_kv_append(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                                   SrcMap src_map, int rows, RowMap map, KvView kv)
+{
+    const int lane = threadIdx.x & 63;
+    const int G = kv.head_dim / 64;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t total = (int64_t)rows * kv.heads * G * 2;
+    if (item >= total)
+        return;
+    const int isv = (int)(item & 1);
+    int64_t rest = item >> 1;
+    const int g = (int)(rest % G);
+    rest /= G;
+    const int head = (int)(rest % kv.heads);
+    const int row = (int)(rest / kv.heads);
+    const int seq = map.seq0 + row / map.rows_per_seq;
+    const int pos = map.pos0 + row % map.rows_per_seq;
+    const uint16_t *src = (isv ? v : k) + (int64_t)(row / map.rows_per_seq) * src_map.seq_stride +
+                          (int64_t)(row % map.rows_per_seq) * src_map.pos_stride +
+                          (int64_t)head * src_map.head_stride + g * 64;
+    const QuantLane q = quantize_lane(h2f(src[lane]));
+    const uint8_t b = pack_pair(q.code);
+    const size_t slab = kv_slab(kv, seq, head);
+    const int cb = kv.head_dim / 2; // code bytes per position
+    if ((lane & 1) == 0) {
+        const int byte = g * 32 + (lane >> 1);
+        if (isv) {
+            kv.vc[(slab * kv.cap + pos) * cb + byte] = b;
+        } else {
+            const int piece = byte >> 4, off = byte & 15;
+            const size_t chunk = (size_t)(pos >> 6);
+            kv.kc[slab * kv.cap * cb + ((chunk * (cb / 16) + piece) * 64 + (pos & 63)) * 16 + off] = b;
+        }
+    }
+    if (lane == 0) {
+        uint32_t *pp = isv ? kv.vp : kv.kp;
+        pp[(slab * kv.cap + pos) * G + g] = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
+    }
+}
+
+__global__ void k_kv_export(KvView kv, int seq, int head, int t0, int n, uint8_t *__restrict__ kc,
+                            uint16_t *__restrict__ ks, uint16_t *__restrict__ kz, uint8_t *__restrict__ vc,
+                            uint16_t *__restrict__ vs, uint16_t *__restrict__ vz)
+{
+    const int cb = kv.head_dim / 2, G = kv.head_dim / 64;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)n * cb)
+        return;
+    const int t = (int)(i / cb), byte = (int)(i % cb), pos = t0 + t;
+    const size_t slab = kv_slab(kv, seq, head);
+    const int piece = byte >> 4, off = byte & 15;
+    kc[i] = kv.kc[slab * kv.cap * cb + (((size_t)(pos >> 6) * (cb / 16) + piece) * 64 + (pos & 63)) * 16 + off];
+    vc[i] = kv.vc[(slab * kv.cap + pos) * cb + byte];
+    if (byte < G) {
+        const uint32_t a = kv.kp[(slab * kv.cap + pos) * G + byte];
+        const uint32_t b = kv.vp[(slab * kv.cap + pos) * G + byte];
+        ks[t * G + byte] = (uint16_t)(a & 0xffff);
+        kz[t * G + byte] = (uint16_t)(a >> 16);
+        vs[t * G + byte] = (uint16_t)(b & 0xffff);
+        vz[t * G + byte] = (uint16_t)(b >> 16);
+    }
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+} // namespace
+
+hipError_t launch_quantize_groupwise(const uint16_t *x, int64_t n, uint8_t *codes, uint16_t *scale, uint16_t *zero,
+                                     hipStream_t st)
+{
+    const int64_t ng = n / 64;
+    if (ng == 0)
+        return hipSuccess;
+    // grid.x is limited to 2^31-1 blocks: 4 groups per block covers n < 2^39
+    hipLaunchKernelGGL(k_quantize_groupwise, dim3(blocks_for(ng, 4)), dim3(256), 0, st, x, ng, codes, scale, zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize_groupwise(const uint8_t *codes, const uint16_t *scale, const uint16_t *zero, int64_t n,
+                                       uint16_t *out, hipStream_t st)
+{
+    if (n == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_dequantize_groupwise, dim3(blocks_for(n / 2, 256)), dim3(256), 0, st, codes, scale, zero,
+                       n / 2, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_repack_w4(const uint8_t *codes, const uint16_t *scale, const uint16_t *zero, int N, int K,
+                            uint32_t *tcodes, uint32_t *tparams, hipStream_t st)
+{
+    const int64_t nwords = (int64_t)N * K / 8;
+    hipLaunchKernelGGL(k_repack_w4, dim3(blocks_for(nwords, 256)), dim3(256), 0, st,
+                       reinterpret_cast<const uint32_t *>(codes), scale, zero, N, K, tcodes, tparams);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_w4(const uint32_t *tcodes, const uint32_t *tparams, int N, int K, uint8_t *codes,
+                            uint16_t *scale, uint16_t *zero, hipStream_t st)
+{
+    const int64_t nwords = (int64_t)N * K / 8;
+    hipLaunchKernelGGL(k_unpack_w4, dim3(blocks_for(nwords, 256)), dim3(256), 0, st, tcodes, tparams, N, K,
+                       reinterpret_cast<uint32_t *>(codes), scale, zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, SrcMap src, int rows, RowMap map, KvView kv,
+                            hipStream_t st)
+{
+    const int64_t items = (int64_t)rows * kv.heads * (kv.head_dim / 64) * 2;
+    if (items == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_kv_append, dim3(blocks_for(items, 4)), dim3(256), 0, st, k, v, src, rows, map, kv);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_export(KvView kv, int seq, int head, int t0, int t1, uint8_t *kc, uint16_t *ks, uint16_t *kz,
+                            uint8_t *vc, uint16_t *vs, uint16_t *vz, hipStream_t st)
+{
+    const int n = t1 - t0;
+    const int64_t items = (int64_t)n * (kv.head_dim / 2);
+    if (items == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_kv_export, dim3(blocks_for(items, 256)), dim3(256), 0, st, kv, seq, head, t0, n, kc, ks, kz,
+                       vc, vs, vz);
+    return hipGetLastError();
+}

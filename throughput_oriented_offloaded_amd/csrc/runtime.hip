@@ -1,0 +1,838 @@
+// Runtime and C ABI of libtod: model state, the zig-zag block driver, the
+// pinned-host weight tier streamed over a copy stream, and test/bench hooks.
+//
+// Schedule (FlexGen guide, "2. The Zig-Zag Block Schedule"): a pass over the
+// stack visits each layer once; while a layer's weights are resident every
+// batch of the block runs through it before the next layer. In a decode step
+// the block's K*b rows form the M dimension of each fused int4 GEMM, so the
+// weights are read once per (step, layer); attention and the KV append are
+// per sequence. Prefill runs the K batches through each layer one after
+// another (M = b * prompt_len per GEMM).
+//
+// Host tier (FlexGen guide, "1. Three-Tier Storage Hierarchy"; TightLLM
+// abstract, static overlap of transfer and compute): fp16 weights live in
+// pinned host memory; a copy stream brings layer l+1 into one of two HBM
+// slots while the compute stream works on layer l; events order slot reuse.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/tod.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIPCHK(expr)                                                                          \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return fail(TOD_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));              \
+    } while (0)
+
+inline hipStream_t S(void *p) { return reinterpret_cast<hipStream_t>(p); }
+
+enum { MAT_QKV = 0, MAT_O, MAT_FC1, MAT_FC2, N_GEMM_MATS };
+
+struct LayerStore {
+    uint32_t *wc[N_GEMM_MATS] = {};   // int4 tiled codes
+    uint32_t *wp[N_GEMM_MATS] = {};   // int4 tiled (scale, zero)
+    uint16_t *bias[N_GEMM_MATS] = {}; // device fp16
+    uint16_t *ln1_g = nullptr, *ln1_b = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
+    uint16_t *host = nullptr;         // host tier: pinned fp16 [qkv | o | fc1 | fc2]
+    bool loaded = false;
+};
+
+} // namespace
+
+struct tod_model {
+    tod_model_config cfg{};
+    tod_run_config run{};
+    int M = 0;      // rows per block (K * b)
+    int cap = 0;    // KV positions per (sequence, head), multiple of 64
+    int n_out[N_GEMM_MATS] = {}, n_in[N_GEMM_MATS] = {};
+    int64_t mat_off[N_GEMM_MATS] = {}; // host tier: element offset of each matrix
+    int64_t layer_elems = 0;           // host tier: elements per layer
+    std::vector<LayerStore> layers;
+    uint16_t *tok_emb = nullptr, *pos_emb = nullptr, *lnf_g = nullptr, *lnf_b = nullptr;
+    bool glob_loaded = false;
+    std::vector<KvView> kv; // [block * L + layer]
+    std::vector<void *> dev_allocs;
+    std::vector<void *> host_allocs;
+    // activations
+    uint16_t *hid = nullptr, *act = nullptr, *qkv = nullptr, *att = nullptr, *ffn = nullptr, *last = nullptr,
+             *logits = nullptr;
+    int32_t *ids = nullptr;
+    float *ws = nullptr;
+    size_t ws_bytes = 0;
+    // load-time staging
+    uint16_t *stage = nullptr;
+    uint8_t *stage_codes = nullptr;
+    uint16_t *stage_scale = nullptr, *stage_zero = nullptr;
+    // host tier streaming
+    uint16_t *slot[2] = {};
+    hipStream_t copy = nullptr;
+    hipEvent_t ev_loaded[2] = {}, ev_free[2] = {};
+    std::vector<int> prefilled, decoded;
+};
+
+struct tod_attn_cache {
+    KvView kv{};
+    int batch = 0;
+    std::vector<void *> allocs;
+};
+
+namespace {
+
+int dev_alloc(tod_model *m, void **p, size_t bytes)
+{
+    if (bytes == 0) {
+        *p = nullptr;
+        return TOD_OK;
+    }
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(TOD_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+    }
+    m->dev_allocs.push_back(*p);
+    return TOD_OK;
+}
+
+#define ALLOC(ptr, bytes)                                                   \
+    do {                                                                    \
+        int rc_ = dev_alloc(m, reinterpret_cast<void **>(&(ptr)), (bytes)); \
+        if (rc_)                                                            \
+            return rc_;                                                     \
+    } while (0)
+
+KvView make_kv_view(uint8_t *kc, uint32_t *kp, uint8_t *vc, uint32_t *vp, int heads, int d, int cap)
+{
+    KvView v;
+    v.kc = kc;
+    v.kp = kp;
+    v.vc = vc;
+    v.vp = vp;
+    v.heads = heads;
+    v.head_dim = d;
+    v.cap = cap;
+    return v;
+}
+
+// bytes of one KV array set for n_slabs (sequence, head) slabs
+size_t kv_bytes(size_t n_slabs, int d, int cap, size_t *kc_b, size_t *kp_b)
+{
+    *kc_b = n_slabs * cap * (size_t)(d / 2);
+    *kp_b = n_slabs * cap * (size_t)(d / 64) * 4;
+    return 2 * (*kc_b + *kp_b);
+}
+
+int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint16_t *wf,
+             uint16_t *y, int64_t ldc, int epi, hipStream_t st)
+{
+    GemmArgs g{};
+    g.a = a;
+    g.lda = m->n_in[mat];
+    if (wf) {
+        g.wf = wf;
+    } else {
+        g.wc = L.wc[mat];
+        g.wp = L.wp[mat];
+    }
+    g.bias = L.bias[mat];
+    g.residual = epi == EPI_BIAS_RES ? y : nullptr;
+    g.y = y;
+    g.ldc = ldc;
+    g.M = rows;
+    g.N = m->n_out[mat];
+    g.K = m->n_in[mat];
+    g.epi = epi;
+    g.ws = m->ws;
+    g.ws_bytes = m->ws_bytes;
+    HIPCHK(launch_gemm(g, st));
+    return TOD_OK;
+}
+
+// One decoder layer for `rows` rows whose hidden states start at `h`.
+// decode: rows = M sequences at position pos; prefill: rows = b * s (b sequences
+// starting at seq0, positions 0..s-1).
+int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, bool prefill_mode, int seq0, int s,
+               int pos, const uint16_t *wslot, hipStream_t st)
+{
+    const int hd = m->cfg.hidden, f = m->cfg.ffn;
+    const LayerStore &L = m->layers[l];
+    const uint16_t *wq = wslot ? wslot + m->mat_off[MAT_QKV] : nullptr;
+    const uint16_t *wo = wslot ? wslot + m->mat_off[MAT_O] : nullptr;
+    const uint16_t *w1 = wslot ? wslot + m->mat_off[MAT_FC1] : nullptr;
+    const uint16_t *w2 = wslot ? wslot + m->mat_off[MAT_FC2] : nullptr;
+    int rc;
+    HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
+    if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wq, m->qkv, 3 * hd, EPI_BIAS, st)))
+        return rc;
+    SrcMap src;
+    RowMap map;
+    if (prefill_mode) {
+        src = {(int64_t)s * 3 * hd, 3 * hd, m->cfg.head_dim};
+        map = {seq0, s, 0};
+    } else {
+        src = {3 * hd, 0, m->cfg.head_dim};
+        map = {seq0, 1, pos};
+    }
+    HIPCHK(launch_kv_append(m->qkv + hd, m->qkv + 2 * hd, src, rows, map, kv, st));
+    if (prefill_mode)
+        HIPCHK(launch_attn_prefill(m->qkv, 3 * hd, m->att, hd, rows / s, seq0, s, kv, st));
+    else
+        HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, kv, st));
+    if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wo, h, hd, EPI_BIAS_RES, st)))
+        return rc;
+    HIPCHK(launch_layernorm(h, rows, hd, L.ln2_g, L.ln2_b, m->act, st));
+    if ((rc = run_gemm(m, m->act, rows, MAT_FC1, L, w1, m->ffn, f, EPI_BIAS_RELU, st)))
+        return rc;
+    if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, w2, h, hd, EPI_BIAS_RES, st)))
+        return rc;
+    return TOD_OK;
+}
+
+// Host tier: enqueue the copy of layer l into slot l % 2 on the copy stream.
+int stream_layer(tod_model *m, int l)
+{
+    const int sl = l & 1;
+    HIPCHK(hipStreamWaitEvent(m->copy, m->ev_free[sl], 0));
+    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[l].host, (size_t)m->layer_elems * 2, hipMemcpyHostToDevice,
+                          m->copy));
+    HIPCHK(hipEventRecord(m->ev_loaded[sl], m->copy));
+    return TOD_OK;
+}
+
+// One pass over all layers. `body(l, wslot)` runs layer l for every batch of the block.
+template <class F>
+int stack_pass(tod_model *m, hipStream_t st, F body)
+{
+    const int L = m->cfg.n_layers;
+    const bool host = m->run.weight_tier == TOD_W_HOST_FP16_STREAM;
+    int rc;
+    if (host && (rc = stream_layer(m, 0)))
+        return rc;
+    for (int l = 0; l < L; l++) {
+        const uint16_t *wslot = nullptr;
+        if (host) {
+            if (l + 1 < L && (rc = stream_layer(m, l + 1)))
+                return rc;
+            HIPCHK(hipStreamWaitEvent(st, m->ev_loaded[l & 1], 0));
+            wslot = m->slot[l & 1];
+        }
+        if ((rc = body(l, wslot)))
+            return rc;
+        if (host)
+            HIPCHK(hipEventRecord(m->ev_free[l & 1], st));
+    }
+    return TOD_OK;
+}
+
+int check_ready(tod_model *m, int block)
+{
+    if (!m)
+        return fail(TOD_EINVAL, "null model");
+    if (block < 0 || block >= m->run.n_blocks)
+        return fail(TOD_ESTATE, "block %d out of range [0, %d)", block, m->run.n_blocks);
+    if (!m->glob_loaded)
+        return fail(TOD_ESTATE, "global weights not set");
+    for (int l = 0; l < m->cfg.n_layers; l++)
+        if (!m->layers[l].loaded)
+            return fail(TOD_ESTATE, "layer %d weights not set", l);
+    return TOD_OK;
+}
+
+// LM head on `rows` final hidden rows: LN_f, tied-embedding logits, argmax.
+int head_pass(tod_model *m, const uint16_t *hrows, int rows, uint16_t *logits, int32_t *next, hipStream_t st)
+{
+    const int hd = m->cfg.hidden, V = m->cfg.vocab;
+    HIPCHK(launch_layernorm(hrows, rows, hd, m->lnf_g, m->lnf_b, m->act, st));
+    GemmArgs g{};
+    g.a = m->act;
+    g.lda = hd;
+    g.wf = m->tok_emb;
+    g.y = logits;
+    g.ldc = V;
+    g.M = rows;
+    g.N = V;
+    g.K = hd;
+    g.epi = EPI_NONE;
+    g.ws = m->ws;
+    g.ws_bytes = m->ws_bytes;
+    HIPCHK(launch_gemm(g, st));
+    HIPCHK(launch_argmax(logits, rows, V, next, st));
+    return TOD_OK;
+}
+
+} // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char *last_error(void) { return g_err.c_str(); }
+
+int free_model(tod_model *m)
+{
+    if (!m)
+        return TOD_OK;
+    (void)hipDeviceSynchronize();
+    for (void *p : m->dev_allocs)
+        (void)hipFree(p);
+    for (void *p : m->host_allocs)
+        (void)hipHostFree(p);
+    for (int i = 0; i < 2; i++) {
+        if (m->ev_loaded[i])
+            (void)hipEventDestroy(m->ev_loaded[i]);
+        if (m->ev_free[i])
+            (void)hipEventDestroy(m->ev_free[i]);
+    }
+    if (m->copy)
+        (void)hipStreamDestroy(m->copy);
+    delete m;
+    return TOD_OK;
+}
+
+static int init_model_impl(const tod_model_config *cfg, const tod_run_config *run, tod_model *m)
+{
+    const tod_model_config &c = *cfg;
+    const tod_run_config &r = *run;
+    if (c.n_layers <= 0 || c.hidden <= 0 || c.n_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 || c.vocab <= 0 ||
+        c.max_pos <= 0)
+        return fail(TOD_EINVAL, "model config fields must be positive");
+    if (c.hidden != c.n_heads * c.head_dim)
+        return fail(TOD_EINVAL, "hidden (%d) != n_heads * head_dim (%d)", c.hidden, c.n_heads * c.head_dim);
+    if (c.head_dim % 64 || c.hidden % 64 || c.ffn % 64 || (c.head_dim != 64 && c.head_dim != 128))
+        return fail(TOD_EINVAL, "head_dim must be 64 or 128; hidden and ffn multiples of 64");
+    if (r.group != TOD_GROUP)
+        return fail(TOD_EINVAL, "group must be 64 (got %d)", r.group);
+    if (r.gpu_batch <= 0 || r.batches_per_block <= 0 || r.prompt_len <= 0 || r.gen_len <= 0 || r.n_blocks <= 0)
+        return fail(TOD_EINVAL, "run config fields must be positive");
+    if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM)
+        return fail(TOD_EINVAL, "unknown weight tier %d", r.weight_tier);
+    if (r.prompt_len + r.gen_len - 1 > c.max_pos)
+        return fail(TOD_EINVAL, "prompt_len + gen_len - 1 exceeds max_pos");
+    m->cfg = c;
+    m->run = r;
+    m->M = r.gpu_batch * r.batches_per_block;
+    m->cap = (r.prompt_len + r.gen_len - 1 + 63) / 64 * 64;
+    const int h = c.hidden, f = c.ffn, L = c.n_layers;
+    m->n_out[MAT_QKV] = 3 * h; m->n_in[MAT_QKV] = h;
+    m->n_out[MAT_O] = h;       m->n_in[MAT_O] = h;
+    m->n_out[MAT_FC1] = f;     m->n_in[MAT_FC1] = h;
+    m->n_out[MAT_FC2] = h;     m->n_in[MAT_FC2] = f;
+    m->mat_off[MAT_QKV] = 0;
+    m->mat_off[MAT_O] = (int64_t)3 * h * h;
+    m->mat_off[MAT_FC1] = (int64_t)4 * h * h;
+    m->mat_off[MAT_FC2] = (int64_t)4 * h * h + (int64_t)f * h;
+    m->layer_elems = (int64_t)4 * h * h + 2 * (int64_t)f * h;
+    m->layers.resize(L);
+    const bool host = r.weight_tier == TOD_W_HOST_FP16_STREAM;
+
+    // weights
+    for (int l = 0; l < L; l++) {
+        LayerStore &S_ = m->layers[l];
+        for (int mat = 0; mat < N_GEMM_MATS; mat++) {
+            const int64_t n = (int64_t)m->n_out[mat] * m->n_in[mat];
+            if (!host) {
+                ALLOC(S_.wc[mat], (size_t)n / 2);
+                ALLOC(S_.wp[mat], (size_t)n / 64 * 4);
+            }
+            ALLOC(S_.bias[mat], (size_t)m->n_out[mat] * 2);
+        }
+        ALLOC(S_.ln1_g, (size_t)h * 2);
+        ALLOC(S_.ln1_b, (size_t)h * 2);
+        ALLOC(S_.ln2_g, (size_t)h * 2);
+        ALLOC(S_.ln2_b, (size_t)h * 2);
+        if (host) {
+            void *p = nullptr;
+            hipError_t e = hipHostMalloc(&p, (size_t)m->layer_elems * 2, hipHostMallocDefault);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(TOD_ENOMEM, "hipHostMalloc(%lld bytes) for layer %d failed: %s",
+                            (long long)m->layer_elems * 2, l, hipGetErrorString(e));
+            }
+            m->host_allocs.push_back(p);
+            S_.host = static_cast<uint16_t *>(p);
+        }
+    }
+    ALLOC(m->tok_emb, (size_t)c.vocab * h * 2);
+    ALLOC(m->pos_emb, (size_t)(c.max_pos + 2) * h * 2);
+    ALLOC(m->lnf_g, (size_t)h * 2);
+    ALLOC(m->lnf_b, (size_t)h * 2);
+
+    // KV caches: per block and layer
+    const size_t slabs = (size_t)m->M * c.n_heads;
+    size_t kc_b, kp_b;
+    kv_bytes(slabs, c.head_dim, m->cap, &kc_b, &kp_b);
+    m->kv.resize((size_t)r.n_blocks * L);
+    for (int b = 0; b < r.n_blocks; b++)
+        for (int l = 0; l < L; l++) {
+            uint8_t *kc, *vc;
+            uint32_t *kp, *vp;
+            ALLOC(kc, kc_b);
+            ALLOC(vc, kc_b);
+            ALLOC(kp, kp_b);
+            ALLOC(vp, kp_b);
+            m->kv[(size_t)b * L + l] = make_kv_view(kc, kp, vc, vp, c.n_heads, c.head_dim, m->cap);
+        }
+
+    // activations: prefill processes one batch (b * s rows) per layer call; the
+    // block's prefill hidden states are kept for all K batches
+    const int64_t prow = (int64_t)r.gpu_batch * r.prompt_len;
+    const int64_t arow = prow > m->M ? prow : m->M;
+    ALLOC(m->hid, (size_t)m->M * r.prompt_len * h * 2);
+    ALLOC(m->act, (size_t)arow * h * 2);
+    ALLOC(m->qkv, (size_t)arow * 3 * h * 2);
+    ALLOC(m->att, (size_t)arow * h * 2);
+    ALLOC(m->ffn, (size_t)arow * f * 2);
+    ALLOC(m->last, (size_t)m->M * h * 2);
+    ALLOC(m->logits, (size_t)m->M * c.vocab * 2);
+    ALLOC(m->ids, (size_t)m->M * 4);
+    size_t ws = 0;
+    const int rows_list[2] = {m->M, (int)prow};
+    for (int ri = 0; ri < 2; ri++)
+        for (int mat = 0; mat < N_GEMM_MATS; mat++) {
+            const size_t b = gemm_workspace_bytes(rows_list[ri], m->n_out[mat], m->n_in[mat], !host);
+            ws = b > ws ? b : ws;
+        }
+    {
+        const size_t b = gemm_workspace_bytes(m->M, c.vocab, h, false);
+        ws = b > ws ? b : ws;
+    }
+    m->ws_bytes = ws;
+    ALLOC(m->ws, ws);
+
+    if (host) {
+        ALLOC(m->slot[0], (size_t)m->layer_elems * 2);
+        ALLOC(m->slot[1], (size_t)m->layer_elems * 2);
+        HIPCHK(hipStreamCreateWithFlags(&m->copy, hipStreamNonBlocking));
+        for (int i = 0; i < 2; i++) {
+            HIPCHK(hipEventCreateWithFlags(&m->ev_loaded[i], hipEventDisableTiming));
+            HIPCHK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
+        }
+    } else {
+        const int64_t big = (int64_t)(f > 3 * h ? f : 3 * h) * h;
+        ALLOC(m->stage, (size_t)big * 2);
+        ALLOC(m->stage_codes, (size_t)big / 2);
+        ALLOC(m->stage_scale, (size_t)big / 64 * 2);
+        ALLOC(m->stage_zero, (size_t)big / 64 * 2);
+    }
+    m->prefilled.assign(r.n_blocks, 0);
+    m->decoded.assign(r.n_blocks, 0);
+    return TOD_OK;
+}
+
+int init_model(const tod_model_config *cfg, const tod_run_config *run, void *stream, tod_model **out)
+{
+    (void)stream;
+    if (!out)
+        return fail(TOD_EINVAL, "null out pointer");
+    *out = nullptr;
+    if (!cfg || !run)
+        return fail(TOD_EINVAL, "null config");
+    tod_model *m = new tod_model();
+    const int rc = init_model_impl(cfg, run, m);
+    if (rc) {
+        const std::string msg = g_err;
+        free_model(m);
+        g_err = msg;
+        return rc;
+    }
+    *out = m;
+    return TOD_OK;
+}
+
+int set_global_weights(tod_model *m, const uint16_t *tok, const uint16_t *pos, const uint16_t *g, const uint16_t *b)
+{
+    if (!m || !tok || !pos || !g || !b)
+        return fail(TOD_EINVAL, "null argument");
+    const int h = m->cfg.hidden;
+    HIPCHK(hipMemcpy(m->tok_emb, tok, (size_t)m->cfg.vocab * h * 2, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(m->pos_emb, pos, (size_t)(m->cfg.max_pos + 2) * h * 2, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(m->lnf_g, g, (size_t)h * 2, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(m->lnf_b, b, (size_t)h * 2, hipMemcpyHostToDevice));
+    m->glob_loaded = true;
+    return TOD_OK;
+}
+
+int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
+{
+    if (!m || !t)
+        return fail(TOD_EINVAL, "null argument");
+    if (layer < 0 || layer >= m->cfg.n_layers)
+        return fail(TOD_EINVAL, "layer %d out of range", layer);
+    for (int i = 0; i < TOD_LAYER_TENSORS; i++)
+        if (!t[i])
+            return fail(TOD_EINVAL, "tensor %d of layer %d is null", i, layer);
+    LayerStore &L = m->layers[layer];
+    const int h = m->cfg.hidden, f = m->cfg.ffn;
+    const size_t hb = (size_t)h * 2;
+    HIPCHK(hipMemcpy(L.ln1_g, t[TOD_LN1_G], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.ln1_b, t[TOD_LN1_B], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.ln2_g, t[TOD_LN2_G], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.ln2_b, t[TOD_LN2_B], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.bias[MAT_QKV], t[TOD_Q_B], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.bias[MAT_QKV] + h, t[TOD_K_B], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.bias[MAT_QKV] + 2 * h, t[TOD_V_B], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.bias[MAT_O], t[TOD_O_B], hb, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.bias[MAT_FC1], t[TOD_FC1_B], (size_t)f * 2, hipMemcpyHostToDevice));
+    HIPCHK(hipMemcpy(L.bias[MAT_FC2], t[TOD_FC2_B], hb, hipMemcpyHostToDevice));
+    // the six matrices: (source tensor, gemm matrix, row offset inside it, rows, cols)
+    struct Part {
+        int tensor, mat, row0, rows, cols;
+    } parts[6] = {{TOD_Q_W, MAT_QKV, 0, h, h},   {TOD_K_W, MAT_QKV, h, h, h}, {TOD_V_W, MAT_QKV, 2 * h, h, h},
+                  {TOD_O_W, MAT_O, 0, h, h},     {TOD_FC1_W, MAT_FC1, 0, f, h}, {TOD_FC2_W, MAT_FC2, 0, h, f}};
+    if (m->run.weight_tier == TOD_W_HOST_FP16_STREAM) {
+        for (const Part &p : parts)
+            memcpy(L.host + m->mat_off[p.mat] + (int64_t)p.row0 * p.cols, t[p.tensor], (size_t)p.rows * p.cols * 2);
+    } else {
+        for (const Part &p : parts) {
+            const int64_t n = (int64_t)p.rows * p.cols;
+            const int KG = p.cols / 64;
+            HIPCHK(hipMemcpy(m->stage, t[p.tensor], (size_t)n * 2, hipMemcpyHostToDevice));
+            HIPCHK(launch_quantize_groupwise(m->stage, n, m->stage_codes, m->stage_scale, m->stage_zero, nullptr));
+            const int64_t nb0 = p.row0 / 32;
+            HIPCHK(launch_repack_w4(m->stage_codes, m->stage_scale, m->stage_zero, p.rows, p.cols,
+                                    L.wc[p.mat] + nb0 * KG * 256, L.wp[p.mat] + nb0 * KG * 32, nullptr));
+        }
+        HIPCHK(hipDeviceSynchronize());
+    }
+    L.loaded = true;
+    return TOD_OK;
+}
+
+int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint16_t *d_logits, void *stream)
+{
+    int rc = check_ready(m, block);
+    if (rc)
+        return rc;
+    if (!d_ids || !d_next)
+        return fail(TOD_EINVAL, "null ids");
+    const hipStream_t st = S(stream);
+    const int b = m->run.gpu_batch, K = m->run.batches_per_block, s = m->run.prompt_len, h = m->cfg.hidden;
+    const int L = m->cfg.n_layers;
+    const int64_t brow = (int64_t)b * s; // rows of one batch
+    for (int k = 0; k < K; k++)
+        HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
+                                m->hid + k * brow * h, st));
+    rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
+        const KvView &kv = m->kv[(size_t)block * L + l];
+        for (int kk = 0; kk < K; kk++) {
+            const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
+            const int r = layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, wslot, st);
+            if (r)
+                return r;
+        }
+        return TOD_OK;
+    });
+    if (rc)
+        return rc;
+    HIPCHK(launch_gather_rows(m->hid + (int64_t)(s - 1) * h, (int64_t)s * h, m->M, h, m->last, st));
+    if ((rc = head_pass(m, m->last, m->M, d_logits ? d_logits : m->logits, d_next, st)))
+        return rc;
+    m->prefilled[block] = 1;
+    m->decoded[block] = 0;
+    return TOD_OK;
+}
+
+int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, int32_t *d_ids_out,
+                 uint16_t *d_logits, void *stream)
+{
+    int rc = check_ready(m, block);
+    if (rc)
+        return rc;
+    if (!d_ids_in || !d_ids_out || n_steps < 0)
+        return fail(TOD_EINVAL, "bad decode arguments");
+    if (!m->prefilled[block])
+        return fail(TOD_ESTATE, "decode_block before prefill on block %d", block);
+    if (m->decoded[block] + n_steps > m->run.gen_len - 1)
+        return fail(TOD_ESTATE, "decode would exceed gen_len - 1 = %d steps (done %d, asked %d)",
+                    m->run.gen_len - 1, m->decoded[block], n_steps);
+    const hipStream_t st = S(stream);
+    const int Mr = m->M, h = m->cfg.hidden, L = m->cfg.n_layers, V = m->cfg.vocab;
+    for (int j = 0; j < n_steps; j++) {
+        const int pos = m->run.prompt_len + m->decoded[block];
+        const int32_t *in = j == 0 ? d_ids_in : d_ids_out + (int64_t)(j - 1) * Mr;
+        HIPCHK(launch_embed(in, Mr, 1, pos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
+        rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
+            return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, wslot, st);
+        });
+        if (rc)
+            return rc;
+        uint16_t *lg = d_logits ? d_logits + (int64_t)j * Mr * V : m->logits;
+        if ((rc = head_pass(m, m->hid, Mr, lg, d_ids_out + (int64_t)j * Mr, st)))
+            return rc;
+        m->decoded[block]++;
+    }
+    return TOD_OK;
+}
+
+int set_decode_position(tod_model *m, int block, int steps)
+{
+    if (!m)
+        return fail(TOD_EINVAL, "null model");
+    if (block < 0 || block >= m->run.n_blocks)
+        return fail(TOD_ESTATE, "block %d out of range", block);
+    if (!m->prefilled[block])
+        return fail(TOD_ESTATE, "block %d has not been prefilled", block);
+    if (steps < 0 || steps > m->run.gen_len - 1)
+        return fail(TOD_EINVAL, "steps %d outside [0, %d]", steps, m->run.gen_len - 1);
+    m->decoded[block] = steps;
+    return TOD_OK;
+}
+
+int quantize_groupwise(const uint16_t *d_x, int64_t n, int group, uint8_t *d_codes, uint16_t *d_scale,
+                       uint16_t *d_zero, void *stream)
+{
+    if (group != TOD_GROUP)
+        return fail(TOD_EINVAL, "group must be 64 (got %d)", group);
+    if (n < 0 || n % group)
+        return fail(TOD_EINVAL, "n (%lld) must be a non-negative multiple of %d", (long long)n, group);
+    if (n && (!d_x || !d_codes || !d_scale || !d_zero))
+        return fail(TOD_EINVAL, "null pointer");
+    HIPCHK(launch_quantize_groupwise(d_x, n, d_codes, d_scale, d_zero, S(stream)));
+    return TOD_OK;
+}
+
+int dequantize_groupwise(const uint8_t *d_codes, const uint16_t *d_scale, const uint16_t *d_zero, int64_t n,
+                         int group, uint16_t *d_out, void *stream)
+{
+    if (group != TOD_GROUP)
+        return fail(TOD_EINVAL, "group must be 64 (got %d)", group);
+    if (n < 0 || n % group)
+        return fail(TOD_EINVAL, "n must be a non-negative multiple of 64");
+    if (n && (!d_codes || !d_scale || !d_zero || !d_out))
+        return fail(TOD_EINVAL, "null pointer");
+    HIPCHK(launch_dequantize_groupwise(d_codes, d_scale, d_zero, n, d_out, S(stream)));
+    return TOD_OK;
+}
+
+int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t *d_scale, uint16_t *d_zero,
+                  void *stream)
+{
+    if (!m || !d_codes || !d_scale || !d_zero)
+        return fail(TOD_EINVAL, "null argument");
+    if (layer < 0 || layer >= m->cfg.n_layers || which < TOD_MAT_Q || which > TOD_MAT_FC2)
+        return fail(TOD_EINVAL, "layer or matrix id out of range");
+    if (m->run.weight_tier != TOD_W_HBM_INT4)
+        return fail(TOD_ESTATE, "the host tier keeps fp16 weights");
+    if (!m->layers[layer].loaded)
+        return fail(TOD_ESTATE, "layer %d weights not set", layer);
+    const int h = m->cfg.hidden, f = m->cfg.ffn;
+    int mat, row0 = 0, rows = h, cols = h;
+    switch (which) {
+    case TOD_MAT_Q: mat = MAT_QKV; break;
+    case TOD_MAT_K: mat = MAT_QKV; row0 = h; break;
+    case TOD_MAT_V: mat = MAT_QKV; row0 = 2 * h; break;
+    case TOD_MAT_O: mat = MAT_O; break;
+    case TOD_MAT_FC1: mat = MAT_FC1; rows = f; break;
+    default: mat = MAT_FC2; cols = f; break;
+    }
+    const int KG = cols / 64;
+    const int64_t nb0 = row0 / 32;
+    const LayerStore &L = m->layers[layer];
+    HIPCHK(launch_unpack_w4(L.wc[mat] + nb0 * KG * 256, L.wp[mat] + nb0 * KG * 32, rows, cols, d_codes, d_scale,
+                            d_zero, S(stream)));
+    return TOD_OK;
+}
+
+int export_kv(tod_model *m, int layer, int block, int row, int head, int t0, int t1, uint8_t *d_kc, uint16_t *d_ks,
+              uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream)
+{
+    if (!m || !d_kc || !d_ks || !d_kz || !d_vc || !d_vs || !d_vz)
+        return fail(TOD_EINVAL, "null argument");
+    if (layer < 0 || layer >= m->cfg.n_layers || block < 0 || block >= m->run.n_blocks || row < 0 || row >= m->M ||
+        head < 0 || head >= m->cfg.n_heads || t0 < 0 || t1 > m->cap || t0 > t1)
+        return fail(TOD_EINVAL, "export_kv index out of range");
+    HIPCHK(launch_kv_export(m->kv[(size_t)block * m->cfg.n_layers + layer], row, head, t0, t1, d_kc, d_ks, d_kz, d_vc,
+                            d_vs, d_vz, S(stream)));
+    return TOD_OK;
+}
+
+static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
+                         const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_w, const uint16_t *d_bias,
+                         const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
+{
+    if (!d_a || !d_y || rows < 0 || rows > 0x7fffffff || in <= 0 || out <= 0)
+        return fail(TOD_EINVAL, "bad linear arguments");
+    if (in % 64)
+        return fail(TOD_EINVAL, "in (%d) must be a multiple of 64", in);
+    const bool int4 = d_codes != nullptr;
+    if (int4 && (out % 32 || !d_scale || !d_zero))
+        return fail(TOD_EINVAL, "int4 linear needs out %% 32 == 0 and scale/zero");
+    const hipStream_t st = S(stream);
+    std::vector<void *> tmp;
+    auto cleanup = [&]() {
+        (void)hipStreamSynchronize(st);
+        for (void *p : tmp)
+            (void)hipFree(p);
+    };
+    auto talloc = [&](size_t bytes) -> void * {
+        void *p = nullptr;
+        if (bytes && hipMalloc(&p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        tmp.push_back(p);
+        return p;
+    };
+    GemmArgs g{};
+    g.a = d_a;
+    g.lda = in;
+    if (int4) {
+        const int64_t n = (int64_t)out * in;
+        uint32_t *tc = static_cast<uint32_t *>(talloc((size_t)n / 2));
+        uint32_t *tp = static_cast<uint32_t *>(talloc((size_t)n / 64 * 4));
+        if (!tc || !tp) {
+            cleanup();
+            return fail(TOD_ENOMEM, "no memory for the repacked weights");
+        }
+        hipError_t e = launch_repack_w4(d_codes, d_scale, d_zero, out, in, tc, tp, st);
+        if (e != hipSuccess) {
+            cleanup();
+            return fail(TOD_EHIP, "repack failed: %s", hipGetErrorString(e));
+        }
+        g.wc = tc;
+        g.wp = tp;
+    } else {
+        if (!d_w)
+            return fail(TOD_EINVAL, "null weights");
+        g.wf = d_w;
+    }
+    g.bias = d_bias;
+    g.residual = d_residual;
+    g.y = d_y;
+    g.ldc = out;
+    g.M = (int)rows;
+    g.N = out;
+    g.K = in;
+    g.epi = relu ? EPI_BIAS_RELU : (d_residual ? EPI_BIAS_RES : (d_bias ? EPI_BIAS : EPI_NONE));
+    if (relu && d_residual) {
+        cleanup();
+        return fail(TOD_EINVAL, "relu with residual is not an epilogue of this library");
+    }
+    g.ws_bytes = gemm_workspace_bytes((int)rows, out, in, int4);
+    g.ws = static_cast<float *>(talloc(g.ws_bytes));
+    if (g.ws_bytes && !g.ws) {
+        cleanup();
+        return fail(TOD_ENOMEM, "no memory for the split-K workspace");
+    }
+    hipError_t e = launch_gemm(g, st);
+    cleanup();
+    if (e != hipSuccess)
+        return fail(TOD_EHIP, "gemm failed: %s", hipGetErrorString(e));
+    return TOD_OK;
+}
+
+int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes, const uint16_t *d_scale,
+              const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
+              void *stream)
+{
+    if (!d_codes)
+        return fail(TOD_EINVAL, "null codes");
+    return linear_common(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y, stream);
+}
+
+int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_t *d_w, const uint16_t *d_bias,
+               const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
+{
+    return linear_common(d_a, rows, in, out, nullptr, nullptr, nullptr, d_w, d_bias, d_residual, relu, d_y, stream);
+}
+
+int attn_cache_create(int batch, int heads, int head_dim, int cap, tod_attn_cache **out)
+{
+    if (!out)
+        return fail(TOD_EINVAL, "null out pointer");
+    *out = nullptr;
+    if (batch <= 0 || heads <= 0 || cap <= 0 || (head_dim != 64 && head_dim != 128))
+        return fail(TOD_EINVAL, "bad attention cache shape");
+    tod_attn_cache *c = new tod_attn_cache();
+    const int capp = (cap + 63) / 64 * 64;
+    size_t kc_b, kp_b;
+    kv_bytes((size_t)batch * heads, head_dim, capp, &kc_b, &kp_b);
+    void *p[4] = {};
+    const size_t sz[4] = {kc_b, kp_b, kc_b, kp_b};
+    for (int i = 0; i < 4; i++) {
+        if (hipMalloc(&p[i], sz[i]) != hipSuccess) {
+            (void)hipGetLastError();
+            for (void *q : c->allocs)
+                (void)hipFree(q);
+            delete c;
+            return fail(TOD_ENOMEM, "hipMalloc of %zu bytes for the attention cache failed", sz[i]);
+        }
+        c->allocs.push_back(p[i]);
+    }
+    c->kv = make_kv_view(static_cast<uint8_t *>(p[0]), static_cast<uint32_t *>(p[1]), static_cast<uint8_t *>(p[2]),
+                         static_cast<uint32_t *>(p[3]), heads, head_dim, capp);
+    c->batch = batch;
+    *out = c;
+    return TOD_OK;
+}
+
+int attn_cache_fill(tod_attn_cache *c, const uint16_t *d_k, const uint16_t *d_v, int t0, int n, void *stream)
+{
+    if (!c || !d_k || !d_v || t0 < 0 || n < 0 || t0 + n > c->kv.cap)
+        return fail(TOD_EINVAL, "bad attention cache fill");
+    // time-major input [n][batch][heads][d]: row r = (sequence r / n, position t0 + r % n)
+    const int d = c->kv.head_dim, H = c->kv.heads;
+    const SrcMap src = {(int64_t)H * d, (int64_t)c->batch * H * d, d};
+    const RowMap map = {0, n, t0};
+    HIPCHK(launch_kv_append(d_k, d_v, src, c->batch * n, map, c->kv, S(stream)));
+    return TOD_OK;
+}
+
+int attn_decode_step(tod_attn_cache *c, int pos, const uint16_t *d_q, const uint16_t *d_k_new,
+                     const uint16_t *d_v_new, uint16_t *d_out, void *stream)
+{
+    if (!c || !d_q || !d_k_new || !d_v_new || !d_out)
+        return fail(TOD_EINVAL, "null argument");
+    if (pos < 0 || pos >= c->kv.cap)
+        return fail(TOD_ESTATE, "position %d outside the cache (capacity %d)", pos, c->kv.cap);
+    const int d = c->kv.head_dim, H = c->kv.heads;
+    const SrcMap src = {(int64_t)H * d, 0, d};
+    const RowMap map = {0, 1, pos};
+    HIPCHK(launch_kv_append(d_k_new, d_v_new, src, c->batch, map, c->kv, S(stream)));
+    HIPCHK(launch_attn_decode(d_q, (int64_t)H * d, d_out, (int64_t)H * d, c->batch, 0, pos + 1, c->kv, S(stream)));
+    return TOD_OK;
+}
+
+int attn_cache_export(tod_attn_cache *c, int seq, int head, int t0, int t1, uint8_t *d_kc, uint16_t *d_ks,
+                      uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream)
+{
+    if (!c || !d_kc || !d_ks || !d_kz || !d_vc || !d_vs || !d_vz)
+        return fail(TOD_EINVAL, "null argument");
+    if (seq < 0 || seq >= c->batch || head < 0 || head >= c->kv.heads || t0 < 0 || t1 > c->kv.cap || t0 > t1)
+        return fail(TOD_EINVAL, "export index out of range");
+    HIPCHK(launch_kv_export(c->kv, seq, head, t0, t1, d_kc, d_ks, d_kz, d_vc, d_vs, d_vz, S(stream)));
+    return TOD_OK;
+}
+
+int attn_cache_free(tod_attn_cache *c)
+{
+    if (!c)
+        return TOD_OK;
+    (void)hipDeviceSynchronize();
+    for (void *p : c->allocs)
+        (void)hipFree(p);
+    delete c;
+    return TOD_OK;
+}
+
+} // extern "C"
