@@ -70,6 +70,7 @@ def _lib() -> ctypes.CDLL:
         "o_embed": ([vp, vp, vp, vp, vp, i32, vp], i32),
         "o_head": ([vp, vp, vp, vp, vp, i32, vp, vp], None),
         "o_generate": ([vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp], i32),
+        "o_set_fp32_accumulation": ([i32], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -96,6 +97,19 @@ def _h(a) -> np.ndarray:
 
 def dims_of(shape, group: int = 64) -> Dims:
     return Dims(shape.hidden, shape.n_heads, shape.head_dim, shape.ffn, shape.vocab, shape.max_pos, group)
+
+
+class fp32_accumulation:
+    """Context manager: run the oracle with every running sum rounded to fp32 (calibration
+    of how far a correct fp32-accumulating implementation drifts from the fp64 oracle)."""
+
+    def __enter__(self):
+        _lib().o_set_fp32_accumulation(1)
+        return self
+
+    def __exit__(self, *exc):
+        _lib().o_set_fp32_accumulation(0)
+        return False
 
 
 # ---------------------------------------------------------------------------- fp16

@@ -179,6 +179,23 @@ int o_dequantize_groupwise(const uint8_t *codes, const uint16_t *scale, const ui
 /* Layer pieces                                                             */
 /* ------------------------------------------------------------------------ */
 
+/*
+ * Accumulation precision. The oracle accumulates in double. For calibration
+ * only, o_set_fp32_accumulation(1) rounds every running sum (dot products,
+ * LayerNorm statistics, softmax sums) to fp32 after each addition, the
+ * precision a GPU accumulator carries: comparing the two settings measures how
+ * far a correct fp32-accumulating implementation may drift from the fp64 one.
+ */
+static int g_acc32 = 0;
+
+void o_set_fp32_accumulation(int on) { g_acc32 = on != 0; }
+
+static inline double acc_add(double acc, double term)
+{
+    const double r = acc + term;
+    return g_acc32 ? (double)(float)r : r;
+}
+
 /* LayerNorm over h features: biased variance, eps 1e-5, one rounding. */
 void o_layernorm(const uint16_t *x, int64_t rows, int h, const uint16_t *gain,
                  const uint16_t *shift, uint16_t *y)
@@ -188,11 +205,11 @@ void o_layernorm(const uint16_t *x, int64_t rows, int h, const uint16_t *gain,
         const uint16_t *xr = x + r * h;
         double mu = 0.0, var = 0.0;
         for (int i = 0; i < h; i++)
-            mu += o_half_to_double(xr[i]);
+            mu = acc_add(mu, o_half_to_double(xr[i]));
         mu /= h;
         for (int i = 0; i < h; i++) {
             const double c = o_half_to_double(xr[i]) - mu;
-            var += c * c;
+            var = acc_add(var, c * c);
         }
         var /= h;
         const double sd = sqrt(var + 1e-5);
@@ -220,11 +237,11 @@ static void linear_rows(const uint16_t *a, int64_t rows, int in, int out, const 
             const float *wo = w + (int64_t)o * in;
             double acc = 0.0;
             for (int k = 0; k < in; k++)
-                acc += am[k] * (double)wo[k];
+                acc = acc_add(acc, am[k] * (double)wo[k]);
             if (bias)
-                acc += o_half_to_double(bias[o]);
+                acc = acc_add(acc, o_half_to_double(bias[o]));
             if (residual)
-                acc += o_half_to_double(residual[m * out + o]);
+                acc = acc_add(acc, o_half_to_double(residual[m * out + o]));
             if (relu && acc < 0.0)
                 acc = 0.0;
             y[m * out + o] = o_double_to_half(acc);
@@ -283,9 +300,9 @@ void o_attend(int d, int group, int T, const uint16_t *q, const uint8_t *kc, con
     for (int t = 0; t < T; t++) {
         double acc = 0.0;
         for (int i = 0; i < d; i++)
-            acc += o_half_to_double(q[i]) *
-                   dequant(code_at(kc + (int64_t)t * (d / 2), i), ks[(int64_t)t * ng + i / group],
-                           kz[(int64_t)t * ng + i / group]);
+            acc = acc_add(acc, o_half_to_double(q[i]) *
+                                   dequant(code_at(kc + (int64_t)t * (d / 2), i), ks[(int64_t)t * ng + i / group],
+                                           kz[(int64_t)t * ng + i / group]));
         score[t] = acc / sqrt((double)d);
         if (score[t] > mx)
             mx = score[t];
@@ -293,13 +310,13 @@ void o_attend(int d, int group, int T, const uint16_t *q, const uint8_t *kc, con
     double den = 0.0;
     for (int t = 0; t < T; t++) {
         score[t] = exp(score[t] - mx);
-        den += score[t];
+        den = acc_add(den, score[t]);
     }
     for (int i = 0; i < d; i++) {
         double acc = 0.0;
         for (int t = 0; t < T; t++)
-            acc += score[t] * dequant(code_at(vc + (int64_t)t * (d / 2), i), vs[(int64_t)t * ng + i / group],
-                                      vz[(int64_t)t * ng + i / group]);
+            acc = acc_add(acc, score[t] * dequant(code_at(vc + (int64_t)t * (d / 2), i),
+                                                  vs[(int64_t)t * ng + i / group], vz[(int64_t)t * ng + i / group]));
         out[i] = o_double_to_half(acc / den);
     }
     free(score);

@@ -1,15 +1,19 @@
 """GPU decode attention over the int4 KV cache and the per-step KV quantize+append.
 
-Cache codes, scales and zeros must equal the oracle's quantizer bit for bit;
-attention outputs (fp16) must agree with the oracle's float64 attention over
-the same dequantized cache to within a few fp16 ulps.
+Cache codes, scales and zeros must equal the oracle's quantizer bit for bit.
+Attention outputs: the oracle attends over dequantized values rounded to fp16
+(zero + c*scale, one rounding each); the GPU kernel uses the factored form
+scale * sum(p*c) + zero * sum(p), which never rounds the dequantized value.
+The two differ by at most half an fp16 ulp of the largest |v| per term, so
+the per-element bar is  |o_gpu - o_oracle| <= ulp16(max|v|)/2 + ulp16(o)/2
++ 1e-5 (fp32 sums and exp), and the mean error must stay well below it.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_util import to_dev, to_np16, torch_cuda, ulps
+from tests.gpu_util import to_dev, to_np16, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +26,18 @@ def _oracle_cache(kseq, vseq):
     G = d // 64
     return (kc.reshape(T, d // 2), ks.reshape(T, G), kz.reshape(T, G), vc.reshape(T, d // 2), vs.reshape(T, G),
             vz.reshape(T, G))
+
+
+def _spacing16(x):
+    return np.spacing(np.abs(np.asarray(x, dtype=np.float64)).astype(np.float16)).astype(np.float64)
+
+
+def _check_attention(got, ref, ref_cache, label):
+    vh = oracle.dequantize_groupwise(ref_cache[3], ref_cache[4], ref_cache[5]).astype(np.float64)
+    tol = 0.5 * _spacing16(np.abs(vh).max()) + 0.5 * _spacing16(ref) + 1e-5
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+    assert np.all(err <= tol), f"{label}: max err {err.max():.3g} (bound {tol.min():.3g}..{tol.max():.3g})"
+    assert err.mean() <= 0.25 * tol.mean(), f"{label}: mean err {err.mean():.3g}"
 
 
 def _export(tod, torch, c, b, h, T, d):
@@ -63,8 +79,7 @@ def test_decode_step_matches_oracle(B, H, d, T):
                 for x, y in zip(gpu_cache, ref_cache):
                     assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
                 ref = oracle.attend(q[b, h], *ref_cache)
-                u = ulps(got[b, h], ref)
-                assert u.max() <= 3, f"(b={b}, h={h}) max {u.max()} ulp"
+                _check_attention(got[b, h], ref, ref_cache, f"(b={b}, h={h})")
     finally:
         tod.attn_cache_free(c)
 
@@ -108,8 +123,7 @@ def test_decode_attention_full_size():
             for x, y in zip(gpu_cache, ref_cache):
                 assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
             ref = oracle.attend(q[b, h], *ref_cache)
-            u = ulps(got[b, h], ref)
-            assert u.max() <= 3, f"(b={b}, h={h}) max {u.max()} ulp"
+            _check_attention(got[b, h], ref, ref_cache, f"(b={b}, h={h})")
     finally:
         tod.attn_cache_free(c)
 
