@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Decode throughput of block-scheduled int4 OPT decode on one MI355X.
+
+Workload (default): OPT-30B-shaped stack (48 layers, hidden 7168, 56 heads of
+128, FFN 28672, vocab 50272), random N(0, 0.02) fp16 weights quantized to
+int4 group-64 in HBM, int4 group-64 KV cache, GPU batch 64 x 8 batches per
+block (512 rows), uniform random prompts of 512 tokens, 32 generated tokens.
+
+A step is one decode step of the whole block through the whole stack: embed,
+48 x (LN, fused int4 QKV GEMM, KV quantize+append, int4-KV attention, out
+GEMM, LN, FC1, FC2), final LN, LM head, greedy argmax. The timed region
+replays decode steps 1..31 (contexts 513..543) after one prefill; the KV
+cache and weights are resident in HBM when it starts.
+
+Prints one JSON line. `value` is decode tokens/s = rows * steps / time.
+`roofline` reports the kernel class with the largest share of the step,
+timed with HIP events on the library's stream inside the timed region.
+`cpu_baseline` times the CPU oracle on a bounded sample (one layer, one
+decode step, one GPU batch of 64 rows, plus the LM head) and extrapolates.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "generated tokens/sec (1 GPU), OPT-30B shape int4 W+KV; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+BPE_INT4 = 0.5 + 4.0 / 64.0   # bytes per int4 element incl. fp16 scale + zero per 64
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_position(shape):
+    """K and V of one (sequence, position, layer): codes + (scale, zero) per 64."""
+    return 2 * shape.hidden * BPE_INT4
+
+
+def step_bytes(shape, rows, context):
+    """Algorithmic HBM bytes of one decode step at a given attended context."""
+    L, h, f, V = shape.n_layers, shape.hidden, shape.ffn, shape.vocab
+    w = L * (4 * h * h + 2 * f * h) * BPE_INT4          # int4 weights, once per step for the whole block
+    lm = V * h * 2                                       # tied fp16 LM head
+    kv_read = rows * L * kv_bytes_per_position(shape) * context
+    kv_write = rows * L * kv_bytes_per_position(shape)
+    logits = rows * V * 2
+    return w + lm + kv_read + kv_write + logits
+
+
+def gemm_shapes(shape, rows):
+    h, f = shape.hidden, shape.ffn
+    return {"gemm_qkv": (rows, 3 * h, h), "gemm_o": (rows, h, h), "gemm_fc1": (rows, f, h),
+            "gemm_fc2": (rows, h, f), "lm_head": (rows, shape.vocab, h)}
+
+
+def build_model(tod, synth, w, log_every=8):
+    shape = w.shape
+    run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
+               gen_len=w.gen_len, weight_tier=w.weight_tier)
+    m = tod.Model(shape, run)
+    g = synth.global_weights(shape)
+    m.set_global_weights(g["tok_emb"], g["pos_emb"], g["lnf_g"], g["lnf_b"])
+    del g
+    for l in range(shape.n_layers):
+        m.set_layer_weights(l, synth.layer_weights(shape, l))
+        if (l + 1) % log_every == 0 or l + 1 == shape.n_layers:
+            log(f"weights: {l + 1}/{shape.n_layers} layers loaded")
+    return m
+
+
+def cpu_baseline(w, rows=64):
+    """Oracle on one layer x one decode step x `rows` sequences at the average decode
+    context, plus the LM head for those rows; extrapolated to the whole stack."""
+    import numpy as np
+
+    import oracle
+    import synth
+    shape = w.shape
+    ctx = w.prompt_len + (w.gen_len - 1) // 2          # average attended context - 1 cached positions
+    layer = oracle.Layer(shape, synth.layer_weights(shape, 0))
+    glob = synth.global_weights(shape)
+    caches = []
+    for r in range(rows):
+        c = oracle.KVCache(shape, ctx + 1)
+        k = synth.normal_f16(4096 + r, 0, (ctx, shape.hidden), 0.0, 1.0)
+        v = synth.normal_f16(4096 + r, 1, (ctx, shape.hidden), 0.0, 1.0)
+        c.store(0, k, v)
+        caches.append(c)
+    hid = synth.normal_f16(8191, 0, (rows, shape.hidden), 0.0, 1.0)
+    t0 = time.perf_counter()
+    for r in range(rows):
+        layer.forward(caches[r], ctx, hid[r:r + 1])
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.head(shape, glob["lnf_g"], glob["lnf_b"], glob["tok_emb"], hid)
+    t_lm = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    tps = rows / (shape.n_layers * t_layer + t_lm)
+    return {"value": tps, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"1 of {shape.n_layers} layers x 1 decode step x {rows} sequences at context {ctx + 1} "
+                       f"({t_layer:.2f} s) + LM head for {rows} rows ({t_lm:.2f} s); extrapolated as "
+                       f"{rows} / ({shape.n_layers} * t_layer + t_lm)")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=31)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="opt-30b")
+    ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (see the design notes on "
+              "sharding); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import throughput_oriented_offloaded_amd as tod
+
+    w = synth.WORKLOADS[args.workload]
+    shape, M = w.shape, w.rows
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    m = build_model(tod, synth, w)
+    prompts = torch.from_numpy(synth.prompt_ids(M, w.prompt_len, shape.vocab)).cuda()
+    first = torch.empty(M, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+
+    # prefill (its own timed region, reported beside the decode metric)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    tod.prefill(m.handle, 0, prompts, first)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_s = e0.elapsed_time(e1) / 1e3
+    log(f"prefill {prefill_s:.2f} s")
+
+    max_steps = w.gen_len - 1
+    out = torch.empty((max_steps, M), dtype=torch.int32, device="cuda")
+
+    def run_steps(n):
+        """n decode steps, replaying steps 1..gen_len-1 from the prefill state."""
+        done = 0
+        state = run_steps.state
+        while done < n:
+            if state["decoded"] == max_steps:
+                tod.set_decode_position(m.handle, 0, 0)
+                state["decoded"], state["ids"] = 0, first
+            k = min(n - done, max_steps - state["decoded"])
+            tod.decode_block(m.handle, 0, k, state["ids"], out[state["decoded"]:state["decoded"] + k])
+            state["ids"] = out[state["decoded"] + k - 1]
+            state["decoded"] += k
+            done += k
+            run_steps.contexts.extend(range(w.prompt_len + state["decoded"] - k + 1,
+                                            w.prompt_len + state["decoded"] + 1))
+    run_steps.state = {"decoded": 0, "ids": first}
+    run_steps.contexts = []
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    tod.set_decode_position(m.handle, 0, 0)
+    run_steps.state = {"decoded": 0, "ids": first}
+    run_steps.contexts = []
+    kinds = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
+             "argmax", "embed")
+    tod.profile_kernels(m.handle, kinds)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    contexts = list(run_steps.contexts)
+    prof = {k: tod.profile_read(m.handle, k) for k in kinds}
+    tod.profile_kernels(m.handle, ())
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = M * args.steps / elapsed
+    ctx_avg = sum(contexts) / len(contexts)
+    bytes_avg = sum(step_bytes(shape, M, c) for c in contexts) / len(contexts)
+    hbm_frac = bytes_avg / (ms_per_step * 1e-3) / (HBM_PEAK_GBS * 1e9)
+
+    # per-kernel-class achieved rates over the timed region
+    kernels = {}
+    shapes = gemm_shapes(shape, M)
+    for k, (ms, n) in prof.items():
+        if n == 0:
+            continue
+        entry = {"launches": n, "avg_us": ms * 1e3 / n, "share": ms / (elapsed * 1e3)}
+        if k in shapes:
+            r, nn, kk = shapes[k]
+            tflops = 2.0 * r * nn * kk * n / (ms * 1e-3) / 1e12
+            entry.update(bound="mfma", achieved_tflops=tflops, frac=tflops / MFMA_F16_PEAK_TFLOPS)
+        elif k == "attn":
+            # per launch (one layer): K and V of every cached position of every row, plus q and the output
+            total = sum((M * kv_bytes_per_position(shape) * c + 2 * M * shape.hidden * 2) * shape.n_layers
+                        for c in contexts)
+            gbs = total / (ms * 1e-3) / 1e9
+            entry.update(bound="hbm", achieved_gbs=gbs, frac=gbs / HBM_PEAK_GBS)
+        kernels[k] = entry
+    dom = max((k for k in kernels if "frac" in kernels[k]), key=lambda k: kernels[k]["share"])
+    d = kernels[dom]
+    if d["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": d["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["frac"], "traffic": None, "kernel": "k_attn_decode<128>"}
+    else:
+        roof = {"bound": "mfma", "achieved": d["achieved_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": d["frac"], "traffic": None, "kernel": f"k_gemm ({dom})"}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}-shaped int4 W+KV block decode", "layers": shape.n_layers,
+                   "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim, "ffn": shape.ffn,
+                   "vocab": shape.vocab, "gpu_batch": w.gpu_batch, "batches_per_block": w.batches_per_block,
+                   "rows": M, "prompt_len": w.prompt_len, "gen_len": w.gen_len, "context_avg": ctx_avg,
+                   "weights": "int4 g64 in HBM" if w.weight_tier == 0 else "fp16 streamed from pinned host"},
+        "roofline": roof,
+        "hbm_frac_step": hbm_frac,
+        "algorithmic_gb_per_step": bytes_avg / 1e9,
+        "prefill_s": prefill_s,
+        "e2e_tokens_per_s": M * w.gen_len / (prefill_s + (w.gen_len - 1) * ms_per_step * 1e-3),
+        "kernels": kernels,
+    }
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    if args.cpu_baseline == "on":
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

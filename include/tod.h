@@ -173,6 +173,22 @@ const char *last_error(void);
 /* Inspection and unit entry points (used by tests and the benchmark).      */
 /* ------------------------------------------------------------------------ */
 
+/* Kernel classes timed by profile_kernels / profile_read. */
+enum {
+    TOD_K_GEMM_QKV = 0, TOD_K_GEMM_O, TOD_K_GEMM_FC1, TOD_K_GEMM_FC2, TOD_K_ATTN, TOD_K_KV_APPEND,
+    TOD_K_LAYERNORM, TOD_K_LM_HEAD, TOD_K_ARGMAX, TOD_K_EMBED, TOD_K_COUNT
+};
+
+/*
+ * profile_kernels: from now on, bracket every launch of the kernel classes
+ * whose bit (1 << TOD_K_*) is set in `mask` with HIP events on the stream it
+ * is launched on (prefill and decode_block); mask 0 stops. Resets the totals.
+ * profile_read: wait for the recorded events and return the summed duration
+ * (ms) and the number of launches of class `kind` since profile_kernels.
+ */
+int profile_kernels(tod_model *m, unsigned mask);
+int profile_read(tod_model *m, int kind, double *total_ms, int64_t *launches);
+
 /*
  * export_weight: copy layer `layer`'s matrix `which` (TOD_MAT_*) back out of
  * the int4 store in the canonical format (device buffers: codes [out*in/2],

@@ -464,12 +464,17 @@ int o_kv_store(o_kv *c, int pos0, int n, const uint16_t *k, const uint16_t *v)
     if (pos0 < 0 || pos0 + n > c->cap)
         return -4;
     int bad = 0;
+#pragma omp parallel for schedule(static) collapse(2) reduction(| : bad)
     for (int t = 0; t < n; t++)
         for (int hd = 0; hd < H; hd++) {
             const int64_t slot = (int64_t)hd * c->cap + pos0 + t;
             const int64_t src = (int64_t)t * H * d + (int64_t)hd * d;
-            bad |= o_quantize_groupwise(k + src, d, G, c->kc + slot * (d / 2), c->ks + slot * ng, c->kz + slot * ng);
-            bad |= o_quantize_groupwise(v + src, d, G, c->vc + slot * (d / 2), c->vs + slot * ng, c->vz + slot * ng);
+            for (int g = 0; g < ng; g++) {
+                bad |= quantize_group(k + src + g * G, G, c->kc + slot * (d / 2) + g * (G / 2), c->ks + slot * ng + g,
+                                      c->kz + slot * ng + g) != 0;
+                bad |= quantize_group(v + src + g * G, G, c->vc + slot * (d / 2) + g * (G / 2), c->vs + slot * ng + g,
+                                      c->vz + slot * ng + g) != 0;
+            }
         }
     return bad ? -1 : 0;
 }

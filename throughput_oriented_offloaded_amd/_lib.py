@@ -25,7 +25,9 @@ LAYER_TENSORS = ("ln1_g", "ln1_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b",
 EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", "decode_block",
             "set_decode_position", "quantize_groupwise", "dequantize_groupwise", "free_model", "last_error",
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
-            "attn_decode_step", "attn_cache_export", "attn_cache_free")
+            "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read")
+KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
+                "argmax", "embed")
 
 
 class TodError(RuntimeError):
@@ -72,6 +74,8 @@ def lib() -> ctypes.CDLL:
         "attn_decode_step": [vp, i32, vp, vp, vp, vp, vp],
         "attn_cache_export": [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
         "attn_cache_free": [vp],
+        "profile_kernels": [vp, ctypes.c_uint],
+        "profile_read": [vp, i32, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -223,3 +227,19 @@ def attn_cache_export(c, seq: int, head: int, t0: int, t1: int, kc, ks, kz, vc, 
 
 def attn_cache_free(c):
     _check("attn_cache_free", lib().attn_cache_free(c))
+
+
+def profile_kernels(m, kinds=()):
+    """Time every launch of the given kernel classes (names in KERNEL_KINDS) with HIP events."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    _check("profile_kernels", lib().profile_kernels(m, mask))
+
+
+def profile_read(m, kind: str):
+    """(total ms, launches) of a profiled kernel class since profile_kernels."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check("profile_read", lib().profile_read(m, KERNEL_KINDS.index(kind), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -88,6 +88,16 @@ struct tod_model {
     hipStream_t copy = nullptr;
     hipEvent_t ev_loaded[2] = {}, ev_free[2] = {};
     std::vector<int> prefilled, decoded;
+    // kernel timing (profile_kernels / profile_read)
+    unsigned prof_mask = 0;
+    std::vector<hipEvent_t> ev_pool;
+    struct Pending {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::vector<Pending> pend;
+    double prof_ms[TOD_K_COUNT] = {};
+    int64_t prof_n[TOD_K_COUNT] = {};
 };
 
 struct tod_attn_cache {
@@ -141,6 +151,54 @@ size_t kv_bytes(size_t n_slabs, int d, int cap, size_t *kc_b, size_t *kp_b)
     return 2 * (*kc_b + *kp_b);
 }
 
+hipEvent_t pooled_event(tod_model *m)
+{
+    if (!m->ev_pool.empty()) {
+        hipEvent_t e = m->ev_pool.back();
+        m->ev_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    return e;
+}
+
+// Brackets the launches issued in its lifetime with events when `kind` is profiled.
+struct ProfScope {
+    tod_model *m;
+    int kind;
+    hipStream_t st;
+    hipEvent_t a = nullptr;
+    ProfScope(tod_model *m_, int kind_, hipStream_t st_) : m(m_), kind(kind_), st(st_)
+    {
+        if (m->prof_mask & (1u << kind)) {
+            a = pooled_event(m);
+            if (a && hipEventRecord(a, st) != hipSuccess) {
+                (void)hipGetLastError();
+                m->ev_pool.push_back(a);
+                a = nullptr;
+            }
+        }
+    }
+    ~ProfScope()
+    {
+        if (!a)
+            return;
+        hipEvent_t b = pooled_event(m);
+        if (b && hipEventRecord(b, st) == hipSuccess) {
+            m->pend.push_back({kind, a, b});
+        } else {
+            (void)hipGetLastError();
+            m->ev_pool.push_back(a);
+            if (b)
+                m->ev_pool.push_back(b);
+        }
+    }
+};
+
 int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint16_t *wf,
              uint16_t *y, int64_t ldc, int epi, hipStream_t st)
 {
@@ -163,6 +221,7 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
     g.epi = epi;
     g.ws = m->ws;
     g.ws_bytes = m->ws_bytes;
+    ProfScope ps(m, TOD_K_GEMM_QKV + mat, st);
     HIPCHK(launch_gemm(g, st));
     return TOD_OK;
 }
@@ -180,7 +239,10 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
     const uint16_t *w1 = wslot ? wslot + m->mat_off[MAT_FC1] : nullptr;
     const uint16_t *w2 = wslot ? wslot + m->mat_off[MAT_FC2] : nullptr;
     int rc;
-    HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
+    {
+        ProfScope ps(m, TOD_K_LAYERNORM, st);
+        HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
+    }
     if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wq, m->qkv, 3 * hd, EPI_BIAS, st)))
         return rc;
     SrcMap src;
@@ -192,14 +254,23 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         src = {3 * hd, 0, m->cfg.head_dim};
         map = {seq0, 1, pos};
     }
-    HIPCHK(launch_kv_append(m->qkv + hd, m->qkv + 2 * hd, src, rows, map, kv, st));
-    if (prefill_mode)
-        HIPCHK(launch_attn_prefill(m->qkv, 3 * hd, m->att, hd, rows / s, seq0, s, kv, st));
-    else
-        HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, kv, st));
+    {
+        ProfScope ps(m, TOD_K_KV_APPEND, st);
+        HIPCHK(launch_kv_append(m->qkv + hd, m->qkv + 2 * hd, src, rows, map, kv, st));
+    }
+    {
+        ProfScope ps(m, TOD_K_ATTN, st);
+        if (prefill_mode)
+            HIPCHK(launch_attn_prefill(m->qkv, 3 * hd, m->att, hd, rows / s, seq0, s, kv, st));
+        else
+            HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, kv, st));
+    }
     if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wo, h, hd, EPI_BIAS_RES, st)))
         return rc;
-    HIPCHK(launch_layernorm(h, rows, hd, L.ln2_g, L.ln2_b, m->act, st));
+    {
+        ProfScope ps(m, TOD_K_LAYERNORM, st);
+        HIPCHK(launch_layernorm(h, rows, hd, L.ln2_g, L.ln2_b, m->act, st));
+    }
     if ((rc = run_gemm(m, m->act, rows, MAT_FC1, L, w1, m->ffn, f, EPI_BIAS_RELU, st)))
         return rc;
     if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, w2, h, hd, EPI_BIAS_RES, st)))
@@ -261,7 +332,10 @@ int check_ready(tod_model *m, int block)
 int head_pass(tod_model *m, const uint16_t *hrows, int rows, uint16_t *logits, int32_t *next, hipStream_t st)
 {
     const int hd = m->cfg.hidden, V = m->cfg.vocab;
-    HIPCHK(launch_layernorm(hrows, rows, hd, m->lnf_g, m->lnf_b, m->act, st));
+    {
+        ProfScope ps(m, TOD_K_LAYERNORM, st);
+        HIPCHK(launch_layernorm(hrows, rows, hd, m->lnf_g, m->lnf_b, m->act, st));
+    }
     GemmArgs g{};
     g.a = m->act;
     g.lda = hd;
@@ -274,8 +348,14 @@ int head_pass(tod_model *m, const uint16_t *hrows, int rows, uint16_t *logits, i
     g.epi = EPI_NONE;
     g.ws = m->ws;
     g.ws_bytes = m->ws_bytes;
-    HIPCHK(launch_gemm(g, st));
-    HIPCHK(launch_argmax(logits, rows, V, next, st));
+    {
+        ProfScope ps(m, TOD_K_LM_HEAD, st);
+        HIPCHK(launch_gemm(g, st));
+    }
+    {
+        ProfScope ps(m, TOD_K_ARGMAX, st);
+        HIPCHK(launch_argmax(logits, rows, V, next, st));
+    }
     return TOD_OK;
 }
 
@@ -305,6 +385,12 @@ int free_model(tod_model *m)
     }
     if (m->copy)
         (void)hipStreamDestroy(m->copy);
+    for (auto &p : m->pend) {
+        (void)hipEventDestroy(p.a);
+        (void)hipEventDestroy(p.b);
+    }
+    for (hipEvent_t e : m->ev_pool)
+        (void)hipEventDestroy(e);
     delete m;
     return TOD_OK;
 }
@@ -529,9 +615,11 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
     const int b = m->run.gpu_batch, K = m->run.batches_per_block, s = m->run.prompt_len, h = m->cfg.hidden;
     const int L = m->cfg.n_layers;
     const int64_t brow = (int64_t)b * s; // rows of one batch
-    for (int k = 0; k < K; k++)
+    for (int k = 0; k < K; k++) {
+        ProfScope ps(m, TOD_K_EMBED, st);
         HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
                                 m->hid + k * brow * h, st));
+    }
     rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
         const KvView &kv = m->kv[(size_t)block * L + l];
         for (int kk = 0; kk < K; kk++) {
@@ -570,7 +658,10 @@ int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, 
     for (int j = 0; j < n_steps; j++) {
         const int pos = m->run.prompt_len + m->decoded[block];
         const int32_t *in = j == 0 ? d_ids_in : d_ids_out + (int64_t)(j - 1) * Mr;
-        HIPCHK(launch_embed(in, Mr, 1, pos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
+        {
+            ProfScope ps(m, TOD_K_EMBED, st);
+            HIPCHK(launch_embed(in, Mr, 1, pos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
+        }
         rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
             return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, wslot, st);
         });
@@ -754,6 +845,42 @@ int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_
                const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
 {
     return linear_common(d_a, rows, in, out, nullptr, nullptr, nullptr, d_w, d_bias, d_residual, relu, d_y, stream);
+}
+
+int profile_kernels(tod_model *m, unsigned mask)
+{
+    if (!m)
+        return fail(TOD_EINVAL, "null model");
+    double ms;
+    int64_t n;
+    int rc = profile_read(m, 0, &ms, &n); // drain pending events
+    if (rc)
+        return rc;
+    m->prof_mask = mask;
+    for (int k = 0; k < TOD_K_COUNT; k++) {
+        m->prof_ms[k] = 0.0;
+        m->prof_n[k] = 0;
+    }
+    return TOD_OK;
+}
+
+int profile_read(tod_model *m, int kind, double *total_ms, int64_t *launches)
+{
+    if (!m || !total_ms || !launches || kind < 0 || kind >= TOD_K_COUNT)
+        return fail(TOD_EINVAL, "bad profile_read arguments");
+    for (auto &p : m->pend) {
+        HIPCHK(hipEventSynchronize(p.b));
+        float ms = 0.0f;
+        HIPCHK(hipEventElapsedTime(&ms, p.a, p.b));
+        m->prof_ms[p.kind] += ms;
+        m->prof_n[p.kind]++;
+        m->ev_pool.push_back(p.a);
+        m->ev_pool.push_back(p.b);
+    }
+    m->pend.clear();
+    *total_ms = m->prof_ms[kind];
+    *launches = m->prof_n[kind];
+    return TOD_OK;
 }
 
 int attn_cache_create(int batch, int heads, int head_dim, int cap, tod_attn_cache **out)
