@@ -7,75 +7,82 @@
 //
 // Decode (one query per (sequence, head)) is HBM-bound: it streams d/2 code
 // bytes plus 4 bytes of (scale, zero) per group per position for K and for V.
-// One 256-thread workgroup per (sequence, head):
-//  1. scores: one thread per cached position; K codes sit in a position-
-//     chunked layout so the 64 lanes of a wave read 64 positions' 16-byte
-//     pieces as one contiguous 1 KiB line. Nibbles become exact fp16 codes
-//     ((nib | 0x6400) - 1024) and meet the query through v_dot2_f32_f16; the
-//     group factorisation  q.khat = scale * sum(q*c) + zero * sum(q)  applies
-//     scale and zero once per group.
-//  2. softmax in fp32 with block max/sum reductions (wave shuffles + LDS).
-//  3. values: 16 (or 8) lanes per position, 8 dims each, accumulate
-//     (p*scale)*c in fp32 and p*zero once per group; partial sums over the
-//     positions handled by each lane row are reduced through LDS.
+// One 256-thread workgroup per (sequence, head) walks the context in chunks
+// of 256 positions with an online softmax (details at k_attn_decode). K codes
+// sit in a position-chunked layout so that the 64 lanes of a wave read 64
+// positions' 16-byte pieces as one contiguous 1 KiB line; V codes stay in the
+// canonical per-position layout, read 16 bytes per lane.
 // Prefill (causal, all prompt positions) uses a tiled variant: 64 queries per
 // workgroup, K/V tiles of 64 positions dequantized into LDS, online softmax.
 #include "common.hpp"
 
 namespace {
 
-template <int D>
-__device__ __forceinline__ float block_reduce_max(float v, float *red)
+// Block-wide reductions over the 4 wavefronts of a 256-thread workgroup.
+__device__ __forceinline__ float block_max(float v, float *red)
 {
     v = wave_max(v);
-    const int w = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0)
-        red[w] = v;
+        red[threadIdx.x >> 6] = v;
     __syncthreads();
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-template <int D>
-__device__ __forceinline__ float block_reduce_sum(float v, float *red)
+__device__ __forceinline__ float block_sum(float v, float *red)
 {
     v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
     __syncthreads();
     if ((threadIdx.x & 63) == 0)
-        red[w] = v;
+        red[threadIdx.x >> 6] = v;
     __syncthreads();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__device__ __forceinline__ half2_t nib_pair(uint32_t w, int j)
+// Codes c_j and c_{j+4} of a canonical word, centred (c - 8, exact) as an fp16 pair:
+// (nibble | 0x6400) is the fp16 value 1024 + c, and 1024 + c - 1032 is exact.
+__device__ __forceinline__ half2_t centred_pair(uint32_t w, int j)
 {
-    const half2_t bias = {(half_t)1024.0f, (half_t)1024.0f};
+    const half2_t bias = {(half_t)1032.0f, (half_t)1032.0f};
     return __builtin_bit_cast(half2_t, ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u) - bias;
 }
 
+// Decode attention of one query per (sequence, head) over cached positions
+// 0..ctx-1, in chunks of 256 positions with an online softmax:
+//  * all global loads of a chunk (the K codes and (scale, zero) of the
+//    thread's position, and 16-byte slices of 256/ (d/32) positions' V codes)
+//    are issued before any of its arithmetic, so each thread keeps ~13
+//    independent loads in flight;
+//  * scores: with centred codes, q.khat = scale * sum(q * (c - 8)) +
+//    (zero + 8 * scale) * sum(q), the first sum by v_dot2_f32_f16;
+//  * values: each thread owns 32 dims of (d/32)-strided positions and
+//    accumulates (p * scale) * c in fp32 plus p * zero per group; the partial
+//    sums are reduced across lanes with shuffles and across waves in LDS.
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict__ q, int64_t q_stride,
                                                      uint16_t *__restrict__ out, int64_t out_stride, int seq0,
                                                      int ctx, KvView kv)
 {
-    constexpr int CB = D / 2;        // code bytes per position
-    constexpr int PIECES = CB / 16;  // 16-byte pieces per position
-    constexpr int G = D / 64;        // groups per head vector
-    constexpr int LPT = D / 8;       // lanes per position in the value pass
-    constexpr int ROWS = 256 / LPT;  // positions in flight in the value pass
-    extern __shared__ float sm[];
-    float *scores = sm;                    // [ctx]
-    float *red = sm + ((ctx + 3) & ~3);    // [4]
-    float *part = red + 4;                 // [ROWS][D]
+    constexpr int CB = D / 2;          // code bytes per position
+    constexpr int PIECES = CB / 16;    // 16-byte pieces per position
+    constexpr int G = D / 64;          // groups per head vector
+    constexpr int VQ = PIECES;         // threads per position in the value pass
+    constexpr int VTOK = 256 / VQ;     // positions per value iteration
+    constexpr int VIT = 256 / VTOK;    // value iterations per chunk of 256 positions
+    __shared__ float sp[256];
+    __shared__ float red[4];
+    __shared__ float part[4 * D];
 
     const int row = blockIdx.x / kv.heads, head = blockIdx.x % kv.heads;
     const int seq = seq0 + row;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t slab = kv_slab(kv, seq, head);
+    const uint8_t *kc = kv.kc + slab * kv.cap * CB;
+    const uint32_t *kp = kv.kp + slab * kv.cap * G;
+    const uint8_t *vc = kv.vc + slab * kv.cap * CB;
+    const uint32_t *vp = kv.vp + slab * kv.cap * G;
 
-    // query in registers, paired to match the nibble extraction order:
-    // word j (elements 8j..8j+7, canonical) yields pairs (0,4) (1,5) (2,6) (3,7)
+    // query in registers, paired (j, j + 4) within each word of 8 to match centred_pair
     const uint16_t *qp = q + (int64_t)row * q_stride + (int64_t)head * D;
     half2_t qv[D / 2];
     float qsum[G];
@@ -84,8 +91,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
         qsum[gi] = 0.0f;
 #pragma unroll
     for (int w = 0; w < D / 8; w++) {
-        const uint4_t raw = *reinterpret_cast<const uint4_t *>(qp + 8 * w);
-        const half8_t h = __builtin_bit_cast(half8_t, raw);
+        const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(qp + 8 * w));
 #pragma unroll
         for (int j = 0; j < 4; j++) {
             qv[4 * w + j] = (half2_t){h[j], h[j + 4]};
@@ -94,79 +100,109 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
     }
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-    // ---- pass 1: scores
-    const uint8_t *kc = kv.kc + slab * kv.cap * CB;
-    const uint32_t *kp = kv.kp + slab * kv.cap * G;
-    float lmax = -INFINITY;
-    for (int t = tid; t < ctx; t += 256) {
-        const uint8_t *base = kc + ((size_t)(t >> 6) * PIECES * 64 + (t & 63)) * 16;
-        float score = 0.0f;
+    const int vq = tid % VQ;             // which 16-byte slice (32 dims) of a position
+    const int vgrp = (vq * 32) / 64;     // its group
+    float acc[32];
 #pragma unroll
-        for (int gi = 0; gi < G; gi++) {
-            float dot = 0.0f;
+    for (int e = 0; e < 32; e++)
+        acc[e] = 0.0f;
+    float zacc = 0.0f, lsum = 0.0f, m_run = -INFINITY;
+
+    for (int c0 = 0; c0 < ctx; c0 += 256) {
+        // ---- issue every load of the chunk
+        const int t = c0 + tid;
+        const bool tk = t < ctx;
+        uint4_t kr[PIECES];
+        uint32_t kpar[G];
+        const uint8_t *kb = kc + ((size_t)(t >> 6) * PIECES * 64 + (t & 63)) * 16;
 #pragma unroll
-            for (int pc = 0; pc < 2; pc++) { // two 16-byte pieces per group of 64
-                const uint4_t raw = *reinterpret_cast<const uint4_t *>(base + (size_t)(2 * gi + pc) * 64 * 16);
+        for (int pc = 0; pc < PIECES; pc++)
+            kr[pc] = tk ? *reinterpret_cast<const uint4_t *>(kb + (size_t)pc * 64 * 16) : (uint4_t){0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int w = 0; w < 4; w++) {
-                    const int qw = (2 * gi + pc) * 4 + w; // word index within the head vector
+        for (int gi = 0; gi < G; gi++)
+            kpar[gi] = tk ? kp[(size_t)t * G + gi] : 0u;
+        uint4_t vr[VIT];
+        uint32_t vpar[VIT];
 #pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        dot = __builtin_amdgcn_fdot2(qv[4 * qw + j], nib_pair(raw[w], j), dot, false);
+        for (int j = 0; j < VIT; j++) {
+            const int tv = c0 + tid / VQ + VTOK * j;
+            const bool ok = tv < ctx;
+            vr[j] = ok ? *reinterpret_cast<const uint4_t *>(vc + (size_t)tv * CB + vq * 16) : (uint4_t){0u, 0u, 0u, 0u};
+            vpar[j] = ok ? vp[(size_t)tv * G + vgrp] : 0u;
+        }
+
+        // ---- scores of this chunk
+        float score = -INFINITY;
+        if (tk) {
+            score = 0.0f;
+#pragma unroll
+            for (int gi = 0; gi < G; gi++) {
+                float dot = 0.0f;
+#pragma unroll
+                for (int pc = 0; pc < 2; pc++) {
+#pragma unroll
+                    for (int w = 0; w < 4; w++) {
+                        const int qw = (2 * gi + pc) * 4 + w;
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            dot = __builtin_amdgcn_fdot2(qv[4 * qw + j], centred_pair(kr[2 * gi + pc][w], j), dot,
+                                                         false);
+                    }
+                }
+                const float s = h2f((uint16_t)(kpar[gi] & 0xffff)), z = h2f((uint16_t)(kpar[gi] >> 16));
+                score += s * dot + (z + 8.0f * s) * qsum[gi];
+            }
+            score *= inv_sqrt_d;
+        }
+        const float m_new = fmaxf(m_run, block_max(score, red));
+        const float corr = __expf(m_run - m_new); // 0 on the first chunk
+        const float p = tk ? __expf(score - m_new) : 0.0f;
+        sp[tid] = p;
+        lsum = lsum * corr + p;
+        zacc *= corr;
+#pragma unroll
+        for (int e = 0; e < 32; e++)
+            acc[e] *= corr;
+        m_run = m_new;
+        __syncthreads();
+
+        // ---- values of this chunk: canonical bytes, byte b = elements 2b (low) and 2b+1 (high)
+#pragma unroll
+        for (int j = 0; j < VIT; j++) {
+            const float pr = sp[tid / VQ + VTOK * j];
+            const float ps = pr * h2f((uint16_t)(vpar[j] & 0xffff));
+            zacc += pr * h2f((uint16_t)(vpar[j] >> 16));
+#pragma unroll
+            for (int w = 0; w < 4; w++) {
+                const uint32_t lo = vr[j][w] & 0x0F0F0F0Fu, hi = (vr[j][w] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    acc[8 * w + 2 * b] += ps * (float)((lo >> (8 * b)) & 0xffu);
+                    acc[8 * w + 2 * b + 1] += ps * (float)((hi >> (8 * b)) & 0xffu);
                 }
             }
-            const uint32_t p = kp[(size_t)t * G + gi];
-            score += h2f((uint16_t)(p & 0xffff)) * dot + h2f((uint16_t)(p >> 16)) * qsum[gi];
         }
-        score *= inv_sqrt_d;
-        scores[t] = score;
-        lmax = fmaxf(lmax, score);
+        __syncthreads(); // sp is rewritten by the next chunk
     }
-    const float mx = block_reduce_max<D>(lmax, red);
 
-    // ---- pass 2: softmax numerators
-    float lsum = 0.0f;
-    for (int t = tid; t < ctx; t += 256) {
-        const float p = __expf(scores[t] - mx);
-        scores[t] = p;
-        lsum += p;
-    }
-    const float den = block_reduce_sum<D>(lsum, red); // also orders the score writes before pass 3
-
-    // ---- pass 3: values
-    const int tr = tid / LPT, dj = tid % LPT; // position row, 8-dim slice
-    const uint32_t *vc = reinterpret_cast<const uint32_t *>(kv.vc + slab * kv.cap * CB);
-    const uint32_t *vp = kv.vp + slab * kv.cap * G;
-    float acc[8];
+    // ---- reduce: lanes sharing vq (lane % VQ) within the wave, then the 4 waves in LDS
+    const float den = block_sum(lsum, red);
 #pragma unroll
-    for (int e = 0; e < 8; e++)
-        acc[e] = 0.0f;
-    float zacc = 0.0f;
-    for (int t = tr; t < ctx; t += ROWS) {
-        const uint32_t w = vc[(size_t)t * (CB / 4) + dj];
-        const uint32_t p = vp[(size_t)t * G + (dj * 8) / 64];
-        const float pr = scores[t];
-        const float ps = pr * h2f((uint16_t)(p & 0xffff));
-        zacc += pr * h2f((uint16_t)(p >> 16));
-        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-        // canonical: byte b holds elements 2b (low nibble) and 2b+1 (high nibble)
-        acc[0] += ps * (float)((lo >> 0) & 0xffu);
-        acc[1] += ps * (float)((hi >> 0) & 0xffu);
-        acc[2] += ps * (float)((lo >> 8) & 0xffu);
-        acc[3] += ps * (float)((hi >> 8) & 0xffu);
-        acc[4] += ps * (float)((lo >> 16) & 0xffu);
-        acc[5] += ps * (float)((hi >> 16) & 0xffu);
-        acc[6] += ps * (float)((lo >> 24) & 0xffu);
-        acc[7] += ps * (float)((hi >> 24) & 0xffu);
-    }
+    for (int e = 0; e < 32; e++) {
+        float v = acc[e] + zacc;
 #pragma unroll
-    for (int e = 0; e < 8; e++)
-        part[tr * D + dj * 8 + e] = acc[e] + zacc;
+        for (int o = VQ; o < 64; o <<= 1)
+            v += __shfl_xor(v, o, 64);
+        acc[e] = v;
+    }
+    if (lane < VQ) {
+#pragma unroll
+        for (int e = 0; e < 32; e++)
+            part[wave * D + lane * 32 + e] = acc[e];
+    }
     __syncthreads();
     if (tid < D) {
-        float o = 0.0f;
-        for (int r = 0; r < ROWS; r++)
-            o += part[r * D + tid];
+        const float o = (part[tid] + part[D + tid]) + (part[2 * D + tid] + part[3 * D + tid]);
         out[(int64_t)row * out_stride + (int64_t)head * D + tid] = f2h(o / den);
     }
 }
@@ -306,15 +342,12 @@ hipError_t launch_attn_decode(const uint16_t *q, int64_t q_stride, uint16_t *out
     if (rows == 0)
         return hipSuccess;
     const dim3 grid((unsigned)rows * kv.heads), block(256);
-    if (kv.head_dim == 128) {
-        const size_t lds = (((size_t)ctx + 3) / 4 * 4 + 4 + (256 / 16) * 128) * sizeof(float);
-        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, lds, st, q, q_stride, out, out_stride, seq0, ctx, kv);
-    } else if (kv.head_dim == 64) {
-        const size_t lds = (((size_t)ctx + 3) / 4 * 4 + 4 + (256 / 8) * 64) * sizeof(float);
-        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, lds, st, q, q_stride, out, out_stride, seq0, ctx, kv);
-    } else {
+    if (kv.head_dim == 128)
+        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, seq0, ctx, kv);
+    else if (kv.head_dim == 64)
+        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, seq0, ctx, kv);
+    else
         return hipErrorInvalidValue;
-    }
     return hipGetLastError();
 }
 

@@ -23,6 +23,9 @@
 //    tile share that XCD's L2.
 //  * When the tile grid is too small to fill 256 CUs the K loop is split and
 //    fp32 partials are reduced by a second kernel (deterministic order).
+#include <cstdio>
+#include <cstdlib>
+
 #include "common.hpp"
 
 namespace {
@@ -56,8 +59,8 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t s2, half2_t 
     return out;
 }
 
-template <int BM, int BN, bool INT4>
-__global__ void __launch_bounds__(256) k_gemm(GemmArgs g, TileMap tm)
+template <int BM, int BN, bool INT4, int MINW>
+__global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MB = WM / 32, NB = WN / 32;
@@ -225,6 +228,264 @@ __global__ void __launch_bounds__(256) k_gemm(GemmArgs g, TileMap tm)
         }
 }
 
+// ---------------------------------------------------------------------------
+// int4 GEMM for M > 128: 256 x 128 workgroup tile (four 256 x 32 wave tiles),
+// fed through a 4-stage LDS ring that direct-to-LDS loads
+// (global_load_lds_dwordx4) fill three K-groups ahead of the MFMAs, so HBM
+// latency of the weight stream is covered without staging registers. A wave
+// dequantizes its 32 columns once for all 256 rows. Stage synchronisation is
+// an explicit vmcnt wait on the wave's own loads plus a workgroup barrier.
+// ---------------------------------------------------------------------------
+namespace w4 {
+constexpr int BM = 256;
+constexpr int A_BYTES = BM * 128; // BM rows x 64 fp16, 16-byte chunks swizzled by row
+template <int BN> struct Cfg {
+    static constexpr int NB = BN / 128;               // 32-column blocks per wave (4 waves side by side)
+    static constexpr int S = BN == 128 ? 4 : 3;       // LDS ring stages
+    static constexpr int W_BYTES = (BN / 32) * 1024;  // per column block: 64 lanes x 16 B of codes
+    static constexpr int P_BYTES = (BN / 32) * 256;   // per column block: 64 x (scale, zero), lanes 32..63 repeat
+    static constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
+    static constexpr int LPS = BM / 32 + 2 * NB;      // loads per wave per stage
+};
+} // namespace w4
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS position of 16-byte chunk `ch` (0..7) of A-tile row `row`: XOR with a row
+// hash that is a bijection on every 8 consecutive rows and, across 16 rows,
+// on the even and on the odd rows separately, so that 8- and 16-lane phases of
+// a ds_read_b128 (rows r..r+15, one chunk column) touch distinct banks.
+__device__ __forceinline__ int a_pos(int row, int ch) { return ch ^ ((row ^ (row >> 3)) & 7); }
+
+// Wait until at most younger * LPS of this wave's vector-memory loads are outstanding.
+template <int LPS>
+__device__ __forceinline__ void wait_vm_loads(int younger)
+{
+    // s_waitcnt simm16 on gfx9: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+    constexpr int n1 = LPS, n2 = 2 * LPS;
+    constexpr int e1 = (n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8);
+    constexpr int e2 = (n2 & 15) | ((n2 >> 4) << 14) | (7 << 4) | (15 << 8);
+    static_assert(n2 < 64, "vmcnt holds 6 bits");
+    if (younger >= 2)
+        __builtin_amdgcn_s_waitcnt(e2);
+    else if (younger == 1)
+        __builtin_amdgcn_s_waitcnt(e1);
+    else
+        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
+template <int BN>
+__global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
+{
+    using namespace w4;
+    using C = Cfg<BN>;
+    constexpr int MB = BM / 32, NB = C::NB, S = C::S, STAGE = C::STAGE;
+    // each wave owns NB 32-column blocks and all BM rows: its weights are
+    // dequantized once and feed BM/32 MFMAs per K-step and column block
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
+
+    const int tile = xcd_tile(blockIdx.x, tm.total);
+    if (tile >= tm.total)
+        return;
+    const int m_tile = tile % tm.mt;
+    const int rest = tile / tm.mt;
+    const int n_tile = rest % tm.nt;
+    const int split = rest / tm.nt;
+    const int m0 = m_tile * BM, n0 = n_tile * BN;
+    const int KG = g.K / KG_ELEMS;
+    const int g0 = split * tm.groups_per_split;
+    const int g1 = min(KG, g0 + tm.groups_per_split);
+    const int nst = g1 - g0;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    auto issue = [&](int buf, int grp) {
+        uint8_t *base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < BM / 32; i++) {
+            const int q = wave + 4 * i;                 // 1 KiB chunk = rows 8q .. 8q+7
+            const int row = 8 * q + (lane >> 3);
+            const int ch = a_pos(row, lane & 7);         // global chunk landing at position lane & 7
+            const int m = min(m0 + row, g.M - 1);
+            __builtin_amdgcn_global_load_lds(g.a + (int64_t)m * g.lda + grp * KG_ELEMS + ch * 8,
+                                             (lds_void *)(base + q * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const int cb = wave * NB + j; // column block within the tile
+            // clamped: blocks past N feed discarded columns
+            const int nb = min((n0 >> 5) + cb, (g.N >> 5) - 1);
+            const int64_t blk = (int64_t)nb * KG + grp;
+            __builtin_amdgcn_global_load_lds(g.wc + (blk * 64 + lane) * 4, (lds_void *)(base + A_BYTES + cb * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(g.wp + blk * 32 + (lane & 31),
+                                             (lds_void *)(base + A_BYTES + C::W_BYTES + cb * 256), 4, 0, 0);
+        }
+    };
+
+    float16_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; i++)
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                acc[i][j][r] = 0.0f;
+
+#pragma unroll
+    for (int s_ = 0; s_ < S - 1; s_++)
+        if (s_ < nst)
+            issue(s_, g0 + s_);
+
+    for (int it = 0; it < nst; it++) {
+        const int younger = min(S - 2, nst - 1 - it);
+        wait_vm_loads<C::LPS>(younger);
+        __builtin_amdgcn_s_barrier();
+        if (it + S - 1 < nst)
+            issue((it + S - 1) % S, g0 + it + S - 1);
+        const uint8_t *base = smem + (it % S) * STAGE;
+        uint4_t bw[NB];
+        half2_t s2[NB], z2[NB];
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const int cb = wave * NB + j;
+            bw[j] = *reinterpret_cast<const uint4_t *>(base + A_BYTES + cb * 1024 + lane * 16);
+            const uint32_t bp = *reinterpret_cast<const uint32_t *>(base + A_BYTES + C::W_BYTES + cb * 256 +
+                                                                    (lane & 31) * 4);
+            s2[j] = __builtin_bit_cast(half2_t, (bp & 0xffffu) * 0x10001u);
+            z2[j] = __builtin_bit_cast(half2_t, (bp >> 16) * 0x10001u);
+        }
+        // Software pipeline over the four K-steps: the A operands (LDS) and the
+        // dequantized weights of step t+1 are produced while the MFMAs of step t
+        // run; sched_barrier keeps the compiler from sinking the LDS reads next
+        // to their MFMAs, where their latency would be exposed.
+        half8_t a_cur[MB], a_nxt[MB], b_cur[NB], b_nxt[NB];
+#pragma unroll
+        for (int i = 0; i < MB; i++) {
+            const int row = i * 32 + (lane & 31);
+            a_cur[i] = *reinterpret_cast<const half8_t *>(base + row * 128 + (a_pos(row, lane >> 5) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < NB; j++)
+            b_cur[j] = dequant_word(bw[j][0], s2[j], z2[j]);
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            if (t < 3) {
+#pragma unroll
+                for (int i = 0; i < MB; i++) {
+                    const int row = i * 32 + (lane & 31);
+                    a_nxt[i] = *reinterpret_cast<const half8_t *>(base + row * 128 +
+                                                                  (a_pos(row, 2 * (t + 1) + (lane >> 5)) << 4));
+                }
+#pragma unroll
+                for (int j = 0; j < NB; j++)
+                    b_nxt[j] = dequant_word(bw[j][t + 1], s2[j], z2[j]);
+            }
+#pragma unroll
+            for (int i = 0; i < MB; i++)
+#pragma unroll
+                for (int j = 0; j < NB; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[i], b_cur[j], acc[i][j], 0, 0, 0);
+            if (t < 3) {
+                // interleave: one MFMA, then LDS reads and dequant VALU of the next step
+#pragma unroll
+                for (int k = 0; k < MB * NB; k++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, MB / (MB * NB) > 0 ? 1 : 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4 / NB, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < MB; i++)
+                a_cur[i] = a_nxt[i];
+#pragma unroll
+            for (int j = 0; j < NB; j++)
+                b_cur[j] = b_nxt[j];
+        }
+    }
+
+    // Epilogue through LDS: each 32 x 32 accumulator block goes to a per-wave
+    // scratch tile in the MFMA lane layout and comes back as 16 consecutive
+    // columns of one row per lane, so bias, residual and output move in 32-byte
+    // runs. The ring is free once every wave has left the main loop.
+    __syncthreads();
+    constexpr int SROW = 36; // padded scratch row (floats)
+    float *scr = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
+    const int lr = lane >> 1, c0 = (lane & 1) * 16;
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        const int gcol = n0 + (wave * NB + j) * 32 + c0;
+        const bool colok = gcol < g.N; // N is a multiple of 32 on this path
+        float bias[16];
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+            bias[e] = 0.0f;
+        if (colok && tm.splits == 1 && g.bias && g.epi != EPI_NONE) {
+            const uint4_t b0 = *reinterpret_cast<const uint4_t *>(g.bias + gcol);
+            const uint4_t b1 = *reinterpret_cast<const uint4_t *>(g.bias + gcol + 8);
+            const half8_t h0 = __builtin_bit_cast(half8_t, b0), h1 = __builtin_bit_cast(half8_t, b1);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                bias[e] = (float)h0[e];
+                bias[8 + e] = (float)h1[e];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MB; i++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                scr[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * SROW + (lane & 31)] = acc[i][j][r];
+            __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 0xc00f); // lgkmcnt(0): scratch written
+            __builtin_amdgcn_wave_barrier();
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float4_t f = *reinterpret_cast<const float4_t *>(scr + lr * SROW + c0 + 4 * q);
+                v[4 * q] = f[0];
+                v[4 * q + 1] = f[1];
+                v[4 * q + 2] = f[2];
+                v[4 * q + 3] = f[3];
+            }
+            __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 0xc00f); // lgkmcnt(0): scratch read
+            __builtin_amdgcn_wave_barrier();
+            const int grow = m0 + i * 32 + lr;
+            if (!colok || grow >= g.M)
+                continue;
+            if (tm.splits > 1) {
+                float *dst = g.ws + ((int64_t)split * g.M + grow) * g.N + gcol;
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    *reinterpret_cast<float4_t *>(dst + 4 * q) =
+                        (float4_t){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+                continue;
+            }
+            half8_t res0 = {}, res1 = {};
+            if (g.epi == EPI_BIAS_RES) {
+                const uint16_t *rp = g.residual + (int64_t)grow * g.ldc + gcol;
+                res0 = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(rp));
+                res1 = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(rp + 8));
+            }
+            half8_t o0, o1;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                float x = v[e] + bias[e];
+                if (g.epi == EPI_BIAS_RES)
+                    x += (float)(e < 8 ? res0[e] : res1[e - 8]);
+                if (g.epi == EPI_BIAS_RELU)
+                    x = fmaxf(x, 0.0f);
+                if (e < 8)
+                    o0[e] = (half_t)x;
+                else
+                    o1[e - 8] = (half_t)x;
+            }
+            uint16_t *yp = g.y + (int64_t)grow * g.ldc + gcol;
+            *reinterpret_cast<uint4_t *>(yp) = __builtin_bit_cast(uint4_t, o0);
+            *reinterpret_cast<uint4_t *>(yp + 8) = __builtin_bit_cast(uint4_t, o1);
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -245,28 +506,73 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
 
 struct Plan {
     int bm, bn;
+    bool pipelined;
     TileMap tm;
 };
 
-Plan plan_gemm(int M, int N, int K)
+// Tuning overrides (read once): TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" selects the
+// register-staged kernel for every M > 64; TOD_GEMM_BN = 128 | 256 sets the column tile of
+// the LDS-pipelined int4 kernel; TOD_GEMM_SPLIT = workgroup count below which the K loop
+// is split in two, four, ...
+struct Tuning {
+    int bm = 0, bn = 0, bn_pipe = 0, split_fill = -1;
+    Tuning()
+    {
+        if (const char *t = getenv("TOD_GEMM_TILE")) {
+            int a = 0, b = 0;
+            if (sscanf(t, "%dx%d", &a, &b) == 2 &&
+                ((a == 64 && b == 64) || (a == 128 && b == 128) || (a == 256 && b == 128))) {
+                bm = a;
+                bn = b;
+            }
+        }
+        if (const char *t = getenv("TOD_GEMM_BN")) {
+            const int v = atoi(t);
+            if (v == 128 || v == 256)
+                bn_pipe = v;
+        }
+        if (const char *t = getenv("TOD_GEMM_SPLIT"))
+            split_fill = atoi(t);
+    }
+};
+
+const Tuning &tuning()
+{
+    static const Tuning t;
+    return t;
+}
+
+Plan plan_gemm(int M, int N, int K, bool int4)
 {
     Plan p;
-    if (M <= 64) {
+    const Tuning &tu = tuning();
+    p.pipelined = int4 && M > 128 && !tu.bm;
+    if (p.pipelined) {
+        // 256 x 256 tiles halve the activation re-reads per MFMA against 256 x 128,
+        // which is what bounds this GEMM (L2 -> LDS traffic), at the price of
+        // fewer workgroups; narrow N is split along K instead.
+        p.bm = w4::BM;
+        p.bn = tu.bn_pipe ? tu.bn_pipe : 256;
+    } else if (M <= 64) {
+        // 128 x 128 tiles keep a wave at ~150 registers, so three workgroups share a
+        // CU and hide each other's load latency.
         p.bm = 64;
         p.bn = 64;
-    } else if (M <= 128) {
+    } else {
         p.bm = 128;
         p.bn = 128;
-    } else {
-        p.bm = 256;
-        p.bn = 128;
+    }
+    if (tu.bm && M > 64) {
+        p.bm = tu.bm;
+        p.bn = tu.bn;
     }
     const int KG = K / KG_ELEMS;
     p.tm.mt = (M + p.bm - 1) / p.bm;
     p.tm.nt = (N + p.bn - 1) / p.bn;
     const int tiles = p.tm.mt * p.tm.nt;
+    const int fill = tu.split_fill >= 0 ? tu.split_fill : (p.pipelined ? 160 : 384);
     int splits = 1;
-    while (tiles * splits < 384 && KG / (splits * 2) >= 8)
+    while (tiles * splits < fill && KG / (splits * 2) >= 8)
         splits *= 2;
     p.tm.groups_per_split = (KG + splits - 1) / splits;
     p.tm.splits = (KG + p.tm.groups_per_split - 1) / p.tm.groups_per_split;
@@ -276,9 +582,9 @@ Plan plan_gemm(int M, int N, int K)
 
 } // namespace
 
-size_t gemm_workspace_bytes(int M, int N, int K, bool)
+size_t gemm_workspace_bytes(int M, int N, int K, bool int4)
 {
-    const Plan p = plan_gemm(M, N, K);
+    const Plan p = plan_gemm(M, N, K, int4);
     return p.tm.splits > 1 ? (size_t)p.tm.splits * M * N * sizeof(float) : 0;
 }
 
@@ -287,7 +593,7 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
     if (g.M <= 0 || g.N <= 0)
         return hipSuccess;
     const bool int4 = g.wc != nullptr;
-    Plan p = plan_gemm(g.M, g.N, g.K);
+    Plan p = plan_gemm(g.M, g.N, g.K, int4);
     const size_t need = p.tm.splits > 1 ? (size_t)p.tm.splits * g.M * g.N * sizeof(float) : 0;
     if (need > g.ws_bytes || (need && !g.ws)) {
         // no room for partials: run unsplit
@@ -296,17 +602,23 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         p.tm.total = p.tm.mt * p.tm.nt;
     }
     const dim3 grid(p.tm.total), block(256);
-#define TOD_GEMM_CASE(BM_, BN_)                                                                      \
+    if (p.pipelined && p.bn == 256)
+        hipLaunchKernelGGL(k_gemm_w4<256>, grid, block, 0, st, g, p.tm);
+    else if (p.pipelined)
+        hipLaunchKernelGGL(k_gemm_w4<128>, grid, block, 0, st, g, p.tm);
+    else {
+#define TOD_GEMM_CASE(BM_, BN_, MINW_)                                                               \
     if (p.bm == BM_ && p.bn == BN_) {                                                                \
         if (int4)                                                                                    \
-            hipLaunchKernelGGL((k_gemm<BM_, BN_, true>), grid, block, 0, st, g, p.tm);               \
+            hipLaunchKernelGGL((k_gemm<BM_, BN_, true, MINW_>), grid, block, 0, st, g, p.tm);        \
         else                                                                                         \
-            hipLaunchKernelGGL((k_gemm<BM_, BN_, false>), grid, block, 0, st, g, p.tm);              \
+            hipLaunchKernelGGL((k_gemm<BM_, BN_, false, MINW_>), grid, block, 0, st, g, p.tm);       \
     }
-    TOD_GEMM_CASE(64, 64)
-    TOD_GEMM_CASE(128, 128)
-    TOD_GEMM_CASE(256, 128)
+    TOD_GEMM_CASE(64, 64, 1)
+    TOD_GEMM_CASE(128, 128, 1)
+    TOD_GEMM_CASE(256, 128, 2)
 #undef TOD_GEMM_CASE
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.tm.splits == 1)
         return e;
