@@ -223,7 +223,9 @@ int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_
 /*
  * Isolated decode attention over an int4 KV cache (one query per sequence).
  * attn_cache_create allocates a cache for batch x heads sequences of up to
- * cap positions with head_dim (multiple of 64) and returns a handle.
+ * cap positions with head_dim 64 or 128 and returns a handle (TOD_EINVAL for
+ * other shapes). Every fp16 buffer passed to fill/step must be 16-byte aligned
+ * (TOD_EINVAL otherwise).
  * attn_cache_fill quantizes and stores fp16 d_k, d_v [n][batch][heads][head_dim]
  * (position-major) at positions [t0, t0+n). attn_decode_step quantizes and appends the new
  * d_k_new, d_v_new [batch][heads][head_dim] at position pos, then writes

@@ -7,203 +7,223 @@
 //
 // Decode (one query per (sequence, head)) is HBM-bound: it streams d/2 code
 // bytes plus 4 bytes of (scale, zero) per group per position for K and for V.
-// One 256-thread workgroup per (sequence, head) walks the context in chunks
-// of 256 positions with an online softmax (details at k_attn_decode). K codes
-// sit in a position-chunked layout so that the 64 lanes of a wave read 64
-// positions' 16-byte pieces as one contiguous 1 KiB line; V codes stay in the
-// canonical per-position layout, read 16 bytes per lane.
+// One wavefront per (sequence, head) walks the context in chunks of 64
+// positions with its own online softmax (details at k_attn_decode); nothing
+// is shared between wavefronts, so there are no workgroup barriers. K and V
+// codes share the canonical per-position layout.
 // Prefill (causal, all prompt positions) uses a tiled variant: 64 queries per
 // workgroup, K/V tiles of 64 positions dequantized into LDS, online softmax.
 #include "common.hpp"
 
 namespace {
 
-// Block-wide reductions over the 4 wavefronts of a 256-thread workgroup.
-__device__ __forceinline__ float block_max(float v, float *red)
+// fp16 pair from two nibble fields of a word: field value f sits in the low
+// mantissa bits under the exponent of 1024, so the half is 1024 + f exactly.
+// One v_and_or_b32 (the mask in an SGPR, the exponent bits in a VGPR).
+__device__ __forceinline__ half2_t magic_pair(uint32_t x, uint32_t mask)
 {
-    v = wave_max(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(0x64006400u));
+    return __builtin_bit_cast(half2_t, r);
 }
 
-__device__ __forceinline__ float block_sum(float v, float *red)
+__device__ __forceinline__ half2_t splat_half(uint32_t bits)
 {
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    const half_t h = __builtin_bit_cast(half_t, (uint16_t)bits);
+    return (half2_t){h, h};
 }
 
-// Codes c_j and c_{j+4} of a canonical word, centred (c - 8, exact) as an fp16 pair:
-// (nibble | 0x6400) is the fp16 value 1024 + c, and 1024 + c - 1032 is exact.
-__device__ __forceinline__ half2_t centred_pair(uint32_t w, int j)
+// One chunk of 64 positions as seen by one lane: L = d/32 lanes share a
+// position, each holding 16 code bytes (32 dims) of K and of V and the
+// (scale, zero) word of its group, for positions slot + (64/L)*j. Lanes past
+// the context load the last position again (always in bounds); their
+// weights are masked to zero.
+template <int L>
+struct KvChunk {
+    uint4_t k[L], v[L];
+    uint32_t kp[L], vp[L];
+};
+
+template <int D>
+__device__ __forceinline__ void load_chunk(KvChunk<D / 32> &c, int c0, int slot, uint32_t pc, int ctx,
+                                           const uint8_t *kc, const uint8_t *vc, const uint8_t *kp, const uint8_t *vp)
 {
-    const half2_t bias = {(half_t)1032.0f, (half_t)1032.0f};
-    return __builtin_bit_cast(half2_t, ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u) - bias;
+    constexpr int L = D / 32, PPI = 64 / L, CB = D / 2, G = D / 64;
+#pragma unroll
+    for (int j = 0; j < L; j++) {
+        const uint32_t t = (uint32_t)min(c0 + slot + PPI * j, ctx - 1);
+        const uint32_t cofs = t * CB + pc * 16, pofs = (t * G + (pc >> 1)) * 4;
+        c.k[j] = *reinterpret_cast<const uint4_t *>(kc + cofs);
+        c.v[j] = *reinterpret_cast<const uint4_t *>(vc + cofs);
+        c.kp[j] = *reinterpret_cast<const uint32_t *>(kp + pofs);
+        c.vp[j] = *reinterpret_cast<const uint32_t *>(vp + pofs);
+    }
+}
+
+// State of one wavefront's online softmax; acc holds the lane's 32 dims.
+struct SoftmaxState {
+    float acc[32];
+    float m_run, lsum, psum, zsum;
+};
+
+// Scores of a chunk and its weighted values.
+//  * K: for each code word (dims e0..e7) the fields e0,e4 / e2,e6 are masked
+//    in place (1024 + c) and e1,e5 / e3,e7 at bit 4 (1024 + 16c); one packed
+//    add or FMA recovers c exactly and one packed FMA gives the fp16 key
+//    fp16(c * scale + zero), rounded once, i.e. the dequantized cache entry
+//    itself; v_dot2 against the matching query pairs sums q.k in fp32.
+//  * V: the same fields feed fp32 accumulators through mixed-precision FMA,
+//    acc_e += (p * scale) * (1024 + c) (or 1024 + 16c); the offsets and the
+//    zero term are removed once at the end from the running sums of
+//    p * scale and p * zero.
+template <int D>
+__device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, int slot, int ctx,
+                                             const half2_t (&qa)[8], const half2_t (&qb)[8], SoftmaxState &st)
+{
+    constexpr int L = D / 32, PPI = 64 / L;
+    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
+    const half2_t m1024 = {(half_t)1024.0f, (half_t)1024.0f};
+    const half2_t r16 = {(half_t)0.0625f, (half_t)0.0625f}, mm64 = {(half_t)-64.0f, (half_t)-64.0f};
+    float sc[L];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < L; j++) {
+        const half2_t s2 = splat_half(c.kp[j] & 0xffffu), z2 = splat_half(c.kp[j] >> 16);
+        float da = 0.0f, db = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            const uint32_t x = c.k[j][w], y = x >> 8;
+            const half2_t k0 = __builtin_elementwise_fma(magic_pair(x, 0x000F000Fu) - m1024, s2, z2);
+            const half2_t k1 = __builtin_elementwise_fma(__builtin_elementwise_fma(magic_pair(x, 0x00F000F0u), r16, mm64), s2, z2);
+            const half2_t k2 = __builtin_elementwise_fma(magic_pair(y, 0x000F000Fu) - m1024, s2, z2);
+            const half2_t k3 = __builtin_elementwise_fma(__builtin_elementwise_fma(magic_pair(y, 0x00F000F0u), r16, mm64), s2, z2);
+            da = __builtin_amdgcn_fdot2(qa[2 * w], k0, da, false);
+            db = __builtin_amdgcn_fdot2(qb[2 * w], k1, db, false);
+            da = __builtin_amdgcn_fdot2(qa[2 * w + 1], k2, da, false);
+            db = __builtin_amdgcn_fdot2(qb[2 * w + 1], k3, db, false);
+        }
+        const float score = reduce_group<L>(da + db, OpAdd()) * inv_sqrt_d;
+        sc[j] = c0 + slot + PPI * j < ctx ? score : -INFINITY;
+        mloc = fmaxf(mloc, sc[j]);
+    }
+    mloc = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                         __builtin_bit_cast(int, reduce_slots<L>(mloc, OpMax())))); // wave-uniform
+    if (mloc > st.m_run) {
+        const float corr = __expf(st.m_run - mloc); // 0 while nothing has been seen
+#pragma unroll
+        for (int e = 0; e < 32; e++)
+            st.acc[e] *= corr;
+        st.lsum *= corr;
+        st.psum *= corr;
+        st.zsum *= corr;
+        st.m_run = mloc;
+    }
+#pragma unroll
+    for (int j = 0; j < L; j++) {
+        const bool live = c0 + slot + PPI * j < ctx;
+        const float p = __expf(sc[j] - st.m_run); // 0 past the context
+        const float ps = live ? p * h2f((uint16_t)(c.vp[j] & 0xffffu)) : 0.0f;
+        st.lsum += p;
+        st.psum += ps;
+        st.zsum += live ? p * h2f((uint16_t)(c.vp[j] >> 16)) : 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            const uint32_t x = c.v[j][w], y = x >> 8;
+            const half2_t a0 = magic_pair(x, 0x000F000Fu), b0 = magic_pair(x, 0x00F000F0u);
+            const half2_t a1 = magic_pair(y, 0x000F000Fu), b1 = magic_pair(y, 0x00F000F0u);
+            float *acc = st.acc + 8 * w;
+            acc[0] = fmaf(ps, (float)a0[0], acc[0]);
+            acc[4] = fmaf(ps, (float)a0[1], acc[4]);
+            acc[1] = fmaf(ps, (float)b0[0], acc[1]);
+            acc[5] = fmaf(ps, (float)b0[1], acc[5]);
+            acc[2] = fmaf(ps, (float)a1[0], acc[2]);
+            acc[6] = fmaf(ps, (float)a1[1], acc[6]);
+            acc[3] = fmaf(ps, (float)b1[0], acc[3]);
+            acc[7] = fmaf(ps, (float)b1[1], acc[7]);
+        }
+    }
 }
 
 // Decode attention of one query per (sequence, head) over cached positions
-// 0..ctx-1, in chunks of 256 positions with an online softmax:
-//  * all global loads of a chunk (the K codes and (scale, zero) of the
-//    thread's position, and 16-byte slices of 256/ (d/32) positions' V codes)
-//    are issued before any of its arithmetic, so each thread keeps ~13
-//    independent loads in flight;
-//  * scores: with centred codes, q.khat = scale * sum(q * (c - 8)) +
-//    (zero + 8 * scale) * sum(q), the first sum by v_dot2_f32_f16;
-//  * values: each thread owns 32 dims of (d/32)-strided positions and
-//    accumulates (p * scale) * c in fp32 plus p * zero per group; the partial
-//    sums are reduced across lanes with shuffles and across waves in LDS.
+// 0..ctx-1: one wavefront per (sequence, head), four per workgroup. L = d/32
+// lanes share a position (32 dims each), so one 16-byte load per lane covers
+// 64/L consecutive positions of K (or V) as one contiguous line. The next
+// chunk's loads are issued before the current chunk's arithmetic (two
+// register buffers), the softmax maximum and sums use DPP/swizzle reductions
+// within the wave, and the final cross-lane sum runs once per (sequence, head).
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict__ q, int64_t q_stride,
-                                                     uint16_t *__restrict__ out, int64_t out_stride, int seq0,
-                                                     int ctx, KvView kv)
+                                                     uint16_t *__restrict__ out, int64_t out_stride, int rows,
+                                                     int seq0, int ctx, KvView kv)
 {
-    constexpr int CB = D / 2;          // code bytes per position
-    constexpr int PIECES = CB / 16;    // 16-byte pieces per position
-    constexpr int G = D / 64;          // groups per head vector
-    constexpr int VQ = PIECES;         // threads per position in the value pass
-    constexpr int VTOK = 256 / VQ;     // positions per value iteration
-    constexpr int VIT = 256 / VTOK;    // value iterations per chunk of 256 positions
-    __shared__ float sp[256];
-    __shared__ float red[4];
-    __shared__ float part[4 * D];
-
-    const int row = blockIdx.x / kv.heads, head = blockIdx.x % kv.heads;
-    const int seq = seq0 + row;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t slab = kv_slab(kv, seq, head);
+    constexpr int L = D / 32, CB = D / 2, G = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (item >= rows * kv.heads)
+        return; // whole wavefront
+    const int row = item / kv.heads, head = item - row * kv.heads;
+    const int pc = lane % L, slot = lane / L;
+    const size_t slab = kv_slab(kv, seq0 + row, head);
+    // per-wave bases (scalar), per-lane 32-bit offsets
     const uint8_t *kc = kv.kc + slab * kv.cap * CB;
-    const uint32_t *kp = kv.kp + slab * kv.cap * G;
     const uint8_t *vc = kv.vc + slab * kv.cap * CB;
-    const uint32_t *vp = kv.vp + slab * kv.cap * G;
+    const uint8_t *kp = reinterpret_cast<const uint8_t *>(kv.kp + slab * kv.cap * G);
+    const uint8_t *vp = reinterpret_cast<const uint8_t *>(kv.vp + slab * kv.cap * G);
 
-    // query in registers, paired (j, j + 4) within each word of 8 to match centred_pair
-    const uint16_t *qp = q + (int64_t)row * q_stride + (int64_t)head * D;
-    half2_t qv[D / 2];
-    float qsum[G];
+    // query dims pc*32 .. pc*32+31, paired to match the code fields
+    const uint16_t *qp = q + (int64_t)row * q_stride + (int64_t)head * D + pc * 32;
+    half2_t qa[8], qb[8];
 #pragma unroll
-    for (int gi = 0; gi < G; gi++)
-        qsum[gi] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < D / 8; w++) {
+    for (int w = 0; w < 4; w++) {
         const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(qp + 8 * w));
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            qv[4 * w + j] = (half2_t){h[j], h[j + 4]};
-            qsum[w / 8] += (float)h[j] + (float)h[j + 4];
-        }
+        qa[2 * w] = (half2_t){h[0], h[4]};
+        qa[2 * w + 1] = (half2_t){h[2], h[6]};
+        qb[2 * w] = (half2_t){h[1], h[5]};
+        qb[2 * w + 1] = (half2_t){h[3], h[7]};
     }
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
 
-    const int vq = tid % VQ;             // which 16-byte slice (32 dims) of a position
-    const int vgrp = (vq * 32) / 64;     // its group
-    float acc[32];
+    SoftmaxState st;
 #pragma unroll
     for (int e = 0; e < 32; e++)
-        acc[e] = 0.0f;
-    float zacc = 0.0f, lsum = 0.0f, m_run = -INFINITY;
+        st.acc[e] = 0.0f;
+    st.m_run = -INFINITY;
+    st.lsum = st.psum = st.zsum = 0.0f;
 
-    for (int c0 = 0; c0 < ctx; c0 += 256) {
-        // ---- issue every load of the chunk
-        const int t = c0 + tid;
-        const bool tk = t < ctx;
-        uint4_t kr[PIECES];
-        uint32_t kpar[G];
-        const uint8_t *kb = kc + ((size_t)(t >> 6) * PIECES * 64 + (t & 63)) * 16;
-#pragma unroll
-        for (int pc = 0; pc < PIECES; pc++)
-            kr[pc] = tk ? *reinterpret_cast<const uint4_t *>(kb + (size_t)pc * 64 * 16) : (uint4_t){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int gi = 0; gi < G; gi++)
-            kpar[gi] = tk ? kp[(size_t)t * G + gi] : 0u;
-        uint4_t vr[VIT];
-        uint32_t vpar[VIT];
-#pragma unroll
-        for (int j = 0; j < VIT; j++) {
-            const int tv = c0 + tid / VQ + VTOK * j;
-            const bool ok = tv < ctx;
-            vr[j] = ok ? *reinterpret_cast<const uint4_t *>(vc + (size_t)tv * CB + vq * 16) : (uint4_t){0u, 0u, 0u, 0u};
-            vpar[j] = ok ? vp[(size_t)tv * G + vgrp] : 0u;
-        }
-
-        // ---- scores of this chunk
-        float score = -INFINITY;
-        if (tk) {
-            score = 0.0f;
-#pragma unroll
-            for (int gi = 0; gi < G; gi++) {
-                float dot = 0.0f;
-#pragma unroll
-                for (int pc = 0; pc < 2; pc++) {
-#pragma unroll
-                    for (int w = 0; w < 4; w++) {
-                        const int qw = (2 * gi + pc) * 4 + w;
-#pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            dot = __builtin_amdgcn_fdot2(qv[4 * qw + j], centred_pair(kr[2 * gi + pc][w], j), dot,
-                                                         false);
-                    }
-                }
-                const float s = h2f((uint16_t)(kpar[gi] & 0xffff)), z = h2f((uint16_t)(kpar[gi] >> 16));
-                score += s * dot + (z + 8.0f * s) * qsum[gi];
-            }
-            score *= inv_sqrt_d;
-        }
-        const float m_new = fmaxf(m_run, block_max(score, red));
-        const float corr = __expf(m_run - m_new); // 0 on the first chunk
-        const float p = tk ? __expf(score - m_new) : 0.0f;
-        sp[tid] = p;
-        lsum = lsum * corr + p;
-        zacc *= corr;
-#pragma unroll
-        for (int e = 0; e < 32; e++)
-            acc[e] *= corr;
-        m_run = m_new;
-        __syncthreads();
-
-        // ---- values of this chunk: canonical bytes, byte b = elements 2b (low) and 2b+1 (high)
-#pragma unroll
-        for (int j = 0; j < VIT; j++) {
-            const float pr = sp[tid / VQ + VTOK * j];
-            const float ps = pr * h2f((uint16_t)(vpar[j] & 0xffff));
-            zacc += pr * h2f((uint16_t)(vpar[j] >> 16));
-#pragma unroll
-            for (int w = 0; w < 4; w++) {
-                const uint32_t lo = vr[j][w] & 0x0F0F0F0Fu, hi = (vr[j][w] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    acc[8 * w + 2 * b] += ps * (float)((lo >> (8 * b)) & 0xffu);
-                    acc[8 * w + 2 * b + 1] += ps * (float)((hi >> (8 * b)) & 0xffu);
-                }
-            }
-        }
-        __syncthreads(); // sp is rewritten by the next chunk
+    // chunks in pairs through two register buffers; loads of a chunk index
+    // past the context are clamped to its last position (cache hits)
+    KvChunk<L> ca, cb;
+    const int nchunks = (ctx + 63) / 64;
+    int c0 = 0;
+    load_chunk<D>(ca, 0, slot, pc, ctx, kc, vc, kp, vp);
+    for (int i = 0; i + 2 <= nchunks; i += 2, c0 += 128) {
+        load_chunk<D>(cb, c0 + 64, slot, pc, ctx, kc, vc, kp, vp);
+        attend_chunk<D>(ca, c0, slot, ctx, qa, qb, st);
+        load_chunk<D>(ca, c0 + 128, slot, pc, ctx, kc, vc, kp, vp);
+        attend_chunk<D>(cb, c0 + 64, slot, ctx, qa, qb, st);
     }
+    if (nchunks & 1)
+        attend_chunk<D>(ca, c0, slot, ctx, qa, qb, st);
 
-    // ---- reduce: lanes sharing vq (lane % VQ) within the wave, then the 4 waves in LDS
-    const float den = block_sum(lsum, red);
+    // remove the field offsets, add the zero term, sum over the wave's positions
+    const float den = reduce_slots<L>(st.lsum, OpAdd());
+    const float off = 1024.0f * st.psum;
+    float o[32];
 #pragma unroll
     for (int e = 0; e < 32; e++) {
-        float v = acc[e] + zacc;
-#pragma unroll
-        for (int o = VQ; o < 64; o <<= 1)
-            v += __shfl_xor(v, o, 64);
-        acc[e] = v;
+        const float f = (e & 1) ? 0.0625f : 1.0f;
+        o[e] = reduce_slots<L>((st.acc[e] - off) * f + st.zsum, OpAdd());
     }
-    if (lane < VQ) {
+    const float inv = 1.0f / den;
+    if (slot == 0) {
+        uint16_t *op = out + (int64_t)row * out_stride + (int64_t)head * D + pc * 32;
 #pragma unroll
-        for (int e = 0; e < 32; e++)
-            part[wave * D + lane * 32 + e] = acc[e];
-    }
-    __syncthreads();
-    if (tid < D) {
-        const float o = (part[tid] + part[D + tid]) + (part[2 * D + tid] + part[3 * D + tid]);
-        out[(int64_t)row * out_stride + (int64_t)head * D + tid] = f2h(o / den);
+        for (int w = 0; w < 4; w++) {
+            uint4_t pk;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                pk[i] = (uint32_t)f2h(o[8 * w + 2 * i] * inv) | ((uint32_t)f2h(o[8 * w + 2 * i + 1] * inv) << 16);
+            *reinterpret_cast<uint4_t *>(op + 8 * w) = pk;
+        }
     }
 }
 
@@ -215,7 +235,7 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
                                                       uint16_t *__restrict__ out, int64_t out_stride, int seq0,
                                                       int len, KvView kv)
 {
-    constexpr int CB = D / 2, PIECES = CB / 16, G = D / 64;
+    constexpr int CB = D / 2, G = D / 64;
     constexpr int DP = D + 2; // padded LDS row (halves)
     constexpr int DPV = 32;   // dims per thread in the PV product
     __shared__ half_t sq[64 * DP];
@@ -257,9 +277,8 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
             const int r = i / CB, byte = i % CB, pos = k0 + r;
             half_t k_lo = (half_t)0.0f, k_hi = (half_t)0.0f, v_lo = (half_t)0.0f, v_hi = (half_t)0.0f;
             if (pos < len) {
-                const int piece = byte >> 4, off = byte & 15, gi = byte / 32;
-                const uint8_t kb =
-                    kv.kc[slab * kv.cap * CB + (((size_t)(pos >> 6) * PIECES + piece) * 64 + (pos & 63)) * 16 + off];
+                const int gi = byte / 32;
+                const uint8_t kb = kv.kc[(slab * kv.cap + pos) * CB + byte];
                 const uint8_t vb = kv.vc[(slab * kv.cap + pos) * CB + byte];
                 const uint32_t kp = kv.kp[(slab * kv.cap + pos) * G + gi];
                 const uint32_t vp = kv.vp[(slab * kv.cap + pos) * G + gi];
@@ -341,11 +360,11 @@ hipError_t launch_attn_decode(const uint16_t *q, int64_t q_stride, uint16_t *out
 {
     if (rows == 0)
         return hipSuccess;
-    const dim3 grid((unsigned)rows * kv.heads), block(256);
+    const dim3 grid((unsigned)(((int64_t)rows * kv.heads + 3) / 4)), block(256);
     if (kv.head_dim == 128)
-        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, seq0, ctx, kv);
+        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, kv);
     else if (kv.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, seq0, ctx, kv);
+        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, kv);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

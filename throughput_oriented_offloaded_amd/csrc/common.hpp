@@ -39,6 +39,71 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// Cross-lane moves without LDS traffic. DPP quad permutations and row
+// rotations stay inside a 16-lane row; ds_swizzle exchanges across rows within
+// each half of the wave; lane ^ 32 goes through ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROR4 = 0x124;    // row_ror:4
+constexpr int DPP_ROR8 = 0x128;    // row_ror:8
+constexpr int DPP_HMIRROR = 0x141; // row_half_mirror: lane i of each 8 reads lane 7 - i
+__device__ __forceinline__ float swizzle_xor16(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float shfl_xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+struct OpAdd {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpMin {
+    __device__ float operator()(float a, float b) const { return fminf(a, b); }
+};
+
+// Combine over the lanes of each aligned group of 8 (all 8 lanes end with the result).
+template <class Op>
+__device__ __forceinline__ float reduce8(float v, Op op)
+{
+    v = op(v, dpp_move<DPP_XOR1>(v));
+    v = op(v, dpp_move<DPP_XOR2>(v));
+    return op(v, dpp_move<DPP_HMIRROR>(v));
+}
+
+// Combine over the lanes that share lane % L (L = 1, 2 or 4), i.e. across the
+// 64 / L slots of a wave whose lanes are grouped L at a time.
+template <int L, class Op>
+__device__ __forceinline__ float reduce_slots(float v, Op op)
+{
+    static_assert(L == 1 || L == 2 || L == 4, "L");
+    if constexpr (L == 1)
+        v = op(v, dpp_move<DPP_XOR1>(v));
+    if constexpr (L <= 2)
+        v = op(v, dpp_move<DPP_XOR2>(v));
+    v = op(v, dpp_move<DPP_ROR4>(v));
+    v = op(v, dpp_move<DPP_ROR8>(v));
+    v = op(v, swizzle_xor16(v));
+    return op(v, shfl_xor32(v));
+}
+
+// Combine within each aligned group of L lanes (L = 1, 2 or 4).
+template <int L, class Op>
+__device__ __forceinline__ float reduce_group(float v, Op op)
+{
+    if constexpr (L >= 2)
+        v = op(v, dpp_move<DPP_XOR1>(v));
+    if constexpr (L >= 4)
+        v = op(v, dpp_move<DPP_XOR2>(v));
+    return v;
+}
+
 // int4 packing inside the GEMM's tiled weight layout: a 32-bit word carries 8
 // consecutive reduction-axis elements e0..e7 with nibble p holding
 // e0 e2 e4 e6 e1 e3 e5 e7 (p = 0..7), so that (w >> 4j) & 0x000F000F yields
@@ -69,8 +134,8 @@ __device__ __forceinline__ uint32_t canonical_word_from_tiled(uint32_t t)
 // ---------------------------------------------------------------------------
 // KV cache view (one layer): for each (sequence, head) "slab" of `cap`
 // positions (cap % 64 == 0):
-//   K codes  : [cap/64][d/32][64 positions][16 B]  (16-B piece j of each
-//              position's d/2 code bytes, 64 positions side by side)
+//   K codes  : [cap][d/2]  canonical bytes (byte b holds elements 2b in the
+//              low nibble and 2b+1 in the high nibble)
 //   K params : [cap][d/64] x uint32 (scale in the low half, zero in the high)
 //   V codes  : [cap][d/2]  canonical bytes
 //   V params : [cap][d/64] x uint32

@@ -16,14 +16,14 @@ namespace {
 
 #pragma clang fp contract(off)
 
-struct QuantLane {
+// Parameters of one group from its minimum and maximum.
+struct GroupQ {
+    float mn, sf, rcp;
     uint16_t scale, zero;
-    int code;
 };
 
-__device__ __forceinline__ QuantLane quantize_lane(float x)
+__device__ __forceinline__ GroupQ group_quant(float mn, float mx)
 {
-    float mn = wave_min(x), mx = wave_max(x);
     // -0 and +0 are one value: a zero minimum is stored as +0, a zero range gives scale +0
     if (mn == 0.0f)
         mn = fabsf(mn);
@@ -32,22 +32,44 @@ __device__ __forceinline__ QuantLane quantize_lane(float x)
     const float range = mx - mn;
     const float s32 = range / 15.0f; // correctly rounded division
     const half_t s16 = (half_t)s32;  // round to nearest even
-    const float sf = (float)s16;
-    int c = 0;
-    if (sf != 0.0f) {
-        const float d = x - mn;
-        c = (int)(d / sf + 0.5f);
-        c = c < 0 ? 0 : (c > 15 ? 15 : c);
-        // exact settlement: c = #{k in 0..14 : d >= (k + 1/2) * scale}
-        while (c < 15 && d >= ((float)c + 0.5f) * sf)
-            c++;
-        while (c > 0 && d < ((float)c - 0.5f) * sf)
-            c--;
-    }
+    GroupQ g;
+    g.mn = mn;
+    g.sf = (float)s16;
+    g.rcp = g.sf != 0.0f ? __builtin_amdgcn_rcpf(g.sf) : 0.0f; // estimate only
+    g.scale = __builtin_bit_cast(uint16_t, s16);
+    g.zero = f2h(mn); // exact: mn is one of the fp16 inputs
+    return g;
+}
+
+// Code of x: the number of k in 0..14 with fl32(x - mn) >= (k + 1/2) * scale.
+// In exact arithmetic that count is clamp(floor(d/scale + 1/2), 0, 15) with
+// d = fl32(x - mn) >= 0. The estimate from the approximate reciprocal is off
+// by at most one (d/scale <= 15.01 and the relative error is below 2^-21), and
+// one exact threshold test in each direction settles it: the thresholds are
+// exact in fp32 (an fp16 scale times a 5-bit multiple of 1/2).
+__device__ __forceinline__ int code_of(float x, const GroupQ &g)
+{
+    const float d = x - g.mn;
+    int c = (int)(d * g.rcp + 0.5f);
+    c = c < 0 ? 0 : (c > 15 ? 15 : c);
+    c += (c < 15 && d >= ((float)c + 0.5f) * g.sf) ? 1 : 0;
+    c -= (c > 0 && d < ((float)c - 0.5f) * g.sf) ? 1 : 0;
+    return g.sf == 0.0f ? 0 : c;
+}
+
+struct QuantLane {
+    uint16_t scale, zero;
+    int code;
+};
+
+// One wavefront per group: lane i holds element i.
+__device__ __forceinline__ QuantLane quantize_lane(float x)
+{
+    const GroupQ g = group_quant(wave_min(x), wave_max(x));
     QuantLane q;
-    q.scale = __builtin_bit_cast(uint16_t, s16);
-    q.zero = f2h(mn); // exact: mn is one of the fp16 inputs
-    q.code = c;
+    q.scale = g.scale;
+    q.zero = g.zero;
+    q.code = code_of(x, g);
     return q;
 }
 
@@ -145,17 +167,18 @@ __global__ void __launch_bounds__(256) k_unpack_w4(const uint32_t *__restrict__ 
     }
 }
 
-// One wave per (row, head, group, K-or-V). The new token's K goes to the
-// position-chunked layout, its V to the canonical layout.
+// Eight lanes per (row, head, group, K or V), eight consecutive elements per
+// lane: one 16-byte load, min/max over the group by DPP, and one 32-bit store
+// of the lane's four code bytes into the canonical per-position layout.
 __global__ void __launch_bounds__(256) k_kv_append(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
                                                    SrcMap src_map, int rows, RowMap map, KvView kv)
 {
-    const int lane = threadIdx.x & 63;
     const int G = kv.head_dim / 64;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
+    const int part = threadIdx.x & 7;
     const int64_t total = (int64_t)rows * kv.heads * G * 2;
     if (item >= total)
-        return;
+        return; // all eight lanes of an item leave together
     const int isv = (int)(item & 1);
     int64_t rest = item >> 1;
     const int g = (int)(rest % G);
@@ -166,24 +189,28 @@ __global__ void __launch_bounds__(256) k_kv_append(const uint16_t *__restrict__ 
     const int pos = map.pos0 + row % map.rows_per_seq;
     const uint16_t *src = (isv ? v : k) + (int64_t)(row / map.rows_per_seq) * src_map.seq_stride +
                           (int64_t)(row % map.rows_per_seq) * src_map.pos_stride +
-                          (int64_t)head * src_map.head_stride + g * 64;
-    const QuantLane q = quantize_lane(h2f(src[lane]));
-    const uint8_t b = pack_pair(q.code);
-    const size_t slab = kv_slab(kv, seq, head);
-    const int cb = kv.head_dim / 2; // code bytes per position
-    if ((lane & 1) == 0) {
-        const int byte = g * 32 + (lane >> 1);
-        if (isv) {
-            kv.vc[(slab * kv.cap + pos) * cb + byte] = b;
-        } else {
-            const int piece = byte >> 4, off = byte & 15;
-            const size_t chunk = (size_t)(pos >> 6);
-            kv.kc[slab * kv.cap * cb + ((chunk * (cb / 16) + piece) * 64 + (pos & 63)) * 16 + off] = b;
-        }
+                          (int64_t)head * src_map.head_stride + g * 64 + part * 8;
+    const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(src));
+    float x[8];
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        x[e] = (float)h[e];
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
     }
-    if (lane == 0) {
+    const GroupQ q = group_quant(reduce8(mn, OpMin()), reduce8(mx, OpMax()));
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+        word |= (uint32_t)code_of(x[e], q) << (4 * e);
+    const size_t at = kv_slab(kv, seq, head) * kv.cap + pos;
+    const int cb = kv.head_dim / 2; // code bytes per position
+    uint8_t *codes = isv ? kv.vc : kv.kc;
+    *reinterpret_cast<uint32_t *>(codes + at * cb + g * 32 + part * 4) = word;
+    if (part == 0) {
         uint32_t *pp = isv ? kv.vp : kv.kp;
-        pp[(slab * kv.cap + pos) * G + g] = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
+        pp[at * G + g] = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
     }
 }
 
@@ -197,8 +224,7 @@ __global__ void k_kv_export(KvView kv, int seq, int head, int t0, int n, uint8_t
         return;
     const int t = (int)(i / cb), byte = (int)(i % cb), pos = t0 + t;
     const size_t slab = kv_slab(kv, seq, head);
-    const int piece = byte >> 4, off = byte & 15;
-    kc[i] = kv.kc[slab * kv.cap * cb + (((size_t)(pos >> 6) * (cb / 16) + piece) * 64 + (pos & 63)) * 16 + off];
+    kc[i] = kv.kc[(slab * kv.cap + pos) * cb + byte];
     vc[i] = kv.vc[(slab * kv.cap + pos) * cb + byte];
     if (byte < G) {
         const uint32_t a = kv.kp[(slab * kv.cap + pos) * G + byte];
@@ -259,7 +285,7 @@ hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, SrcMap src, in
     const int64_t items = (int64_t)rows * kv.heads * (kv.head_dim / 64) * 2;
     if (items == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_kv_append, dim3(blocks_for(items, 4)), dim3(256), 0, st, k, v, src, rows, map, kv);
+    hipLaunchKernelGGL(k_kv_append, dim3(blocks_for(items, 32)), dim3(256), 0, st, k, v, src, rows, map, kv);
     return hipGetLastError();
 }
 

@@ -883,6 +883,8 @@ int profile_read(tod_model *m, int kind, double *total_ms, int64_t *launches)
     return TOD_OK;
 }
 
+inline bool misaligned16(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
 int attn_cache_create(int batch, int heads, int head_dim, int cap, tod_attn_cache **out)
 {
     if (!out)
@@ -917,6 +919,8 @@ int attn_cache_fill(tod_attn_cache *c, const uint16_t *d_k, const uint16_t *d_v,
 {
     if (!c || !d_k || !d_v || t0 < 0 || n < 0 || t0 + n > c->kv.cap)
         return fail(TOD_EINVAL, "bad attention cache fill");
+    if (misaligned16(d_k) || misaligned16(d_v))
+        return fail(TOD_EINVAL, "K/V buffers must be 16-byte aligned");
     // time-major input [n][batch][heads][d]: row r = (sequence r / n, position t0 + r % n)
     const int d = c->kv.head_dim, H = c->kv.heads;
     const SrcMap src = {(int64_t)H * d, (int64_t)c->batch * H * d, d};
@@ -932,6 +936,8 @@ int attn_decode_step(tod_attn_cache *c, int pos, const uint16_t *d_q, const uint
         return fail(TOD_EINVAL, "null argument");
     if (pos < 0 || pos >= c->kv.cap)
         return fail(TOD_ESTATE, "position %d outside the cache (capacity %d)", pos, c->kv.cap);
+    if (misaligned16(d_q) || misaligned16(d_k_new) || misaligned16(d_v_new) || misaligned16(d_out))
+        return fail(TOD_EINVAL, "q, k, v and out buffers must be 16-byte aligned");
     const int d = c->kv.head_dim, H = c->kv.heads;
     const SrcMap src = {(int64_t)H * d, 0, d};
     const RowMap map = {0, 1, pos};
