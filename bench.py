@@ -110,6 +110,55 @@ def cpu_baseline(w, rows=64):
                        f"{rows} / ({shape.n_layers} * t_layer + t_lm)")}
 
 
+# HBM traffic of the dominant kernel, measured separately with rocprofv3 counters
+# (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the same counters on a plain
+# copy of known size) and kept with the profiles. It is reported only while the
+# kernel's sources are unchanged since the counters were taken.
+TRAFFIC_FILES = {"k_attn_decode<128>": ("profiles/k_attn_decode_opt30b_counters.txt",
+                                        ("throughput_oriented_offloaded_amd/csrc/attn.hip",
+                                         "throughput_oriented_offloaded_amd/csrc/common.hpp"))}
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """Bytes per launch from the counter summary, or None if absent or stale."""
+    if kernel not in TRAFFIC_FILES:
+        return None
+    summary, sources = TRAFFIC_FILES[kernel]
+    try:
+        with open(os.path.join(ROOT, summary)) as f:
+            fields = dict(line.split(":", 1) for line in f if line.startswith(("traffic_bytes_per_launch:",
+                                                                               "source_sha256:")))
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != source_digest(sources):
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(mib):
+    """A plain device copy of known size, for calibrating the HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.bitwise_not(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +166,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="opt-30b")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path (see the design notes on "
@@ -124,6 +175,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import synth
     import throughput_oriented_offloaded_amd as tod
@@ -212,8 +267,10 @@ def main():
     dom = max((k for k in kernels if "frac" in kernels[k]), key=lambda k: kernels[k]["share"])
     d = kernels[dom]
     if d["bound"] == "hbm":
+        kname = f"k_attn_decode<{shape.head_dim}>"
         roof = {"bound": "hbm", "achieved": d["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["frac"], "traffic": None, "kernel": "k_attn_decode<128>"}
+                "frac": d["frac"], "traffic": measured_traffic(kname) if w.name == "opt-30b" else None,
+                "kernel": kname}
     else:
         roof = {"bound": "mfma", "achieved": d["achieved_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": d["frac"], "traffic": None, "kernel": f"k_gemm ({dom})"}
