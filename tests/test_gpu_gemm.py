@@ -30,6 +30,8 @@ def _gpu_codes(w16, torch):
 CASES = [  # rows, in, out, epilogue
     (1, 64, 32, "bias"), (13, 192, 96, "res"), (64, 768, 2304, "relu"), (100, 768, 768, "none"),
     (129, 256, 160, "res"), (300, 1024, 256, "bias"), (512, 3072, 768, "res"), (37, 4096, 64, "relu"),
+    # pipelined kernel with ragged M and N tiles, split along K
+    (300, 1280, 480, "relu"), (640, 2048, 1056, "res"), (257, 4096, 288, "bias"),
 ]
 
 
@@ -119,3 +121,23 @@ def test_full_size_opt30b_decode_gemms(name):
     u = ulps(to_np16(y)[sample], ref)
     assert u.max() <= 2, f"max {u.max()} ulp"
     assert (u == 0).mean() > 0.99
+
+
+def test_split_k_is_repeatable():
+    """Split-K partials are reduced in a fixed order, so repeated launches give identical bits."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    rows, k, n = 512, 3072, 768
+    a = synth.normal_f16(41, 1, (rows, k), 0.0, 1.0)
+    w = synth.normal_f16(41, 2, (n, k), 0.0, 0.02)
+    codes, scale, zero = _gpu_codes(w, torch)
+    ad = to_dev(a, torch)
+    outs = []
+    for _ in range(4):
+        y = torch.empty((rows, n), dtype=torch.float16, device="cuda")
+        tod.linear_w4(ad, codes, scale, zero, n, y)
+        torch.cuda.synchronize()
+        outs.append(to_np16(y))
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint16), outs[0].view(np.uint16))
+

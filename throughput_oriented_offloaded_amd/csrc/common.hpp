@@ -105,29 +105,28 @@ __device__ __forceinline__ float reduce_group(float v, Op op)
 }
 
 // int4 packing inside the GEMM's tiled weight layout: a 32-bit word carries 8
-// consecutive reduction-axis elements e0..e7 with nibble p holding
-// e0 e2 e4 e6 e1 e3 e5 e7 (p = 0..7), so that (w >> 4j) & 0x000F000F yields
-// the ordered pair (e_2j, e_2j+1) in the two 16-bit halves.
+// consecutive reduction-axis elements e0..e7; the low nibbles of its four
+// bytes hold e0, e1, e2, e3 and the high nibbles e4, e5, e6, e7 (nibble slot p
+// holds e_(p/2) for even p and e_(4+p/2) for odd p). Masking the low (or
+// shifted high) nibbles leaves bytes whose pairs (bytes 0,1 and 2,3) are the
+// ordered element pairs the MFMA operand needs.
+__device__ __forceinline__ int tiled_slot(int e) { return e < 4 ? 2 * e : 2 * (e - 4) + 1; }
+
 __device__ __forceinline__ uint32_t tiled_word_from_canonical(uint32_t c)
 {
     // canonical: nibble p holds element p
     uint32_t r = 0;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const uint32_t v = (c >> (4 * e)) & 15u;
-        const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
-        r |= v << (4 * p);
-    }
+    for (int e = 0; e < 8; e++)
+        r |= ((c >> (4 * e)) & 15u) << (4 * tiled_slot(e));
     return r;
 }
 __device__ __forceinline__ uint32_t canonical_word_from_tiled(uint32_t t)
 {
     uint32_t r = 0;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-        const int p = (e & 1) ? 4 + (e >> 1) : (e >> 1);
-        r |= ((t >> (4 * p)) & 15u) << (4 * e);
-    }
+    for (int e = 0; e < 8; e++)
+        r |= ((t >> (4 * tiled_slot(e))) & 15u) << (4 * e);
     return r;
 }
 

@@ -44,19 +44,24 @@ __device__ __forceinline__ int xcd_tile(int b, int total)
     return x * q + (x < r ? x : r) + k;
 }
 
+// Eight weights of one tiled word (nibble slots 0,2,4,6 hold e0..e3 and slots
+// 1,3,5,7 hold e4..e7, see tiled_word_from_canonical). A byte 0000cccc read as
+// fp8 e4m3 is exactly c * 2^-9 (subnormal for c < 8, exponent 1 above), so one
+// v_cvt_scalef32_pk_f16_fp8 with scale 2^9 turns two masked bytes into two
+// exact fp16 codes; one v_pk_fma_f16 with (scale, zero) then rounds once, so
+// each weight equals fp16(zero + c*scale).
 __device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t s2, half2_t z2)
 {
-    const half2_t bias = {(half_t)1024.0f, (half_t)1024.0f};
-    half8_t out;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const uint32_t u = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-        const half2_t c = __builtin_bit_cast(half2_t, u) - bias; // exact codes
-        const half2_t x = __builtin_elementwise_fma(c, s2, z2);  // one rounding
-        out[2 * j] = x[0];
-        out[2 * j + 1] = x[1];
-    }
-    return out;
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const half2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
+    const half2_t c23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
+    const half2_t c45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
+    const half2_t c67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
+    const half2_t x01 = __builtin_elementwise_fma(c01, s2, z2);
+    const half2_t x23 = __builtin_elementwise_fma(c23, s2, z2);
+    const half2_t x45 = __builtin_elementwise_fma(c45, s2, z2);
+    const half2_t x67 = __builtin_elementwise_fma(c67, s2, z2);
+    return (half8_t){x01[0], x01[1], x23[0], x23[1], x45[0], x45[1], x67[0], x67[1]};
 }
 
 template <int BM, int BN, bool INT4, int MINW>
@@ -229,24 +234,26 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 }
 
 // ---------------------------------------------------------------------------
-// int4 GEMM for M > 128: 256 x 128 workgroup tile (four 256 x 32 wave tiles),
-// fed through a 4-stage LDS ring that direct-to-LDS loads
-// (global_load_lds_dwordx4) fill three K-groups ahead of the MFMAs, so HBM
-// latency of the weight stream is covered without staging registers. A wave
-// dequantizes its 32 columns once for all 256 rows. Stage synchronisation is
-// an explicit vmcnt wait on the wave's own loads plus a workgroup barrier.
+// int4 GEMM for M > 128: 256 x 256 workgroup tiles, eight wavefronts (two per
+// SIMD) as a 2 x 4 grid of 128 x 64 wave tiles, fed through a 3-stage LDS ring
+// that direct-to-LDS loads (global_load_lds_dwordx4) fill two K-groups ahead
+// of the MFMAs, so the weight stream's HBM latency is covered without staging
+// registers. With two waves per SIMD one wave's LDS reads and dequantization
+// run while the other's MFMAs issue. Stage synchronisation is an explicit
+// vmcnt wait on the wave's own loads plus a workgroup barrier.
 // ---------------------------------------------------------------------------
 namespace w4 {
-constexpr int BM = 256;
-constexpr int A_BYTES = BM * 128; // BM rows x 64 fp16, 16-byte chunks swizzled by row
-template <int BN> struct Cfg {
-    static constexpr int NB = BN / 128;               // 32-column blocks per wave (4 waves side by side)
-    static constexpr int S = BN == 128 ? 4 : 3;       // LDS ring stages
-    static constexpr int W_BYTES = (BN / 32) * 1024;  // per column block: 64 lanes x 16 B of codes
-    static constexpr int P_BYTES = (BN / 32) * 256;   // per column block: 64 x (scale, zero), lanes 32..63 repeat
-    static constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
-    static constexpr int LPS = BM / 32 + 2 * NB;      // loads per wave per stage
-};
+constexpr int BM = 256, BN = 256, WAVES = 8;
+constexpr int RB = BM / 2;                   // rows per wave (2 wave rows)
+constexpr int MB = RB / 32;                  // 32-row blocks per wave
+constexpr int NB = 2;                        // 32-column blocks per wave (4 wave columns)
+constexpr int A_BYTES = BM * 128;            // BM rows x 64 fp16, 16-byte chunks swizzled by row
+constexpr int W_BYTES = (BN / 32) * 1024;    // per column block: 64 lanes x 16 B of codes
+constexpr int P_BYTES = (BN / 32) * 256;     // per column block: 64 x (scale, zero), lanes 32..63 repeat
+constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
+constexpr int S = 3;                         // ring stages
+constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
+constexpr int LPS = AL + 2;                  // loads per wave per stage: A chunks, one code block, one param block
 } // namespace w4
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -257,31 +264,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 // a ds_read_b128 (rows r..r+15, one chunk column) touch distinct banks.
 __device__ __forceinline__ int a_pos(int row, int ch) { return ch ^ ((row ^ (row >> 3)) & 7); }
 
-// Wait until at most younger * LPS of this wave's vector-memory loads are outstanding.
-template <int LPS>
+// Wait until at most `younger` stages' worth (LPS loads each) of this wave's
+// vector-memory loads are outstanding (younger is 0 or 1 with three stages).
 __device__ __forceinline__ void wait_vm_loads(int younger)
 {
     // s_waitcnt simm16 on gfx9: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-    constexpr int n1 = LPS, n2 = 2 * LPS;
+    constexpr int n1 = w4::LPS;
     constexpr int e1 = (n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8);
-    constexpr int e2 = (n2 & 15) | ((n2 >> 4) << 14) | (7 << 4) | (15 << 8);
-    static_assert(n2 < 64, "vmcnt holds 6 bits");
-    if (younger >= 2)
-        __builtin_amdgcn_s_waitcnt(e2);
-    else if (younger == 1)
+    static_assert(n1 < 64, "vmcnt holds 6 bits");
+    if (younger >= 1)
         __builtin_amdgcn_s_waitcnt(e1);
     else
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <int BN>
-__global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
+__global__ void __launch_bounds__(512, 1) k_gemm_w4(GemmArgs g, TileMap tm)
 {
     using namespace w4;
-    using C = Cfg<BN>;
-    constexpr int MB = BM / 32, NB = C::NB, S = C::S, STAGE = C::STAGE;
-    // each wave owns NB 32-column blocks and all BM rows: its weights are
-    // dequantized once and feed BM/32 MFMAs per K-step and column block
     __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
 
     const int tile = xcd_tile(blockIdx.x, tm.total);
@@ -298,29 +297,37 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
     const int nst = g1 - g0;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3; // wave tile: rows wm*128.., column blocks wn*2..
+
+    // Loads of one stage: wave w brings A chunks w, w+8, w+16, w+24 (8 rows
+    // each), and the codes and params of column block w. Per-lane byte offsets
+    // are fixed for the whole K loop; the per-group part of each address is
+    // wave-uniform, so the LDS destinations (m0) are scalar.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t a_off[AL];
+#pragma unroll
+    for (int i = 0; i < AL; i++) {
+        const int row = 8 * (wv + WAVES * i) + (lane >> 3);
+        const int ch = a_pos(row, lane & 7); // global chunk landing at LDS position lane & 7
+        const int m = min(m0 + row, g.M - 1);
+        a_off[i] = (uint32_t)((m - m0) * g.lda + ch * 8) * 2u;
+    }
+    const int nbw = min((n0 >> 5) + wv, (g.N >> 5) - 1); // clamped: blocks past N feed discarded columns
+    const uint8_t *a_tile = reinterpret_cast<const uint8_t *>(g.a + (int64_t)m0 * g.lda);
+    const uint8_t *wc8 = reinterpret_cast<const uint8_t *>(g.wc);
+    const uint8_t *wp8 = reinterpret_cast<const uint8_t *>(g.wp);
 
     auto issue = [&](int buf, int grp) {
         uint8_t *base = smem + buf * STAGE;
+        const uint8_t *ag = a_tile + grp * (KG_ELEMS * 2);
 #pragma unroll
-        for (int i = 0; i < BM / 32; i++) {
-            const int q = wave + 4 * i;                 // 1 KiB chunk = rows 8q .. 8q+7
-            const int row = 8 * q + (lane >> 3);
-            const int ch = a_pos(row, lane & 7);         // global chunk landing at position lane & 7
-            const int m = min(m0 + row, g.M - 1);
-            __builtin_amdgcn_global_load_lds(g.a + (int64_t)m * g.lda + grp * KG_ELEMS + ch * 8,
-                                             (lds_void *)(base + q * 1024), 16, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < NB; j++) {
-            const int cb = wave * NB + j; // column block within the tile
-            // clamped: blocks past N feed discarded columns
-            const int nb = min((n0 >> 5) + cb, (g.N >> 5) - 1);
-            const int64_t blk = (int64_t)nb * KG + grp;
-            __builtin_amdgcn_global_load_lds(g.wc + (blk * 64 + lane) * 4, (lds_void *)(base + A_BYTES + cb * 1024),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(g.wp + blk * 32 + (lane & 31),
-                                             (lds_void *)(base + A_BYTES + C::W_BYTES + cb * 256), 4, 0, 0);
-        }
+        for (int i = 0; i < AL; i++)
+            __builtin_amdgcn_global_load_lds(ag + a_off[i], (lds_void *)(base + (wv + WAVES * i) * 1024), 16, 0, 0);
+        const int64_t blk = (int64_t)nbw * KG + grp;
+        __builtin_amdgcn_global_load_lds(wc8 + blk * 1024 + lane * 16, (lds_void *)(base + A_BYTES + wv * 1024), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds(wp8 + blk * 128 + (lane & 31) * 4,
+                                         (lds_void *)(base + A_BYTES + W_BYTES + wv * 256), 4, 0, 0);
     };
 
     float16_t acc[MB][NB];
@@ -338,8 +345,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
             issue(s_, g0 + s_);
 
     for (int it = 0; it < nst; it++) {
-        const int younger = min(S - 2, nst - 1 - it);
-        wait_vm_loads<C::LPS>(younger);
+        wait_vm_loads(min(S - 2, nst - 1 - it));
         __builtin_amdgcn_s_barrier();
         if (it + S - 1 < nst)
             issue((it + S - 1) % S, g0 + it + S - 1);
@@ -348,21 +354,20 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
         half2_t s2[NB], z2[NB];
 #pragma unroll
         for (int j = 0; j < NB; j++) {
-            const int cb = wave * NB + j;
+            const int cb = wn * NB + j;
             bw[j] = *reinterpret_cast<const uint4_t *>(base + A_BYTES + cb * 1024 + lane * 16);
-            const uint32_t bp = *reinterpret_cast<const uint32_t *>(base + A_BYTES + C::W_BYTES + cb * 256 +
-                                                                    (lane & 31) * 4);
+            const uint32_t bp =
+                *reinterpret_cast<const uint32_t *>(base + A_BYTES + W_BYTES + cb * 256 + (lane & 31) * 4);
             s2[j] = __builtin_bit_cast(half2_t, (bp & 0xffffu) * 0x10001u);
             z2[j] = __builtin_bit_cast(half2_t, (bp >> 16) * 0x10001u);
         }
-        // Software pipeline over the four K-steps: the A operands (LDS) and the
-        // dequantized weights of step t+1 are produced while the MFMAs of step t
-        // run; sched_barrier keeps the compiler from sinking the LDS reads next
-        // to their MFMAs, where their latency would be exposed.
+        // Four K-steps of 16: the A operands of step t+1 (LDS) and its dequantized
+        // weights are produced before the MFMAs of step t; the other wave on the
+        // SIMD fills the gaps.
         half8_t a_cur[MB], a_nxt[MB], b_cur[NB], b_nxt[NB];
 #pragma unroll
         for (int i = 0; i < MB; i++) {
-            const int row = i * 32 + (lane & 31);
+            const int row = wm * RB + i * 32 + (lane & 31);
             a_cur[i] = *reinterpret_cast<const half8_t *>(base + row * 128 + (a_pos(row, lane >> 5) << 4));
         }
 #pragma unroll
@@ -373,7 +378,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
             if (t < 3) {
 #pragma unroll
                 for (int i = 0; i < MB; i++) {
-                    const int row = i * 32 + (lane & 31);
+                    const int row = wm * RB + i * 32 + (lane & 31);
                     a_nxt[i] = *reinterpret_cast<const half8_t *>(base + row * 128 +
                                                                   (a_pos(row, 2 * (t + 1) + (lane >> 5)) << 4));
                 }
@@ -386,16 +391,6 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
 #pragma unroll
                 for (int j = 0; j < NB; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[i], b_cur[j], acc[i][j], 0, 0, 0);
-            if (t < 3) {
-                // interleave: one MFMA, then LDS reads and dequant VALU of the next step
-#pragma unroll
-                for (int k = 0; k < MB * NB; k++) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, MB / (MB * NB) > 0 ? 1 : 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4 / NB, 0);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < MB; i++)
                 a_cur[i] = a_nxt[i];
@@ -411,11 +406,12 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
     // runs. The ring is free once every wave has left the main loop.
     __syncthreads();
     constexpr int SROW = 36; // padded scratch row (floats)
+    static_assert(WAVES * 32 * SROW * 4 <= STAGE, "scratch fits the first stage");
     float *scr = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
     const int lr = lane >> 1, c0 = (lane & 1) * 16;
 #pragma unroll
     for (int j = 0; j < NB; j++) {
-        const int gcol = n0 + (wave * NB + j) * 32 + c0;
+        const int gcol = n0 + (wn * NB + j) * 32 + c0;
         const bool colok = gcol < g.N; // N is a multiple of 32 on this path
         float bias[16];
 #pragma unroll
@@ -449,7 +445,7 @@ __global__ void __launch_bounds__(256, 1) k_gemm_w4(GemmArgs g, TileMap tm)
             }
             __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 0xc00f); // lgkmcnt(0): scratch read
             __builtin_amdgcn_wave_barrier();
-            const int grow = m0 + i * 32 + lr;
+            const int grow = m0 + wm * RB + i * 32 + lr;
             if (!colok || grow >= g.M)
                 continue;
             if (tm.splits > 1) {
@@ -511,11 +507,10 @@ struct Plan {
 };
 
 // Tuning overrides (read once): TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" selects the
-// register-staged kernel for every M > 64; TOD_GEMM_BN = 128 | 256 sets the column tile of
-// the LDS-pipelined int4 kernel; TOD_GEMM_SPLIT = workgroup count below which the K loop
-// is split in two, four, ...
+// register-staged kernel for every M > 64; TOD_GEMM_SPLIT = workgroup count below which the
+// K loop is split.
 struct Tuning {
-    int bm = 0, bn = 0, bn_pipe = 0, split_fill = -1;
+    int bm = 0, bn = 0, split_fill = -1;
     Tuning()
     {
         if (const char *t = getenv("TOD_GEMM_TILE")) {
@@ -525,11 +520,6 @@ struct Tuning {
                 bm = a;
                 bn = b;
             }
-        }
-        if (const char *t = getenv("TOD_GEMM_BN")) {
-            const int v = atoi(t);
-            if (v == 128 || v == 256)
-                bn_pipe = v;
         }
         if (const char *t = getenv("TOD_GEMM_SPLIT"))
             split_fill = atoi(t);
@@ -552,7 +542,7 @@ Plan plan_gemm(int M, int N, int K, bool int4)
         // which is what bounds this GEMM (L2 -> LDS traffic), at the price of
         // fewer workgroups; narrow N is split along K instead.
         p.bm = w4::BM;
-        p.bn = tu.bn_pipe ? tu.bn_pipe : 256;
+        p.bn = w4::BN;
     } else if (M <= 64) {
         // 128 x 128 tiles keep a wave at ~150 registers, so three workgroups share a
         // CU and hide each other's load latency.
@@ -602,10 +592,8 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         p.tm.total = p.tm.mt * p.tm.nt;
     }
     const dim3 grid(p.tm.total), block(256);
-    if (p.pipelined && p.bn == 256)
-        hipLaunchKernelGGL(k_gemm_w4<256>, grid, block, 0, st, g, p.tm);
-    else if (p.pipelined)
-        hipLaunchKernelGGL(k_gemm_w4<128>, grid, block, 0, st, g, p.tm);
+    if (p.pipelined)
+        hipLaunchKernelGGL(k_gemm_w4, grid, dim3(64 * w4::WAVES), 0, st, g, p.tm);
     else {
 #define TOD_GEMM_CASE(BM_, BN_, MINW_)                                                               \
     if (p.bm == BM_ && p.bn == BN_) {                                                                \
