@@ -68,9 +68,9 @@ enum { TOD_MAT_Q = 0, TOD_MAT_K, TOD_MAT_V, TOD_MAT_O, TOD_MAT_FC1, TOD_MAT_FC2 
 
 typedef struct tod_model tod_model;
 
-/* OPT decoder stack shape. hidden = n_heads * head_dim; head_dim % 64 == 0;
- * hidden % 64 == 0; ffn % 64 == 0; max_pos = rows of the position table
- * minus the two offset rows. */
+/* OPT decoder stack shape. hidden = n_heads * head_dim; head_dim is 64 or
+ * 128; hidden % 64 == 0 and hidden <= 16384; ffn % 64 == 0; max_pos = rows of
+ * the position table minus the two offset rows. */
 typedef struct {
     int32_t n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos;
 } tod_model_config;
@@ -148,6 +148,17 @@ int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, 
  * the cache from that position on. Lets a caller replay decode steps.
  */
 int set_decode_position(tod_model *m, int block, int steps);
+
+/*
+ * set_decode_graph: with enable != 0 (the default) decode_block on the HBM
+ * tier captures one decode step of each block into a HIP graph at its first
+ * use and replays it per step on a stream of the model's own, ordered after
+ * the caller's stream and before its later work; the step reads its position
+ * and token ids from device memory, so one graph serves every step. Outputs
+ * are identical to the step-by-step launches, which run instead when enable is
+ * 0, on the host tier, while profile_kernels is active, or if capture fails.
+ */
+int set_decode_graph(tod_model *m, int enable);
 
 /*
  * quantize_groupwise: group-wise int4 quantization of d_x fp16 [n] into the

@@ -214,6 +214,50 @@ def test_decode_is_deterministic_and_replayable():
     m.close()
 
 
+@pytest.mark.parametrize("blocks", [1, 2])
+def test_graph_decode_matches_step_launches(blocks):
+    """Captured decode steps (one graph per block, replayed) give the same bits as
+    step-by-step launches: every replay is checked, with eager work and device
+    synchronisations between the replays, across two blocks sharing the model."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_125M.replace(n_layers=3)
+    s, g = 20, 7
+    run = dict(gpu_batch=3, batches_per_block=2, prompt_len=s, gen_len=g, n_blocks=blocks)
+    m, _ = build_gpu_model(shape, run)
+    rows = 6
+    ref = {}
+    for blk in range(blocks):
+        prompts = to_dev(synth.prompt_ids(rows, s, shape.vocab, seed=1 + blk), torch)
+        first = torch.empty(rows, dtype=torch.int32, device="cuda")
+        tod.prefill(m.handle, blk, prompts, first)
+        tod.set_decode_graph(m.handle, False)
+        out = torch.empty((g - 1, rows), dtype=torch.int32, device="cuda")
+        lg = torch.empty((g - 1, rows, shape.vocab), dtype=torch.float16, device="cuda")
+        tod.decode_block(m.handle, blk, g - 1, first, out, lg)
+        torch.cuda.synchronize()
+        ref[blk] = (first, out.clone(), lg.clone())
+    tod.set_decode_graph(m.handle, True)
+    for blk in range(blocks):
+        first, out_ref, lg_ref = ref[blk]
+        tod.set_decode_position(m.handle, blk, 0)
+        ids = first
+        done = 0
+        for n in (1, 2, g - 4):  # several calls, replays in each
+            out = torch.empty((n, rows), dtype=torch.int32, device="cuda")
+            lg = torch.empty((n, rows, shape.vocab), dtype=torch.float16, device="cuda")
+            tod.decode_block(m.handle, blk, n, ids, out, lg)
+            scratch = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(out, out_ref[done:done + n]), f"block {blk} steps {done}..{done + n - 1}"
+            assert torch.equal(lg.view(torch.int16), lg_ref[done:done + n].view(torch.int16))
+            ids = out[-1].contiguous()
+            done += n
+        assert done == g - 1
+        del scratch
+    m.close()
+
+
 def test_state_errors():
     torch = torch_cuda()
     import throughput_oriented_offloaded_amd as tod

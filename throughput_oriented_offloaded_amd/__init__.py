@@ -11,12 +11,12 @@ from . import _lib
 from ._lib import (TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM, TodError, attn_cache_create, attn_cache_export,
                    attn_cache_fill, attn_cache_free, attn_decode_step, decode_block, dequantize_groupwise,
                    export_kv, export_weight, free_model, init_model, last_error, linear_f16, linear_w4, prefill,
-                   profile_kernels, profile_read, quantize_groupwise, set_decode_position, set_global_weights,
-                   set_layer_weights)
+                   profile_kernels, profile_read, quantize_groupwise, set_decode_graph, set_decode_position,
+                   set_global_weights, set_layer_weights)
 
 __all__ = ["Model", "TodError", "init_model", "set_global_weights", "set_layer_weights", "prefill",
-           "decode_block", "set_decode_position", "quantize_groupwise", "dequantize_groupwise", "free_model",
-           "last_error", "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create",
+           "decode_block", "set_decode_position", "set_decode_graph", "quantize_groupwise", "dequantize_groupwise",
+           "free_model", "last_error", "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create",
            "attn_cache_fill", "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels",
            "profile_read",
            "TOD_W_HBM_INT4", "TOD_W_HOST_FP16_STREAM"]

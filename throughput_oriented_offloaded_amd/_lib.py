@@ -23,7 +23,8 @@ LAYER_TENSORS = ("ln1_g", "ln1_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b",
                  "o_w", "o_b", "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
 
 EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", "decode_block",
-            "set_decode_position", "quantize_groupwise", "dequantize_groupwise", "free_model", "last_error",
+            "set_decode_position", "set_decode_graph", "quantize_groupwise", "dequantize_groupwise", "free_model",
+            "last_error",
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
             "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read")
 KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
@@ -62,6 +63,7 @@ def lib() -> ctypes.CDLL:
         "prefill": [vp, i32, vp, vp, vp, vp],
         "decode_block": [vp, i32, i32, vp, vp, vp, vp],
         "set_decode_position": [vp, i32, i32],
+        "set_decode_graph": [vp, i32],
         "quantize_groupwise": [vp, i64, i32, vp, vp, vp, vp],
         "dequantize_groupwise": [vp, vp, vp, i64, i32, vp, vp],
         "free_model": [vp],
@@ -158,6 +160,10 @@ def decode_block(m, block: int, n_steps: int, ids_in, ids_out, logits=None, stre
 
 def set_decode_position(m, block: int, steps: int):
     _check("set_decode_position", lib().set_decode_position(m, block, steps))
+
+
+def set_decode_graph(m, enable: bool):
+    _check("set_decode_graph", lib().set_decode_graph(m, int(bool(enable))))
 
 
 def free_model(m):

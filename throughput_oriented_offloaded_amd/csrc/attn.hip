@@ -154,8 +154,10 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict__ q, int64_t q_stride,
                                                      uint16_t *__restrict__ out, int64_t out_stride, int rows,
-                                                     int seq0, int ctx, KvView kv)
+                                                     int seq0, int ctx, const int *__restrict__ dctx, KvView kv)
 {
+    if (dctx)
+        ctx = *dctx + 1;
     constexpr int L = D / 32, CB = D / 2, G = D / 64;
     const int lane = threadIdx.x & 63;
     const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
@@ -356,15 +358,15 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
 } // namespace
 
 hipError_t launch_attn_decode(const uint16_t *q, int64_t q_stride, uint16_t *out, int64_t out_stride, int rows,
-                              int seq0, int ctx, KvView kv, hipStream_t st)
+                              int seq0, int ctx, const int *dctx, KvView kv, hipStream_t st)
 {
     if (rows == 0)
         return hipSuccess;
     const dim3 grid((unsigned)(((int64_t)rows * kv.heads + 3) / 4)), block(256);
     if (kv.head_dim == 128)
-        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, kv);
+        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, dctx, kv);
     else if (kv.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, kv);
+        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, dctx, kv);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

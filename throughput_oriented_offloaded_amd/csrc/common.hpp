@@ -154,6 +154,7 @@ __device__ __forceinline__ size_t kv_slab(const KvView &v, int seq, int head) { 
 // sequence seq0 + r / rows_per_seq at position pos0 + r % rows_per_seq.
 struct RowMap {
     int seq0, rows_per_seq, pos0;
+    const int *dpos; // if non-null, pos0 is read from device memory (captured decode steps)
 };
 
 enum Epilogue { EPI_BIAS = 0, EPI_BIAS_RES = 1, EPI_BIAS_RELU = 2, EPI_NONE = 3 };
@@ -181,8 +182,9 @@ hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, SrcMap src, in
 hipError_t launch_kv_export(KvView kv, int seq, int head, int t0, int t1, uint8_t *kc, uint16_t *ks, uint16_t *kz,
                             uint8_t *vc, uint16_t *vs, uint16_t *vz, hipStream_t st);
 // decode attention: each of `rows` rows is one sequence (seq0 + r) attending positions 0..ctx-1
+// ctx = *dctx + 1 when dctx is non-null (the position of the step, read on the device)
 hipError_t launch_attn_decode(const uint16_t *q, int64_t q_stride, uint16_t *out, int64_t out_stride, int rows,
-                              int seq0, int ctx, KvView kv, hipStream_t st);
+                              int seq0, int ctx, const int *dctx, KvView kv, hipStream_t st);
 // causal prefill attention: `n_seq` sequences starting at seq0, `len` positions each, from position 0
 hipError_t launch_attn_prefill(const uint16_t *q, int64_t q_stride, uint16_t *out, int64_t out_stride, int n_seq,
                                int seq0, int len, KvView kv, hipStream_t st);
@@ -208,8 +210,12 @@ size_t gemm_workspace_bytes(int M, int N, int K, bool int4);
 hipError_t launch_layernorm(const uint16_t *x, int rows, int h, const uint16_t *g, const uint16_t *b, uint16_t *y,
                             hipStream_t st);
 // h[r] = fp16(E[ids[r]] + P[pos + 2]), pos = pos0 + r % rows_per_seq
-hipError_t launch_embed(const int32_t *ids, int rows, int rows_per_seq, int pos0, const uint16_t *tok, int vocab,
-                        const uint16_t *posemb, int h, uint16_t *out, hipStream_t st);
+// pos0 = *dpos when dpos is non-null
+hipError_t launch_embed(const int32_t *ids, int rows, int rows_per_seq, int pos0, const int *dpos, const uint16_t *tok,
+                        int vocab, const uint16_t *posemb, int h, uint16_t *out, hipStream_t st);
+// *p = v; and *p += 1 (a captured decode step advances its own position)
+hipError_t launch_set_int(int *p, int v, hipStream_t st);
+hipError_t launch_increment_int(int *p, hipStream_t st);
 // ids[r] = argmax over fp16 logits [rows][V], lowest index on ties
 hipError_t launch_argmax(const uint16_t *logits, int rows, int V, int32_t *ids, hipStream_t st);
 // dst[r][i] = src[r * src_step + i], i < h (e.g. the last prompt position of each sequence)

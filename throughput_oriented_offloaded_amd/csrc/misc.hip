@@ -5,38 +5,60 @@
 
 namespace {
 
-// One 256-thread workgroup per row; fp32 statistics (two passes over the row,
-// which stays in L1/L2), biased variance, eps 1e-5, one rounding to fp16.
-__global__ void __launch_bounds__(256) k_layernorm(const uint16_t *__restrict__ x, int h,
+// One wavefront per row (four rows per workgroup): the row is read once with
+// 16-byte loads and held in registers as fp16 (up to 8 * 64 * K elements),
+// fp32 statistics in two passes over the registers (mean, then the biased
+// variance of x - mean), DPP reductions, eps 1e-5, one rounding to fp16.
+template <int K>
+__global__ void __launch_bounds__(256) k_layernorm(const uint16_t *__restrict__ x, int rows, int h,
                                                    const uint16_t *__restrict__ g, const uint16_t *__restrict__ b,
                                                    uint16_t *__restrict__ y)
 {
-    __shared__ float red[4];
-    const int64_t r = blockIdx.x;
-    const uint16_t *xr = x + r * h;
-    const int tid = threadIdx.x;
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (row >= rows)
+        return; // whole wavefront
+    const int lane = threadIdx.x & 63, nch = h >> 3;
+    const uint16_t *xr = x + (int64_t)row * h;
+    uint4_t v[K];
     float s = 0.0f;
-    for (int i = tid; i < h; i += 256)
-        s += h2f(xr[i]);
-    s = wave_sum(s);
-    if ((tid & 63) == 0)
-        red[tid >> 6] = s;
-    __syncthreads();
-    const float mu = ((red[0] + red[1]) + (red[2] + red[3])) / (float)h;
-    __syncthreads();
-    float v = 0.0f;
-    for (int i = tid; i < h; i += 256) {
-        const float c = h2f(xr[i]) - mu;
-        v += c * c;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        const int c = lane + 64 * k;
+        v[k] = c < nch ? *reinterpret_cast<const uint4_t *>(xr + 8 * c) : (uint4_t){0u, 0u, 0u, 0u};
+        const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            s += (float)hv[e];
     }
-    v = wave_sum(v);
-    if ((tid & 63) == 0)
-        red[tid >> 6] = v;
-    __syncthreads();
-    const float var = ((red[0] + red[1]) + (red[2] + red[3])) / (float)h;
+    const float mu = reduce_slots<1>(s, OpAdd()) / (float)h;
+    float q = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        if (lane + 64 * k < nch) {
+            const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float c = (float)hv[e] - mu;
+                q += c * c;
+            }
+        }
+    }
+    const float var = reduce_slots<1>(q, OpAdd()) / (float)h;
     const float rs = 1.0f / sqrtf(var + 1e-5f);
-    for (int i = tid; i < h; i += 256)
-        y[r * h + i] = f2h((h2f(xr[i]) - mu) * rs * h2f(g[i]) + h2f(b[i]));
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        const int c = lane + 64 * k;
+        if (c < nch) {
+            const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
+            const half8_t gv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g + 8 * c));
+            const half8_t bv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(b + 8 * c));
+            half8_t o;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                o[e] = (half_t)(((float)hv[e] - mu) * rs * (float)gv[e] + (float)bv[e]);
+            *reinterpret_cast<uint4_t *>(y + (int64_t)row * h + 8 * c) = __builtin_bit_cast(uint4_t, o);
+        }
+    }
 }
 
 // The sum of two fp16 values rounded to fp32 and then to fp16 equals its
@@ -44,9 +66,12 @@ __global__ void __launch_bounds__(256) k_layernorm(const uint16_t *__restrict__ 
 // exactly fp16(E[id] + P[pos + 2]). Ids outside [0, vocab) are clamped into it
 // (they are outside the contract; clamping keeps every read in bounds).
 __global__ void __launch_bounds__(256) k_embed(const int32_t *__restrict__ ids, int rows, int rows_per_seq, int pos0,
-                                               const uint16_t *__restrict__ tok, int vocab,
-                                               const uint16_t *__restrict__ posemb, int h, uint16_t *__restrict__ out)
+                                               const int *__restrict__ dpos, const uint16_t *__restrict__ tok,
+                                               int vocab, const uint16_t *__restrict__ posemb, int h,
+                                               uint16_t *__restrict__ out)
 {
+    if (dpos)
+        pos0 = *dpos;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)rows * h)
         return;
@@ -64,7 +89,9 @@ __device__ __forceinline__ void better(float &bv, int &bi, float v, int i)
     }
 }
 
-// One workgroup per row: strided scan, then wave shuffles and LDS.
+// One workgroup per row: 16-byte loads when rows are 16-byte aligned (V a
+// multiple of 8), element loads otherwise; then DPP/shuffle reductions within
+// each wave and LDS across the four waves. Ties go to the lowest index.
 __global__ void __launch_bounds__(256) k_argmax(const uint16_t *__restrict__ logits, int V, int32_t *__restrict__ ids)
 {
     __shared__ float sv[4];
@@ -73,8 +100,18 @@ __global__ void __launch_bounds__(256) k_argmax(const uint16_t *__restrict__ log
     const uint16_t *lr = logits + r * V;
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int i = threadIdx.x; i < V; i += 256)
-        better(bv, bi, h2f(lr[i]), i);
+    if ((V & 7) == 0) {
+        const int nch = V >> 3;
+        for (int c = threadIdx.x; c < nch; c += 256) {
+            const half8_t hv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(lr + 8 * c));
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                better(bv, bi, (float)hv[e], 8 * c + e);
+        }
+    } else {
+        for (int i = threadIdx.x; i < V; i += 256)
+            better(bv, bi, h2f(lr[i]), i);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(bv, o, 64);
@@ -103,25 +140,52 @@ __global__ void __launch_bounds__(256) k_gather_rows(const uint16_t *__restrict_
     dst[i] = src[r * step + c];
 }
 
+__global__ void k_set_int(int *p, int v) { *p = v; }
+__global__ void k_increment_int(int *p) { *p += 1; }
+
 } // namespace
+
+hipError_t launch_set_int(int *p, int v, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, st, p, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_increment_int(int *p, hipStream_t st)
+{
+    hipLaunchKernelGGL(k_increment_int, dim3(1), dim3(1), 0, st, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_layernorm(const uint16_t *x, int rows, int h, const uint16_t *g, const uint16_t *b, uint16_t *y,
                             hipStream_t st)
 {
     if (rows == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_layernorm, dim3(rows), dim3(256), 0, st, x, h, g, b, y);
+    // h is a multiple of 64 (checked at init), so rows are 16-byte aligned
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const int chunks = (h / 8 + 63) / 64; // 16-byte chunks per lane
+    if (chunks <= 2)
+        hipLaunchKernelGGL(k_layernorm<2>, grid, block, 0, st, x, rows, h, g, b, y);
+    else if (chunks <= 8)
+        hipLaunchKernelGGL(k_layernorm<8>, grid, block, 0, st, x, rows, h, g, b, y);
+    else if (chunks <= 16)
+        hipLaunchKernelGGL(k_layernorm<16>, grid, block, 0, st, x, rows, h, g, b, y);
+    else if (chunks <= 32)
+        hipLaunchKernelGGL(k_layernorm<32>, grid, block, 0, st, x, rows, h, g, b, y);
+    else
+        return hipErrorInvalidValue; // hidden > 16384
     return hipGetLastError();
 }
 
-hipError_t launch_embed(const int32_t *ids, int rows, int rows_per_seq, int pos0, const uint16_t *tok, int vocab,
-                        const uint16_t *posemb, int h, uint16_t *out, hipStream_t st)
+hipError_t launch_embed(const int32_t *ids, int rows, int rows_per_seq, int pos0, const int *dpos, const uint16_t *tok,
+                        int vocab, const uint16_t *posemb, int h, uint16_t *out, hipStream_t st)
 {
     const int64_t n = (int64_t)rows * h;
     if (n == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, rows, rows_per_seq, pos0, tok,
-                       vocab, posemb, h, out);
+    hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, rows, rows_per_seq, pos0, dpos,
+                       tok, vocab, posemb, h, out);
     return hipGetLastError();
 }
 

@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(256) k_kv_append(const uint16_t *__restrict__ 
     const int head = (int)(rest % kv.heads);
     const int row = (int)(rest / kv.heads);
     const int seq = map.seq0 + row / map.rows_per_seq;
-    const int pos = map.pos0 + row % map.rows_per_seq;
+    const int pos = (map.dpos ? *map.dpos : map.pos0) + row % map.rows_per_seq;
     const uint16_t *src = (isv ? v : k) + (int64_t)(row / map.rows_per_seq) * src_map.seq_stride +
                           (int64_t)(row % map.rows_per_seq) * src_map.pos_stride +
                           (int64_t)head * src_map.head_stride + g * 64 + part * 8;

@@ -88,6 +88,16 @@ struct tod_model {
     hipStream_t copy = nullptr;
     hipEvent_t ev_loaded[2] = {}, ev_free[2] = {};
     std::vector<int> prefilled, decoded;
+    // captured decode steps (HBM tier): one graph per block, replayed on gstream;
+    // the step reads its position from gpos and its token ids from gids (the
+    // argmax writes the next ids back there) and advances gpos itself
+    bool graphs_on = true;
+    int *gpos = nullptr;
+    int32_t *gids = nullptr;
+    hipStream_t gstream = nullptr;
+    hipEvent_t gev_in = nullptr, gev_out = nullptr;
+    std::vector<hipGraphExec_t> gexec; // [block], null until captured
+    std::vector<int> gfail;            // [block], capture failed: stay eager
     // kernel timing (profile_kernels / profile_read)
     unsigned prof_mask = 0;
     std::vector<hipEvent_t> ev_pool;
@@ -230,7 +240,7 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
 // decode: rows = M sequences at position pos; prefill: rows = b * s (b sequences
 // starting at seq0, positions 0..s-1).
 int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, bool prefill_mode, int seq0, int s,
-               int pos, const uint16_t *wslot, hipStream_t st)
+               int pos, const int *dpos, const uint16_t *wslot, hipStream_t st)
 {
     const int hd = m->cfg.hidden, f = m->cfg.ffn;
     const LayerStore &L = m->layers[l];
@@ -249,10 +259,10 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
     RowMap map;
     if (prefill_mode) {
         src = {(int64_t)s * 3 * hd, 3 * hd, m->cfg.head_dim};
-        map = {seq0, s, 0};
+        map = {seq0, s, 0, nullptr};
     } else {
         src = {3 * hd, 0, m->cfg.head_dim};
-        map = {seq0, 1, pos};
+        map = {seq0, 1, pos, dpos};
     }
     {
         ProfScope ps(m, TOD_K_KV_APPEND, st);
@@ -263,7 +273,7 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         if (prefill_mode)
             HIPCHK(launch_attn_prefill(m->qkv, 3 * hd, m->att, hd, rows / s, seq0, s, kv, st));
         else
-            HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, kv, st));
+            HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, dpos, kv, st));
     }
     if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wo, h, hd, EPI_BIAS_RES, st)))
         return rc;
@@ -385,6 +395,15 @@ int free_model(tod_model *m)
     }
     if (m->copy)
         (void)hipStreamDestroy(m->copy);
+    for (hipGraphExec_t e : m->gexec)
+        if (e)
+            (void)hipGraphExecDestroy(e);
+    if (m->gstream)
+        (void)hipStreamDestroy(m->gstream);
+    if (m->gev_in)
+        (void)hipEventDestroy(m->gev_in);
+    if (m->gev_out)
+        (void)hipEventDestroy(m->gev_out);
     for (auto &p : m->pend) {
         (void)hipEventDestroy(p.a);
         (void)hipEventDestroy(p.b);
@@ -406,6 +425,8 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         return fail(TOD_EINVAL, "hidden (%d) != n_heads * head_dim (%d)", c.hidden, c.n_heads * c.head_dim);
     if (c.head_dim % 64 || c.hidden % 64 || c.ffn % 64 || (c.head_dim != 64 && c.head_dim != 128))
         return fail(TOD_EINVAL, "head_dim must be 64 or 128; hidden and ffn multiples of 64");
+    if (c.hidden > 16384)
+        return fail(TOD_EINVAL, "hidden (%d) above 16384", c.hidden);
     if (r.group != TOD_GROUP)
         return fail(TOD_EINVAL, "group must be 64 (got %d)", r.group);
     if (r.gpu_batch <= 0 || r.batches_per_block <= 0 || r.prompt_len <= 0 || r.gen_len <= 0 || r.n_blocks <= 0)
@@ -522,6 +543,15 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     }
     m->prefilled.assign(r.n_blocks, 0);
     m->decoded.assign(r.n_blocks, 0);
+    m->gexec.assign(r.n_blocks, nullptr);
+    m->gfail.assign(r.n_blocks, 0);
+    if (!host) {
+        ALLOC(m->gpos, sizeof(int));
+        ALLOC(m->gids, (size_t)m->M * 4);
+        HIPCHK(hipStreamCreateWithFlags(&m->gstream, hipStreamNonBlocking));
+        HIPCHK(hipEventCreateWithFlags(&m->gev_in, hipEventDisableTiming));
+        HIPCHK(hipEventCreateWithFlags(&m->gev_out, hipEventDisableTiming));
+    }
     return TOD_OK;
 }
 
@@ -617,14 +647,15 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
     const int64_t brow = (int64_t)b * s; // rows of one batch
     for (int k = 0; k < K; k++) {
         ProfScope ps(m, TOD_K_EMBED, st);
-        HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
+        HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, nullptr, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
                                 m->hid + k * brow * h, st));
     }
     rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
         const KvView &kv = m->kv[(size_t)block * L + l];
         for (int kk = 0; kk < K; kk++) {
             const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
-            const int r = layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, wslot, st);
+            const int r =
+                layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, nullptr, wslot, st);
             if (r)
                 return r;
         }
@@ -638,6 +669,57 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
     m->prefilled[block] = 1;
     m->decoded[block] = 0;
     return TOD_OK;
+}
+
+// One decode step of a block: embed the ids at `pos`, every layer, head and argmax
+// into `out`. With dpos set (captured steps), the position is read from device
+// memory and advanced by the step itself.
+static int decode_step(tod_model *m, int block, const int32_t *in, int pos, const int *dpos, uint16_t *logits,
+                       int32_t *out, hipStream_t st)
+{
+    const int Mr = m->M, h = m->cfg.hidden, L = m->cfg.n_layers;
+    {
+        ProfScope ps(m, TOD_K_EMBED, st);
+        HIPCHK(launch_embed(in, Mr, 1, pos, dpos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
+    }
+    int rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
+        return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, dpos, wslot, st);
+    });
+    if (rc)
+        return rc;
+    if ((rc = head_pass(m, m->hid, Mr, logits, out, st)))
+        return rc;
+    if (dpos)
+        HIPCHK(launch_increment_int(const_cast<int *>(dpos), st));
+    return TOD_OK;
+}
+
+// Capture one decode step of `block` into a graph (kernels only: no memsets,
+// copies or events inside). Returns false if capture is not possible here.
+static bool capture_step(tod_model *m, int block)
+{
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(m->gstream, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    const int rc = decode_step(m, block, m->gids, 0, m->gpos, m->logits, m->gids, m->gstream);
+    const hipError_t e = hipStreamEndCapture(m->gstream, &graph);
+    if (rc || e != hipSuccess || !graph) {
+        (void)hipGetLastError();
+        if (graph)
+            (void)hipGraphDestroy(graph);
+        return false;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess || !exec) {
+        (void)hipGetLastError();
+        return false;
+    }
+    m->gexec[block] = exec;
+    return true;
 }
 
 int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, int32_t *d_ids_out,
@@ -654,24 +736,45 @@ int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, 
         return fail(TOD_ESTATE, "decode would exceed gen_len - 1 = %d steps (done %d, asked %d)",
                     m->run.gen_len - 1, m->decoded[block], n_steps);
     const hipStream_t st = S(stream);
-    const int Mr = m->M, h = m->cfg.hidden, L = m->cfg.n_layers, V = m->cfg.vocab;
+    const int Mr = m->M, V = m->cfg.vocab;
+    const bool graph = n_steps > 0 && m->graphs_on && !m->prof_mask && m->gstream &&
+                       m->run.weight_tier == TOD_W_HBM_INT4 && !m->gfail[block] &&
+                       (m->gexec[block] || capture_step(m, block) || (m->gfail[block] = 1, false));
+    if (graph) {
+        // replay on the model's stream, ordered after and before the caller's
+        HIPCHK(hipEventRecord(m->gev_in, st));
+        HIPCHK(hipStreamWaitEvent(m->gstream, m->gev_in, 0));
+        HIPCHK(hipMemcpyAsync(m->gids, d_ids_in, (size_t)Mr * 4, hipMemcpyDeviceToDevice, m->gstream));
+        HIPCHK(launch_set_int(m->gpos, m->run.prompt_len + m->decoded[block], m->gstream));
+        for (int j = 0; j < n_steps; j++) {
+            HIPCHK(hipGraphLaunch(m->gexec[block], m->gstream));
+            HIPCHK(hipMemcpyAsync(d_ids_out + (int64_t)j * Mr, m->gids, (size_t)Mr * 4, hipMemcpyDeviceToDevice,
+                                  m->gstream));
+            if (d_logits)
+                HIPCHK(hipMemcpyAsync(d_logits + (int64_t)j * Mr * V, m->logits, (size_t)Mr * V * 2,
+                                      hipMemcpyDeviceToDevice, m->gstream));
+            m->decoded[block]++;
+        }
+        HIPCHK(hipEventRecord(m->gev_out, m->gstream));
+        HIPCHK(hipStreamWaitEvent(st, m->gev_out, 0));
+        return TOD_OK;
+    }
     for (int j = 0; j < n_steps; j++) {
         const int pos = m->run.prompt_len + m->decoded[block];
         const int32_t *in = j == 0 ? d_ids_in : d_ids_out + (int64_t)(j - 1) * Mr;
-        {
-            ProfScope ps(m, TOD_K_EMBED, st);
-            HIPCHK(launch_embed(in, Mr, 1, pos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
-        }
-        rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
-            return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, wslot, st);
-        });
-        if (rc)
-            return rc;
         uint16_t *lg = d_logits ? d_logits + (int64_t)j * Mr * V : m->logits;
-        if ((rc = head_pass(m, m->hid, Mr, lg, d_ids_out + (int64_t)j * Mr, st)))
+        if ((rc = decode_step(m, block, in, pos, nullptr, lg, d_ids_out + (int64_t)j * Mr, st)))
             return rc;
         m->decoded[block]++;
     }
+    return TOD_OK;
+}
+
+int set_decode_graph(tod_model *m, int enable)
+{
+    if (!m)
+        return fail(TOD_EINVAL, "null model");
+    m->graphs_on = enable != 0;
     return TOD_OK;
 }
 
@@ -924,7 +1027,7 @@ int attn_cache_fill(tod_attn_cache *c, const uint16_t *d_k, const uint16_t *d_v,
     // time-major input [n][batch][heads][d]: row r = (sequence r / n, position t0 + r % n)
     const int d = c->kv.head_dim, H = c->kv.heads;
     const SrcMap src = {(int64_t)H * d, (int64_t)c->batch * H * d, d};
-    const RowMap map = {0, n, t0};
+    const RowMap map = {0, n, t0, nullptr};
     HIPCHK(launch_kv_append(d_k, d_v, src, c->batch * n, map, c->kv, S(stream)));
     return TOD_OK;
 }
@@ -940,9 +1043,10 @@ int attn_decode_step(tod_attn_cache *c, int pos, const uint16_t *d_q, const uint
         return fail(TOD_EINVAL, "q, k, v and out buffers must be 16-byte aligned");
     const int d = c->kv.head_dim, H = c->kv.heads;
     const SrcMap src = {(int64_t)H * d, 0, d};
-    const RowMap map = {0, 1, pos};
+    const RowMap map = {0, 1, pos, nullptr};
     HIPCHK(launch_kv_append(d_k_new, d_v_new, src, c->batch, map, c->kv, S(stream)));
-    HIPCHK(launch_attn_decode(d_q, (int64_t)H * d, d_out, (int64_t)H * d, c->batch, 0, pos + 1, c->kv, S(stream)));
+    HIPCHK(launch_attn_decode(d_q, (int64_t)H * d, d_out, (int64_t)H * d, c->batch, 0, pos + 1, nullptr, c->kv,
+                              S(stream)));
     return TOD_OK;
 }
 
