@@ -77,6 +77,117 @@ def build_model(tod, synth, w, log_every=8):
     return m
 
 
+def measure_h2d(torch, nbytes, reps=3):
+    """Pinned host -> HBM copy rate (GB/s) for one copy of nbytes on a side stream."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        dst.copy_(src, non_blocking=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src, non_blocking=True)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def host_tier_bench(args, w, tod, synth, torch):
+    """Decode with fp16 weights streamed per layer from pinned host memory.
+
+    The step is bound by the host link (every layer's fp16 matrices cross it
+    once per step), so the report is tokens/s and link GB/s against a
+    measured pinned -> HBM copy of the same size. Only --host-layers distinct
+    layers keep pinned matrices (the others stream layer % host_layers), so the
+    stack fits host memory; the prompt is shortened (--prompt-len, default 16)
+    because prefill at 512 tokens would take minutes of fp16 GEMMs, and a
+    link-bound step does not depend on the attended context."""
+    import dataclasses
+    w = dataclasses.replace(w, prompt_len=args.prompt_len or 16)
+    shape, M = w.shape, w.rows
+    L, h, f = shape.n_layers, shape.hidden, shape.ffn
+    P = min(args.host_layers, L)
+    run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
+               gen_len=w.gen_len, weight_tier=1, host_layers=P)
+    t_setup = time.perf_counter()
+    m = tod.Model(shape, run)
+    g = synth.global_weights(shape)
+    m.set_global_weights(g["tok_emb"], g["pos_emb"], g["lnf_g"], g["lnf_b"])
+    del g
+    mats = ("q_w", "k_w", "v_w", "o_w", "fc1_w", "fc2_w")
+    shared = None
+    for l in range(L):
+        if l < P:
+            t = synth.layer_weights(shape, l)
+            if shared is None:
+                shared = {n: t[n] for n in mats}  # placeholders for layers that stream a shared copy
+        else:
+            t = {n: synth.draw_tensor(shape, n, l) for n in synth.LAYER_TENSORS if n not in mats}
+            t.update(shared)
+        m.set_layer_weights(l, t)
+        del t
+        if (l + 1) % 8 == 0 or l + 1 == L:
+            log(f"weights: {l + 1}/{L} layers set ({P} with pinned matrices)")
+    del shared
+    prompts = torch.from_numpy(synth.prompt_ids(M, w.prompt_len, shape.vocab)).cuda()
+    first = torch.empty(M, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    tod.prefill(m.handle, 0, prompts, first)
+    e1.record()
+    torch.cuda.synchronize()
+    prefill_s = e0.elapsed_time(e1) / 1e3
+    log(f"prefill {prefill_s:.2f} s")
+    out = torch.empty((w.gen_len - 1, M), dtype=torch.int32, device="cuda")
+    steps, warm = args.steps, args.warmup
+    if warm:
+        tod.decode_block(m.handle, 0, warm, first, out[:warm])
+    torch.cuda.synchronize()
+    log(f"warm-up {warm} step(s) done")
+    ids = out[warm - 1] if warm else first
+    t0 = time.perf_counter()
+    tod.decode_block(m.handle, 0, steps, ids, out[warm:warm + steps])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    layer_bytes = (4 * h * h + 2 * f * h) * 2
+    link_gbs = L * layer_bytes * steps / elapsed / 1e9
+    log("measuring pinned -> HBM copy rate ...")
+    h2d = measure_h2d(torch, layer_bytes)
+    return {
+        "metric": "generated tokens/sec (1 GPU), OPT-175B shape fp16 weights streamed from pinned host; "
+                  "% of measured host-link bandwidth",
+        "value": M * steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}-shaped fp16 host-streamed block decode", "layers": L, "hidden": h,
+                   "heads": shape.n_heads, "head_dim": shape.head_dim, "ffn": f, "vocab": shape.vocab,
+                   "gpu_batch": w.gpu_batch, "batches_per_block": w.batches_per_block, "rows": M,
+                   "prompt_len": w.prompt_len, "gen_len": w.gen_len, "host_layers_pinned": P,
+                   "weights": "fp16 in pinned host memory, 2 HBM layer slots, copies on a side stream"},
+        "roofline": {"bound": "link", "achieved": link_gbs, "peak": h2d, "unit": "GB/s", "frac": link_gbs / h2d,
+                     "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"},
+        "link_bytes_per_step": L * layer_bytes,
+        "h2d_measured_gbs": h2d,
+        "prefill_s": prefill_s,
+    }
+
+
 def cpu_baseline(w, rows=64):
     """Oracle on one layer x one decode step x `rows` sequences at the average decode
     context, plus the LM head for those rows; extrapolated to the whole stack."""
@@ -163,10 +274,13 @@ def copy_probe(mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=31)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default 31; host tier 2)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed decode steps first (default 2; host tier 1)")
     ap.add_argument("--workload", default="opt-30b")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
+    ap.add_argument("--prompt-len", type=int, default=0, help="host tier only: prompt length (default 16)")
+    ap.add_argument("--host-layers", type=int, default=8,
+                    help="host tier only: layers with their own pinned matrices (default 8)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -185,6 +299,13 @@ def main():
     import throughput_oriented_offloaded_amd as tod
 
     w = synth.WORKLOADS[args.workload]
+    if args.steps is None:
+        args.steps = 2 if w.weight_tier == 1 else 31
+    if args.warmup is None:
+        args.warmup = 1 if w.weight_tier == 1 else 2
+    if w.weight_tier == 1:
+        print(json.dumps(host_tier_bench(args, w, tod, synth, torch)), flush=True)
+        return
     shape, M = w.shape, w.rows
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()

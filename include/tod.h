@@ -79,9 +79,15 @@ typedef struct {
  * its K*gpu_batch rows are row k*gpu_batch + i for batch k. Every sequence
  * has prompt_len prompt tokens and at most gen_len generated tokens, so the
  * KV cache holds prompt_len + gen_len - 1 positions. n_blocks blocks are
- * resident at once (each has its own KV cache). group must be 64. */
+ * resident at once (each has its own KV cache). group must be 64.
+ * host_layers (host tier only; 0 = n_layers): pinned host memory is kept for
+ * the six matrices of layers 0..host_layers-1 only, and layer l streams the
+ * matrices of layer l % host_layers (its vectors stay its own). This exists to
+ * measure stacks whose fp16 weights exceed the host's memory: copy sizes,
+ * streams and overlap are those of distinct layers. */
 typedef struct {
     int32_t gpu_batch, batches_per_block, prompt_len, gen_len, group, weight_tier, n_blocks;
+    int32_t host_layers;
 } tod_run_config;
 
 /*
@@ -111,7 +117,9 @@ int set_global_weights(tod_model *m, const uint16_t *h_tok_emb, const uint16_t *
  * int4 group-64 (FlexGen guide, "3. Group-Wise 4-Bit Quantization"); host
  * buffers may be freed on return.
  * TOD_W_HOST_FP16_STREAM: the matrices are copied into the library's pinned
- * host tier and streamed to HBM on every pass over the layer.
+ * host tier and streamed to HBM on every pass over the layer; for layers at
+ * or past run.host_layers (when set) the matrices are not read (the layer
+ * streams those of layer % host_layers), only the vectors.
  */
 int set_layer_weights(tod_model *m, int layer, const uint16_t *const *h_tensors);
 

@@ -37,6 +37,29 @@ def test_binding_names_match_header():
     assert set(_lib.EXPORTED) == set(_declared())
 
 
+def _struct_fields(name):
+    """Field names of `typedef struct { ... } name;` in the header, in order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct\s*\{([^}]*)\}\s*" + name + r"\s*;", text).group(1)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if decl:
+            assert decl.startswith("int32_t "), decl
+            fields += [f.strip() for f in decl[len("int32_t "):].split(",")]
+    return fields
+
+
+@pytest.mark.parametrize("cname,pyname", [("tod_model_config", "ModelConfig"), ("tod_run_config", "RunConfig")])
+def test_binding_structs_match_header(cname, pyname):
+    """The ctypes mirrors of the config structs have the header's fields, in order, all int32."""
+    from throughput_oriented_offloaded_amd import _lib
+    py = getattr(_lib, pyname)
+    assert [f for f, _ in py._fields_] == _struct_fields(cname)
+    assert all(t is ctypes.c_int32 for _, t in py._fields_)
+    assert ctypes.sizeof(py) == 4 * len(py._fields_)
+
+
 def test_argument_errors_without_gpu():
     """Validation happens before any HIP call: these return TOD_EINVAL and set last_error."""
     lib = ctypes.CDLL(LIB)

@@ -110,6 +110,39 @@ def test_opt125m_full_generation(tier):
     m.close()
 
 
+def test_host_layers_stream_the_shared_matrices():
+    """Host tier with host_layers = 2 of 4: layers 2 and 3 stream the matrices of
+    layers 0 and 1 with their own vectors; identical bits to a model whose layers
+    2 and 3 are given those matrices outright."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_125M.replace(n_layers=4)
+    s, g = 16, 4
+    run = dict(gpu_batch=2, batches_per_block=2, prompt_len=s, gen_len=g, weight_tier=1)
+    glob = synth.global_weights(shape, variant="full")
+    lw = [synth.layer_weights(shape, l, variant="full") for l in range(4)]
+    mats = ("q_w", "k_w", "v_w", "o_w", "fc1_w", "fc2_w")
+    prompts = to_dev(synth.prompt_ids(4, s, shape.vocab), torch)
+    outs = []
+    for host_layers in (2, 0):
+        m = tod.Model(shape, dict(run, host_layers=host_layers))
+        m.set_global_weights(glob["tok_emb"], glob["pos_emb"], glob["lnf_g"], glob["lnf_b"])
+        for l in range(4):
+            t = dict(lw[l])
+            if l >= 2:
+                for n in mats:  # aliased layers: the streamed matrices are layer l - 2's
+                    t[n] = lw[l - 2][n] if host_layers == 0 else np.zeros_like(lw[l][n])
+            m.set_layer_weights(l, t)
+        toks, logits = m.generate(prompts, g, return_logits=True)
+        torch.cuda.synchronize()
+        outs.append((toks.cpu(), logits.cpu()))
+        m.close()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    with pytest.raises(tod.TodError):  # host_layers is a host-tier option
+        tod.Model(shape, dict(run, weight_tier=0, host_layers=2))
+
+
 @pytest.mark.parametrize("n_layers", [1, 2])
 def test_opt125m_shallow_meets_stated_bar(n_layers):
     """At depth 1-2 the stated logit bar applies as is."""

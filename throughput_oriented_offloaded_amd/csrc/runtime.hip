@@ -67,6 +67,7 @@ struct tod_model {
     int n_out[N_GEMM_MATS] = {}, n_in[N_GEMM_MATS] = {};
     int64_t mat_off[N_GEMM_MATS] = {}; // host tier: element offset of each matrix
     int64_t layer_elems = 0;           // host tier: elements per layer
+    int host_layers = 0;               // host tier: layers with their own pinned matrices
     std::vector<LayerStore> layers;
     uint16_t *tok_emb = nullptr, *pos_emb = nullptr, *lnf_g = nullptr, *lnf_b = nullptr;
     bool glob_loaded = false;
@@ -293,8 +294,8 @@ int stream_layer(tod_model *m, int l)
 {
     const int sl = l & 1;
     HIPCHK(hipStreamWaitEvent(m->copy, m->ev_free[sl], 0));
-    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[l].host, (size_t)m->layer_elems * 2, hipMemcpyHostToDevice,
-                          m->copy));
+    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[l % m->host_layers].host, (size_t)m->layer_elems * 2,
+                          hipMemcpyHostToDevice, m->copy));
     HIPCHK(hipEventRecord(m->ev_loaded[sl], m->copy));
     return TOD_OK;
 }
@@ -451,6 +452,9 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     m->layer_elems = (int64_t)4 * h * h + 2 * (int64_t)f * h;
     m->layers.resize(L);
     const bool host = r.weight_tier == TOD_W_HOST_FP16_STREAM;
+    if (r.host_layers < 0 || (r.host_layers && !host))
+        return fail(TOD_EINVAL, "host_layers (%d) applies to the host tier only and must be >= 0", r.host_layers);
+    m->host_layers = r.host_layers > 0 && r.host_layers < L ? r.host_layers : L;
 
     // weights
     for (int l = 0; l < L; l++) {
@@ -467,7 +471,7 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         ALLOC(S_.ln1_b, (size_t)h * 2);
         ALLOC(S_.ln2_g, (size_t)h * 2);
         ALLOC(S_.ln2_b, (size_t)h * 2);
-        if (host) {
+        if (host && l < m->host_layers) {
             void *p = nullptr;
             hipError_t e = hipHostMalloc(&p, (size_t)m->layer_elems * 2, hipHostMallocDefault);
             if (e != hipSuccess) {
@@ -616,8 +620,10 @@ int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
     } parts[6] = {{TOD_Q_W, MAT_QKV, 0, h, h},   {TOD_K_W, MAT_QKV, h, h, h}, {TOD_V_W, MAT_QKV, 2 * h, h, h},
                   {TOD_O_W, MAT_O, 0, h, h},     {TOD_FC1_W, MAT_FC1, 0, f, h}, {TOD_FC2_W, MAT_FC2, 0, h, f}};
     if (m->run.weight_tier == TOD_W_HOST_FP16_STREAM) {
-        for (const Part &p : parts)
-            memcpy(L.host + m->mat_off[p.mat] + (int64_t)p.row0 * p.cols, t[p.tensor], (size_t)p.rows * p.cols * 2);
+        if (layer < m->host_layers) // later layers stream the matrices of layer % host_layers
+            for (const Part &p : parts)
+                memcpy(L.host + m->mat_off[p.mat] + (int64_t)p.row0 * p.cols, t[p.tensor],
+                       (size_t)p.rows * p.cols * 2);
     } else {
         for (const Part &p : parts) {
             const int64_t n = (int64_t)p.rows * p.cols;
