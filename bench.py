@@ -188,6 +188,53 @@ def host_tier_bench(args, w, tod, synth, torch):
     }
 
 
+def attention_bench(args, tod, synth, torch):
+    """The isolated decode-attention + KV-quantize workload: batch x heads
+    sequences with `context` cached int4 positions; each step quantizes and
+    appends one new K/V per sequence and attends over everything cached.
+    Inputs come from torch's seeded device generator, N(0, 1) fp16 (same
+    shapes and distribution as the parity tests' host-generated data)."""
+    W = synth.ATTN_WORKLOAD
+    B, H, d, T = W["batch"], W["heads"], W["head_dim"], W["context"]
+    steps, warm = args.steps, args.warmup
+    c = tod.attn_cache_create(B, H, d, T + warm + steps)
+    gen = torch.Generator(device="cuda").manual_seed(2)
+    for t0 in range(0, T, 128):
+        n = min(128, T - t0)
+        k = torch.randn((n, B, H, d), generator=gen, device="cuda", dtype=torch.float16)
+        v = torch.randn((n, B, H, d), generator=gen, device="cuda", dtype=torch.float16)
+        tod.attn_cache_fill(c, k, v, t0)
+        del k, v
+    q = [torch.randn((B, H, d), generator=gen, device="cuda", dtype=torch.float16) for _ in range(3 * (warm + steps))]
+    out = torch.empty((B, H, d), dtype=torch.float16, device="cuda")
+    for i in range(warm):
+        tod.attn_decode_step(c, T + i, q[3 * i], q[3 * i + 1], q[3 * i + 2], out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(warm, warm + steps):
+        tod.attn_decode_step(c, T + i, q[3 * i], q[3 * i + 1], q[3 * i + 2], out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tod.attn_cache_free(c)
+    G = d // 64
+    per_pos = 2 * (d // 2 + 4 * G)                 # K and V codes + (scale, zero) per group
+    ctx_avg = T + warm + (steps + 1) / 2.0          # attended positions, averaged over the timed steps
+    kv_read = B * H * per_pos * ctx_avg
+    other = B * H * d * 2 * 4 + B * H * per_pos     # q, k_new, v_new, out (fp16) + the appended codes
+    gbs = (kv_read + other) / (ms * 1e-3) / 1e9
+    return {
+        "metric": "decode attention + KV quantize step over an int4 cache (1 GPU); % of HBM roofline",
+        "value": ms, "unit": "ms/step", "n_gpus": 1, "steps": steps, "warmup": warm, "ms_per_step": ms,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "isolated decode attention + KV append", "batch": B, "heads": H, "head_dim": d,
+                   "cached_context": T, "context_avg": ctx_avg},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "k_kv_append + k_attn_decode<128>"},
+    }
+
+
 def cpu_baseline(w, rows=64):
     """Oracle on one layer x one decode step x `rows` sequences at the average decode
     context, plus the LM head for those rows; extrapolated to the whole stack."""
@@ -276,11 +323,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default 31; host tier 2)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed decode steps first (default 2; host tier 1)")
-    ap.add_argument("--workload", default="opt-30b")
+    ap.add_argument("--workload", default="opt-30b",
+                    help="opt-125m | opt-6.7b | opt-30b (default) | opt-175b (host tier) | attention")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--prompt-len", type=int, default=0, help="host tier only: prompt length (default 16)")
     ap.add_argument("--host-layers", type=int, default=8,
                     help="host tier only: layers with their own pinned matrices (default 8)")
+    ap.add_argument("--progress", action="store_true",
+                    help="one decode step per call with a log line each (long profiler runs); not for the metric")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -298,6 +348,11 @@ def main():
     import synth
     import throughput_oriented_offloaded_amd as tod
 
+    if args.workload == "attention":
+        args.steps = args.steps or 16
+        args.warmup = 2 if args.warmup is None else args.warmup
+        print(json.dumps(attention_bench(args, tod, synth, torch)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     if args.steps is None:
         args.steps = 2 if w.weight_tier == 1 else 31
@@ -336,14 +391,20 @@ def main():
                 tod.set_decode_position(m.handle, 0, 0)
                 state["decoded"], state["ids"] = 0, first
             k = min(n - done, max_steps - state["decoded"])
+            if args.progress:
+                k = 1  # one step per call, so every step can report
             tod.decode_block(m.handle, 0, k, state["ids"], out[state["decoded"]:state["decoded"] + k])
             state["ids"] = out[state["decoded"] + k - 1]
             state["decoded"] += k
             done += k
+            if args.progress:
+                torch.cuda.synchronize()
+                log(f"{run_steps.label}: {done}/{n} decode steps")
             run_steps.contexts.extend(range(w.prompt_len + state["decoded"] - k + 1,
                                             w.prompt_len + state["decoded"] + 1))
     run_steps.state = {"decoded": 0, "ids": first}
     run_steps.contexts = []
+    run_steps.label = "timed pass"
 
     def restart():
         tod.set_decode_position(m.handle, 0, 0)
@@ -365,6 +426,7 @@ def main():
     # per-kernel averages: the same steps again, each launch bracketed by HIP
     # events on the library's stream (step-by-step launches while timing)
     restart()
+    run_steps.label = "profiled pass"
     kinds = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
              "argmax", "embed")
     tod.profile_kernels(m.handle, kinds)
