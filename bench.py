@@ -96,11 +96,12 @@ def measure_h2d(torch, nbytes, reps=3):
 
 
 def host_tier_bench(args, w, tod, synth, torch):
-    """Decode with fp16 weights streamed per layer from pinned host memory.
+    """Decode with weights streamed per layer from pinned host memory: fp16
+    (weight tier 1) or the tiled int4 image (tier 2, 0.5625 byte per weight).
 
-    The step is bound by the host link (every layer's fp16 matrices cross it
-    once per step), so the report is tokens/s and link GB/s against a
-    measured pinned -> HBM copy of the same size. Only --host-layers distinct
+    The step is bound by the host link (every layer's matrices cross it once
+    per step), so the report is tokens/s and link GB/s against a measured
+    pinned -> HBM copy of the same size. Only --host-layers distinct
     layers keep pinned matrices (the others stream layer % host_layers), so the
     stack fits host memory; the prompt is shortened (--prompt-len, default 16)
     because prefill at 512 tokens would take minutes of fp16 GEMMs, and a
@@ -111,7 +112,7 @@ def host_tier_bench(args, w, tod, synth, torch):
     L, h, f = shape.n_layers, shape.hidden, shape.ffn
     P = min(args.host_layers, L)
     run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
-               gen_len=w.gen_len, weight_tier=1, host_layers=P)
+               gen_len=w.gen_len, weight_tier=w.weight_tier, host_layers=P)
     t_setup = time.perf_counter()
     m = tod.Model(shape, run)
     g = synth.global_weights(shape)
@@ -157,13 +158,15 @@ def host_tier_bench(args, w, tod, synth, torch):
     m.close()
     del m
     torch.cuda.empty_cache()
-    layer_bytes = (4 * h * h + 2 * f * h) * 2
+    int4 = w.weight_tier == 2
+    layer_weights = 4 * h * h + 2 * f * h
+    layer_bytes = layer_weights // 2 + layer_weights // 16 if int4 else layer_weights * 2
     link_gbs = L * layer_bytes * steps / elapsed / 1e9
     log("measuring pinned -> HBM copy rate ...")
     h2d = measure_h2d(torch, layer_bytes)
     return {
-        "metric": "generated tokens/sec (1 GPU), OPT-175B shape fp16 weights streamed from pinned host; "
-                  "% of measured host-link bandwidth",
+        "metric": f"generated tokens/sec (1 GPU), OPT-175B shape {'int4' if int4 else 'fp16'} weights streamed "
+                  "from pinned host; % of measured host-link bandwidth",
         "value": M * steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -173,13 +176,15 @@ def host_tier_bench(args, w, tod, synth, torch):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "int4-f16" if int4 else "f16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}-shaped fp16 host-streamed block decode", "layers": L, "hidden": h,
+        "config": {"workload": f"{w.name}-shaped {'int4' if int4 else 'fp16'} host-streamed block decode",
+                   "layers": L, "hidden": h,
                    "heads": shape.n_heads, "head_dim": shape.head_dim, "ffn": f, "vocab": shape.vocab,
                    "gpu_batch": w.gpu_batch, "batches_per_block": w.batches_per_block, "rows": M,
                    "prompt_len": w.prompt_len, "gen_len": w.gen_len, "host_layers_pinned": P,
-                   "weights": "fp16 in pinned host memory, 2 HBM layer slots, copies on a side stream"},
+                   "weights": ("int4 group-64 (tiled codes + fp16 scale/zero)" if int4 else "fp16")
+                   + " in pinned host memory, 2 HBM layer slots, copies on a side stream"},
         "roofline": {"bound": "link", "achieved": link_gbs, "peak": h2d, "unit": "GB/s", "frac": link_gbs / h2d,
                      "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"},
         "link_bytes_per_step": L * layer_bytes,
@@ -321,14 +326,15 @@ def copy_probe(mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default 31; host tier 2)")
-    ap.add_argument("--warmup", type=int, default=None, help="untimed decode steps first (default 2; host tier 1)")
+    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default 31; fp16 host tier 2, int4 host tier 6)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed decode steps first (default 2; host tiers 1)")
     ap.add_argument("--workload", default="opt-30b",
-                    help="opt-125m | opt-6.7b | opt-30b (default) | opt-175b (host tier) | attention")
+                    help="opt-125m | opt-6.7b | opt-30b (default) | opt-175b (fp16 host tier) | "
+                         "opt-175b-int4 (int4 host tier) | attention")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
-    ap.add_argument("--prompt-len", type=int, default=0, help="host tier only: prompt length (default 16)")
+    ap.add_argument("--prompt-len", type=int, default=0, help="host tiers only: prompt length (default 16)")
     ap.add_argument("--host-layers", type=int, default=8,
-                    help="host tier only: layers with their own pinned matrices (default 8)")
+                    help="host tiers only: layers with their own pinned matrices (default 8)")
     ap.add_argument("--progress", action="store_true",
                     help="one decode step per call with a log line each (long profiler runs); not for the metric")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -355,10 +361,10 @@ def main():
         return
     w = synth.WORKLOADS[args.workload]
     if args.steps is None:
-        args.steps = 2 if w.weight_tier == 1 else 31
+        args.steps = {1: 2, 2: 6}.get(w.weight_tier, 31)
     if args.warmup is None:
-        args.warmup = 1 if w.weight_tier == 1 else 2
-    if w.weight_tier == 1:
+        args.warmup = 1 if w.weight_tier else 2
+    if w.weight_tier:
         print(json.dumps(host_tier_bench(args, w, tod, synth, torch)), flush=True)
         return
     shape, M = w.shape, w.rows

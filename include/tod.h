@@ -55,6 +55,7 @@ extern "C" {
 /* Where a model's six decoder matrices per layer live. */
 #define TOD_W_HBM_INT4 0         /* int4 group-64 in HBM, quantized at load */
 #define TOD_W_HOST_FP16_STREAM 1 /* fp16 in pinned host memory, streamed per layer into a 2-slot HBM buffer */
+#define TOD_W_HOST_INT4_STREAM 2 /* int4 group-64 (tiled codes + params) in pinned host memory, streamed per layer */
 
 /* Order of the 16 per-layer tensors passed to set_layer_weights. */
 enum {
@@ -80,7 +81,7 @@ typedef struct {
  * has prompt_len prompt tokens and at most gen_len generated tokens, so the
  * KV cache holds prompt_len + gen_len - 1 positions. n_blocks blocks are
  * resident at once (each has its own KV cache). group must be 64.
- * host_layers (host tier only; 0 = n_layers): pinned host memory is kept for
+ * host_layers (host tiers only; 0 = n_layers): pinned host memory is kept for
  * the six matrices of layers 0..host_layers-1 only, and layer l streams the
  * matrices of layer l % host_layers (its vectors stay its own). This exists to
  * measure stacks whose fp16 weights exceed the host's memory: copy sizes,
@@ -117,9 +118,16 @@ int set_global_weights(tod_model *m, const uint16_t *h_tok_emb, const uint16_t *
  * int4 group-64 (FlexGen guide, "3. Group-Wise 4-Bit Quantization"); host
  * buffers may be freed on return.
  * TOD_W_HOST_FP16_STREAM: the matrices are copied into the library's pinned
- * host tier and streamed to HBM on every pass over the layer; for layers at
- * or past run.host_layers (when set) the matrices are not read (the layer
- * streams those of layer % host_layers), only the vectors.
+ * host tier and streamed to HBM on every pass over the layer.
+ * TOD_W_HOST_INT4_STREAM: the matrices are quantized in HBM as for
+ * TOD_W_HBM_INT4 and their tiled int4 image (0.5625 byte per weight) is kept
+ * in pinned host memory and streamed on every pass: the packed 4-bit weights
+ * cross the host link instead of fp16 (FlexGen guide, "3. Group-Wise 4-Bit
+ * Quantization", transfer of packed 4-bit data over PCIe); results are
+ * identical to TOD_W_HBM_INT4.
+ * On both host tiers, layers at or past run.host_layers (when set) do not
+ * read their matrices (they stream those of layer % host_layers), only their
+ * vectors.
  */
 int set_layer_weights(tod_model *m, int layer, const uint16_t *const *h_tensors);
 
@@ -141,7 +149,7 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
  * at position prompt_len + (decode steps already run since prefill), appends that
  * position's quantized K/V, and writes the picks to d_ids_out int32
  * [n_steps][K*b]; d_logits (nullable) receives fp16 [n_steps][K*b][vocab].
- * Within a step every layer's weights are read from HBM (or streamed from the
+ * Within a step every layer's weights are read from HBM (or streamed from a
  * host tier) once for the whole block: the block's rows form the M dimension
  * of each fused int4 GEMM (FlexGen guide, "2. The Zig-Zag Block Schedule";
  * comparison table, "Weight Reuse per Load").
@@ -164,7 +172,7 @@ int set_decode_position(tod_model *m, int block, int steps);
  * the caller's stream and before its later work; the step reads its position
  * and token ids from device memory, so one graph serves every step. Outputs
  * are identical to the step-by-step launches, which run instead when enable is
- * 0, on the host tier, while profile_kernels is active, or if capture fails.
+ * 0, on the host tiers, while profile_kernels is active, or if capture fails.
  */
 int set_decode_graph(tod_model *m, int enable);
 
@@ -211,7 +219,9 @@ int profile_read(tod_model *m, int kind, double *total_ms, int64_t *launches);
 /*
  * export_weight: copy layer `layer`'s matrix `which` (TOD_MAT_*) back out of
  * the int4 store in the canonical format (device buffers: codes [out*in/2],
- * scale and zero [out*in/64]). TOD_ESTATE for the fp16 host tier.
+ * scale and zero [out*in/64]). On the int4 host tier the layer's pinned image
+ * (that of layer % host_layers) is read back through an idle streaming slot;
+ * the call synchronizes the device first. TOD_ESTATE for the fp16 host tier.
  */
 int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t *d_scale, uint16_t *d_zero,
                   void *stream);

@@ -138,7 +138,7 @@ class Workload:
     batches_per_block: int
     prompt_len: int
     gen_len: int
-    weight_tier: int = 0   # 0: int4 weights resident in HBM; 1: fp16 weights streamed from pinned host memory
+    weight_tier: int = 0   # 0: int4 weights resident in HBM; 1: fp16 / 2: int4 weights streamed from pinned host memory
 
     @property
     def rows(self) -> int:
@@ -158,6 +158,7 @@ WORKLOADS = {
     "opt-6.7b": Workload("opt-6.7b", OPT_6_7B, 64, 4, 512, 32),
     "opt-30b": Workload("opt-30b", OPT_30B, 64, 8, 512, 32),
     "opt-175b": Workload("opt-175b", OPT_175B, 32, 8, 512, 32, weight_tier=1),
+    "opt-175b-int4": Workload("opt-175b-int4", OPT_175B, 32, 8, 512, 32, weight_tier=2),
 }
 
 # Isolated decode attention + KV quantize workload.

@@ -72,7 +72,7 @@ def fp32_bars(shape, layers, glob, prompts, g, K, ref_tokens, ref_logits):
     return max(LOGIT_MAX_ABS, 2.0 * d.max()), max(LOGIT_MEAN_ABS, 1.5 * d.mean())
 
 
-@pytest.mark.parametrize("tier", [0, 1])
+@pytest.mark.parametrize("tier", [0, 1, 2])
 def test_opt125m_full_generation(tier):
     """OPT-125m shape, 4 x 2 batches, prompt 32, 8 generated tokens: every logit checked."""
     torch = torch_cuda()
@@ -86,7 +86,7 @@ def test_opt125m_full_generation(tier):
     torch.cuda.synchronize()
     gt = toks.cpu().numpy()
     gl = to_np16(logits)
-    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full"), int4_weights=tier == 0)
+    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full"), int4_weights=tier != 1)
               for l in range(shape.n_layers)]
     ot, ol, loads = oracle.generate(shape, layers, glob, prompts, w.gen_len, w.batches_per_block,
                                     oracle.SCHED_ZIGZAG)
@@ -94,7 +94,7 @@ def test_opt125m_full_generation(tier):
     print(f"token agreement with the oracle: {np.mean(gt == ot):.4f}", flush=True)
     max_bar, mean_bar = fp32_bars(shape, layers, glob, prompts, w.gen_len, w.batches_per_block, ot, ol)
     compare(gt, gl, ot, ol, f"opt-125m tier {tier}", max_bar, mean_bar)
-    if tier == 0:
+    if tier != 1:
         import throughput_oriented_offloaded_amd as tod
         for l in (0, shape.n_layers - 1):
             for which in oracle.MATRICES:
@@ -110,15 +110,16 @@ def test_opt125m_full_generation(tier):
     m.close()
 
 
-def test_host_layers_stream_the_shared_matrices():
-    """Host tier with host_layers = 2 of 4: layers 2 and 3 stream the matrices of
+@pytest.mark.parametrize("tier", [1, 2])
+def test_host_layers_stream_the_shared_matrices(tier):
+    """Host tiers with host_layers = 2 of 4: layers 2 and 3 stream the matrices of
     layers 0 and 1 with their own vectors; identical bits to a model whose layers
     2 and 3 are given those matrices outright."""
     torch = torch_cuda()
     import throughput_oriented_offloaded_amd as tod
     shape = synth.OPT_125M.replace(n_layers=4)
     s, g = 16, 4
-    run = dict(gpu_batch=2, batches_per_block=2, prompt_len=s, gen_len=g, weight_tier=1)
+    run = dict(gpu_batch=2, batches_per_block=2, prompt_len=s, gen_len=g, weight_tier=tier)
     glob = synth.global_weights(shape, variant="full")
     lw = [synth.layer_weights(shape, l, variant="full") for l in range(4)]
     mats = ("q_w", "k_w", "v_w", "o_w", "fc1_w", "fc2_w")
@@ -141,6 +142,28 @@ def test_host_layers_stream_the_shared_matrices():
     assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
     with pytest.raises(tod.TodError):  # host_layers is a host-tier option
         tod.Model(shape, dict(run, weight_tier=0, host_layers=2))
+
+
+def test_int4_host_tier_matches_hbm_tier():
+    """The int4 host tier streams the same tiled int4 image the HBM tier keeps
+    resident, so prefill + decode give identical bits (tokens and logits) on a
+    block whose M takes the pipelined GEMM (4 x 40 rows) and on a smaller one."""
+    torch = torch_cuda()
+    shape = synth.OPT_125M.replace(n_layers=3)
+    s, g = 24, 5
+    for b, K in ((40, 4), (3, 2)):
+        prompts = to_dev(synth.prompt_ids(b * K, s, shape.vocab), torch)
+        outs = []
+        for tier in (0, 2):
+            m, _ = build_gpu_model(shape, dict(gpu_batch=b, batches_per_block=K, prompt_len=s, gen_len=g,
+                                               weight_tier=tier))
+            toks, logits = m.generate(prompts, g, return_logits=True)
+            torch.cuda.synchronize()
+            outs.append((toks.cpu(), logits.cpu()))
+            m.close()
+        print(f"b={b} K={K}: tokens equal {torch.equal(outs[0][0], outs[1][0])}", flush=True)
+        assert torch.equal(outs[0][0], outs[1][0])
+        assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
 
 
 @pytest.mark.parametrize("n_layers", [1, 2])

@@ -8,7 +8,7 @@ streams.
 from __future__ import annotations
 
 from . import _lib
-from ._lib import (TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM, TodError, attn_cache_create, attn_cache_export,
+from ._lib import (TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM, TOD_W_HOST_INT4_STREAM, TodError, attn_cache_create, attn_cache_export,
                    attn_cache_fill, attn_cache_free, attn_decode_step, decode_block, dequantize_groupwise,
                    export_kv, export_weight, free_model, init_model, last_error, linear_f16, linear_w4, prefill,
                    profile_kernels, profile_read, quantize_groupwise, set_decode_graph, set_decode_position,
@@ -19,7 +19,7 @@ __all__ = ["Model", "TodError", "init_model", "set_global_weights", "set_layer_w
            "free_model", "last_error", "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create",
            "attn_cache_fill", "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels",
            "profile_read",
-           "TOD_W_HBM_INT4", "TOD_W_HOST_FP16_STREAM"]
+           "TOD_W_HBM_INT4", "TOD_W_HOST_FP16_STREAM", "TOD_W_HOST_INT4_STREAM"]
 
 
 class Model:
@@ -27,7 +27,8 @@ class Model:
 
     shape: object with n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos.
     run:   dict with gpu_batch, batches_per_block, prompt_len, gen_len,
-           optional weight_tier (0 int4 in HBM, 1 fp16 streamed from pinned host) and n_blocks.
+           optional weight_tier (0 int4 in HBM, 1 fp16 or 2 int4 streamed from pinned host),
+           n_blocks and host_layers.
     """
 
     def __init__(self, shape, run: dict):

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtod.so")
 
 TOD_OK, TOD_EINVAL, TOD_ENOMEM, TOD_EHIP, TOD_ESTATE = 0, -1, -2, -3, -4
-TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM = 0, 1
+TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM, TOD_W_HOST_INT4_STREAM = 0, 1, 2
 MATRICES = ("q", "k", "v", "o", "fc1", "fc2")
 LAYER_TENSORS = ("ln1_g", "ln1_b", "q_w", "q_b", "k_w", "k_b", "v_w", "v_b",
                  "o_w", "o_b", "ln2_g", "ln2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")

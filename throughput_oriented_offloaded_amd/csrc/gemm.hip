@@ -8,16 +8,20 @@
 // tile is fetched from HBM once per step for the whole block (FlexGen guide,
 // "2. The Zig-Zag Block Schedule").
 //
-// gfx950 design:
-//  * v_mfma_f32_32x32x16_f16, fp32 accumulation; 256-thread workgroups as a
-//    2x2 grid of wavefronts, each owning a (BM/2) x (BN/2) output tile.
-//  * The activation tile (BM x 64, one quantization group of K) is staged in
-//    LDS, double-buffered, 16-byte chunks XOR-swizzled by row to spread banks.
-//  * Weights never touch LDS: the int4 store is pre-tiled so that one 16-byte
-//    load per lane brings exactly the 32 nibbles that lane feeds to four MFMA
-//    K-steps as its B operand. Dequantization is two packed-fp16 ops per pair:
-//    (nibbles | 0x6400) - 1024 gives exact codes, then one v_pk_fma_f16 with
-//    (scale, zero) rounds once, so each weight equals fp16(zero + c*scale).
+// gfx950 design (two kernels, fp32 accumulation in v_mfma_f32_32x32x16_f16):
+//  * k_gemm_w4 (int4 weights, M > 128; the decode and prefill path): 256 x 256
+//    tiles, eight wavefronts (two per SIMD), activations, codes and params fed
+//    through a 3-stage LDS ring by direct-to-LDS loads; described at the kernel.
+//  * k_gemm (M <= 128, and fp16 weights: LM head, host tier): 256-thread
+//    workgroups as a 2x2 grid of wavefronts, each owning a (BM/2) x (BN/2)
+//    output tile; the activation tile (BM x 64, one quantization group of K)
+//    is double-buffered in LDS with 16-byte chunks XOR-swizzled by row, and
+//    weights go from HBM straight to registers: the int4 store is pre-tiled so
+//    that one 16-byte load per lane brings exactly the 32 nibbles that lane
+//    feeds to four MFMA K-steps as its B operand.
+//  * Dequantization (dequant_word): masked nibbles become exact fp16 codes by
+//    one fp8 -> fp16 convert per pair, then one v_pk_fma_f16 with (scale,
+//    zero) rounds once, so each weight equals fp16(zero + c*scale).
 //  * Workgroup ids are remapped so that each XCD (ids round-robin over 8 XCDs)
 //    gets a contiguous run of tiles, M fastest: workgroups sharing a weight
 //    tile share that XCD's L2.

@@ -53,7 +53,7 @@ struct LayerStore {
     uint32_t *wp[N_GEMM_MATS] = {};   // int4 tiled (scale, zero)
     uint16_t *bias[N_GEMM_MATS] = {}; // device fp16
     uint16_t *ln1_g = nullptr, *ln1_b = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
-    uint16_t *host = nullptr;         // host tier: pinned fp16 [qkv | o | fc1 | fc2]
+    uint8_t *host = nullptr;          // host tiers: pinned image of the layer's matrices
     bool loaded = false;
 };
 
@@ -65,8 +65,11 @@ struct tod_model {
     int M = 0;      // rows per block (K * b)
     int cap = 0;    // KV positions per (sequence, head), multiple of 64
     int n_out[N_GEMM_MATS] = {}, n_in[N_GEMM_MATS] = {};
-    int64_t mat_off[N_GEMM_MATS] = {}; // host tier: element offset of each matrix
-    int64_t layer_elems = 0;           // host tier: elements per layer
+    // host tiers: byte offsets of each matrix's image in a layer (fp16 values, or
+    // tiled int4 codes followed by their tiled params) and the layer's size
+    int64_t mat_off[N_GEMM_MATS] = {}, par_off[N_GEMM_MATS] = {};
+    int64_t layer_bytes = 0;
+    bool streamed = false, int4 = true; // weights streamed from host; int4 GEMMs
     int host_layers = 0;               // host tier: layers with their own pinned matrices
     std::vector<LayerStore> layers;
     uint16_t *tok_emb = nullptr, *pos_emb = nullptr, *lnf_g = nullptr, *lnf_b = nullptr;
@@ -85,7 +88,7 @@ struct tod_model {
     uint8_t *stage_codes = nullptr;
     uint16_t *stage_scale = nullptr, *stage_zero = nullptr;
     // host tier streaming
-    uint16_t *slot[2] = {};
+    uint8_t *slot[2] = {};
     hipStream_t copy = nullptr;
     hipEvent_t ev_loaded[2] = {}, ev_free[2] = {};
     std::vector<int> prefilled, decoded;
@@ -210,18 +213,28 @@ struct ProfScope {
     }
 };
 
-int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint16_t *wf,
+// Weights of matrix `mat` of layer L: HBM int4, or the layer's image in a
+// streamed slot (fp16 values, or tiled int4 codes and params).
+void weights_of(const tod_model *m, const LayerStore &L, int mat, const uint8_t *slot, GemmArgs &g)
+{
+    if (!slot) {
+        g.wc = L.wc[mat];
+        g.wp = L.wp[mat];
+    } else if (m->int4) {
+        g.wc = reinterpret_cast<const uint32_t *>(slot + m->mat_off[mat]);
+        g.wp = reinterpret_cast<const uint32_t *>(slot + m->par_off[mat]);
+    } else {
+        g.wf = reinterpret_cast<const uint16_t *>(slot + m->mat_off[mat]);
+    }
+}
+
+int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint8_t *slot,
              uint16_t *y, int64_t ldc, int epi, hipStream_t st)
 {
     GemmArgs g{};
     g.a = a;
     g.lda = m->n_in[mat];
-    if (wf) {
-        g.wf = wf;
-    } else {
-        g.wc = L.wc[mat];
-        g.wp = L.wp[mat];
-    }
+    weights_of(m, L, mat, slot, g);
     g.bias = L.bias[mat];
     g.residual = epi == EPI_BIAS_RES ? y : nullptr;
     g.y = y;
@@ -241,20 +254,16 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
 // decode: rows = M sequences at position pos; prefill: rows = b * s (b sequences
 // starting at seq0, positions 0..s-1).
 int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, bool prefill_mode, int seq0, int s,
-               int pos, const int *dpos, const uint16_t *wslot, hipStream_t st)
+               int pos, const int *dpos, const uint8_t *wslot, hipStream_t st)
 {
     const int hd = m->cfg.hidden, f = m->cfg.ffn;
     const LayerStore &L = m->layers[l];
-    const uint16_t *wq = wslot ? wslot + m->mat_off[MAT_QKV] : nullptr;
-    const uint16_t *wo = wslot ? wslot + m->mat_off[MAT_O] : nullptr;
-    const uint16_t *w1 = wslot ? wslot + m->mat_off[MAT_FC1] : nullptr;
-    const uint16_t *w2 = wslot ? wslot + m->mat_off[MAT_FC2] : nullptr;
     int rc;
     {
         ProfScope ps(m, TOD_K_LAYERNORM, st);
         HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
     }
-    if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wq, m->qkv, 3 * hd, EPI_BIAS, st)))
+    if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wslot, m->qkv, 3 * hd, EPI_BIAS, st)))
         return rc;
     SrcMap src;
     RowMap map;
@@ -276,15 +285,15 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         else
             HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, dpos, kv, st));
     }
-    if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wo, h, hd, EPI_BIAS_RES, st)))
+    if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wslot, h, hd, EPI_BIAS_RES, st)))
         return rc;
     {
         ProfScope ps(m, TOD_K_LAYERNORM, st);
         HIPCHK(launch_layernorm(h, rows, hd, L.ln2_g, L.ln2_b, m->act, st));
     }
-    if ((rc = run_gemm(m, m->act, rows, MAT_FC1, L, w1, m->ffn, f, EPI_BIAS_RELU, st)))
+    if ((rc = run_gemm(m, m->act, rows, MAT_FC1, L, wslot, m->ffn, f, EPI_BIAS_RELU, st)))
         return rc;
-    if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, w2, h, hd, EPI_BIAS_RES, st)))
+    if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, wslot, h, hd, EPI_BIAS_RES, st)))
         return rc;
     return TOD_OK;
 }
@@ -294,7 +303,7 @@ int stream_layer(tod_model *m, int l)
 {
     const int sl = l & 1;
     HIPCHK(hipStreamWaitEvent(m->copy, m->ev_free[sl], 0));
-    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[l % m->host_layers].host, (size_t)m->layer_elems * 2,
+    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[l % m->host_layers].host, (size_t)m->layer_bytes,
                           hipMemcpyHostToDevice, m->copy));
     HIPCHK(hipEventRecord(m->ev_loaded[sl], m->copy));
     return TOD_OK;
@@ -305,12 +314,12 @@ template <class F>
 int stack_pass(tod_model *m, hipStream_t st, F body)
 {
     const int L = m->cfg.n_layers;
-    const bool host = m->run.weight_tier == TOD_W_HOST_FP16_STREAM;
+    const bool host = m->streamed;
     int rc;
     if (host && (rc = stream_layer(m, 0)))
         return rc;
     for (int l = 0; l < L; l++) {
-        const uint16_t *wslot = nullptr;
+        const uint8_t *wslot = nullptr;
         if (host) {
             if (l + 1 < L && (rc = stream_layer(m, l + 1)))
                 return rc;
@@ -432,7 +441,8 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         return fail(TOD_EINVAL, "group must be 64 (got %d)", r.group);
     if (r.gpu_batch <= 0 || r.batches_per_block <= 0 || r.prompt_len <= 0 || r.gen_len <= 0 || r.n_blocks <= 0)
         return fail(TOD_EINVAL, "run config fields must be positive");
-    if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM)
+    if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM &&
+        r.weight_tier != TOD_W_HOST_INT4_STREAM)
         return fail(TOD_EINVAL, "unknown weight tier %d", r.weight_tier);
     if (r.prompt_len + r.gen_len - 1 > c.max_pos)
         return fail(TOD_EINVAL, "prompt_len + gen_len - 1 exceeds max_pos");
@@ -445,15 +455,26 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     m->n_out[MAT_O] = h;       m->n_in[MAT_O] = h;
     m->n_out[MAT_FC1] = f;     m->n_in[MAT_FC1] = h;
     m->n_out[MAT_FC2] = h;     m->n_in[MAT_FC2] = f;
-    m->mat_off[MAT_QKV] = 0;
-    m->mat_off[MAT_O] = (int64_t)3 * h * h;
-    m->mat_off[MAT_FC1] = (int64_t)4 * h * h;
-    m->mat_off[MAT_FC2] = (int64_t)4 * h * h + (int64_t)f * h;
-    m->layer_elems = (int64_t)4 * h * h + 2 * (int64_t)f * h;
+    m->streamed = r.weight_tier != TOD_W_HBM_INT4;
+    m->int4 = r.weight_tier != TOD_W_HOST_FP16_STREAM;
+    // a layer's image on the host tiers: the four GEMM matrices back to back,
+    // fp16 values, or tiled int4 codes each followed by its tiled params
+    int64_t off = 0;
+    for (int mat = 0; mat < N_GEMM_MATS; mat++) {
+        const int64_t n = (int64_t)m->n_out[mat] * m->n_in[mat];
+        m->mat_off[mat] = off;
+        if (m->int4) {
+            m->par_off[mat] = off + n / 2;
+            off += n / 2 + n / 16;
+        } else {
+            off += n * 2;
+        }
+    }
+    m->layer_bytes = off;
     m->layers.resize(L);
-    const bool host = r.weight_tier == TOD_W_HOST_FP16_STREAM;
+    const bool host = m->streamed;
     if (r.host_layers < 0 || (r.host_layers && !host))
-        return fail(TOD_EINVAL, "host_layers (%d) applies to the host tier only and must be >= 0", r.host_layers);
+        return fail(TOD_EINVAL, "host_layers (%d) applies to the host tiers only and must be >= 0", r.host_layers);
     m->host_layers = r.host_layers > 0 && r.host_layers < L ? r.host_layers : L;
 
     // weights
@@ -473,14 +494,14 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         ALLOC(S_.ln2_b, (size_t)h * 2);
         if (host && l < m->host_layers) {
             void *p = nullptr;
-            hipError_t e = hipHostMalloc(&p, (size_t)m->layer_elems * 2, hipHostMallocDefault);
+            hipError_t e = hipHostMalloc(&p, (size_t)m->layer_bytes, hipHostMallocDefault);
             if (e != hipSuccess) {
                 (void)hipGetLastError();
                 return fail(TOD_ENOMEM, "hipHostMalloc(%lld bytes) for layer %d failed: %s",
-                            (long long)m->layer_elems * 2, l, hipGetErrorString(e));
+                            (long long)m->layer_bytes, l, hipGetErrorString(e));
             }
             m->host_allocs.push_back(p);
-            S_.host = static_cast<uint16_t *>(p);
+            S_.host = static_cast<uint8_t *>(p);
         }
     }
     ALLOC(m->tok_emb, (size_t)c.vocab * h * 2);
@@ -520,7 +541,7 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     const int rows_list[2] = {m->M, (int)prow};
     for (int ri = 0; ri < 2; ri++)
         for (int mat = 0; mat < N_GEMM_MATS; mat++) {
-            const size_t b = gemm_workspace_bytes(rows_list[ri], m->n_out[mat], m->n_in[mat], !host);
+            const size_t b = gemm_workspace_bytes(rows_list[ri], m->n_out[mat], m->n_in[mat], m->int4);
             ws = b > ws ? b : ws;
         }
     {
@@ -531,14 +552,15 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     ALLOC(m->ws, ws);
 
     if (host) {
-        ALLOC(m->slot[0], (size_t)m->layer_elems * 2);
-        ALLOC(m->slot[1], (size_t)m->layer_elems * 2);
+        ALLOC(m->slot[0], (size_t)m->layer_bytes);
+        ALLOC(m->slot[1], (size_t)m->layer_bytes);
         HIPCHK(hipStreamCreateWithFlags(&m->copy, hipStreamNonBlocking));
         for (int i = 0; i < 2; i++) {
             HIPCHK(hipEventCreateWithFlags(&m->ev_loaded[i], hipEventDisableTiming));
             HIPCHK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
         }
-    } else {
+    }
+    if (m->int4) { // quantization staging for the HBM and int4 host tiers
         const int64_t big = (int64_t)(f > 3 * h ? f : 3 * h) * h;
         ALLOC(m->stage, (size_t)big * 2);
         ALLOC(m->stage_codes, (size_t)big / 2);
@@ -619,22 +641,31 @@ int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
         int tensor, mat, row0, rows, cols;
     } parts[6] = {{TOD_Q_W, MAT_QKV, 0, h, h},   {TOD_K_W, MAT_QKV, h, h, h}, {TOD_V_W, MAT_QKV, 2 * h, h, h},
                   {TOD_O_W, MAT_O, 0, h, h},     {TOD_FC1_W, MAT_FC1, 0, f, h}, {TOD_FC2_W, MAT_FC2, 0, h, f}};
-    if (m->run.weight_tier == TOD_W_HOST_FP16_STREAM) {
-        if (layer < m->host_layers) // later layers stream the matrices of layer % host_layers
-            for (const Part &p : parts)
-                memcpy(L.host + m->mat_off[p.mat] + (int64_t)p.row0 * p.cols, t[p.tensor],
-                       (size_t)p.rows * p.cols * 2);
+    if (m->streamed && layer >= m->host_layers) {
+        // this layer streams the matrices of layer % host_layers
+    } else if (!m->int4) {
+        for (const Part &p : parts)
+            memcpy(L.host + m->mat_off[p.mat] + ((int64_t)p.row0 * p.cols) * 2, t[p.tensor],
+                   (size_t)p.rows * p.cols * 2);
     } else {
+        // quantize in HBM; the int4 host tier builds the layer's image in slot 0
+        // (idle outside a pass) and copies it to its pinned buffer
+        HIPCHK(hipDeviceSynchronize());
         for (const Part &p : parts) {
             const int64_t n = (int64_t)p.rows * p.cols;
             const int KG = p.cols / 64;
             HIPCHK(hipMemcpy(m->stage, t[p.tensor], (size_t)n * 2, hipMemcpyHostToDevice));
             HIPCHK(launch_quantize_groupwise(m->stage, n, m->stage_codes, m->stage_scale, m->stage_zero, nullptr));
             const int64_t nb0 = p.row0 / 32;
+            GemmArgs dst{};
+            weights_of(m, L, p.mat, m->streamed ? m->slot[0] : nullptr, dst);
             HIPCHK(launch_repack_w4(m->stage_codes, m->stage_scale, m->stage_zero, p.rows, p.cols,
-                                    L.wc[p.mat] + nb0 * KG * 256, L.wp[p.mat] + nb0 * KG * 32, nullptr));
+                                    const_cast<uint32_t *>(dst.wc) + nb0 * KG * 256,
+                                    const_cast<uint32_t *>(dst.wp) + nb0 * KG * 32, nullptr));
         }
         HIPCHK(hipDeviceSynchronize());
+        if (m->streamed)
+            HIPCHK(hipMemcpy(L.host, m->slot[0], (size_t)m->layer_bytes, hipMemcpyDeviceToHost));
     }
     L.loaded = true;
     return TOD_OK;
@@ -656,7 +687,7 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
         HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, nullptr, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
                                 m->hid + k * brow * h, st));
     }
-    rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
+    rc = stack_pass(m, st, [&](int l, const uint8_t *wslot) -> int {
         const KvView &kv = m->kv[(size_t)block * L + l];
         for (int kk = 0; kk < K; kk++) {
             const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
@@ -688,7 +719,7 @@ static int decode_step(tod_model *m, int block, const int32_t *in, int pos, cons
         ProfScope ps(m, TOD_K_EMBED, st);
         HIPCHK(launch_embed(in, Mr, 1, pos, dpos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
     }
-    int rc = stack_pass(m, st, [&](int l, const uint16_t *wslot) -> int {
+    int rc = stack_pass(m, st, [&](int l, const uint8_t *wslot) -> int {
         return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, dpos, wslot, st);
     });
     if (rc)
@@ -831,10 +862,17 @@ int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t
         return fail(TOD_EINVAL, "null argument");
     if (layer < 0 || layer >= m->cfg.n_layers || which < TOD_MAT_Q || which > TOD_MAT_FC2)
         return fail(TOD_EINVAL, "layer or matrix id out of range");
-    if (m->run.weight_tier != TOD_W_HBM_INT4)
-        return fail(TOD_ESTATE, "the host tier keeps fp16 weights");
+    if (!m->int4)
+        return fail(TOD_ESTATE, "the fp16 host tier keeps fp16 weights");
     if (!m->layers[layer].loaded)
         return fail(TOD_ESTATE, "layer %d weights not set", layer);
+    const uint8_t *slot = nullptr;
+    if (m->streamed) { // bring the layer's pinned image into slot 0 (idle outside a pass)
+        HIPCHK(hipDeviceSynchronize());
+        HIPCHK(hipMemcpy(m->slot[0], m->layers[layer % m->host_layers].host, (size_t)m->layer_bytes,
+                         hipMemcpyHostToDevice));
+        slot = m->slot[0];
+    }
     const int h = m->cfg.hidden, f = m->cfg.ffn;
     int mat, row0 = 0, rows = h, cols = h;
     switch (which) {
@@ -847,9 +885,10 @@ int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t
     }
     const int KG = cols / 64;
     const int64_t nb0 = row0 / 32;
-    const LayerStore &L = m->layers[layer];
-    HIPCHK(launch_unpack_w4(L.wc[mat] + nb0 * KG * 256, L.wp[mat] + nb0 * KG * 32, rows, cols, d_codes, d_scale,
-                            d_zero, S(stream)));
+    GemmArgs src{};
+    weights_of(m, m->layers[layer], mat, slot, src);
+    HIPCHK(launch_unpack_w4(src.wc + nb0 * KG * 256, src.wp + nb0 * KG * 32, rows, cols, d_codes, d_scale, d_zero,
+                            S(stream)));
     return TOD_OK;
 }
 
