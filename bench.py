@@ -99,20 +99,25 @@ def host_tier_bench(args, w, tod, synth, torch):
     """Decode with weights streamed per layer from pinned host memory: fp16
     (weight tier 1) or the tiled int4 image (tier 2, 0.5625 byte per weight).
 
-    The step is bound by the host link (every layer's matrices cross it once
-    per step), so the report is tokens/s and link GB/s against a measured
-    pinned -> HBM copy of the same size. Only --host-layers distinct
-    layers keep pinned matrices (the others stream layer % host_layers), so the
-    stack fits host memory; the prompt is shortened (--prompt-len, default 16)
-    because prefill at 512 tokens would take minutes of fp16 GEMMs, and a
-    link-bound step does not depend on the attended context."""
+    The step is bound by the host link (every streamed layer's matrices cross
+    it once per step), so the report is tokens/s and link GB/s against a
+    measured pinned -> HBM copy of the same size. --hbm-layers R keeps the
+    first R layers' images resident in HBM (they never cross the link); of the
+    streamed layers only --host-layers distinct ones keep pinned matrices (the
+    others stream those in turn), so the stack fits host memory, and resident
+    layers other than layer 0 are given layer 0's matrices with their own
+    vectors (values do not change the work). The prompt is shortened
+    (--prompt-len, default 16) because prefill at 512 tokens would take minutes
+    of fp16 GEMMs, and a link-bound step does not depend on the attended
+    context."""
     import dataclasses
     w = dataclasses.replace(w, prompt_len=args.prompt_len or 16)
     shape, M = w.shape, w.rows
     L, h, f = shape.n_layers, shape.hidden, shape.ffn
-    P = min(args.host_layers, L)
+    R = min(max(args.hbm_layers, 0), L)
+    P = min(args.host_layers, L - R)
     run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
-               gen_len=w.gen_len, weight_tier=w.weight_tier, host_layers=P)
+               gen_len=w.gen_len, weight_tier=w.weight_tier, host_layers=P, hbm_layers=R)
     t_setup = time.perf_counter()
     m = tod.Model(shape, run)
     g = synth.global_weights(shape)
@@ -121,17 +126,17 @@ def host_tier_bench(args, w, tod, synth, torch):
     mats = ("q_w", "k_w", "v_w", "o_w", "fc1_w", "fc2_w")
     shared = None
     for l in range(L):
-        if l < P:
+        if l == 0 or R <= l < R + P:
             t = synth.layer_weights(shape, l)
             if shared is None:
-                shared = {n: t[n] for n in mats}  # placeholders for layers that stream a shared copy
+                shared = {n: t[n] for n in mats}  # placeholders for layers that reuse a copy
         else:
             t = {n: synth.draw_tensor(shape, n, l) for n in synth.LAYER_TENSORS if n not in mats}
             t.update(shared)
         m.set_layer_weights(l, t)
         del t
         if (l + 1) % 8 == 0 or l + 1 == L:
-            log(f"weights: {l + 1}/{L} layers set ({P} with pinned matrices)")
+            log(f"weights: {l + 1}/{L} layers set ({R} resident in HBM, {P} with pinned matrices)")
     del shared
     prompts = torch.from_numpy(synth.prompt_ids(M, w.prompt_len, shape.vocab)).cuda()
     first = torch.empty(M, dtype=torch.int32, device="cuda")
@@ -161,7 +166,7 @@ def host_tier_bench(args, w, tod, synth, torch):
     int4 = w.weight_tier == 2
     layer_weights = 4 * h * h + 2 * f * h
     layer_bytes = layer_weights // 2 + layer_weights // 16 if int4 else layer_weights * 2
-    link_gbs = L * layer_bytes * steps / elapsed / 1e9
+    link_gbs = (L - R) * layer_bytes * steps / elapsed / 1e9
     log("measuring pinned -> HBM copy rate ...")
     h2d = measure_h2d(torch, layer_bytes)
     return {
@@ -182,12 +187,12 @@ def host_tier_bench(args, w, tod, synth, torch):
                    "layers": L, "hidden": h,
                    "heads": shape.n_heads, "head_dim": shape.head_dim, "ffn": f, "vocab": shape.vocab,
                    "gpu_batch": w.gpu_batch, "batches_per_block": w.batches_per_block, "rows": M,
-                   "prompt_len": w.prompt_len, "gen_len": w.gen_len, "host_layers_pinned": P,
+                   "prompt_len": w.prompt_len, "gen_len": w.gen_len, "hbm_layers": R, "host_layers_pinned": P,
                    "weights": ("int4 group-64 (tiled codes + fp16 scale/zero)" if int4 else "fp16")
                    + " in pinned host memory, 2 HBM layer slots, copies on a side stream"},
         "roofline": {"bound": "link", "achieved": link_gbs, "peak": h2d, "unit": "GB/s", "frac": link_gbs / h2d,
                      "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"},
-        "link_bytes_per_step": L * layer_bytes,
+        "link_bytes_per_step": (L - R) * layer_bytes,
         "h2d_measured_gbs": h2d,
         "prefill_s": prefill_s,
     }
@@ -333,6 +338,8 @@ def main():
                          "opt-175b-int4 (int4 host tier) | attention")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--prompt-len", type=int, default=0, help="host tiers only: prompt length (default 16)")
+    ap.add_argument("--hbm-layers", type=int, default=0,
+                    help="host tiers only: leading layers whose weights stay resident in HBM (default 0)")
     ap.add_argument("--host-layers", type=int, default=8,
                     help="host tiers only: layers with their own pinned matrices (default 8)")
     ap.add_argument("--progress", action="store_true",

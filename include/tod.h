@@ -81,14 +81,23 @@ typedef struct {
  * has prompt_len prompt tokens and at most gen_len generated tokens, so the
  * KV cache holds prompt_len + gen_len - 1 positions. n_blocks blocks are
  * resident at once (each has its own KV cache). group must be 64.
- * host_layers (host tiers only; 0 = n_layers): pinned host memory is kept for
- * the six matrices of layers 0..host_layers-1 only, and layer l streams the
- * matrices of layer l % host_layers (its vectors stay its own). This exists to
- * measure stacks whose fp16 weights exceed the host's memory: copy sizes,
+ * hbm_layers (host tiers only; 0..n_layers, default 0): layers 0..hbm_layers-1
+ * keep their weight image (the bytes a streamed layer would copy) resident in
+ * HBM and never cross the host link; the remaining layers stream. This is the
+ * placement choice the FlexLLMGen overview ("A 175B-parameter model on one
+ * GPU, if you can wait": what it does; caveats, the manual placement flags)
+ * leaves to the user: what share of the weights sits on the GPU versus host
+ * memory. Results are identical for every hbm_layers.
+ * host_layers (host tiers only; 0 = every streamed layer): pinned host memory
+ * is kept for the six matrices of the first host_layers streamed layers only,
+ * and a later streamed layer l streams those of layer
+ * hbm_layers + (l - hbm_layers) % host_layers (its vectors stay its own). This
+ * exists to measure stacks whose weights exceed the host's memory: copy sizes,
  * streams and overlap are those of distinct layers. */
 typedef struct {
     int32_t gpu_batch, batches_per_block, prompt_len, gen_len, group, weight_tier, n_blocks;
     int32_t host_layers;
+    int32_t hbm_layers;
 } tod_run_config;
 
 /*
@@ -125,9 +134,8 @@ int set_global_weights(tod_model *m, const uint16_t *h_tok_emb, const uint16_t *
  * cross the host link instead of fp16 (FlexGen guide, "3. Group-Wise 4-Bit
  * Quantization", transfer of packed 4-bit data over PCIe); results are
  * identical to TOD_W_HBM_INT4.
- * On both host tiers, layers at or past run.host_layers (when set) do not
- * read their matrices (they stream those of layer % host_layers), only their
- * vectors.
+ * On both host tiers, streamed layers that reuse an earlier layer's pinned
+ * image (run.host_layers) do not read their matrices, only their vectors.
  */
 int set_layer_weights(tod_model *m, int layer, const uint16_t *const *h_tensors);
 
@@ -219,9 +227,9 @@ int profile_read(tod_model *m, int kind, double *total_ms, int64_t *launches);
 /*
  * export_weight: copy layer `layer`'s matrix `which` (TOD_MAT_*) back out of
  * the int4 store in the canonical format (device buffers: codes [out*in/2],
- * scale and zero [out*in/64]). On the int4 host tier the layer's pinned image
- * (that of layer % host_layers) is read back through an idle streaming slot;
- * the call synchronizes the device first. TOD_ESTATE for the fp16 host tier.
+ * scale and zero [out*in/64]). On the int4 host tier a streamed layer's
+ * pinned image (see run.host_layers) is read back through an idle streaming
+ * slot, after a device synchronize. TOD_ESTATE for the fp16 host tier.
  */
 int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t *d_scale, uint16_t *d_zero,
                   void *stream);

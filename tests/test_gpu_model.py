@@ -111,10 +111,13 @@ def test_opt125m_full_generation(tier):
 
 
 @pytest.mark.parametrize("tier", [1, 2])
-def test_host_layers_stream_the_shared_matrices(tier):
-    """Host tiers with host_layers = 2 of 4: layers 2 and 3 stream the matrices of
-    layers 0 and 1 with their own vectors; identical bits to a model whose layers
-    2 and 3 are given those matrices outright."""
+def test_layer_placements_give_identical_bits(tier):
+    """Host tiers, a 4-layer stack whose layer 3 has layer 1's matrices: every
+    placement gives the same tokens and logits, and (int4 tier) the same
+    exported weights. Placements (hbm_layers, host_layers): all streamed; two
+    or all four layers resident in HBM; one resident and two pinned images
+    shared by the three streamed layers, where layer 3 streams layer 1's image
+    and its own matrices (given as zeros) are never read."""
     torch = torch_cuda()
     import throughput_oriented_offloaded_amd as tod
     shape = synth.OPT_125M.replace(n_layers=4)
@@ -123,25 +126,67 @@ def test_host_layers_stream_the_shared_matrices(tier):
     glob = synth.global_weights(shape, variant="full")
     lw = [synth.layer_weights(shape, l, variant="full") for l in range(4)]
     mats = ("q_w", "k_w", "v_w", "o_w", "fc1_w", "fc2_w")
+    for n in mats:
+        lw[3][n] = lw[1][n]
     prompts = to_dev(synth.prompt_ids(4, s, shape.vocab), torch)
     outs = []
-    for host_layers in (2, 0):
-        m = tod.Model(shape, dict(run, host_layers=host_layers))
+    for hbm_layers, host_layers in ((0, 0), (2, 0), (4, 0), (1, 2)):
+        m = tod.Model(shape, dict(run, hbm_layers=hbm_layers, host_layers=host_layers))
         m.set_global_weights(glob["tok_emb"], glob["pos_emb"], glob["lnf_g"], glob["lnf_b"])
         for l in range(4):
             t = dict(lw[l])
-            if l >= 2:
-                for n in mats:  # aliased layers: the streamed matrices are layer l - 2's
-                    t[n] = lw[l - 2][n] if host_layers == 0 else np.zeros_like(lw[l][n])
+            if host_layers and l >= hbm_layers + host_layers:
+                for n in mats:
+                    t[n] = np.zeros_like(lw[l][n])
             m.set_layer_weights(l, t)
         toks, logits = m.generate(prompts, g, return_logits=True)
+        exported = []
+        if tier == 2:
+            for l in (0, 3):
+                codes = torch.empty(shape.ffn * shape.hidden // 2, dtype=torch.uint8, device="cuda")
+                scale = torch.empty(shape.ffn * shape.hidden // 64, dtype=torch.float16, device="cuda")
+                zero = torch.empty_like(scale)
+                tod.export_weight(m.handle, l, "fc1", codes, scale, zero)
+                exported += [codes.cpu(), scale.cpu().view(torch.int16), zero.cpu().view(torch.int16)]
         torch.cuda.synchronize()
-        outs.append((toks.cpu(), logits.cpu()))
+        outs.append((toks.cpu(), logits.cpu().view(torch.int16), exported))
         m.close()
-    assert torch.equal(outs[0][0], outs[1][0])
-    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
-    with pytest.raises(tod.TodError):  # host_layers is a host-tier option
-        tod.Model(shape, dict(run, weight_tier=0, host_layers=2))
+        print(f"tier {tier} hbm_layers {hbm_layers} host_layers {host_layers}: tokens equal "
+              f"{torch.equal(outs[0][0], outs[-1][0])}", flush=True)
+    for toks, logits, exported in outs[1:]:
+        assert torch.equal(outs[0][0], toks)
+        assert torch.equal(outs[0][1], logits)
+        assert all(torch.equal(x, y) for x, y in zip(outs[0][2], exported))
+    for bad in (dict(weight_tier=0, host_layers=2), dict(weight_tier=0, hbm_layers=1), dict(hbm_layers=5),
+                dict(hbm_layers=-1)):
+        with pytest.raises(tod.TodError):  # placement fields belong to the host tiers, within the stack
+            tod.Model(shape, dict(run, **bad))
+
+
+@pytest.mark.parametrize("tier", [1, 2])
+def test_weights_set_after_a_pass_are_streamed(tier):
+    """A pass leaves the next pass's first streamed layer copied ahead into a
+    slot; setting that layer's weights afterwards must replace it: generating
+    again equals a fresh model built with the new weights."""
+    torch = torch_cuda()
+    shape = synth.OPT_125M.replace(n_layers=3)
+    s, g = 16, 3
+    run = dict(gpu_batch=2, batches_per_block=2, prompt_len=s, gen_len=g, weight_tier=tier, hbm_layers=1)
+    prompts = to_dev(synth.prompt_ids(4, s, shape.vocab), torch)
+    m, _ = build_gpu_model(shape, run)
+    m.generate(prompts, g)
+    m.set_layer_weights(1, synth.layer_weights(shape, 2, variant="full"))
+    toks, logits = m.generate(prompts, g, return_logits=True)
+    torch.cuda.synchronize()
+    got = (toks.cpu(), logits.cpu().view(torch.int16))
+    m.close()
+    ref, _ = build_gpu_model(shape, run)
+    ref.set_layer_weights(1, synth.layer_weights(shape, 2, variant="full"))
+    toks, logits = ref.generate(prompts, g, return_logits=True)
+    torch.cuda.synchronize()
+    ref.close()
+    assert torch.equal(got[0], toks.cpu())
+    assert torch.equal(got[1], logits.cpu().view(torch.int16))
 
 
 def test_int4_host_tier_matches_hbm_tier():

@@ -28,7 +28,7 @@ class Model:
     shape: object with n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos.
     run:   dict with gpu_batch, batches_per_block, prompt_len, gen_len,
            optional weight_tier (0 int4 in HBM, 1 fp16 or 2 int4 streamed from pinned host),
-           n_blocks and host_layers.
+           n_blocks, host_layers and hbm_layers.
     """
 
     def __init__(self, shape, run: dict):

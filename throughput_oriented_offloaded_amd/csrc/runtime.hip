@@ -54,6 +54,7 @@ struct LayerStore {
     uint16_t *bias[N_GEMM_MATS] = {}; // device fp16
     uint16_t *ln1_g = nullptr, *ln1_b = nullptr, *ln2_g = nullptr, *ln2_b = nullptr;
     uint8_t *host = nullptr;          // host tiers: pinned image of the layer's matrices
+    uint8_t *dev = nullptr;           // host tiers, resident layers: that image kept in HBM
     bool loaded = false;
 };
 
@@ -70,7 +71,8 @@ struct tod_model {
     int64_t mat_off[N_GEMM_MATS] = {}, par_off[N_GEMM_MATS] = {};
     int64_t layer_bytes = 0;
     bool streamed = false, int4 = true; // weights streamed from host; int4 GEMMs
-    int host_layers = 0;               // host tier: layers with their own pinned matrices
+    int hbm_layers = 0;                // host tiers: leading layers whose image stays in HBM
+    int host_layers = 0;               // host tiers: streamed layers with their own pinned image
     std::vector<LayerStore> layers;
     uint16_t *tok_emb = nullptr, *pos_emb = nullptr, *lnf_g = nullptr, *lnf_b = nullptr;
     bool glob_loaded = false;
@@ -91,6 +93,7 @@ struct tod_model {
     uint8_t *slot[2] = {};
     hipStream_t copy = nullptr;
     hipEvent_t ev_loaded[2] = {}, ev_free[2] = {};
+    bool prefetched = false; // slot 0 holds, or is being filled with, the first streamed layer
     std::vector<int> prefilled, decoded;
     // captured decode steps (HBM tier): one graph per block, replayed on gstream;
     // the step reads its position from gpos and its token ids from gids (the
@@ -298,12 +301,21 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
     return TOD_OK;
 }
 
-// Host tier: enqueue the copy of layer l into slot l % 2 on the copy stream.
+// Host tiers: the layer whose pinned image streamed layer l copies. Streamed
+// layers past the first host_layers reuse theirs, in turn.
+int image_layer(const tod_model *m, int l)
+{
+    const int R = m->hbm_layers;
+    return l < R + m->host_layers ? l : R + (l - R) % m->host_layers;
+}
+
+// Host tiers: enqueue the copy of streamed layer l into its slot (streamed
+// layers alternate between the two) on the copy stream.
 int stream_layer(tod_model *m, int l)
 {
-    const int sl = l & 1;
+    const int sl = (l - m->hbm_layers) & 1;
     HIPCHK(hipStreamWaitEvent(m->copy, m->ev_free[sl], 0));
-    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[l % m->host_layers].host, (size_t)m->layer_bytes,
+    HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[image_layer(m, l)].host, (size_t)m->layer_bytes,
                           hipMemcpyHostToDevice, m->copy));
     HIPCHK(hipEventRecord(m->ev_loaded[sl], m->copy));
     return TOD_OK;
@@ -313,23 +325,33 @@ int stream_layer(tod_model *m, int l)
 template <class F>
 int stack_pass(tod_model *m, hipStream_t st, F body)
 {
-    const int L = m->cfg.n_layers;
-    const bool host = m->streamed;
+    // layers below R run from HBM (the int4 store, or a host tier's resident
+    // image); the others stream. The first streamed layer's copy is issued at
+    // the end of the previous pass (layer images never change during passes),
+    // so it overlaps that pass's tail, the head and this pass's resident layers.
+    const int L = m->cfg.n_layers, R = m->streamed ? m->hbm_layers : L;
     int rc;
-    if (host && (rc = stream_layer(m, 0)))
+    if (R < L && !m->prefetched && (rc = stream_layer(m, R)))
         return rc;
+    m->prefetched = false;
     for (int l = 0; l < L; l++) {
-        const uint8_t *wslot = nullptr;
-        if (host) {
+        const uint8_t *wslot = l < R ? m->layers[l].dev : nullptr;
+        const int sl = (l - R) & 1;
+        if (l >= R) {
             if (l + 1 < L && (rc = stream_layer(m, l + 1)))
                 return rc;
-            HIPCHK(hipStreamWaitEvent(st, m->ev_loaded[l & 1], 0));
-            wslot = m->slot[l & 1];
+            HIPCHK(hipStreamWaitEvent(st, m->ev_loaded[sl], 0));
+            wslot = m->slot[sl];
         }
         if ((rc = body(l, wslot)))
             return rc;
-        if (host)
-            HIPCHK(hipEventRecord(m->ev_free[l & 1], st));
+        if (l >= R)
+            HIPCHK(hipEventRecord(m->ev_free[sl], st));
+    }
+    if (R < L) { // the next pass's first copy, ordered after this pass's use of its slot
+        if ((rc = stream_layer(m, R)))
+            return rc;
+        m->prefetched = true;
     }
     return TOD_OK;
 }
@@ -475,7 +497,12 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     const bool host = m->streamed;
     if (r.host_layers < 0 || (r.host_layers && !host))
         return fail(TOD_EINVAL, "host_layers (%d) applies to the host tiers only and must be >= 0", r.host_layers);
-    m->host_layers = r.host_layers > 0 && r.host_layers < L ? r.host_layers : L;
+    if (r.hbm_layers < 0 || r.hbm_layers > L || (r.hbm_layers && !host))
+        return fail(TOD_EINVAL, "hbm_layers (%d) applies to the host tiers only and must be in [0, n_layers]",
+                    r.hbm_layers);
+    m->hbm_layers = host ? r.hbm_layers : 0;
+    const int n_streamed = host ? L - m->hbm_layers : 0;
+    m->host_layers = r.host_layers > 0 && r.host_layers < n_streamed ? r.host_layers : n_streamed;
 
     // weights
     for (int l = 0; l < L; l++) {
@@ -492,7 +519,9 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         ALLOC(S_.ln1_b, (size_t)h * 2);
         ALLOC(S_.ln2_g, (size_t)h * 2);
         ALLOC(S_.ln2_b, (size_t)h * 2);
-        if (host && l < m->host_layers) {
+        if (host && l < m->hbm_layers)
+            ALLOC(S_.dev, (size_t)m->layer_bytes);
+        if (host && l >= m->hbm_layers && l < m->hbm_layers + m->host_layers) {
             void *p = nullptr;
             hipError_t e = hipHostMalloc(&p, (size_t)m->layer_bytes, hipHostMallocDefault);
             if (e != hipSuccess) {
@@ -552,8 +581,10 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     ALLOC(m->ws, ws);
 
     if (host) {
-        ALLOC(m->slot[0], (size_t)m->layer_bytes);
-        ALLOC(m->slot[1], (size_t)m->layer_bytes);
+        if (n_streamed > 0) {
+            ALLOC(m->slot[0], (size_t)m->layer_bytes);
+            ALLOC(m->slot[1], (size_t)m->layer_bytes);
+        }
         HIPCHK(hipStreamCreateWithFlags(&m->copy, hipStreamNonBlocking));
         for (int i = 0; i < 2; i++) {
             HIPCHK(hipEventCreateWithFlags(&m->ev_loaded[i], hipEventDisableTiming));
@@ -641,15 +672,27 @@ int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
         int tensor, mat, row0, rows, cols;
     } parts[6] = {{TOD_Q_W, MAT_QKV, 0, h, h},   {TOD_K_W, MAT_QKV, h, h, h}, {TOD_V_W, MAT_QKV, 2 * h, h, h},
                   {TOD_O_W, MAT_O, 0, h, h},     {TOD_FC1_W, MAT_FC1, 0, f, h}, {TOD_FC2_W, MAT_FC2, 0, h, f}};
-    if (m->streamed && layer >= m->host_layers) {
-        // this layer streams the matrices of layer % host_layers
+    const bool resident = m->streamed && layer < m->hbm_layers;
+    if (m->streamed) { // slot 0 serves as scratch below and an image may change: drop the prefetch
+        HIPCHK(hipDeviceSynchronize());
+        m->prefetched = false;
+    }
+    if (m->streamed && !resident && image_layer(m, layer) != layer) {
+        // this streamed layer reuses the pinned image of an earlier one
     } else if (!m->int4) {
-        for (const Part &p : parts)
-            memcpy(L.host + m->mat_off[p.mat] + ((int64_t)p.row0 * p.cols) * 2, t[p.tensor],
-                   (size_t)p.rows * p.cols * 2);
+        for (const Part &p : parts) {
+            const int64_t off = m->mat_off[p.mat] + ((int64_t)p.row0 * p.cols) * 2;
+            const size_t bytes = (size_t)p.rows * p.cols * 2;
+            if (resident)
+                HIPCHK(hipMemcpy(L.dev + off, t[p.tensor], bytes, hipMemcpyHostToDevice));
+            else
+                memcpy(L.host + off, t[p.tensor], bytes);
+        }
     } else {
-        // quantize in HBM; the int4 host tier builds the layer's image in slot 0
-        // (idle outside a pass) and copies it to its pinned buffer
+        // quantize in HBM; on the int4 host tier a resident layer's image is
+        // built in place, a streamed one's in slot 0 (idle outside a pass) and
+        // then copied to its pinned buffer
+        const uint8_t *image = !m->streamed ? nullptr : resident ? L.dev : m->slot[0];
         HIPCHK(hipDeviceSynchronize());
         for (const Part &p : parts) {
             const int64_t n = (int64_t)p.rows * p.cols;
@@ -658,13 +701,13 @@ int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
             HIPCHK(launch_quantize_groupwise(m->stage, n, m->stage_codes, m->stage_scale, m->stage_zero, nullptr));
             const int64_t nb0 = p.row0 / 32;
             GemmArgs dst{};
-            weights_of(m, L, p.mat, m->streamed ? m->slot[0] : nullptr, dst);
+            weights_of(m, L, p.mat, image, dst);
             HIPCHK(launch_repack_w4(m->stage_codes, m->stage_scale, m->stage_zero, p.rows, p.cols,
                                     const_cast<uint32_t *>(dst.wc) + nb0 * KG * 256,
                                     const_cast<uint32_t *>(dst.wp) + nb0 * KG * 32, nullptr));
         }
         HIPCHK(hipDeviceSynchronize());
-        if (m->streamed)
+        if (m->streamed && !resident)
             HIPCHK(hipMemcpy(L.host, m->slot[0], (size_t)m->layer_bytes, hipMemcpyDeviceToHost));
     }
     L.loaded = true;
@@ -867,10 +910,15 @@ int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t
     if (!m->layers[layer].loaded)
         return fail(TOD_ESTATE, "layer %d weights not set", layer);
     const uint8_t *slot = nullptr;
-    if (m->streamed) { // bring the layer's pinned image into slot 0 (idle outside a pass)
+    if (m->streamed && layer < m->hbm_layers) {
+        slot = m->layers[layer].dev;
+    } else if (m->streamed) { // bring the layer's pinned image into slot 0 (idle outside a pass)
+        const int src = image_layer(m, layer);
+        if (!m->layers[src].loaded)
+            return fail(TOD_ESTATE, "layer %d (whose image layer %d streams) weights not set", src, layer);
         HIPCHK(hipDeviceSynchronize());
-        HIPCHK(hipMemcpy(m->slot[0], m->layers[layer % m->host_layers].host, (size_t)m->layer_bytes,
-                         hipMemcpyHostToDevice));
+        m->prefetched = false; // slot 0 is overwritten here
+        HIPCHK(hipMemcpy(m->slot[0], m->layers[src].host, (size_t)m->layer_bytes, hipMemcpyHostToDevice));
         slot = m->slot[0];
     }
     const int h = m->cfg.hidden, f = m->cfg.ffn;
