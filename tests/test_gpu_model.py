@@ -14,6 +14,8 @@ random-weight stack amplifies such changes layer after layer.)
 Greedy picks must equal the oracle's, or (tie-aware) have an oracle logit
 within 2e-2 of the oracle's best. int4 weight codes must be bit-exact.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -267,6 +269,67 @@ def test_layer0_kv_codes_match_oracle():
     print(f"layer-0 KV byte agreement {rate:.6f}", flush=True)
     assert rate >= 0.999
     m.close()
+
+
+def test_full_size_opt30b_kv_codes_sampled():
+    """The benchmark's own configuration (OPT-30B shape: 48 layers, 512 rows,
+    512-token prompts, plain weights, captured decode steps): after prefill and
+    one decode step, the int4 K/V codes of layers 0 and 1 for a sampled
+    sequence are compared with the oracle running those two layers over the
+    sequence's 513 positions (the GPU's first token fed back). Layer 0 depends
+    only on the embedding, one LayerNorm and one linear: its bytes agree to
+    0.999. Layer 1 also depends on layer 0's arithmetic, and the int4 quantizer
+    turns one-ulp differences at a group's min or max into moved codes: a
+    correct fp32-accumulating oracle agrees with the fp64 oracle only to the
+    fraction stored in golden/fullsize_kv_calibration.txt (written by
+    golden/calibrate_fullsize_kv.py), and the GPU must come within 0.02 of it."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    w = synth.WORKLOADS["opt-30b"]
+    shape, M, s = w.shape, w.rows, w.prompt_len
+    run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=s, gen_len=w.gen_len)
+    m, glob = build_gpu_model(shape, run, variant="plain")
+    prompts = synth.prompt_ids(M, s, shape.vocab)
+    first = torch.empty(M, dtype=torch.int32, device="cuda")
+    tod.prefill(m.handle, 0, to_dev(prompts, torch), first)
+    out = torch.empty((1, M), dtype=torch.int32, device="cuda")
+    tod.decode_block(m.handle, 0, 1, first, out)
+    torch.cuda.synchronize()
+    print("GPU prefill + 1 decode step done", flush=True)
+    row, T, d = M - 1, s + 1, shape.head_dim
+    ids = np.concatenate([prompts[row], first.cpu().numpy()[row:row + 1]]).astype(np.int32)
+    hid = oracle.embed(shape, glob["tok_emb"], glob["pos_emb"], ids, np.arange(T, dtype=np.int32))
+    rates = []
+    for layer in (0, 1):
+        lo = oracle.Layer(shape, synth.layer_weights(shape, layer))
+        cache = oracle.KVCache(shape, T)
+        hid = lo.forward(cache, 0, hid)
+        del lo
+        agree = total = 0
+        for head in (0, shape.n_heads // 2, shape.n_heads - 1):
+            ref = cache.export(head, 0, T)
+            kc = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+            vc = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+            ks, kz, vs, vz = (torch.empty((T, d // 64), dtype=torch.float16, device="cuda") for _ in range(4))
+            tod.export_kv(m.handle, layer, 0, row, head, 0, T, kc, ks, kz, vc, vs, vz)
+            torch.cuda.synchronize()
+            got = (kc.cpu().numpy(), to_np16(ks), to_np16(kz), vc.cpu().numpy(), to_np16(vs), to_np16(vz))
+            for x, y in zip(got, ref):
+                x, y = np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)
+                agree += int((x == y).sum())
+                total += x.size
+        rates.append(agree / total)
+        print(f"layer {layer}: KV byte agreement {rates[-1]:.6f} over {total} bytes", flush=True)
+    m.close()
+    calib = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "fullsize_kv_calibration.txt")) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                calib[k.strip()] = float(v)
+    print(f"calibration (fp32-accumulating oracle vs fp64): {calib}", flush=True)
+    assert rates[0] >= 0.999
+    assert rates[1] >= calib["layer1_fp32_agreement"] - 0.02
 
 
 @pytest.mark.parametrize("name", ["opt-6.7b", "opt-30b"])
