@@ -32,6 +32,10 @@ CASES = [  # rows, in, out, epilogue
     (129, 256, 160, "res"), (300, 1024, 256, "bias"), (512, 3072, 768, "res"), (37, 4096, 64, "relu"),
     # pipelined kernel with ragged M and N tiles, split along K
     (300, 1280, 480, "relu"), (640, 2048, 1056, "res"), (257, 4096, 288, "bias"),
+    # pipelined kernel, one wave of tiles: 192-row tiles (QKV-like width; ragged M and N)
+    (512, 512, 21504, "bias"), (450, 768, 20384, "res"),
+    # 256-row tiles, where 192-row ones would need a second wave (fc1-like width; ragged M and N)
+    (500, 512, 28640, "relu"),
 ]
 
 

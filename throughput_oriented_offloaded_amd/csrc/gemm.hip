@@ -9,9 +9,10 @@
 // "2. The Zig-Zag Block Schedule").
 //
 // gfx950 design (two kernels, fp32 accumulation in v_mfma_f32_32x32x16_f16):
-//  * k_gemm_w4 (int4 weights, M > 128; the decode and prefill path): 256 x 256
-//    tiles, eight wavefronts (two per SIMD), activations, codes and params fed
-//    through a 3-stage LDS ring by direct-to-LDS loads; described at the kernel.
+//  * k_gemm_w4_256 / k_gemm_w4_192 (int4 weights, M > 128; the decode and
+//    prefill path): 256 x 256 or 192 x 256 tiles, eight wavefronts (two per
+//    SIMD), activations, codes and params fed through a 3-stage LDS ring by
+//    direct-to-LDS loads; described at the kernel body (gemm_w4_body).
 //  * k_gemm (M <= 128, and fp16 weights: LM head, host tier): 256-thread
 //    workgroups as a 2x2 grid of wavefronts, each owning a (BM/2) x (BN/2)
 //    output tile; the activation tile (BM x 64, one quantization group of K)
@@ -238,27 +239,29 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 }
 
 // ---------------------------------------------------------------------------
-// int4 GEMM for M > 128: 256 x 256 workgroup tiles, eight wavefronts (two per
-// SIMD) as a 2 x 4 grid of 128 x 64 wave tiles, fed through a 3-stage LDS ring
+// int4 GEMM for M > 128: BM x 256 workgroup tiles (BM = 256, or 192 where
+// that fills more of the chip), eight wavefronts (two per SIMD) as a 2 x 4
+// grid of BM/2 x 64 wave tiles, fed through a 3-stage LDS ring
 // that direct-to-LDS loads (global_load_lds_dwordx4) fill two K-groups ahead
 // of the MFMAs, so the weight stream's HBM latency is covered without staging
 // registers. With two waves per SIMD one wave's LDS reads and dequantization
 // run while the other's MFMAs issue. Stage synchronisation is an explicit
 // vmcnt wait on the wave's own loads plus a workgroup barrier.
 // ---------------------------------------------------------------------------
-namespace w4 {
-constexpr int BM = 256, BN = 256, WAVES = 8;
-constexpr int RB = BM / 2;                   // rows per wave (2 wave rows)
-constexpr int MB = RB / 32;                  // 32-row blocks per wave
-constexpr int NB = 2;                        // 32-column blocks per wave (4 wave columns)
-constexpr int A_BYTES = BM * 128;            // BM rows x 64 fp16, 16-byte chunks swizzled by row
-constexpr int W_BYTES = (BN / 32) * 1024;    // per column block: 64 lanes x 16 B of codes
-constexpr int P_BYTES = (BN / 32) * 256;     // per column block: 64 x (scale, zero), lanes 32..63 repeat
-constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
-constexpr int S = 3;                         // ring stages
-constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
-constexpr int LPS = AL + 2;                  // loads per wave per stage: A chunks, one code block, one param block
-} // namespace w4
+template <int BM_> struct W4 {
+    static constexpr int BM = BM_, BN = 256, WAVES = 8;
+    static constexpr int RB = BM / 2;                   // rows per wave (2 wave rows)
+    static constexpr int MB = RB / 32;                  // 32-row blocks per wave
+    static constexpr int NB = 2;                        // 32-column blocks per wave (4 wave columns)
+    static constexpr int A_BYTES = BM * 128;            // BM rows x 64 fp16, 16-byte chunks swizzled by row
+    static constexpr int W_BYTES = (BN / 32) * 1024;    // per column block: 64 lanes x 16 B of codes
+    static constexpr int P_BYTES = (BN / 32) * 256;     // per column block: 64 x (scale, zero), lanes 32..63 repeat
+    static constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
+    static constexpr int S = 3;                         // ring stages
+    static constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
+    static constexpr int LPS = AL + 2;                  // loads per wave per stage: A chunks, one code block, one param block
+    static_assert(BM % 64 == 0 && (BM / 8) % WAVES == 0, "A chunks split evenly over the waves");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -270,10 +273,11 @@ __device__ __forceinline__ int a_pos(int row, int ch) { return ch ^ ((row ^ (row
 
 // Wait until at most `younger` stages' worth (LPS loads each) of this wave's
 // vector-memory loads are outstanding (younger is 0 or 1 with three stages).
+template <int LPS_>
 __device__ __forceinline__ void wait_vm_loads(int younger)
 {
     // s_waitcnt simm16 on gfx9: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-    constexpr int n1 = w4::LPS;
+    constexpr int n1 = LPS_;
     constexpr int e1 = (n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8);
     static_assert(n1 < 64, "vmcnt holds 6 bits");
     if (younger >= 1)
@@ -282,9 +286,12 @@ __device__ __forceinline__ void wait_vm_loads(int younger)
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-__global__ void __launch_bounds__(512, 1) k_gemm_w4(GemmArgs g, TileMap tm)
+template <int BM_>
+__device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &tm)
 {
-    using namespace w4;
+    using C = W4<BM_>;
+    constexpr int BM = C::BM, BN = C::BN, WAVES = C::WAVES, RB = C::RB, MB = C::MB, NB = C::NB;
+    constexpr int A_BYTES = C::A_BYTES, W_BYTES = C::W_BYTES, STAGE = C::STAGE, S = C::S, AL = C::AL;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
 
     const int tile = xcd_tile(blockIdx.x, tm.total);
@@ -349,7 +356,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4(GemmArgs g, TileMap tm)
             issue(s_, g0 + s_);
 
     for (int it = 0; it < nst; it++) {
-        wait_vm_loads(min(S - 2, nst - 1 - it));
+        wait_vm_loads<C::LPS>(min(S - 2, nst - 1 - it));
         __builtin_amdgcn_s_barrier();
         if (it + S - 1 < nst)
             issue((it + S - 1) % S, g0 + it + S - 1);
@@ -410,7 +417,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4(GemmArgs g, TileMap tm)
     // runs. The ring is free once every wave has left the main loop.
     __syncthreads();
     constexpr int SROW = 36; // padded scratch row (floats)
-    static_assert(WAVES * 32 * SROW * 4 <= STAGE, "scratch fits the first stage");
+    static_assert(WAVES * 32 * SROW * 4 <= S * STAGE, "scratch fits the ring");
     float *scr = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
     const int lr = lane >> 1, c0 = (lane & 1) * 16;
 #pragma unroll
@@ -486,6 +493,9 @@ __global__ void __launch_bounds__(512, 1) k_gemm_w4(GemmArgs g, TileMap tm)
     }
 }
 
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_256(GemmArgs g, TileMap tm) { gemm_w4_body<256>(g, tm); }
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_192(GemmArgs g, TileMap tm) { gemm_w4_body<192>(g, tm); }
+
 __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -512,11 +522,14 @@ struct Plan {
 
 // Tuning overrides (read once): TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" selects the
 // register-staged kernel for every M > 64; TOD_GEMM_SPLIT = workgroup count below which the
-// K loop is split.
+// K loop is split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined kernel's tile height to 256 | 192.
 struct Tuning {
     int bm = 0, bn = 0, split_fill = -1;
+    int bm192 = -1; // pipelined tile height: -1 cost model, 0 always 256, 1 always 192
     Tuning()
     {
+        if (const char *t = getenv("TOD_GEMM_BM192"))
+            bm192 = atoi(t) > 0 ? 1 : atoi(t) == 0 ? 0 : -1;
         if (const char *t = getenv("TOD_GEMM_TILE")) {
             int a = 0, b = 0;
             if (sscanf(t, "%dx%d", &a, &b) == 2 &&
@@ -536,6 +549,29 @@ const Tuning &tuning()
     return t;
 }
 
+// Tile grid for bm x bn tiles; the K loop is split (powers of two) while the
+// workgroups would fill less than `fill` CUs.
+Plan split_plan(int M, int N, int K, int bm, int bn, bool pipelined)
+{
+    const Tuning &tu = tuning();
+    Plan p{};
+    p.bm = bm;
+    p.bn = bn;
+    p.pipelined = pipelined;
+    const int KG = K / KG_ELEMS;
+    p.tm.mt = (M + bm - 1) / bm;
+    p.tm.nt = (N + bn - 1) / bn;
+    const int tiles = p.tm.mt * p.tm.nt;
+    const int fill = tu.split_fill >= 0 ? tu.split_fill : (pipelined ? 160 : 384);
+    int splits = 1;
+    while (tiles * splits < fill && KG / (splits * 2) >= 8)
+        splits *= 2;
+    p.tm.groups_per_split = (KG + splits - 1) / splits;
+    p.tm.splits = (KG + p.tm.groups_per_split - 1) / p.tm.groups_per_split;
+    p.tm.total = tiles * p.tm.splits;
+    return p;
+}
+
 Plan plan_gemm(int M, int N, int K, bool int4)
 {
     Plan p;
@@ -543,10 +579,24 @@ Plan plan_gemm(int M, int N, int K, bool int4)
     p.pipelined = int4 && M > 128 && !tu.bm;
     if (p.pipelined) {
         // 256 x 256 tiles halve the activation re-reads per MFMA against 256 x 128,
-        // which is what bounds this GEMM (L2 -> LDS traffic), at the price of
-        // fewer workgroups; narrow N is split along K instead.
-        p.bm = w4::BM;
-        p.bn = w4::BN;
+        // at the price of fewer workgroups; narrow N is split along K instead.
+        // 192-row tiles are taken where their extra workgroups finish the GEMM
+        // sooner: the cost is waves of workgroups x rows x K-groups per workgroup
+        // (one 256-CU wave of 192-row tiles takes 3/4 of one of 256-row tiles).
+        p.bn = 256;
+        p.bm = 256;
+        if (tu.bm192 != 0) {
+            long best = -1;
+            for (int bm : {256, 192}) {
+                const Plan q = split_plan(M, N, K, bm, 256, true);
+                const long waves = (q.tm.total + 255) / 256;
+                const long cost = waves * bm * q.tm.groups_per_split;
+                if ((tu.bm192 < 0 && (best < 0 || cost < best)) || (tu.bm192 > 0 && bm == 192)) {
+                    best = cost;
+                    p.bm = bm;
+                }
+            }
+        }
     } else if (M <= 64) {
         // 128 x 128 tiles keep a wave at ~150 registers, so three workgroups share a
         // CU and hide each other's load latency.
@@ -560,17 +610,8 @@ Plan plan_gemm(int M, int N, int K, bool int4)
         p.bm = tu.bm;
         p.bn = tu.bn;
     }
-    const int KG = K / KG_ELEMS;
-    p.tm.mt = (M + p.bm - 1) / p.bm;
-    p.tm.nt = (N + p.bn - 1) / p.bn;
-    const int tiles = p.tm.mt * p.tm.nt;
-    const int fill = tu.split_fill >= 0 ? tu.split_fill : (p.pipelined ? 160 : 384);
-    int splits = 1;
-    while (tiles * splits < fill && KG / (splits * 2) >= 8)
-        splits *= 2;
-    p.tm.groups_per_split = (KG + splits - 1) / splits;
-    p.tm.splits = (KG + p.tm.groups_per_split - 1) / p.tm.groups_per_split;
-    p.tm.total = tiles * p.tm.splits;
+    const Plan q = split_plan(M, N, K, p.bm, p.bn, p.pipelined);
+    p.tm = q.tm;
     return p;
 }
 
@@ -596,8 +637,10 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         p.tm.total = p.tm.mt * p.tm.nt;
     }
     const dim3 grid(p.tm.total), block(256);
-    if (p.pipelined)
-        hipLaunchKernelGGL(k_gemm_w4, grid, dim3(64 * w4::WAVES), 0, st, g, p.tm);
+    if (p.pipelined && p.bm == 192)
+        hipLaunchKernelGGL(k_gemm_w4_192, grid, dim3(64 * W4<192>::WAVES), 0, st, g, p.tm);
+    else if (p.pipelined)
+        hipLaunchKernelGGL(k_gemm_w4_256, grid, dim3(64 * W4<256>::WAVES), 0, st, g, p.tm);
     else {
 #define TOD_GEMM_CASE(BM_, BN_, MINW_)                                                               \
     if (p.bm == BM_ && p.bn == BN_) {                                                                \
