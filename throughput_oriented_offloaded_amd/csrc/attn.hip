@@ -53,10 +53,10 @@ __device__ __forceinline__ void load_chunk(KvChunk<D / 32> &c, int c0, int slot,
     for (int j = 0; j < L; j++) {
         const uint32_t t = (uint32_t)min(c0 + slot + PPI * j, ctx - 1);
         const uint32_t cofs = t * CB + pc * 16, pofs = (t * G + (pc >> 1)) * 4;
-        c.k[j] = *reinterpret_cast<const uint4_t *>(kc + cofs);
-        c.v[j] = *reinterpret_cast<const uint4_t *>(vc + cofs);
-        c.kp[j] = *reinterpret_cast<const uint32_t *>(kp + pofs);
-        c.vp[j] = *reinterpret_cast<const uint32_t *>(vp + pofs);
+        c.k[j] = __builtin_nontemporal_load(reinterpret_cast<const uint4_t *>(kc + cofs));
+        c.v[j] = __builtin_nontemporal_load(reinterpret_cast<const uint4_t *>(vc + cofs));
+        c.kp[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(kp + pofs));
+        c.vp[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(vp + pofs));
     }
 }
 
