@@ -27,6 +27,14 @@ __device__ __forceinline__ half2_t magic_pair(uint32_t x, uint32_t mask)
     return __builtin_bit_cast(half2_t, r);
 }
 
+// Exact codes of bytes 0,1 (HI = false) or 2,3 (HI = true) of a word whose
+// bytes each hold one 4-bit code: the byte read as fp8 e4m3 is c * 2^-9.
+template <bool HI> __device__ __forceinline__ half2_t code_pair(uint32_t nibbles)
+{
+    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nibbles, 512.0f, HI);
+    return c;
+}
+
 __device__ __forceinline__ half2_t splat_half(uint32_t bits)
 {
     const half_t h = __builtin_bit_cast(half_t, (uint16_t)bits);
@@ -67,11 +75,12 @@ struct SoftmaxState {
 };
 
 // Scores of a chunk and its weighted values.
-//  * K: for each code word (dims e0..e7) the fields e0,e4 / e2,e6 are masked
-//    in place (1024 + c) and e1,e5 / e3,e7 at bit 4 (1024 + 16c); one packed
-//    add or FMA recovers c exactly and one packed FMA gives the fp16 key
-//    fp16(c * scale + zero), rounded once, i.e. the dequantized cache entry
-//    itself; v_dot2 against the matching query pairs sums q.k in fp32.
+//  * K: each code word (dims e0..e7, two per byte) is split into its low and
+//    high nibbles (one byte each); read as fp8 e4m3 a byte 0000cccc is
+//    c * 2^-9, so a scaled fp8 -> fp16 conversion gives the code pairs
+//    (e0,e2) (e4,e6) (e1,e3) (e5,e7) exactly, and one packed FMA gives the
+//    fp16 key fp16(c * scale + zero), rounded once, i.e. the dequantized cache
+//    entry itself; v_dot2 against the matching query pairs sums q.k in fp32.
 //  * V: the same fields feed fp32 accumulators through mixed-precision FMA,
 //    acc_e += (p * scale) * (1024 + c) (or 1024 + 16c); the offsets and the
 //    zero term are removed once at the end from the running sums of
@@ -82,8 +91,6 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
 {
     constexpr int L = D / 32, PPI = 64 / L;
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const half2_t m1024 = {(half_t)1024.0f, (half_t)1024.0f};
-    const half2_t r16 = {(half_t)0.0625f, (half_t)0.0625f}, mm64 = {(half_t)-64.0f, (half_t)-64.0f};
     float sc[L];
     float mloc = -INFINITY;
 #pragma unroll
@@ -92,15 +99,15 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
         float da = 0.0f, db = 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-            const uint32_t x = c.k[j][w], y = x >> 8;
-            const half2_t k0 = __builtin_elementwise_fma(magic_pair(x, 0x000F000Fu) - m1024, s2, z2);
-            const half2_t k1 = __builtin_elementwise_fma(__builtin_elementwise_fma(magic_pair(x, 0x00F000F0u), r16, mm64), s2, z2);
-            const half2_t k2 = __builtin_elementwise_fma(magic_pair(y, 0x000F000Fu) - m1024, s2, z2);
-            const half2_t k3 = __builtin_elementwise_fma(__builtin_elementwise_fma(magic_pair(y, 0x00F000F0u), r16, mm64), s2, z2);
-            da = __builtin_amdgcn_fdot2(qa[2 * w], k0, da, false);
-            db = __builtin_amdgcn_fdot2(qb[2 * w], k1, db, false);
-            da = __builtin_amdgcn_fdot2(qa[2 * w + 1], k2, da, false);
-            db = __builtin_amdgcn_fdot2(qb[2 * w + 1], k3, db, false);
+            const uint32_t x = c.k[j][w], lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+            const half2_t k02 = __builtin_elementwise_fma(code_pair<false>(lo), s2, z2);
+            const half2_t k46 = __builtin_elementwise_fma(code_pair<true>(lo), s2, z2);
+            const half2_t k13 = __builtin_elementwise_fma(code_pair<false>(hi), s2, z2);
+            const half2_t k57 = __builtin_elementwise_fma(code_pair<true>(hi), s2, z2);
+            da = __builtin_amdgcn_fdot2(qa[2 * w], k02, da, false);
+            db = __builtin_amdgcn_fdot2(qb[2 * w], k13, db, false);
+            da = __builtin_amdgcn_fdot2(qa[2 * w + 1], k46, da, false);
+            db = __builtin_amdgcn_fdot2(qb[2 * w + 1], k57, db, false);
         }
         const float score = reduce_group<L>(da + db, OpAdd()) * inv_sqrt_d;
         sc[j] = c0 + slot + PPI * j < ctx ? score : -INFINITY;
@@ -172,16 +179,16 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
     const uint8_t *kp = reinterpret_cast<const uint8_t *>(kv.kp + slab * kv.cap * G);
     const uint8_t *vp = reinterpret_cast<const uint8_t *>(kv.vp + slab * kv.cap * G);
 
-    // query dims pc*32 .. pc*32+31, paired to match the code fields
+    // query dims pc*32 .. pc*32+31, paired to match the decoded key pairs
     const uint16_t *qp = q + (int64_t)row * q_stride + (int64_t)head * D + pc * 32;
     half2_t qa[8], qb[8];
 #pragma unroll
     for (int w = 0; w < 4; w++) {
         const half8_t h = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(qp + 8 * w));
-        qa[2 * w] = (half2_t){h[0], h[4]};
-        qa[2 * w + 1] = (half2_t){h[2], h[6]};
-        qb[2 * w] = (half2_t){h[1], h[5]};
-        qb[2 * w + 1] = (half2_t){h[3], h[7]};
+        qa[2 * w] = (half2_t){h[0], h[2]};
+        qa[2 * w + 1] = (half2_t){h[4], h[6]};
+        qb[2 * w] = (half2_t){h[1], h[3]};
+        qb[2 * w + 1] = (half2_t){h[5], h[7]};
     }
 
     SoftmaxState st;
