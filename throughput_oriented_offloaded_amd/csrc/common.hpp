@@ -130,6 +130,68 @@ __device__ __forceinline__ uint32_t canonical_word_from_tiled(uint32_t t)
     return r;
 }
 
+// LayerNorm of one row held by one 256-thread workgroup: thread t holds the
+// 16-byte chunks c = t + 256k (k < K) of the row's nch = h/8 chunks (zeros
+// past nch). fp32 statistics in two passes over the registers (mean, then the
+// biased variance of x - mean): DPP reductions within each wavefront, then the
+// four wavefront sums added in a fixed order through LDS (`red`, 8 floats);
+// eps 1e-5, one rounding to fp16. Shared by the LayerNorm kernel and the
+// split-K reduction that fuses it, so both give identical bits.
+template <int K>
+__device__ __forceinline__ void layernorm_row(const uint4_t (&v)[K], int nch, int h, const uint16_t *__restrict__ g,
+                                              const uint16_t *__restrict__ b, uint16_t *__restrict__ yrow, float *red)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            s += (float)hv[e];
+    }
+    s = reduce_slots<1>(s, OpAdd());
+    if (lane == 0)
+        red[wave] = s;
+    __syncthreads();
+    const float mu = (((red[0] + red[1]) + red[2]) + red[3]) / (float)h;
+    float q = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        if (tid + 256 * k < nch) {
+            const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+                const float c = (float)hv[e] - mu;
+                q += c * c;
+            }
+        }
+    }
+    q = reduce_slots<1>(q, OpAdd());
+    if (lane == 0)
+        red[4 + wave] = q;
+    __syncthreads();
+    const float var = (((red[4] + red[5]) + red[6]) + red[7]) / (float)h;
+    const float rs = 1.0f / sqrtf(var + 1e-5f);
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        const int c = tid + 256 * k;
+        if (c < nch) {
+            const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
+            const half8_t gv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g + 8 * c));
+            const half8_t bv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(b + 8 * c));
+            half8_t o;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                o[e] = (half_t)(((float)hv[e] - mu) * rs * (float)gv[e] + (float)bv[e]);
+            *reinterpret_cast<uint4_t *>(yrow + 8 * c) = __builtin_bit_cast(uint4_t, o);
+        }
+    }
+}
+
+// 16-byte chunks per thread for a row of h fp16 values (h % 8 == 0, h <= 16384)
+inline int layernorm_chunks(int h) { return (h / 8 + 255) / 256; }
+
 // ---------------------------------------------------------------------------
 // KV cache view (one layer): for each (sequence, head) "slab" of `cap`
 // positions (cap % 64 == 0):
@@ -203,6 +265,10 @@ struct GemmArgs {
     int epi;
     float *ws;       // split-K workspace (fp32 [splits][M][N]) or null
     size_t ws_bytes;
+    // optional LayerNorm of the output rows (ldc == N): ln_y [M][N] = LN(y) with
+    // gamma ln_g, beta ln_b; fused into the split-K reduction when there is one
+    const uint16_t *ln_g, *ln_b;
+    uint16_t *ln_y;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
 size_t gemm_workspace_bytes(int M, int N, int K, bool int4);

@@ -514,6 +514,61 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
     g.y[(int64_t)row * g.ldc + col] = f2h(v);
 }
 
+// Split-K reduction fused with the LayerNorm of the output rows: one
+// 256-thread workgroup per row, thread chunks c = t + 256k of 8 columns. Each
+// output is summed over the splits, bias and residual added and rounded
+// exactly as in k_splitk_reduce; the fp16 row stays in registers for
+// layernorm_row, the same code as the LayerNorm kernel.
+template <int K>
+__global__ void __launch_bounds__(256) k_splitk_reduce_ln(GemmArgs g, int splits)
+{
+    __shared__ float red[8];
+    const int row = blockIdx.x, nch = g.N >> 3;
+    const int64_t mn = (int64_t)g.M * g.N;
+    uint4_t v[K];
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+        const int c = threadIdx.x + 256 * k;
+        v[k] = (uint4_t){0u, 0u, 0u, 0u};
+        if (c >= nch)
+            continue;
+        const int64_t i0 = (int64_t)row * g.N + 8 * c;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            x[e] = 0.0f;
+        for (int sp = 0; sp < splits; sp++) {
+            const float4_t p0 = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0);
+            const float4_t p1 = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0 + 4);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                x[e] += p0[e];
+                x[4 + e] += p1[e];
+            }
+        }
+        half8_t bias = {}, res = {};
+        if (g.bias && g.epi != EPI_NONE)
+            bias = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g.bias + 8 * c));
+        if (g.epi == EPI_BIAS_RES)
+            res = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g.residual + (int64_t)row * g.ldc + 8 * c));
+        half8_t o;
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float t = x[e];
+            if (g.bias && g.epi != EPI_NONE)
+                t += (float)bias[e];
+            if (g.epi == EPI_BIAS_RES)
+                t += (float)res[e];
+            if (g.epi == EPI_BIAS_RELU)
+                t = fmaxf(t, 0.0f);
+            o[e] = (half_t)t;
+        }
+        v[k] = __builtin_bit_cast(uint4_t, o);
+        *reinterpret_cast<uint4_t *>(g.y + (int64_t)row * g.ldc + 8 * c) = v[k];
+    }
+    layernorm_row<K>(v, nch, g.N, g.ln_g, g.ln_b, g.ln_y + (int64_t)row * g.N, red);
+}
+
 struct Plan {
     int bm, bn;
     bool pipelined;
@@ -627,6 +682,8 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
 {
     if (g.M <= 0 || g.N <= 0)
         return hipSuccess;
+    if (g.ln_y && (g.ldc != g.N || g.N % 8 || g.N > 16384 || !g.ln_g || !g.ln_b))
+        return hipErrorInvalidValue; // LayerNorm of the output needs dense rows of at most 16384
     const bool int4 = g.wc != nullptr;
     Plan p = plan_gemm(g.M, g.N, g.K, int4);
     const size_t need = p.tm.splits > 1 ? (size_t)p.tm.splits * g.M * g.N * sizeof(float) : 0;
@@ -655,8 +712,23 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
 #undef TOD_GEMM_CASE
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.tm.splits == 1)
+    if (e != hipSuccess)
         return e;
+    if (p.tm.splits == 1)
+        return g.ln_y ? launch_layernorm(g.y, g.M, g.N, g.ln_g, g.ln_b, g.ln_y, st) : hipSuccess;
+    if (g.ln_y) {
+        const dim3 grid((unsigned)g.M), block(256);
+        const int chunks = layernorm_chunks(g.N);
+        if (chunks <= 1)
+            hipLaunchKernelGGL(k_splitk_reduce_ln<1>, grid, block, 0, st, g, p.tm.splits);
+        else if (chunks <= 2)
+            hipLaunchKernelGGL(k_splitk_reduce_ln<2>, grid, block, 0, st, g, p.tm.splits);
+        else if (chunks <= 4)
+            hipLaunchKernelGGL(k_splitk_reduce_ln<4>, grid, block, 0, st, g, p.tm.splits);
+        else
+            hipLaunchKernelGGL(k_splitk_reduce_ln<8>, grid, block, 0, st, g, p.tm.splits);
+        return hipGetLastError();
+    }
     const int64_t n = (int64_t)g.M * g.N;
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g, p.tm.splits);
     return hipGetLastError();

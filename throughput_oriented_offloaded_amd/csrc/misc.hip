@@ -5,60 +5,24 @@
 
 namespace {
 
-// One wavefront per row (four rows per workgroup): the row is read once with
-// 16-byte loads and held in registers as fp16 (up to 8 * 64 * K elements),
-// fp32 statistics in two passes over the registers (mean, then the biased
-// variance of x - mean), DPP reductions, eps 1e-5, one rounding to fp16.
+// One 256-thread workgroup per row: the row is read once with 16-byte loads
+// and held in registers as fp16 (up to 8 * 256 * K elements); the statistics
+// and the output are layernorm_row's.
 template <int K>
 __global__ void __launch_bounds__(256) k_layernorm(const uint16_t *__restrict__ x, int rows, int h,
                                                    const uint16_t *__restrict__ g, const uint16_t *__restrict__ b,
                                                    uint16_t *__restrict__ y)
 {
-    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-    if (row >= rows)
-        return; // whole wavefront
-    const int lane = threadIdx.x & 63, nch = h >> 3;
+    __shared__ float red[8];
+    const int row = blockIdx.x, nch = h >> 3;
     const uint16_t *xr = x + (int64_t)row * h;
     uint4_t v[K];
-    float s = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; k++) {
-        const int c = lane + 64 * k;
+        const int c = threadIdx.x + 256 * k;
         v[k] = c < nch ? *reinterpret_cast<const uint4_t *>(xr + 8 * c) : (uint4_t){0u, 0u, 0u, 0u};
-        const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-            s += (float)hv[e];
     }
-    const float mu = reduce_slots<1>(s, OpAdd()) / (float)h;
-    float q = 0.0f;
-#pragma unroll
-    for (int k = 0; k < K; k++) {
-        if (lane + 64 * k < nch) {
-            const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-                const float c = (float)hv[e] - mu;
-                q += c * c;
-            }
-        }
-    }
-    const float var = reduce_slots<1>(q, OpAdd()) / (float)h;
-    const float rs = 1.0f / sqrtf(var + 1e-5f);
-#pragma unroll
-    for (int k = 0; k < K; k++) {
-        const int c = lane + 64 * k;
-        if (c < nch) {
-            const half8_t hv = __builtin_bit_cast(half8_t, v[k]);
-            const half8_t gv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g + 8 * c));
-            const half8_t bv = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(b + 8 * c));
-            half8_t o;
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                o[e] = (half_t)(((float)hv[e] - mu) * rs * (float)gv[e] + (float)bv[e]);
-            *reinterpret_cast<uint4_t *>(y + (int64_t)row * h + 8 * c) = __builtin_bit_cast(uint4_t, o);
-        }
-    }
+    layernorm_row<K>(v, nch, h, g, b, y + (int64_t)row * h, red);
 }
 
 // The sum of two fp16 values rounded to fp32 and then to fp16 equals its
@@ -163,16 +127,16 @@ hipError_t launch_layernorm(const uint16_t *x, int rows, int h, const uint16_t *
     if (rows == 0)
         return hipSuccess;
     // h is a multiple of 64 (checked at init), so rows are 16-byte aligned
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    const int chunks = (h / 8 + 63) / 64; // 16-byte chunks per lane
-    if (chunks <= 2)
+    const dim3 grid((unsigned)rows), block(256);
+    const int chunks = layernorm_chunks(h);
+    if (chunks <= 1)
+        hipLaunchKernelGGL(k_layernorm<1>, grid, block, 0, st, x, rows, h, g, b, y);
+    else if (chunks <= 2)
         hipLaunchKernelGGL(k_layernorm<2>, grid, block, 0, st, x, rows, h, g, b, y);
+    else if (chunks <= 4)
+        hipLaunchKernelGGL(k_layernorm<4>, grid, block, 0, st, x, rows, h, g, b, y);
     else if (chunks <= 8)
         hipLaunchKernelGGL(k_layernorm<8>, grid, block, 0, st, x, rows, h, g, b, y);
-    else if (chunks <= 16)
-        hipLaunchKernelGGL(k_layernorm<16>, grid, block, 0, st, x, rows, h, g, b, y);
-    else if (chunks <= 32)
-        hipLaunchKernelGGL(k_layernorm<32>, grid, block, 0, st, x, rows, h, g, b, y);
     else
         return hipErrorInvalidValue; // hidden > 16384
     return hipGetLastError();

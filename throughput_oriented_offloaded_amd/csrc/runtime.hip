@@ -231,8 +231,11 @@ void weights_of(const tod_model *m, const LayerStore &L, int mat, const uint8_t 
     }
 }
 
+// ln_g/ln_b (nullable): also write LayerNorm(y) into m->act, fused into the
+// GEMM's split-K reduction when it has one.
 int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint8_t *slot,
-             uint16_t *y, int64_t ldc, int epi, hipStream_t st)
+             uint16_t *y, int64_t ldc, int epi, hipStream_t st, const uint16_t *ln_g = nullptr,
+             const uint16_t *ln_b = nullptr)
 {
     GemmArgs g{};
     g.a = a;
@@ -248,6 +251,11 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
     g.epi = epi;
     g.ws = m->ws;
     g.ws_bytes = m->ws_bytes;
+    if (ln_g) {
+        g.ln_g = ln_g;
+        g.ln_b = ln_b;
+        g.ln_y = m->act;
+    }
     ProfScope ps(m, TOD_K_GEMM_QKV + mat, st);
     HIPCHK(launch_gemm(g, st));
     return TOD_OK;
@@ -255,14 +263,18 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
 
 // One decoder layer for `rows` rows whose hidden states start at `h`.
 // decode: rows = M sequences at position pos; prefill: rows = b * s (b sequences
-// starting at seq0, positions 0..s-1).
+// starting at seq0, positions 0..s-1). act_ready: m->act already holds LN1(h)
+// (written by the previous layer's fc2); next_g/next_b (nullable): the fc2
+// GEMM also writes that LayerNorm of the new h into m->act for the next layer
+// (or the head). LN2 comes out of the out-projection GEMM the same way.
 int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, bool prefill_mode, int seq0, int s,
-               int pos, const int *dpos, const uint8_t *wslot, hipStream_t st)
+               int pos, const int *dpos, const uint8_t *wslot, hipStream_t st, bool act_ready = false,
+               const uint16_t *next_g = nullptr, const uint16_t *next_b = nullptr)
 {
     const int hd = m->cfg.hidden, f = m->cfg.ffn;
     const LayerStore &L = m->layers[l];
     int rc;
-    {
+    if (!act_ready) {
         ProfScope ps(m, TOD_K_LAYERNORM, st);
         HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
     }
@@ -288,15 +300,11 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         else
             HIPCHK(launch_attn_decode(m->qkv, 3 * hd, m->att, hd, rows, seq0, pos + 1, dpos, kv, st));
     }
-    if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wslot, h, hd, EPI_BIAS_RES, st)))
+    if ((rc = run_gemm(m, m->att, rows, MAT_O, L, wslot, h, hd, EPI_BIAS_RES, st, L.ln2_g, L.ln2_b)))
         return rc;
-    {
-        ProfScope ps(m, TOD_K_LAYERNORM, st);
-        HIPCHK(launch_layernorm(h, rows, hd, L.ln2_g, L.ln2_b, m->act, st));
-    }
     if ((rc = run_gemm(m, m->act, rows, MAT_FC1, L, wslot, m->ffn, f, EPI_BIAS_RELU, st)))
         return rc;
-    if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, wslot, h, hd, EPI_BIAS_RES, st)))
+    if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, wslot, h, hd, EPI_BIAS_RES, st, next_g, next_b)))
         return rc;
     return TOD_OK;
 }
@@ -371,10 +379,12 @@ int check_ready(tod_model *m, int block)
 }
 
 // LM head on `rows` final hidden rows: LN_f, tied-embedding logits, argmax.
-int head_pass(tod_model *m, const uint16_t *hrows, int rows, uint16_t *logits, int32_t *next, hipStream_t st)
+// act_ready: m->act already holds LN_f of the rows (fused into the last fc2).
+int head_pass(tod_model *m, const uint16_t *hrows, int rows, uint16_t *logits, int32_t *next, hipStream_t st,
+              bool act_ready = false)
 {
     const int hd = m->cfg.hidden, V = m->cfg.vocab;
-    {
+    if (!act_ready) {
         ProfScope ps(m, TOD_K_LAYERNORM, st);
         HIPCHK(launch_layernorm(hrows, rows, hd, m->lnf_g, m->lnf_b, m->act, st));
     }
@@ -762,12 +772,18 @@ static int decode_step(tod_model *m, int block, const int32_t *in, int pos, cons
         ProfScope ps(m, TOD_K_EMBED, st);
         HIPCHK(launch_embed(in, Mr, 1, pos, dpos, m->tok_emb, m->cfg.vocab, m->pos_emb, h, m->hid, st));
     }
+    // all M rows pass each layer together, so every LayerNorm after the first
+    // comes out of the GEMM before it (the last one is the head's LN_f)
     int rc = stack_pass(m, st, [&](int l, const uint8_t *wslot) -> int {
-        return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, dpos, wslot, st);
+        const bool last = l + 1 == L;
+        const uint16_t *ng = last ? m->lnf_g : m->layers[l + 1].ln1_g;
+        const uint16_t *nb = last ? m->lnf_b : m->layers[l + 1].ln1_b;
+        return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, dpos, wslot, st, l > 0,
+                          ng, nb);
     });
     if (rc)
         return rc;
-    if ((rc = head_pass(m, m->hid, Mr, logits, out, st)))
+    if ((rc = head_pass(m, m->hid, Mr, logits, out, st, true)))
         return rc;
     if (dpos)
         HIPCHK(launch_increment_int(const_cast<int *>(dpos), st));
