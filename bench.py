@@ -95,6 +95,14 @@ def measure_h2d(torch, nbytes, reps=3):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def cost_model_check(tod, shape, run, measured_ms):
+    """The library's cost model (estimate_decode, default measured rates) for this run beside the
+    measured step time."""
+    est = tod.estimate_decode(shape, run)
+    return {"predicted_ms_per_step": est["step_s"] * 1e3, "measured_over_predicted": measured_ms / (est["step_s"] * 1e3),
+            "predicted_hbm_gb": est["hbm_bytes"] / 1e9, "predicted_host_gb": est["host_bytes"] / 1e9}
+
+
 def host_tier_bench(args, w, tod, synth, torch):
     """Decode with weights streamed per layer from pinned host memory: fp16
     (weight tier 1) or the tiled int4 image (tier 2, 0.5625 byte per weight).
@@ -195,6 +203,7 @@ def host_tier_bench(args, w, tod, synth, torch):
         "link_bytes_per_step": (L - R) * layer_bytes,
         "h2d_measured_gbs": h2d,
         "prefill_s": prefill_s,
+        "cost_model": cost_model_check(tod, shape, run, elapsed * 1e3 / steps),
     }
 
 
@@ -511,6 +520,9 @@ def main():
         "prefill_s": prefill_s,
         "e2e_tokens_per_s": M * w.gen_len / (prefill_s + (w.gen_len - 1) * ms_per_step * 1e-3),
         "kernels": kernels,
+        "cost_model": cost_model_check(tod, shape, dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block,
+                                                        prompt_len=w.prompt_len, gen_len=w.gen_len),
+                                       ms_per_step),
     }
     m.close()
     del m

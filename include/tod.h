@@ -280,6 +280,56 @@ int attn_cache_export(tod_attn_cache *c, int seq, int head, int t0, int t1, uint
                       uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream);
 int attn_cache_free(tod_attn_cache *c);
 
+/*
+ * Cost model and placement search (host computation only; no device calls).
+ * The FlexGen guide's simulator ("Implementation: Simulating FlexGen's Zig-Zag
+ * Block Scheduling in Python") prices a step by the weight bytes moved over
+ * PCIe; the FlexLLMGen overview ("A 175B-parameter model on one GPU, if you
+ * can wait": caveats) tunes placement by hand, an automatic policy optimiser
+ * being future work. Here a decode step is priced from measured rates:
+ *
+ * tod_hw: attn_gbs = decode-attention read rate, mem_gbs = streaming rate of
+ * the other row-wise kernels and weight reads, link_gbs = pinned -> HBM copy
+ * rate (GB/s); int4_tflops / fp16_tflops = GEMM rates by weight type; launch_us
+ * = floor per kernel; hbm_bytes / host_bytes = capacities the model may use.
+ * default_hw fills the figures measured on MI355X for this library.
+ *
+ * estimate_decode prices one decode step of the block `run` describes at the
+ * average decode context (prompt_len + gen_len / 2): per layer, each GEMM takes
+ * the larger of flops / rate and weight bytes / mem_gbs (at least launch_us),
+ * attention M * heads * (ctx * (d + d/8) + 4d) bytes / attn_gbs, the KV append
+ * M * heads * (4d + d + d/8) bytes / mem_gbs; plus embedding, one LayerNorm, the
+ * fp16 LM head and the argmax. On the host tiers the L - hbm_layers streamed
+ * layers each copy one layer image (weights x 2 B fp16, or x 0.5625 B int4) at
+ * link_gbs while the GPU computes; the resident layers run while at most two
+ * copies (one per slot) are in flight, so step = max(compute, link + idle),
+ * idle = max(0, hbm_layers * t_layer - min(2, streamed) * t_copy). out also
+ * gets the device and pinned-host bytes init_model would allocate (the device
+ * figure includes workspace_bytes, the GEMMs' split-K partials), and fits =
+ * both within the capacities. Errors: TOD_EINVAL on a null pointer, a run
+ * configuration init_model would reject, or a non-positive rate.
+ *
+ * plan_decode searches weight tier (0, 1, 2), GPU batch b and batches per
+ * block K (powers of two, b * K <= max_rows) and, on the host tiers,
+ * hbm_layers (0..n_layers), for the most decode tokens per second among the
+ * configurations that fit; ties keep the earliest in the order lower tier,
+ * larger b, smaller K, smaller hbm_layers (decode cost depends on b * K only;
+ * b sets prefill's batch of b * prompt_len rows, so the largest b that fits
+ * is kept). *best is a complete run configuration (group 64, one
+ * block, host_layers 0) and *est its estimate. TOD_ENOMEM if nothing fits.
+ */
+typedef struct {
+    double attn_gbs, mem_gbs, link_gbs, int4_tflops, fp16_tflops, launch_us, hbm_bytes, host_bytes;
+} tod_hw;
+typedef struct {
+    double step_s, tokens_per_s, compute_s, link_s, hbm_bytes, host_bytes, workspace_bytes;
+    int32_t fits;
+} tod_estimate;
+void default_hw(tod_hw *hw);
+int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out);
+int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int max_rows, const tod_hw *hw,
+                tod_run_config *best, tod_estimate *est);
+
 #ifdef __cplusplus
 }
 #endif

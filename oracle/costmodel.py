@@ -17,6 +17,20 @@ Two models are given:
   block, row-by-row execution streams the model once per micro-batch per
   token, the zig-zag schedule once per token for the whole block, so
   row-by-row moves K times the bytes.
+
+A third part, ``decode_step`` / ``footprint`` / ``plan``, prices one decode
+step of the library's block schedule from measured rates, and searches the
+run configurations for the most tokens per second under memory capacities.
+It extends the simulator's "time = bytes moved / link rate" with the
+roofline terms of the step (GEMM flops, KV-cache reads) and with the
+placement choices that the FlexLLMGen overview ("A 175B-parameter model on
+one GPU, if you can wait": caveats) leaves to manual flags. It is written
+from that definition, term by term, for the parity tests of the library's
+own cost model. With free compute and an all-streamed fp16 model it reduces
+to the simulator's formula (pinned against the printed figures). The device
+footprint here leaves out the library's split-K workspace, a GEMM-plan
+detail of a few tens of MB; the parity tests keep capacities far from every
+candidate's footprint so that the omission cannot change a fit decision.
 """
 from __future__ import annotations
 
@@ -49,3 +63,130 @@ def throughput(model_bytes: float, link_bytes_s: float, tokens: int, batch: int,
     """Tokens/s when the link is the only cost: block of ``micro_batches`` batches of ``batch`` rows."""
     t = weight_bytes(model_bytes, tokens, micro_batches, schedule) / link_bytes_s
     return batch * micro_batches * tokens / t
+
+
+# ---------------------------------------------------------------------------
+# decode step model, footprint and configuration search
+# ---------------------------------------------------------------------------
+
+TIER_HBM_INT4, TIER_HOST_FP16, TIER_HOST_INT4 = 0, 1, 2
+
+
+def _layer_weights(shape) -> float:
+    """Elements of the four GEMM matrices of a layer: qkv 3h x h, out h x h, fc1 f x h, fc2 h x f."""
+    h, f = float(shape.hidden), float(shape.ffn)
+    return 3 * h * h + h * h + f * h + h * f
+
+
+def _bytes_per_weight(tier: int) -> float:
+    # fp16 on the fp16 host tier; otherwise a 4-bit code plus a (scale, zero) fp16 pair per 64 weights
+    return 2.0 if tier == TIER_HOST_FP16 else 0.5 + 4.0 / 64
+
+
+def _kernel(seconds: float, hw: dict) -> float:
+    return max(seconds, hw["launch_us"] * 1e-6)
+
+
+def decode_step(shape, run: dict, hw: dict) -> dict:
+    """Seconds per decode step at the average decode context, and tokens/s."""
+    tier = run.get("weight_tier", TIER_HBM_INT4)
+    rows = run["gpu_batch"] * run["batches_per_block"]
+    h, f, d, heads, vocab = shape.hidden, shape.ffn, shape.head_dim, shape.n_heads, shape.vocab
+    mem = hw["mem_gbs"] * 1e9
+    gemm_rate = (hw["fp16_tflops"] if tier == TIER_HOST_FP16 else hw["int4_tflops"]) * 1e12
+    context = run["prompt_len"] + run["gen_len"] / 2.0
+
+    layer = 0.0
+    for n_out, n_in in ((3 * h, h), (h, h), (f, h), (h, f)):
+        flops = 2.0 * rows * n_out * n_in
+        weight_bytes_ = n_out * n_in * _bytes_per_weight(tier)
+        layer += _kernel(max(flops / gemm_rate, weight_bytes_ / mem), hw)
+    per_position = 2 * (d / 2 + 4 * (d / 64))          # K and V: codes + (scale, zero) per group
+    attention_bytes = rows * heads * (context * per_position + 4 * d)   # cache, plus q and out in fp16
+    layer += _kernel(attention_bytes / (hw["attn_gbs"] * 1e9), hw)
+    layer += _kernel(rows * heads * (2 * 2 * d + per_position) / mem, hw)  # append: read k, v; write codes
+
+    head = _kernel(rows * h * 4.0 / mem, hw)            # embedding: two table rows in, one row out
+    head += _kernel(rows * h * 4.0 / mem, hw)           # the first layer's LayerNorm
+    head += _kernel(max(2.0 * rows * vocab * h / (hw["fp16_tflops"] * 1e12), vocab * h * 2.0 / mem), hw)
+    head += _kernel(rows * vocab * 2.0 / mem, hw)       # argmax over the fp16 logits
+    compute = shape.n_layers * layer + head
+
+    link = 0.0
+    step = compute
+    if tier != TIER_HBM_INT4:
+        resident = run.get("hbm_layers", 0)
+        streamed = shape.n_layers - resident
+        copy = _layer_weights(shape) * _bytes_per_weight(tier) / (hw["link_gbs"] * 1e9)
+        link = streamed * copy
+        if streamed > 0:
+            # the resident layers run while at most two copies (one per slot) are in flight
+            idle = max(0.0, resident * layer - min(2, streamed) * copy)
+            step = max(compute, link + idle)
+    return {"step_s": step, "tokens_per_s": rows / step, "compute_s": compute, "link_s": link}
+
+
+def footprint(shape, run: dict) -> tuple:
+    """(device bytes without the split-K workspace, pinned host bytes) of a run configuration."""
+    tier = run.get("weight_tier", TIER_HBM_INT4)
+    rows = run["gpu_batch"] * run["batches_per_block"]
+    h, f, d, heads, vocab, L = shape.hidden, shape.ffn, shape.head_dim, shape.n_heads, shape.vocab, shape.n_layers
+    image = _layer_weights(shape) * _bytes_per_weight(tier)
+    device = 0.0
+    if tier == TIER_HBM_INT4:
+        device += L * image
+        streamed = 0
+    else:
+        resident = run.get("hbm_layers", 0)
+        streamed = L - resident
+        device += resident * image + (2 * image if streamed else 0)
+    device += L * 2.0 * ((3 * h + h + f + h) + 4 * h)   # biases and LayerNorm vectors, fp16
+    device += 2.0 * h * (vocab + shape.max_pos + 2 + 2)  # token and position tables, final LayerNorm
+    capacity = -(-(run["prompt_len"] + run["gen_len"] - 1) // 64) * 64
+    per_slab_position = 2 * (d / 2 + 4 * (d / 64))
+    device += run.get("n_blocks", 1) * L * rows * heads * capacity * per_slab_position
+    prefill_rows = run["gpu_batch"] * run["prompt_len"]
+    work_rows = max(prefill_rows, rows)
+    device += 2.0 * (rows * run["prompt_len"] * h         # block hidden states during prefill
+                     + work_rows * (h + 3 * h + h + f)     # LayerNorm out, qkv, attention out, fc1 out
+                     + rows * h + rows * vocab)            # last-position rows, logits
+    device += 4.0 * rows                                   # token ids
+    if tier != TIER_HOST_FP16:                             # quantization staging
+        largest = max(f, 3 * h) * h
+        device += largest * 2 + largest / 2 + 2 * (largest / 64 * 2)
+    if tier == TIER_HBM_INT4:                              # decode-graph position and ids
+        device += 4 + 4.0 * rows
+    pinned = 0
+    if tier != TIER_HBM_INT4:
+        held = run.get("host_layers", 0)
+        pinned = (held if 0 < held < streamed else streamed) * image
+    return device, float(pinned)
+
+
+def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
+    """Most decode tokens/s over tier, GPU batch b, batches per block K (powers of two, b * K <= max_rows)
+    and resident layers, among configurations whose footprint fits hw's capacities. Ties keep the first
+    found in the order: tier ascending, b descending, K ascending, resident layers ascending (the step
+    depends on b * K only, and the largest b gives prefill its largest batches). Returns (run, estimate)
+    or None."""
+    best = None
+    top = 1
+    while top * 2 <= max_rows:
+        top *= 2
+    for tier in (TIER_HBM_INT4, TIER_HOST_FP16, TIER_HOST_INT4):
+        b = top
+        while b >= 1:
+            k = 1
+            while b * k <= max_rows:
+                for resident in range(0, (shape.n_layers if tier != TIER_HBM_INT4 else 0) + 1):
+                    run = dict(gpu_batch=b, batches_per_block=k, prompt_len=prompt_len, gen_len=gen_len,
+                               group=64, weight_tier=tier, n_blocks=1, host_layers=0, hbm_layers=resident)
+                    device, pinned = footprint(shape, run)
+                    if device > hw["hbm_bytes"] or pinned > hw["host_bytes"]:
+                        continue
+                    est = decode_step(shape, run, hw)
+                    if best is None or est["tokens_per_s"] > best[1]["tokens_per_s"]:
+                        best = (run, est)
+                k *= 2
+            b //= 2
+    return best

@@ -450,3 +450,24 @@ def test_state_errors():
     tod.decode_block(m.handle, 0, 2, ids, out)
     torch.cuda.synchronize()
     m.close()
+
+
+@pytest.mark.parametrize("tier,resident", [(0, 0), (1, 1), (2, 2)])
+def test_footprint_matches_device_allocation(tier, resident):
+    """The cost model's device footprint of a run configuration (estimate_decode) against the device
+    memory init_model actually takes: 4 layers at OPT-6.7B width, 64 rows, prompt 128."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_6_7B.replace(n_layers=4)
+    run = dict(gpu_batch=16, batches_per_block=4, prompt_len=128, gen_len=16, weight_tier=tier,
+               hbm_layers=resident)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    m = tod.Model(shape, run)
+    torch.cuda.synchronize()
+    used = free0 - torch.cuda.mem_get_info()[0]
+    m.close()
+    est = tod.estimate_decode(shape, run)
+    print(f"tier {tier} resident {resident}: allocated {used / 2**20:.1f} MiB, predicted "
+          f"{est['hbm_bytes'] / 2**20:.1f} MiB", flush=True)
+    assert abs(used - est["hbm_bytes"]) <= 0.03 * est["hbm_bytes"] + 128 * 2**20

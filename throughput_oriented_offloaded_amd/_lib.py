@@ -26,7 +26,8 @@ EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", 
             "set_decode_position", "set_decode_graph", "quantize_groupwise", "dequantize_groupwise", "free_model",
             "last_error",
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
-            "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read")
+            "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read",
+            "default_hw", "estimate_decode", "plan_decode")
 KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
                 "argmax", "embed")
 
@@ -48,6 +49,16 @@ class RunConfig(ctypes.Structure):
                 ("prompt_len", ctypes.c_int32), ("gen_len", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("weight_tier", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("host_layers", ctypes.c_int32),
                 ("hbm_layers", ctypes.c_int32)]
+
+
+class HW(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in ("attn_gbs", "mem_gbs", "link_gbs", "int4_tflops", "fp16_tflops",
+                                                 "launch_us", "hbm_bytes", "host_bytes")]
+
+
+class Estimate(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in ("step_s", "tokens_per_s", "compute_s", "link_s", "hbm_bytes",
+                                                 "host_bytes", "workspace_bytes")] + [("fits", ctypes.c_int32)]
 
 
 @functools.lru_cache(maxsize=None)
@@ -79,6 +90,8 @@ def lib() -> ctypes.CDLL:
         "attn_cache_free": [vp],
         "profile_kernels": [vp, ctypes.c_uint],
         "profile_read": [vp, i32, vp, vp],
+        "estimate_decode": [vp, vp, vp, vp],
+        "plan_decode": [vp, i32, i32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -86,6 +99,8 @@ def lib() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     L.last_error.argtypes = []
     L.last_error.restype = ctypes.c_char_p
+    L.default_hw.argtypes = [vp]
+    L.default_hw.restype = None
     return L
 
 
@@ -252,3 +267,46 @@ def profile_read(m, kind: str):
     n = ctypes.c_int64()
     _check("profile_read", lib().profile_read(m, KERNEL_KINDS.index(kind), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+# ---------------------------------------------------------------------------- cost model
+
+def _struct_dict(st) -> dict:
+    return {n: getattr(st, n) for n, _ in st._fields_}
+
+
+def default_hw() -> dict:
+    """The library's measured MI355X rates and capacities (see tod.h, default_hw)."""
+    hw = HW()
+    lib().default_hw(ctypes.byref(hw))
+    return _struct_dict(hw)
+
+
+def _model_config(cfg) -> ModelConfig:
+    return ModelConfig(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.max_pos)
+
+
+def _run_config(run: dict) -> RunConfig:
+    return RunConfig(run["gpu_batch"], run["batches_per_block"], run["prompt_len"], run["gen_len"],
+                     run.get("group", 64), run.get("weight_tier", 0), run.get("n_blocks", 1),
+                     run.get("host_layers", 0), run.get("hbm_layers", 0))
+
+
+def estimate_decode(cfg, run: dict, hw: dict | None = None) -> dict:
+    """Predicted decode step (seconds, tokens/s) and footprint of a run configuration."""
+    h = HW(**(hw or default_hw()))
+    est = Estimate()
+    mc, rc_ = _model_config(cfg), _run_config(run)
+    _check("estimate_decode", lib().estimate_decode(ctypes.byref(mc), ctypes.byref(rc_), ctypes.byref(h),
+                                                    ctypes.byref(est)))
+    return _struct_dict(est)
+
+
+def plan_decode(cfg, prompt_len: int, gen_len: int, max_rows: int, hw: dict | None = None):
+    """Best run configuration (dict) for decode tokens/s under the capacities, and its estimate."""
+    h = HW(**(hw or default_hw()))
+    best, est = RunConfig(), Estimate()
+    mc = _model_config(cfg)
+    _check("plan_decode", lib().plan_decode(ctypes.byref(mc), prompt_len, gen_len, max_rows, ctypes.byref(h),
+                                            ctypes.byref(best), ctypes.byref(est)))
+    return _struct_dict(best), _struct_dict(est)

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtod.so")
-SOURCES = ("quant.hip", "gemm.hip", "attn.hip", "misc.hip", "runtime.hip")
+SOURCES = ("quant.hip", "gemm.hip", "attn.hip", "misc.hip", "runtime.hip", "policy.hip")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,218 @@
+// Cost model and placement search for block decode (host code only).
+//
+// The FlexGen guide's cost simulator ("Implementation: Simulating FlexGen's
+// Zig-Zag Block Scheduling in Python") prices a generation step as the time to
+// move the weights over PCIe; the FlexLLMGen overview ("A 175B-parameter model
+// on one GPU, if you can wait": what it does; caveats) places tensors across
+// the memory hierarchy with a policy that is tuned by hand through flags, an
+// automatic optimiser being future work. Here the step is priced from the
+// measured rates of this build's kernels and of the host link, and the search
+// enumerates the run-configuration choices the library offers (weight tier,
+// resident layers, GPU batch and batches per block) under the device and
+// pinned-host capacities.
+//
+// Step model at the average decode context c = prompt_len + gen_len / 2:
+//  * each int4 GEMM (or fp16 on the fp16 host tier) costs the larger of its
+//    flops at the GEMM rate and its weight bytes at the streaming rate, and at
+//    least one kernel's launch floor;
+//  * decode attention moves M * heads * (c * (d + d/8) + 4d) bytes at the
+//    attention rate; the KV append reads 4d and writes d + d/8 bytes per
+//    (row, head); one LayerNorm per step (the others are fused); the LM head is
+//    an fp16 GEMM plus the logits' write and the argmax's read;
+//  * on the host tiers the L - R streamed layers each copy one layer image at
+//    the link rate while the GPU computes; the first streamed copies (at most
+//    two, one per slot) overlap the R resident layers, which leaves the link
+//    idle for max(0, R * t_layer - min(2, L - R) * t_copy), so the step takes
+//    max(compute, link + idle).
+// The footprint mirrors init_model's allocations.
+#include <cmath>
+
+#include "common.hpp"
+#include "tod.h"
+
+namespace {
+
+struct Shape {
+    double L, h, H, d, f, V, P;
+};
+
+double weights_per_layer(const Shape &s) { return 4.0 * s.h * s.h + 2.0 * s.h * s.f; }
+
+double image_bytes(const Shape &s, int tier)
+{
+    return weights_per_layer(s) * (tier == TOD_W_HOST_FP16_STREAM ? 2.0 : 0.5625);
+}
+
+bool valid(const tod_model_config *c, const tod_run_config *r)
+{
+    return c && r && c->n_layers > 0 && c->hidden > 0 && c->n_heads > 0 && c->head_dim > 0 && c->ffn > 0 &&
+           c->vocab > 0 && r->gpu_batch > 0 && r->batches_per_block > 0 && r->prompt_len > 0 && r->gen_len > 0 &&
+           r->n_blocks > 0 && r->weight_tier >= TOD_W_HBM_INT4 && r->weight_tier <= TOD_W_HOST_INT4_STREAM &&
+           r->hbm_layers >= 0 && r->hbm_layers <= c->n_layers && r->host_layers >= 0 &&
+           (r->weight_tier != TOD_W_HBM_INT4 || (r->hbm_layers == 0 && r->host_layers == 0));
+}
+
+// Device and pinned-host bytes init_model allocates for this configuration.
+void footprint(const tod_model_config *c, const tod_run_config *r, double *hbm, double *host, double *wsb)
+{
+    const Shape s{(double)c->n_layers, (double)c->hidden, (double)c->n_heads, (double)c->head_dim,
+                  (double)c->ffn, (double)c->vocab, (double)c->max_pos};
+    const int tier = r->weight_tier;
+    const bool streamed = tier != TOD_W_HBM_INT4, int4 = tier != TOD_W_HOST_FP16_STREAM;
+    const double M = (double)r->gpu_batch * r->batches_per_block;
+    const double L = s.L, h = s.h, f = s.f;
+    const int R = streamed ? r->hbm_layers : 0;
+    const int S = streamed ? c->n_layers - R : 0;
+    const int P = r->host_layers > 0 && r->host_layers < S ? r->host_layers : S;
+    const double img = image_bytes(s, tier);
+    double dev = 0.0;
+    // weights: int4 store (tier 0) or resident images and two slots; biases and LayerNorm vectors
+    dev += streamed ? R * img + (S > 0 ? 2.0 * img : 0.0) : L * image_bytes(s, TOD_W_HBM_INT4);
+    dev += L * ((5.0 * h + f) * 2.0 + 4.0 * h * 2.0);
+    dev += s.V * h * 2.0 + (s.P + 2.0) * h * 2.0 + 2.0 * h * 2.0;
+    // KV cache: per block, layer and (row, head) slab, codes and params of K and V
+    const double cap = std::ceil((r->prompt_len + r->gen_len - 1) / 64.0) * 64.0;
+    const double slabs = M * s.H;
+    dev += r->n_blocks * L * 2.0 * (slabs * cap * s.d / 2.0 + slabs * cap * (s.d / 64.0) * 4.0);
+    // activations
+    const double prow = (double)r->gpu_batch * r->prompt_len, arow = prow > M ? prow : M;
+    dev += M * r->prompt_len * h * 2.0 + arow * (h + 3.0 * h + h + f) * 2.0 + M * h * 2.0 + M * s.V * 2.0 +
+           M * 4.0;
+    // split-K workspace
+    const int mats[4][2] = {{3 * c->hidden, c->hidden}, {c->hidden, c->hidden}, {c->ffn, c->hidden},
+                            {c->hidden, c->ffn}};
+    size_t ws = gemm_workspace_bytes((int)M, c->vocab, c->hidden, false);
+    for (int rows : {(int)M, (int)prow})
+        for (const auto &mk : mats) {
+            const size_t b = gemm_workspace_bytes(rows, mk[0], mk[1], int4);
+            ws = b > ws ? b : ws;
+        }
+    dev += (double)ws;
+    *wsb = (double)ws;
+    // quantization staging (int4 tiers) and the decode-graph buffers (tier 0)
+    if (int4) {
+        const double big = (f > 3.0 * h ? f : 3.0 * h) * h;
+        dev += big * 2.0 + big / 2.0 + 2.0 * (big / 64.0 * 2.0);
+    }
+    if (!streamed)
+        dev += 4.0 + M * 4.0;
+    *hbm = dev;
+    *host = streamed ? P * img : 0.0;
+}
+
+double kernel_time(double work_s, const tod_hw *hw) { return work_s > hw->launch_us * 1e-6 ? work_s : hw->launch_us * 1e-6; }
+
+void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw *hw, tod_estimate *e)
+{
+    const Shape s{(double)c->n_layers, (double)c->hidden, (double)c->n_heads, (double)c->head_dim,
+                  (double)c->ffn, (double)c->vocab, (double)c->max_pos};
+    const int tier = r->weight_tier;
+    const bool streamed = tier != TOD_W_HBM_INT4;
+    const double M = (double)r->gpu_batch * r->batches_per_block;
+    const double h = s.h, f = s.f, d = s.d;
+    const double wbpe = tier == TOD_W_HOST_FP16_STREAM ? 2.0 : 0.5625; // weight bytes per element
+    const double rate = (tier == TOD_W_HOST_FP16_STREAM ? hw->fp16_tflops : hw->int4_tflops) * 1e12;
+    const double mem = hw->mem_gbs * 1e9;
+    const double ctx = r->prompt_len + r->gen_len / 2.0;
+    // one layer
+    const double nk[4][2] = {{3.0 * h, h}, {h, h}, {f, h}, {h, f}};
+    double t_layer = 0.0;
+    for (const auto &g : nk) {
+        const double flop = 2.0 * M * g[0] * g[1], wb = g[0] * g[1] * wbpe;
+        const double t = flop / rate > wb / mem ? flop / rate : wb / mem;
+        t_layer += kernel_time(t, hw);
+    }
+    const double kvpos = d + d / 8.0; // K and V codes and params per (head, position)
+    t_layer += kernel_time(M * s.H * (ctx * kvpos + 4.0 * d) / (hw->attn_gbs * 1e9), hw);
+    t_layer += kernel_time(M * s.H * (4.0 * d + kvpos) / mem, hw);
+    // head: embedding, the first LayerNorm, LM head GEMM, argmax
+    double t_head = kernel_time(M * h * 2.0 * 2.0 / mem, hw) + kernel_time(M * h * 4.0 / mem, hw);
+    const double lm_flop = 2.0 * M * s.V * h, lm_w = s.V * h * 2.0;
+    t_head += kernel_time(lm_flop / (hw->fp16_tflops * 1e12) > lm_w / mem ? lm_flop / (hw->fp16_tflops * 1e12)
+                                                                            : lm_w / mem,
+                          hw);
+    t_head += kernel_time(M * s.V * 2.0 / mem, hw);
+    const double t_comp = s.L * t_layer + t_head;
+    double t_link = 0.0, idle = 0.0;
+    if (streamed) {
+        const int R = r->hbm_layers, S = c->n_layers - R;
+        const double t_copy = weights_per_layer(s) * wbpe / (hw->link_gbs * 1e9);
+        t_link = S * t_copy;
+        if (S > 0) {
+            const double overlap = (S < 2 ? S : 2) * t_copy;
+            idle = R * t_layer > overlap ? R * t_layer - overlap : 0.0;
+        }
+    }
+    e->compute_s = t_comp;
+    e->link_s = t_link;
+    e->step_s = streamed && t_link + idle > t_comp ? t_link + idle : t_comp;
+    e->tokens_per_s = M / e->step_s;
+}
+
+} // namespace
+
+void default_hw(tod_hw *hw)
+{
+    if (!hw)
+        return;
+    hw->attn_gbs = 6250.0;    // decode attention, int4 cache, OPT-30B shape
+    hw->mem_gbs = 7100.0;     // streaming reads with nontemporal 16-byte loads
+    hw->link_gbs = 57.2;      // one pinned -> HBM copy of a layer image
+    hw->int4_tflops = 930.0;  // fused int4 GEMMs at 512 rows, real data
+    hw->fp16_tflops = 410.0;  // fp16-weight GEMM (LM head)
+    hw->launch_us = 4.0;      // per kernel inside a replayed decode graph
+    hw->hbm_bytes = 280e9;    // device memory a model may use
+    hw->host_bytes = 270e9;   // pinned host memory a process may hold
+}
+
+int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out)
+{
+    if (!out || !hw || !valid(cfg, run))
+        return TOD_EINVAL;
+    if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
+          hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0))
+        return TOD_EINVAL;
+    step_model(cfg, run, hw, out);
+    footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes);
+    out->fits = out->hbm_bytes <= hw->hbm_bytes && out->host_bytes <= hw->host_bytes;
+    return TOD_OK;
+}
+
+int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int max_rows, const tod_hw *hw,
+                tod_run_config *best, tod_estimate *est)
+{
+    if (!cfg || !hw || !best || !est || prompt_len <= 0 || gen_len <= 0 || max_rows <= 0)
+        return TOD_EINVAL;
+    bool found = false;
+    tod_estimate cur{};
+    int b_top = 1;
+    while (b_top * 2 <= max_rows)
+        b_top *= 2;
+    for (int tier = TOD_W_HBM_INT4; tier <= TOD_W_HOST_INT4_STREAM; tier++)
+        for (int b = b_top; b >= 1; b /= 2)
+            for (int K = 1; b * K <= max_rows; K *= 2) {
+                const int r_max = tier == TOD_W_HBM_INT4 ? 0 : cfg->n_layers;
+                for (int R = 0; R <= r_max; R++) {
+                    tod_run_config r{};
+                    r.gpu_batch = b;
+                    r.batches_per_block = K;
+                    r.prompt_len = prompt_len;
+                    r.gen_len = gen_len;
+                    r.group = 64;
+                    r.weight_tier = tier;
+                    r.n_blocks = 1;
+                    r.host_layers = 0;
+                    r.hbm_layers = R;
+                    const int rc = estimate_decode(cfg, &r, hw, &cur);
+                    if (rc)
+                        return rc;
+                    // strictly better only: ties keep the earlier (lower tier, larger b, then smaller K, R)
+                    if (cur.fits && (!found || cur.tokens_per_s > est->tokens_per_s)) {
+                        *best = r;
+                        *est = cur;
+                        found = true;
+                    }
+                }
+            }
+    return found ? TOD_OK : TOD_ENOMEM;
+}
