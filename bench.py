@@ -62,10 +62,10 @@ def gemm_shapes(shape, rows):
             "gemm_fc2": (rows, h, f), "lm_head": (rows, shape.vocab, h)}
 
 
-def build_model(tod, synth, w, log_every=8):
+def build_model(tod, synth, w, log_every=8, kv_host_layers=0):
     shape = w.shape
     run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
-               gen_len=w.gen_len, weight_tier=w.weight_tier)
+               gen_len=w.gen_len, weight_tier=w.weight_tier, kv_host_layers=kv_host_layers)
     m = tod.Model(shape, run)
     g = synth.global_weights(shape)
     m.set_global_weights(g["tok_emb"], g["pos_emb"], g["lnf_g"], g["lnf_b"])
@@ -347,6 +347,9 @@ def main():
                          "opt-175b-int4 (int4 host tier) | attention")
     ap.add_argument("--cpu-baseline", choices=("on", "off"), default="on")
     ap.add_argument("--prompt-len", type=int, default=0, help="host tiers only: prompt length (default 16)")
+    ap.add_argument("--kv-host-layers", type=int, default=0,
+                    help="HBM-weight workloads: trailing layers whose KV cache lives in pinned host memory "
+                         "(default 0; not the headline configuration)")
     ap.add_argument("--hbm-layers", type=int, default=0,
                     help="host tiers only: leading layers whose weights stay resident in HBM (default 0)")
     ap.add_argument("--host-layers", type=int, default=8,
@@ -386,7 +389,7 @@ def main():
     shape, M = w.shape, w.rows
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
-    m = build_model(tod, synth, w)
+    m = build_model(tod, synth, w, kv_host_layers=args.kv_host_layers)
     prompts = torch.from_numpy(synth.prompt_ids(M, w.prompt_len, shape.vocab)).cuda()
     first = torch.empty(M, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
@@ -512,7 +515,8 @@ def main():
                    "hidden": shape.hidden, "heads": shape.n_heads, "head_dim": shape.head_dim, "ffn": shape.ffn,
                    "vocab": shape.vocab, "gpu_batch": w.gpu_batch, "batches_per_block": w.batches_per_block,
                    "rows": M, "prompt_len": w.prompt_len, "gen_len": w.gen_len, "context_avg": ctx_avg,
-                   "weights": "int4 g64 in HBM" if w.weight_tier == 0 else "fp16 streamed from pinned host"},
+                   "weights": "int4 g64 in HBM" if w.weight_tier == 0 else "fp16 streamed from pinned host",
+                   "kv_host_layers": args.kv_host_layers},
         "roofline": roof,
         "hbm_frac_step": hbm_frac,
         "algorithmic_gb_per_step": bytes_avg / 1e9,
@@ -521,7 +525,8 @@ def main():
         "e2e_tokens_per_s": M * w.gen_len / (prefill_s + (w.gen_len - 1) * ms_per_step * 1e-3),
         "kernels": kernels,
         "cost_model": cost_model_check(tod, shape, dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block,
-                                                        prompt_len=w.prompt_len, gen_len=w.gen_len),
+                                                        prompt_len=w.prompt_len, gen_len=w.gen_len,
+                                                        kv_host_layers=args.kv_host_layers),
                                        ms_per_step),
     }
     m.close()

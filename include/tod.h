@@ -93,11 +93,20 @@ typedef struct {
  * and a later streamed layer l streams those of layer
  * hbm_layers + (l - hbm_layers) % host_layers (its vectors stay its own). This
  * exists to measure stacks whose weights exceed the host's memory: copy sizes,
- * streams and overlap are those of distinct layers. */
+ * streams and overlap are those of distinct layers.
+ * kv_host_layers (0..n_layers, default 0; any weight tier): the KV caches of
+ * the last kv_host_layers layers live in pinned host memory (FlexGen guide,
+ * "1. Three-Tier Storage Hierarchy": the cache spills to CPU memory). Each
+ * pass copies such a layer's cached positions into one of two HBM slots on a
+ * copy stream while the previous layers compute; the append writes each new
+ * position into the slot and through to the host cache, and attention reads
+ * the slot. Results are identical for every kv_host_layers; decode steps are
+ * then launched one by one (no decode graph). */
 typedef struct {
     int32_t gpu_batch, batches_per_block, prompt_len, gen_len, group, weight_tier, n_blocks;
     int32_t host_layers;
     int32_t hbm_layers;
+    int32_t kv_host_layers;
 } tod_run_config;
 
 /*
@@ -303,7 +312,11 @@ int attn_cache_free(tod_attn_cache *c);
  * layers each copy one layer image (weights x 2 B fp16, or x 0.5625 B int4) at
  * link_gbs while the GPU computes; the resident layers run while at most two
  * copies (one per slot) are in flight, so step = max(compute, link + idle),
- * idle = max(0, hbm_layers * t_layer - min(2, streamed) * t_copy). out also
+ * idle = max(0, hbm_layers * t_layer - min(2, streamed) * t_copy). Each
+ * host-KV layer (run.kv_host_layers) adds M * heads * ctx * (d + d/8) bytes of
+ * copies to the link (its cached positions in, the new one written through);
+ * with no streamed weights the idle term is max(0, (L - kv_host) * t_layer -
+ * min(2, kv_host) * t_kv). out also
  * gets the device and pinned-host bytes init_model would allocate (the device
  * figure includes workspace_bytes, the GEMMs' split-K partials), and fits =
  * both within the capacities. Errors: TOD_EINVAL on a null pointer, a run
@@ -315,7 +328,8 @@ int attn_cache_free(tod_attn_cache *c);
  * configurations that fit; ties keep the earliest in the order lower tier,
  * larger b, smaller K, smaller hbm_layers (decode cost depends on b * K only;
  * b sets prefill's batch of b * prompt_len rows, so the largest b that fits
- * is kept). *best is a complete run configuration (group 64, one
+ * is kept). A candidate whose device footprint exceeds the capacity gets the
+ * fewest host-KV layers (run.kv_host_layers) that make it fit, if any. *best is a complete run configuration (group 64, one
  * block, host_layers 0) and *est its estimate. TOD_ENOMEM if nothing fits.
  */
 typedef struct {

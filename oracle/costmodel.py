@@ -34,6 +34,8 @@ candidate's footprint so that the omission cannot change a fit decision.
 """
 from __future__ import annotations
 
+import math
+
 PCIE_GB_S = 16.0  # simulator's PCIe constant (guide, Step 1)
 
 
@@ -113,7 +115,8 @@ def decode_step(shape, run: dict, hw: dict) -> dict:
     compute = shape.n_layers * layer + head
 
     link = 0.0
-    step = compute
+    idle = 0.0
+    streamed = 0
     if tier != TIER_HBM_INT4:
         resident = run.get("hbm_layers", 0)
         streamed = shape.n_layers - resident
@@ -122,7 +125,15 @@ def decode_step(shape, run: dict, hw: dict) -> dict:
         if streamed > 0:
             # the resident layers run while at most two copies (one per slot) are in flight
             idle = max(0.0, resident * layer - min(2, streamed) * copy)
-            step = max(compute, link + idle)
+    kv_host = run.get("kv_host_layers", 0)
+    if kv_host > 0:
+        # per host-KV layer: context - 1 cached positions in, the appended one written through
+        kv_copy = rows * heads * context * per_position / (hw["link_gbs"] * 1e9)
+        link += kv_host * kv_copy
+        if streamed == 0:
+            # the first two host-KV copies (one per slot) overlap the layers in front of them
+            idle = max(0.0, (shape.n_layers - kv_host) * layer - min(2, kv_host) * kv_copy)
+    step = max(compute, link + idle) if link > 0 else compute
     return {"step_s": step, "tokens_per_s": rows / step, "compute_s": compute, "link_s": link}
 
 
@@ -144,7 +155,9 @@ def footprint(shape, run: dict) -> tuple:
     device += 2.0 * h * (vocab + shape.max_pos + 2 + 2)  # token and position tables, final LayerNorm
     capacity = -(-(run["prompt_len"] + run["gen_len"] - 1) // 64) * 64
     per_slab_position = 2 * (d / 2 + 4 * (d / 64))
-    device += run.get("n_blocks", 1) * L * rows * heads * capacity * per_slab_position
+    cache = rows * heads * capacity * per_slab_position   # one block-layer
+    kv_host = run.get("kv_host_layers", 0)
+    device += run.get("n_blocks", 1) * (L - kv_host) * cache + (2 * cache if kv_host else 0)
     prefill_rows = run["gpu_batch"] * run["prompt_len"]
     work_rows = max(prefill_rows, rows)
     device += 2.0 * (rows * run["prompt_len"] * h         # block hidden states during prefill
@@ -160,7 +173,16 @@ def footprint(shape, run: dict) -> tuple:
     if tier != TIER_HBM_INT4:
         held = run.get("host_layers", 0)
         pinned = (held if 0 < held < streamed else streamed) * image
+    pinned += run.get("n_blocks", 1) * kv_host * cache
     return device, float(pinned)
+
+
+def _cache_bytes(shape, run: dict) -> float:
+    """One block-layer's KV cache: every (row, head) slab's capacity of K and V codes and params."""
+    capacity = -(-(run["prompt_len"] + run["gen_len"] - 1) // 64) * 64
+    rows = run["gpu_batch"] * run["batches_per_block"]
+    d = shape.head_dim
+    return rows * shape.n_heads * capacity * 2 * (d / 2 + 4 * (d / 64))
 
 
 def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
@@ -180,8 +202,18 @@ def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
             while b * k <= max_rows:
                 for resident in range(0, (shape.n_layers if tier != TIER_HBM_INT4 else 0) + 1):
                     run = dict(gpu_batch=b, batches_per_block=k, prompt_len=prompt_len, gen_len=gen_len,
-                               group=64, weight_tier=tier, n_blocks=1, host_layers=0, hbm_layers=resident)
+                               group=64, weight_tier=tier, n_blocks=1, host_layers=0, hbm_layers=resident,
+                               kv_host_layers=0)
                     device, pinned = footprint(shape, run)
+                    if device > hw["hbm_bytes"]:
+                        # move the fewest layers' caches to the host that make it fit (the first
+                        # one also adds two device slots)
+                        cache = _cache_bytes(shape, run)
+                        need = math.ceil((device + 2 * cache - hw["hbm_bytes"]) / cache)
+                        if need > shape.n_layers:
+                            continue
+                        run["kv_host_layers"] = max(1, need)
+                        device, pinned = footprint(shape, run)
                     if device > hw["hbm_bytes"] or pinned > hw["host_bytes"]:
                         continue
                     est = decode_step(shape, run, hw)

@@ -191,6 +191,39 @@ def test_weights_set_after_a_pass_are_streamed(tier):
     assert torch.equal(got[1], logits.cpu().view(torch.int16))
 
 
+@pytest.mark.parametrize("tier", [0, 2])
+def test_host_kv_tier_gives_identical_bits(tier):
+    """KV caches of the last 0, 2 or 4 of 4 layers in pinned host memory (two blocks, so the
+    host caches are per block): identical tokens, logits and exported cache bytes."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_125M.replace(n_layers=4)
+    s, g, b, K = 24, 5, 4, 2
+    prompts = [to_dev(synth.prompt_ids(b * K, s, shape.vocab, seed=1 + blk), torch) for blk in range(2)]
+    outs = []
+    for kv_host in (0, 2, 4):
+        run = dict(gpu_batch=b, batches_per_block=K, prompt_len=s, gen_len=g, weight_tier=tier, n_blocks=2,
+                   kv_host_layers=kv_host)
+        m, _ = build_gpu_model(shape, run)
+        res = []
+        for blk in range(2):
+            toks, logits = m.generate(prompts[blk], g, block=blk, return_logits=True)
+            res += [toks.cpu(), logits.cpu().view(torch.int16)]
+        T, d = s + g - 1, shape.head_dim
+        for layer, blk, row, head in ((3, 1, 5, 7), (0, 0, 2, 3)):
+            kc = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+            vc = torch.empty_like(kc)
+            ks, kz, vs, vz = (torch.empty((T, d // 64), dtype=torch.float16, device="cuda") for _ in range(4))
+            tod.export_kv(m.handle, layer, blk, row, head, 0, T, kc, ks, kz, vc, vs, vz)
+            res += [x.cpu() for x in (kc, vc)] + [x.cpu().view(torch.int16) for x in (ks, kz, vs, vz)]
+        torch.cuda.synchronize()
+        m.close()
+        outs.append(res)
+        print(f"tier {tier} kv_host_layers {kv_host}: tokens equal {torch.equal(outs[0][0], res[0])}", flush=True)
+    for res in outs[1:]:
+        assert all(torch.equal(x, y) for x, y in zip(outs[0], res))
+
+
 def test_int4_host_tier_matches_hbm_tier():
     """The int4 host tier streams the same tiled int4 image the HBM tier keeps
     resident, so prefill + decode give identical bits (tokens and logits) on a

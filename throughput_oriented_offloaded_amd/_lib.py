@@ -48,7 +48,7 @@ class RunConfig(ctypes.Structure):
     _fields_ = [("gpu_batch", ctypes.c_int32), ("batches_per_block", ctypes.c_int32),
                 ("prompt_len", ctypes.c_int32), ("gen_len", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("weight_tier", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("host_layers", ctypes.c_int32),
-                ("hbm_layers", ctypes.c_int32)]
+                ("hbm_layers", ctypes.c_int32), ("kv_host_layers", ctypes.c_int32)]
 
 
 class HW(ctypes.Structure):
@@ -143,11 +143,11 @@ def _host16(a: np.ndarray) -> np.ndarray:
 def init_model(cfg, run, stream=None) -> ctypes.c_void_p:
     """cfg: synth.ModelShape-like (n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos);
     run: dict with gpu_batch, batches_per_block, prompt_len, gen_len, and optional group, weight_tier,
-    n_blocks, host_layers, hbm_layers."""
+    n_blocks, host_layers, hbm_layers, kv_host_layers."""
     mc = ModelConfig(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.max_pos)
     rc_ = RunConfig(run["gpu_batch"], run["batches_per_block"], run["prompt_len"], run["gen_len"],
                     run.get("group", 64), run.get("weight_tier", 0), run.get("n_blocks", 1),
-                    run.get("host_layers", 0), run.get("hbm_layers", 0))
+                    run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0))
     h = ctypes.c_void_p()
     _check("init_model", lib().init_model(ctypes.byref(mc), ctypes.byref(rc_), _stream(stream), ctypes.byref(h)))
     return h
@@ -289,7 +289,7 @@ def _model_config(cfg) -> ModelConfig:
 def _run_config(run: dict) -> RunConfig:
     return RunConfig(run["gpu_batch"], run["batches_per_block"], run["prompt_len"], run["gen_len"],
                      run.get("group", 64), run.get("weight_tier", 0), run.get("n_blocks", 1),
-                     run.get("host_layers", 0), run.get("hbm_layers", 0))
+                     run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0))
 
 
 def estimate_decode(cfg, run: dict, hw: dict | None = None) -> dict:

@@ -238,9 +238,10 @@ hipError_t launch_unpack_w4(const uint32_t *tcodes, const uint32_t *tparams, int
 struct SrcMap {
     int64_t seq_stride, pos_stride, head_stride;
 };
-// quantize + store the K and V vectors of `rows` rows into the cache
+// quantize + store the K and V vectors of `rows` rows into the cache (and, when
+// mirror is given, the same bytes into that second cache of the same shape)
 hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, SrcMap src, int rows, RowMap map, KvView kv,
-                            hipStream_t st);
+                            hipStream_t st, const KvView *mirror = nullptr);
 hipError_t launch_kv_export(KvView kv, int seq, int head, int t0, int t1, uint8_t *kc, uint16_t *ks, uint16_t *kz,
                             uint8_t *vc, uint16_t *vs, uint16_t *vz, hipStream_t st);
 // decode attention: each of `rows` rows is one sequence (seq0 + r) attending positions 0..ctx-1

@@ -23,8 +23,15 @@
 //    the link rate while the GPU computes; the first streamed copies (at most
 //    two, one per slot) overlap the R resident layers, which leaves the link
 //    idle for max(0, R * t_layer - min(2, L - R) * t_copy), so the step takes
-//    max(compute, link + idle).
-// The footprint mirrors init_model's allocations.
+//    max(compute, link + idle);
+//  * each of the last kv_host layers (host KV tier) also copies its ctx - 1
+//    cached positions and writes its appended one through, M * heads * ctx *
+//    (d + d/8) bytes, over the same link. When no weights stream, the first
+//    two host-KV copies (one per slot) can start as soon as the previous pass
+//    frees their slots and overlap the L - kv_host layers before them; the
+//    link idles for max(0, (L - kv_host) * t_layer - min(2, kv_host) * t_kv).
+// The footprint mirrors init_model's allocations. The search takes, for each
+// candidate, the fewest host-KV layers that make it fit.
 #include <cmath>
 
 #include "common.hpp"
@@ -48,7 +55,8 @@ bool valid(const tod_model_config *c, const tod_run_config *r)
     return c && r && c->n_layers > 0 && c->hidden > 0 && c->n_heads > 0 && c->head_dim > 0 && c->ffn > 0 &&
            c->vocab > 0 && r->gpu_batch > 0 && r->batches_per_block > 0 && r->prompt_len > 0 && r->gen_len > 0 &&
            r->n_blocks > 0 && r->weight_tier >= TOD_W_HBM_INT4 && r->weight_tier <= TOD_W_HOST_INT4_STREAM &&
-           r->hbm_layers >= 0 && r->hbm_layers <= c->n_layers && r->host_layers >= 0 &&
+           r->hbm_layers >= 0 && r->hbm_layers <= c->n_layers && r->host_layers >= 0 && r->kv_host_layers >= 0 &&
+           r->kv_host_layers <= c->n_layers &&
            (r->weight_tier != TOD_W_HBM_INT4 || (r->hbm_layers == 0 && r->host_layers == 0));
 }
 
@@ -70,10 +78,13 @@ void footprint(const tod_model_config *c, const tod_run_config *r, double *hbm, 
     dev += streamed ? R * img + (S > 0 ? 2.0 * img : 0.0) : L * image_bytes(s, TOD_W_HBM_INT4);
     dev += L * ((5.0 * h + f) * 2.0 + 4.0 * h * 2.0);
     dev += s.V * h * 2.0 + (s.P + 2.0) * h * 2.0 + 2.0 * h * 2.0;
-    // KV cache: per block, layer and (row, head) slab, codes and params of K and V
+    // KV cache: per block, layer and (row, head) slab, codes and params of K and V; the
+    // host KV tier keeps its layers' caches pinned and two HBM slots of one block-layer
     const double cap = std::ceil((r->prompt_len + r->gen_len - 1) / 64.0) * 64.0;
     const double slabs = M * s.H;
-    dev += r->n_blocks * L * 2.0 * (slabs * cap * s.d / 2.0 + slabs * cap * (s.d / 64.0) * 4.0);
+    const double kv_layer = 2.0 * (slabs * cap * s.d / 2.0 + slabs * cap * (s.d / 64.0) * 4.0);
+    const int KVH = r->kv_host_layers;
+    dev += r->n_blocks * (L - KVH) * kv_layer + (KVH > 0 ? 2.0 * kv_layer : 0.0);
     // activations
     const double prow = (double)r->gpu_batch * r->prompt_len, arow = prow > M ? prow : M;
     dev += M * r->prompt_len * h * 2.0 + arow * (h + 3.0 * h + h + f) * 2.0 + M * h * 2.0 + M * s.V * 2.0 +
@@ -97,7 +108,15 @@ void footprint(const tod_model_config *c, const tod_run_config *r, double *hbm, 
     if (!streamed)
         dev += 4.0 + M * 4.0;
     *hbm = dev;
-    *host = streamed ? P * img : 0.0;
+    *host = (streamed ? P * img : 0.0) + r->n_blocks * (double)KVH * kv_layer;
+}
+
+// Bytes of one block-layer's KV cache (codes and params of K and V).
+double kv_layer_bytes(const tod_model_config *c, const tod_run_config *r)
+{
+    const double cap = std::ceil((r->prompt_len + r->gen_len - 1) / 64.0) * 64.0;
+    const double slabs = (double)r->gpu_batch * r->batches_per_block * c->n_heads;
+    return slabs * cap * (c->head_dim + c->head_dim / 8.0);
 }
 
 double kernel_time(double work_s, const tod_hw *hw) { return work_s > hw->launch_us * 1e-6 ? work_s : hw->launch_us * 1e-6; }
@@ -134,8 +153,10 @@ void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw
     t_head += kernel_time(M * s.V * 2.0 / mem, hw);
     const double t_comp = s.L * t_layer + t_head;
     double t_link = 0.0, idle = 0.0;
+    int S = 0;
     if (streamed) {
-        const int R = r->hbm_layers, S = c->n_layers - R;
+        const int R = r->hbm_layers;
+        S = c->n_layers - R;
         const double t_copy = weights_per_layer(s) * wbpe / (hw->link_gbs * 1e9);
         t_link = S * t_copy;
         if (S > 0) {
@@ -143,9 +164,19 @@ void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw
             idle = R * t_layer > overlap ? R * t_layer - overlap : 0.0;
         }
     }
+    const int KVH = r->kv_host_layers;
+    if (KVH > 0) {
+        // ctx - 1 cached positions loaded and the new one written through, per host-KV layer
+        const double t_kv = M * s.H * ctx * kvpos / (hw->link_gbs * 1e9);
+        t_link += KVH * t_kv;
+        if (S == 0) { // the first two host-KV copies (one per slot) overlap the layers before them
+            const double front = (c->n_layers - KVH) * t_layer, overlap = (KVH < 2 ? KVH : 2) * t_kv;
+            idle = front > overlap ? front - overlap : 0.0;
+        }
+    }
     e->compute_s = t_comp;
     e->link_s = t_link;
-    e->step_s = streamed && t_link + idle > t_comp ? t_link + idle : t_comp;
+    e->step_s = t_link > 0.0 && t_link + idle > t_comp ? t_link + idle : t_comp;
     e->tokens_per_s = M / e->step_s;
 }
 
@@ -203,9 +234,29 @@ int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int ma
                     r.n_blocks = 1;
                     r.host_layers = 0;
                     r.hbm_layers = R;
-                    const int rc = estimate_decode(cfg, &r, hw, &cur);
+                    r.kv_host_layers = 0;
+                    int rc = estimate_decode(cfg, &r, hw, &cur);
                     if (rc)
                         return rc;
+                    if (cur.hbm_bytes > hw->hbm_bytes) {
+                        // the fewest host-KV layers that bring the device footprint within the
+                        // capacity: each moves one layer's cache out, the first also adds two
+                        // slots. Counted without the split-K workspace, then raised while the
+                        // workspace still keeps it from fitting.
+                        const double kv_layer = kv_layer_bytes(cfg, &r);
+                        const double need = std::ceil((cur.hbm_bytes - cur.workspace_bytes + 2.0 * kv_layer -
+                                                       hw->hbm_bytes) / kv_layer);
+                        if (need > cfg->n_layers)
+                            continue;
+                        r.kv_host_layers = need < 1.0 ? 1 : (int)need;
+                        if ((rc = estimate_decode(cfg, &r, hw, &cur)))
+                            return rc;
+                        while (cur.hbm_bytes > hw->hbm_bytes && r.kv_host_layers < cfg->n_layers) {
+                            r.kv_host_layers++;
+                            if ((rc = estimate_decode(cfg, &r, hw, &cur)))
+                                return rc;
+                        }
+                    }
                     // strictly better only: ties keep the earlier (lower tier, larger b, then smaller K, R)
                     if (cur.fits && (!found || cur.tokens_per_s > est->tokens_per_s)) {
                         *best = r;

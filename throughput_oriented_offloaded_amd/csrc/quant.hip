@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(256) k_unpack_w4(const uint32_t *__restrict__ 
 // lane: one 16-byte load, min/max over the group by DPP, and one 32-bit store
 // of the lane's four code bytes into the canonical per-position layout.
 __global__ void __launch_bounds__(256) k_kv_append(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-                                                   SrcMap src_map, int rows, RowMap map, KvView kv)
+                                                   SrcMap src_map, int rows, RowMap map, KvView kv, KvView mirror)
 {
     const int G = kv.head_dim / 64;
     const int64_t item = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 3;
@@ -206,11 +206,18 @@ __global__ void __launch_bounds__(256) k_kv_append(const uint16_t *__restrict__ 
         word |= (uint32_t)code_of(x[e], q) << (4 * e);
     const size_t at = kv_slab(kv, seq, head) * kv.cap + pos;
     const int cb = kv.head_dim / 2; // code bytes per position
+    const uint32_t param = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
     uint8_t *codes = isv ? kv.vc : kv.kc;
     *reinterpret_cast<uint32_t *>(codes + at * cb + g * 32 + part * 4) = word;
     if (part == 0) {
         uint32_t *pp = isv ? kv.vp : kv.kp;
-        pp[at * G + g] = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
+        pp[at * G + g] = param;
+    }
+    if (mirror.kc) { // the same bytes into a second cache of the same shape (pinned host memory)
+        uint8_t *mc = isv ? mirror.vc : mirror.kc;
+        *reinterpret_cast<uint32_t *>(mc + at * cb + g * 32 + part * 4) = word;
+        if (part == 0)
+            (isv ? mirror.vp : mirror.kp)[at * G + g] = param;
     }
 }
 
@@ -280,12 +287,15 @@ hipError_t launch_unpack_w4(const uint32_t *tcodes, const uint32_t *tparams, int
 }
 
 hipError_t launch_kv_append(const uint16_t *k, const uint16_t *v, SrcMap src, int rows, RowMap map, KvView kv,
-                            hipStream_t st)
+                            hipStream_t st, const KvView *mirror)
 {
     const int64_t items = (int64_t)rows * kv.heads * (kv.head_dim / 64) * 2;
     if (items == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_kv_append, dim3(blocks_for(items, 32)), dim3(256), 0, st, k, v, src, rows, map, kv);
+    KvView mv{};
+    if (mirror)
+        mv = *mirror;
+    hipLaunchKernelGGL(k_kv_append, dim3(blocks_for(items, 32)), dim3(256), 0, st, k, v, src, rows, map, kv, mv);
     return hipGetLastError();
 }
 

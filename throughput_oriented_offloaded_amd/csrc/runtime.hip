@@ -94,6 +94,12 @@ struct tod_model {
     hipStream_t copy = nullptr;
     hipEvent_t ev_loaded[2] = {}, ev_free[2] = {};
     bool prefetched = false; // slot 0 holds, or is being filled with, the first streamed layer
+    // host KV tier: the last kv_host layers keep their caches in pinned host memory; a
+    // step copies a layer's cached positions into one of two HBM slots, and the append
+    // writes each new position into the slot and through to the host cache
+    int kv_host = 0;
+    KvView kvslot[2] = {};
+    hipEvent_t ev_kv_loaded[2] = {}, ev_kv_free[2] = {};
     std::vector<int> prefilled, decoded;
     // captured decode steps (HBM tier): one graph per block, replayed on gstream;
     // the step reads its position from gpos and its token ids from gids (the
@@ -269,7 +275,7 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
 // (or the head). LN2 comes out of the out-projection GEMM the same way.
 int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, bool prefill_mode, int seq0, int s,
                int pos, const int *dpos, const uint8_t *wslot, hipStream_t st, bool act_ready = false,
-               const uint16_t *next_g = nullptr, const uint16_t *next_b = nullptr)
+               const uint16_t *next_g = nullptr, const uint16_t *next_b = nullptr, const KvView *kv_mirror = nullptr)
 {
     const int hd = m->cfg.hidden, f = m->cfg.ffn;
     const LayerStore &L = m->layers[l];
@@ -291,7 +297,7 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
     }
     {
         ProfScope ps(m, TOD_K_KV_APPEND, st);
-        HIPCHK(launch_kv_append(m->qkv + hd, m->qkv + 2 * hd, src, rows, map, kv, st));
+        HIPCHK(launch_kv_append(m->qkv + hd, m->qkv + 2 * hd, src, rows, map, kv, st, kv_mirror));
     }
     {
         ProfScope ps(m, TOD_K_ATTN, st);
@@ -329,19 +335,47 @@ int stream_layer(tod_model *m, int l)
     return TOD_OK;
 }
 
-// One pass over all layers. `body(l, wslot)` runs layer l for every batch of the block.
+// Host KV tier: enqueue the copy of positions [0, npos) of layer l's host cache
+// (block `block`) into its HBM slot on the copy stream (host-KV layers alternate
+// between the two slots), after the slot's previous user has finished.
+int stream_kv(tod_model *m, int block, int l, int npos)
+{
+    const int sl = (l - (m->cfg.n_layers - m->kv_host)) & 1;
+    HIPCHK(hipStreamWaitEvent(m->copy, m->ev_kv_free[sl], 0));
+    if (npos > 0) {
+        const KvView &src = m->kv[(size_t)block * m->cfg.n_layers + l];
+        const KvView &dst = m->kvslot[sl];
+        const size_t slabs = (size_t)m->M * m->cfg.n_heads, cb = (size_t)m->cfg.head_dim / 2,
+                     pb = (size_t)m->cfg.head_dim / 64 * 4, cap = (size_t)m->cap;
+        // per slab the first npos positions of each array: one 2D copy per array
+        HIPCHK(hipMemcpy2DAsync(dst.kc, cap * cb, src.kc, cap * cb, npos * cb, slabs, hipMemcpyHostToDevice, m->copy));
+        HIPCHK(hipMemcpy2DAsync(dst.vc, cap * cb, src.vc, cap * cb, npos * cb, slabs, hipMemcpyHostToDevice, m->copy));
+        HIPCHK(hipMemcpy2DAsync(dst.kp, cap * pb, src.kp, cap * pb, npos * pb, slabs, hipMemcpyHostToDevice, m->copy));
+        HIPCHK(hipMemcpy2DAsync(dst.vp, cap * pb, src.vp, cap * pb, npos * pb, slabs, hipMemcpyHostToDevice, m->copy));
+    }
+    HIPCHK(hipEventRecord(m->ev_kv_loaded[sl], m->copy));
+    return TOD_OK;
+}
+
+// One pass over all layers of block `block`. `body(l, wslot, kv, mirror)` runs
+// layer l for every batch of the block against the KV cache `kv` (mirror: the
+// host cache the appended positions are also written to, or null). Host-KV
+// layers get an HBM slot holding their first kv_npos cached positions.
 template <class F>
-int stack_pass(tod_model *m, hipStream_t st, F body)
+int stack_pass(tod_model *m, hipStream_t st, int block, int kv_npos, F body)
 {
     // layers below R run from HBM (the int4 store, or a host tier's resident
     // image); the others stream. The first streamed layer's copy is issued at
     // the end of the previous pass (layer images never change during passes),
     // so it overlaps that pass's tail, the head and this pass's resident layers.
     const int L = m->cfg.n_layers, R = m->streamed ? m->hbm_layers : L;
+    const int KH = L - m->kv_host; // first layer whose KV cache lives on the host
     int rc;
     if (R < L && !m->prefetched && (rc = stream_layer(m, R)))
         return rc;
     m->prefetched = false;
+    if (KH == 0 && L > 0 && (rc = stream_kv(m, block, 0, kv_npos)))
+        return rc;
     for (int l = 0; l < L; l++) {
         const uint8_t *wslot = l < R ? m->layers[l].dev : nullptr;
         const int sl = (l - R) & 1;
@@ -351,10 +385,22 @@ int stack_pass(tod_model *m, hipStream_t st, F body)
             HIPCHK(hipStreamWaitEvent(st, m->ev_loaded[sl], 0));
             wslot = m->slot[sl];
         }
-        if ((rc = body(l, wslot)))
+        if (l + 1 < L && l + 1 >= KH && (rc = stream_kv(m, block, l + 1, kv_npos)))
+            return rc;
+        const KvView *kv = &m->kv[(size_t)block * L + l];
+        const KvView *mirror = nullptr;
+        const int ks = (l - KH) & 1;
+        if (l >= KH) {
+            HIPCHK(hipStreamWaitEvent(st, m->ev_kv_loaded[ks], 0));
+            mirror = kv;
+            kv = &m->kvslot[ks];
+        }
+        if ((rc = body(l, wslot, *kv, mirror)))
             return rc;
         if (l >= R)
             HIPCHK(hipEventRecord(m->ev_free[sl], st));
+        if (l >= KH)
+            HIPCHK(hipEventRecord(m->ev_kv_free[ks], st));
     }
     if (R < L) { // the next pass's first copy, ordered after this pass's use of its slot
         if ((rc = stream_layer(m, R)))
@@ -434,6 +480,10 @@ int free_model(tod_model *m)
             (void)hipEventDestroy(m->ev_loaded[i]);
         if (m->ev_free[i])
             (void)hipEventDestroy(m->ev_free[i]);
+        if (m->ev_kv_loaded[i])
+            (void)hipEventDestroy(m->ev_kv_loaded[i]);
+        if (m->ev_kv_free[i])
+            (void)hipEventDestroy(m->ev_kv_free[i]);
     }
     if (m->copy)
         (void)hipStreamDestroy(m->copy);
@@ -511,6 +561,9 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         return fail(TOD_EINVAL, "hbm_layers (%d) applies to the host tiers only and must be in [0, n_layers]",
                     r.hbm_layers);
     m->hbm_layers = host ? r.hbm_layers : 0;
+    if (r.kv_host_layers < 0 || r.kv_host_layers > L)
+        return fail(TOD_EINVAL, "kv_host_layers (%d) must be in [0, n_layers]", r.kv_host_layers);
+    m->kv_host = r.kv_host_layers;
     const int n_streamed = host ? L - m->hbm_layers : 0;
     m->host_layers = r.host_layers > 0 && r.host_layers < n_streamed ? r.host_layers : n_streamed;
 
@@ -557,11 +610,40 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         for (int l = 0; l < L; l++) {
             uint8_t *kc, *vc;
             uint32_t *kp, *vp;
+            if (l >= L - m->kv_host) {
+                // host KV tier: pinned and coherent, so the append kernel's stores through to it
+                // are visible to the later copies into the HBM slot
+                void *p = nullptr;
+                const size_t bytes = 2 * (kc_b + kp_b);
+                hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocCoherent);
+                if (e != hipSuccess) {
+                    (void)hipGetLastError();
+                    return fail(TOD_ENOMEM, "hipHostMalloc(%zu bytes) for the KV cache of layer %d failed: %s", bytes,
+                                l, hipGetErrorString(e));
+                }
+                m->host_allocs.push_back(p);
+                uint8_t *base = static_cast<uint8_t *>(p);
+                kc = base;
+                vc = base + kc_b;
+                kp = reinterpret_cast<uint32_t *>(base + 2 * kc_b);
+                vp = reinterpret_cast<uint32_t *>(base + 2 * kc_b + kp_b);
+            } else {
+                ALLOC(kc, kc_b);
+                ALLOC(vc, kc_b);
+                ALLOC(kp, kp_b);
+                ALLOC(vp, kp_b);
+            }
+            m->kv[(size_t)b * L + l] = make_kv_view(kc, kp, vc, vp, c.n_heads, c.head_dim, m->cap);
+        }
+    if (m->kv_host > 0) // two HBM slots of one block-layer each
+        for (int i = 0; i < 2; i++) {
+            uint8_t *kc, *vc;
+            uint32_t *kp, *vp;
             ALLOC(kc, kc_b);
             ALLOC(vc, kc_b);
             ALLOC(kp, kp_b);
             ALLOC(vp, kp_b);
-            m->kv[(size_t)b * L + l] = make_kv_view(kc, kp, vc, vp, c.n_heads, c.head_dim, m->cap);
+            m->kvslot[i] = make_kv_view(kc, kp, vc, vp, c.n_heads, c.head_dim, m->cap);
         }
 
     // activations: prefill processes one batch (b * s rows) per layer call; the
@@ -590,15 +672,17 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     m->ws_bytes = ws;
     ALLOC(m->ws, ws);
 
-    if (host) {
-        if (n_streamed > 0) {
-            ALLOC(m->slot[0], (size_t)m->layer_bytes);
-            ALLOC(m->slot[1], (size_t)m->layer_bytes);
-        }
+    if (host && n_streamed > 0) {
+        ALLOC(m->slot[0], (size_t)m->layer_bytes);
+        ALLOC(m->slot[1], (size_t)m->layer_bytes);
+    }
+    if (host || m->kv_host > 0) { // the copy stream and the events that order slot reuse
         HIPCHK(hipStreamCreateWithFlags(&m->copy, hipStreamNonBlocking));
         for (int i = 0; i < 2; i++) {
             HIPCHK(hipEventCreateWithFlags(&m->ev_loaded[i], hipEventDisableTiming));
             HIPCHK(hipEventCreateWithFlags(&m->ev_free[i], hipEventDisableTiming));
+            HIPCHK(hipEventCreateWithFlags(&m->ev_kv_loaded[i], hipEventDisableTiming));
+            HIPCHK(hipEventCreateWithFlags(&m->ev_kv_free[i], hipEventDisableTiming));
         }
     }
     if (m->int4) { // quantization staging for the HBM and int4 host tiers
@@ -740,12 +824,11 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
         HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, nullptr, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
                                 m->hid + k * brow * h, st));
     }
-    rc = stack_pass(m, st, [&](int l, const uint8_t *wslot) -> int {
-        const KvView &kv = m->kv[(size_t)block * L + l];
+    rc = stack_pass(m, st, block, 0, [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
         for (int kk = 0; kk < K; kk++) {
             const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
-            const int r =
-                layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, nullptr, wslot, st);
+            const int r = layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, nullptr, wslot,
+                                     st, false, nullptr, nullptr, mirror);
             if (r)
                 return r;
         }
@@ -774,12 +857,13 @@ static int decode_step(tod_model *m, int block, const int32_t *in, int pos, cons
     }
     // all M rows pass each layer together, so every LayerNorm after the first
     // comes out of the GEMM before it (the last one is the head's LN_f)
-    int rc = stack_pass(m, st, [&](int l, const uint8_t *wslot) -> int {
+    // host-KV layers load the pos positions cached before this step (the graph path,
+    // whose position lives on the device, is not taken when there are any)
+    int rc = stack_pass(m, st, block, pos, [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
         const bool last = l + 1 == L;
         const uint16_t *ng = last ? m->lnf_g : m->layers[l + 1].ln1_g;
         const uint16_t *nb = last ? m->lnf_b : m->layers[l + 1].ln1_b;
-        return layer_pass(m, l, m->kv[(size_t)block * L + l], m->hid, Mr, false, 0, 1, pos, dpos, wslot, st, l > 0,
-                          ng, nb);
+        return layer_pass(m, l, kv, m->hid, Mr, false, 0, 1, pos, dpos, wslot, st, l > 0, ng, nb, mirror);
     });
     if (rc)
         return rc;
@@ -834,7 +918,7 @@ int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, 
     const hipStream_t st = S(stream);
     const int Mr = m->M, V = m->cfg.vocab;
     const bool graph = n_steps > 0 && m->graphs_on && !m->prof_mask && m->gstream &&
-                       m->run.weight_tier == TOD_W_HBM_INT4 && !m->gfail[block] &&
+                       m->run.weight_tier == TOD_W_HBM_INT4 && m->kv_host == 0 && !m->gfail[block] &&
                        (m->gexec[block] || capture_step(m, block) || (m->gfail[block] = 1, false));
     if (graph) {
         // replay on the model's stream, ordered after and before the caller's
