@@ -95,6 +95,35 @@ def measure_h2d(torch, nbytes, reps=3):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def measure_disk_read(path, image_bytes, n_images):
+    """GB/s of reads of the weight file's images, one image per read as the library issues them,
+    no copy to the device: the better of direct (O_DIRECT) reads and buffered reads whose pages are
+    dropped from the page cache afterwards (the library's method). Returns (best, direct, buffered)."""
+    import mmap
+    stride = -(-image_bytes // 4096) * 4096
+    buf = mmap.mmap(-1, stride)  # page-aligned, as O_DIRECT needs
+    rates = []
+    for flags in (getattr(os, "O_DIRECT", 0), 0):
+        fd = os.open(path, os.O_RDONLY | flags)
+        try:
+            for i in range(n_images):  # start cold
+                os.posix_fadvise(fd, i * stride, stride, os.POSIX_FADV_DONTNEED)
+            t0 = time.perf_counter()
+            for i in range(n_images):
+                done = 0
+                while done < stride:
+                    n = os.preadv(fd, [memoryview(buf)[done:]], i * stride + done)
+                    if n <= 0:
+                        raise OSError("short read of the weight file")
+                    done += n
+                os.posix_fadvise(fd, i * stride, stride, os.POSIX_FADV_DONTNEED)
+            rates.append(n_images * image_bytes / (time.perf_counter() - t0) / 1e9)
+        finally:
+            os.close(fd)
+    buf.close()
+    return max(rates), rates[0], rates[1]
+
+
 def cost_model_check(tod, shape, run, measured_ms):
     """The library's cost model (estimate_decode, default measured rates) for this run beside the
     measured step time."""
@@ -124,10 +153,12 @@ def host_tier_bench(args, w, tod, synth, torch):
     L, h, f = shape.n_layers, shape.hidden, shape.ffn
     R = min(max(args.hbm_layers, 0), L)
     P = min(args.host_layers, L - R)
+    on_disk = bool(args.weight_file)
     run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
-               gen_len=w.gen_len, weight_tier=w.weight_tier, host_layers=P, hbm_layers=R)
+               gen_len=w.gen_len, weight_tier=w.weight_tier, host_layers=P, hbm_layers=R,
+               weights_on_disk=int(on_disk))
     t_setup = time.perf_counter()
-    m = tod.Model(shape, run)
+    m = tod.Model(shape, run, weight_file=args.weight_file or None)
     g = synth.global_weights(shape)
     m.set_global_weights(g["tok_emb"], g["pos_emb"], g["lnf_g"], g["lnf_b"])
     del g
@@ -177,6 +208,11 @@ def host_tier_bench(args, w, tod, synth, torch):
     link_gbs = (L - R) * layer_bytes * steps / elapsed / 1e9
     log("measuring pinned -> HBM copy rate ...")
     h2d = measure_h2d(torch, layer_bytes)
+    disk = disk_direct = disk_buffered = None
+    if on_disk:
+        log("measuring direct reads of the weight file ...")
+        disk, disk_direct, disk_buffered = measure_disk_read(args.weight_file, layer_bytes, P)
+        os.remove(args.weight_file)
     return {
         "metric": f"generated tokens/sec (1 GPU), OPT-175B shape {'int4' if int4 else 'fp16'} weights streamed "
                   "from pinned host; % of measured host-link bandwidth",
@@ -197,9 +233,16 @@ def host_tier_bench(args, w, tod, synth, torch):
                    "gpu_batch": w.gpu_batch, "batches_per_block": w.batches_per_block, "rows": M,
                    "prompt_len": w.prompt_len, "gen_len": w.gen_len, "hbm_layers": R, "host_layers_pinned": P,
                    "weights": ("int4 group-64 (tiled codes + fp16 scale/zero)" if int4 else "fp16")
-                   + " in pinned host memory, 2 HBM layer slots, copies on a side stream"},
-        "roofline": {"bound": "link", "achieved": link_gbs, "peak": h2d, "unit": "GB/s", "frac": link_gbs / h2d,
-                     "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"},
+                   + (" in a file on disk, read into 2 pinned staging buffers" if on_disk else
+                      " in pinned host memory") + ", 2 HBM layer slots, copies on a side stream"},
+        "roofline": ({"bound": "link", "achieved": link_gbs, "peak": h2d, "unit": "GB/s", "frac": link_gbs / h2d,
+                      "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"} if not on_disk else
+                     {"bound": "disk", "achieved": link_gbs, "peak": min(disk, h2d), "unit": "GB/s",
+                      "frac": link_gbs / min(disk, h2d), "traffic": None,
+                      "kernel": "pread -> pinned staging -> hipMemcpyAsync -> HBM, one layer per read"}),
+        "disk_read_measured_gbs": disk,
+        "disk_read_direct_gbs": disk_direct if on_disk else None,
+        "disk_read_buffered_gbs": disk_buffered if on_disk else None,
         "link_bytes_per_step": (L - R) * layer_bytes,
         "h2d_measured_gbs": h2d,
         "prefill_s": prefill_s,
@@ -350,6 +393,8 @@ def main():
     ap.add_argument("--kv-host-layers", type=int, default=0,
                     help="HBM-weight workloads: trailing layers whose KV cache lives in pinned host memory "
                          "(default 0; not the headline configuration)")
+    ap.add_argument("--weight-file", default="",
+                    help="host tiers only: keep the streamed images in this file (created; O_DIRECT reads)")
     ap.add_argument("--hbm-layers", type=int, default=0,
                     help="host tiers only: leading layers whose weights stay resident in HBM (default 0)")
     ap.add_argument("--host-layers", type=int, default=8,

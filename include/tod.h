@@ -101,13 +101,35 @@ typedef struct {
  * copy stream while the previous layers compute; the append writes each new
  * position into the slot and through to the host cache, and attention reads
  * the slot. Results are identical for every kv_host_layers; decode steps are
- * then launched one by one (no decode graph). */
+ * then launched one by one (no decode graph).
+ * weights_on_disk (host tiers only; 0 or 1): the streamed layers' images live
+ * in a file named by set_weight_file instead of pinned memory (FlexGen guide,
+ * "1. Three-Tier Storage Hierarchy": the disk tier below CPU memory). */
 typedef struct {
     int32_t gpu_batch, batches_per_block, prompt_len, gen_len, group, weight_tier, n_blocks;
     int32_t host_layers;
     int32_t hbm_layers;
     int32_t kv_host_layers;
+    int32_t weights_on_disk;
 } tod_run_config;
+
+/*
+ * set_weight_file: for a model created with run.weights_on_disk, create (or
+ * truncate) the file at `path` that holds the streamed layers' images; call it
+ * once, before set_layer_weights. set_layer_weights then writes each image
+ * that a streamed layer owns (see host_layers) to the file, 4 KiB-aligned, and
+ * every pass reads it back into one of two pinned staging buffers on an I/O
+ * stream, from which the copy stream moves it into the HBM slot; reads of one
+ * layer overlap the copy of the previous one. Direct I/O cannot target pinned
+ * memory, so the reads are buffered, and each image is dropped from the page
+ * cache after it is written and after every read: each pass reads the disk. Results are identical to the pinned
+ * tiers. A failed read makes the next prefill / decode_block return TOD_EHIP
+ * (the outputs of the pass it happened in are undefined). The library keeps
+ * the file open until free_model and never deletes it.
+ * Errors: TOD_EINVAL (null argument, cannot open), TOD_ESTATE (not a disk-tier
+ * model, file already set, or weights already set).
+ */
+int set_weight_file(tod_model *m, const char *path);
 
 /*
  * init_model: allocate a model (weights store, KV caches, activation buffers).
@@ -300,7 +322,8 @@ int attn_cache_free(tod_attn_cache *c);
  * tod_hw: attn_gbs = decode-attention read rate, mem_gbs = streaming rate of
  * the other row-wise kernels and weight reads, link_gbs = pinned -> HBM copy
  * rate (GB/s); int4_tflops / fp16_tflops = GEMM rates by weight type; launch_us
- * = floor per kernel; hbm_bytes / host_bytes = capacities the model may use.
+ * = floor per kernel; hbm_bytes / host_bytes = capacities the model may use;
+ * disk_gbs / disk_bytes = read rate and free space of the weight file's disk.
  * default_hw fills the figures measured on MI355X for this library.
  *
  * estimate_decode prices one decode step of the block `run` describes at the
@@ -316,7 +339,10 @@ int attn_cache_free(tod_attn_cache *c);
  * host-KV layer (run.kv_host_layers) adds M * heads * ctx * (d + d/8) bytes of
  * copies to the link (its cached positions in, the new one written through);
  * with no streamed weights the idle term is max(0, (L - kv_host) * t_layer -
- * min(2, kv_host) * t_kv). out also
+ * min(2, kv_host) * t_kv). With run.weights_on_disk a streamed layer's copy
+ * takes max(image / link_gbs, image / disk_gbs) (disk reads and link copies of
+ * consecutive layers overlap), the pinned memory is two staging images and
+ * disk_bytes the file. out also
  * gets the device and pinned-host bytes init_model would allocate (the device
  * figure includes workspace_bytes, the GEMMs' split-K partials), and fits =
  * both within the capacities. Errors: TOD_EINVAL on a null pointer, a run
@@ -329,14 +355,17 @@ int attn_cache_free(tod_attn_cache *c);
  * larger b, smaller K, smaller hbm_layers (decode cost depends on b * K only;
  * b sets prefill's batch of b * prompt_len rows, so the largest b that fits
  * is kept). A candidate whose device footprint exceeds the capacity gets the
- * fewest host-KV layers (run.kv_host_layers) that make it fit, if any. *best is a complete run configuration (group 64, one
+ * fewest host-KV layers (run.kv_host_layers) that make it fit, if any. Host
+ * tiers are tried with pinned images first and then with images on disk
+ * (run.weights_on_disk), within disk_bytes. *best is a complete run configuration (group 64, one
  * block, host_layers 0) and *est its estimate. TOD_ENOMEM if nothing fits.
  */
 typedef struct {
-    double attn_gbs, mem_gbs, link_gbs, int4_tflops, fp16_tflops, launch_us, hbm_bytes, host_bytes;
+    double attn_gbs, mem_gbs, link_gbs, int4_tflops, fp16_tflops, launch_us, hbm_bytes, host_bytes, disk_gbs,
+        disk_bytes;
 } tod_hw;
 typedef struct {
-    double step_s, tokens_per_s, compute_s, link_s, hbm_bytes, host_bytes, workspace_bytes;
+    double step_s, tokens_per_s, compute_s, link_s, hbm_bytes, host_bytes, workspace_bytes, disk_bytes;
     int32_t fits;
 } tod_estimate;
 void default_hw(tod_hw *hw);

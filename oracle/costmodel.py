@@ -120,7 +120,11 @@ def decode_step(shape, run: dict, hw: dict) -> dict:
     if tier != TIER_HBM_INT4:
         resident = run.get("hbm_layers", 0)
         streamed = shape.n_layers - resident
-        copy = _layer_weights(shape) * _bytes_per_weight(tier) / (hw["link_gbs"] * 1e9)
+        image = _layer_weights(shape) * _bytes_per_weight(tier)
+        copy = image / (hw["link_gbs"] * 1e9)
+        if run.get("weights_on_disk", 0):
+            # reads from the file and copies over the link overlap across layers
+            copy = max(copy, image / (hw["disk_gbs"] * 1e9))
         link = streamed * copy
         if streamed > 0:
             # the resident layers run while at most two copies (one per slot) are in flight
@@ -171,10 +175,30 @@ def footprint(shape, run: dict) -> tuple:
         device += 4 + 4.0 * rows
     pinned = 0
     if tier != TIER_HBM_INT4:
-        held = run.get("host_layers", 0)
-        pinned = (held if 0 < held < streamed else streamed) * image
+        if run.get("weights_on_disk", 0):
+            pinned = 2 * _aligned_image(image)   # two staging buffers; the images are in the file
+        else:
+            pinned = _owned_images(run, streamed) * image
     pinned += run.get("n_blocks", 1) * kv_host * cache
     return device, float(pinned)
+
+
+def _aligned_image(image: float) -> float:
+    return math.ceil(image / 4096) * 4096
+
+
+def _owned_images(run: dict, streamed: int) -> int:
+    held = run.get("host_layers", 0)
+    return held if 0 < held < streamed else streamed
+
+
+def disk_bytes(shape, run: dict) -> float:
+    """Bytes of the weight file: the streamed layers' own images, each 4 KiB-aligned."""
+    tier = run.get("weight_tier", TIER_HBM_INT4)
+    if tier == TIER_HBM_INT4 or not run.get("weights_on_disk", 0):
+        return 0.0
+    streamed = shape.n_layers - run.get("hbm_layers", 0)
+    return _owned_images(run, streamed) * _aligned_image(_layer_weights(shape) * _bytes_per_weight(tier))
 
 
 def _cache_bytes(shape, run: dict) -> float:
@@ -188,14 +212,16 @@ def _cache_bytes(shape, run: dict) -> float:
 def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
     """Most decode tokens/s over tier, GPU batch b, batches per block K (powers of two, b * K <= max_rows)
     and resident layers, among configurations whose footprint fits hw's capacities. Ties keep the first
-    found in the order: tier ascending, b descending, K ascending, resident layers ascending (the step
+    found in the order: tier ascending (pinned images before images on disk), b descending, K
+    ascending, resident layers ascending (the step
     depends on b * K only, and the largest b gives prefill its largest batches). Returns (run, estimate)
     or None."""
     best = None
     top = 1
     while top * 2 <= max_rows:
         top *= 2
-    for tier in (TIER_HBM_INT4, TIER_HOST_FP16, TIER_HOST_INT4):
+    for tier, on_disk in ((TIER_HBM_INT4, 0), (TIER_HOST_FP16, 0), (TIER_HOST_FP16, 1), (TIER_HOST_INT4, 0),
+                          (TIER_HOST_INT4, 1)):
         b = top
         while b >= 1:
             k = 1
@@ -203,7 +229,7 @@ def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
                 for resident in range(0, (shape.n_layers if tier != TIER_HBM_INT4 else 0) + 1):
                     run = dict(gpu_batch=b, batches_per_block=k, prompt_len=prompt_len, gen_len=gen_len,
                                group=64, weight_tier=tier, n_blocks=1, host_layers=0, hbm_layers=resident,
-                               kv_host_layers=0)
+                               kv_host_layers=0, weights_on_disk=on_disk)
                     device, pinned = footprint(shape, run)
                     if device > hw["hbm_bytes"]:
                         # move the fewest layers' caches to the host that make it fit (the first
@@ -214,7 +240,7 @@ def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
                             continue
                         run["kv_host_layers"] = max(1, need)
                         device, pinned = footprint(shape, run)
-                    if device > hw["hbm_bytes"] or pinned > hw["host_bytes"]:
+                    if device > hw["hbm_bytes"] or pinned > hw["host_bytes"] or disk_bytes(shape, run) > hw["disk_bytes"]:
                         continue
                     est = decode_step(shape, run, hw)
                     if best is None or est["tokens_per_s"] > best[1]["tokens_per_s"]:

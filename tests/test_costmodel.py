@@ -56,9 +56,9 @@ class _Shape:
 
 
 FREE = dict(attn_gbs=1e12, mem_gbs=1e12, link_gbs=16.0, int4_tflops=1e12, fp16_tflops=1e12, launch_us=0.0,
-            hbm_bytes=1e15, host_bytes=1e15)
+            hbm_bytes=1e15, host_bytes=1e15, disk_gbs=1e12, disk_bytes=1e15)
 MI355X = dict(attn_gbs=6250.0, mem_gbs=7100.0, link_gbs=57.2, int4_tflops=930.0, fp16_tflops=410.0,
-              launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9)
+              launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9, disk_gbs=7.4, disk_bytes=80e9)
 
 
 def test_free_compute_reduces_to_the_printed_simulator():
@@ -113,3 +113,20 @@ def test_footprint_terms():
     assert p0 == pytest.approx(4 * image, rel=1e-12) and p2 == pytest.approx(3 * image, rel=1e-12)
     _, p3 = costmodel.footprint(shape, dict(run, host_layers=1))
     assert p3 == pytest.approx(image, rel=1e-12)
+
+
+def test_images_on_disk():
+    """With the images in a file, the slower of the disk read and the link copy paces each streamed
+    layer; pinned memory is two staging images and the file holds the owned images, 4 KiB-aligned."""
+    shape = _Shape(96, 12288, 96, 128, 49152, 50272)
+    image = (4 * 12288 ** 2 + 2 * 12288 * 49152) * (0.5 + 4 / 64)
+    run = dict(gpu_batch=32, batches_per_block=8, prompt_len=16, gen_len=32, weight_tier=2, hbm_layers=16,
+               host_layers=8, weights_on_disk=1)
+    est = costmodel.decode_step(shape, run, MI355X)
+    assert est["link_s"] == pytest.approx(80 * image / 7.4e9, rel=1e-12)
+    fast_disk = dict(MI355X, disk_gbs=1e6)
+    assert costmodel.decode_step(shape, run, fast_disk)["link_s"] == pytest.approx(80 * image / 57.2e9, rel=1e-12)
+    aligned = -(-image // 4096) * 4096
+    assert costmodel.footprint(shape, run)[1] == pytest.approx(2 * aligned, rel=1e-12)
+    assert costmodel.disk_bytes(shape, run) == pytest.approx(8 * aligned, rel=1e-12)
+    assert costmodel.disk_bytes(shape, dict(run, weights_on_disk=0)) == 0.0

@@ -224,6 +224,50 @@ def test_host_kv_tier_gives_identical_bits(tier):
         assert all(torch.equal(x, y) for x, y in zip(outs[0], res))
 
 
+@pytest.mark.parametrize("tier", [1, 2])
+def test_weights_on_disk_give_identical_bits(tier, tmp_path):
+    """Streamed images read back from a file (4 layers: one resident, two owned images, layer 3
+    streaming layer 1's): identical tokens, logits and (int4) exported weights to pinned images."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_125M.replace(n_layers=4)
+    s, g = 16, 4
+    run = dict(gpu_batch=2, batches_per_block=2, prompt_len=s, gen_len=g, weight_tier=tier, hbm_layers=1,
+               host_layers=2)
+    glob = synth.global_weights(shape, variant="full")
+    lw = [synth.layer_weights(shape, l, variant="full") for l in range(4)]
+    for n in ("q_w", "k_w", "v_w", "o_w", "fc1_w", "fc2_w"):
+        lw[3][n] = lw[1][n]
+    prompts = to_dev(synth.prompt_ids(4, s, shape.vocab), torch)
+    outs = []
+    for on_disk in (0, 1):
+        path = str(tmp_path / f"images_{tier}.bin")
+        m = tod.Model(shape, dict(run, weights_on_disk=on_disk), weight_file=path if on_disk else None)
+        m.set_global_weights(glob["tok_emb"], glob["pos_emb"], glob["lnf_g"], glob["lnf_b"])
+        for l in range(4):
+            m.set_layer_weights(l, lw[l])
+        res = []
+        for rep in range(2):  # two passes: the second reads every image from the file again
+            toks, logits = m.generate(prompts, g, return_logits=True)
+            res += [toks.cpu(), logits.cpu().view(torch.int16)]
+        if tier == 2:
+            for l in (0, 1, 3):
+                codes = torch.empty(shape.ffn * shape.hidden // 2, dtype=torch.uint8, device="cuda")
+                scale = torch.empty(shape.ffn * shape.hidden // 64, dtype=torch.float16, device="cuda")
+                zero = torch.empty_like(scale)
+                tod.export_weight(m.handle, l, "fc2", codes, scale, zero)
+                res += [codes.cpu(), scale.cpu().view(torch.int16), zero.cpu().view(torch.int16)]
+        torch.cuda.synchronize()
+        m.close()
+        outs.append(res)
+        if on_disk:
+            import os
+            print(f"tier {tier}: weight file {os.path.getsize(path)} bytes", flush=True)
+    assert all(torch.equal(x, y) for x, y in zip(outs[0], outs[1]))
+    with pytest.raises(tod.TodError):  # images on disk belong to the host tiers
+        tod.Model(shape, dict(run, weight_tier=0, hbm_layers=0, host_layers=0, weights_on_disk=1))
+
+
 def test_int4_host_tier_matches_hbm_tier():
     """The int4 host tier streams the same tiled int4 image the HBM tier keeps
     resident, so prefill + decode give identical bits (tokens and logits) on a

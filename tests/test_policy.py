@@ -28,13 +28,13 @@ def test_estimate_matches_oracle(name):
     hw = tod.default_hw()
     shape = synth.WORKLOADS[name].shape
     L = shape.n_layers
-    for tier, (b, k), resident, (s, g), held, kv_host in itertools.product(
+    for tier, (b, k), resident, (s, g), held, kv_host, on_disk in itertools.product(
             (0, 1, 2), ((1, 1), (4, 2), (64, 8), (32, 8)), (0, 1, L // 2, L), ((16, 32), (512, 32), (100, 7)),
-            (0, 3), (0, 1, L)):
-        if tier == 0 and (resident or held):
+            (0, 3), (0, 1, L), (0, 1)):
+        if tier == 0 and (resident or held or on_disk):
             continue
         run = dict(gpu_batch=b, batches_per_block=k, prompt_len=s, gen_len=g, weight_tier=tier,
-                   hbm_layers=resident, host_layers=held, kv_host_layers=kv_host)
+                   hbm_layers=resident, host_layers=held, kv_host_layers=kv_host, weights_on_disk=on_disk)
         got = tod.estimate_decode(shape, run, hw)
         ref = costmodel.decode_step(shape, run, hw)
         for key in ("step_s", "tokens_per_s", "compute_s", "link_s"):
@@ -42,8 +42,10 @@ def test_estimate_matches_oracle(name):
         device, pinned = costmodel.footprint(shape, run)
         assert got["hbm_bytes"] - got["workspace_bytes"] == pytest.approx(device, rel=1e-12), run
         assert got["host_bytes"] == pytest.approx(pinned, rel=1e-12), run
+        assert got["disk_bytes"] == pytest.approx(costmodel.disk_bytes(shape, run), rel=1e-12), run
         assert 0 <= got["workspace_bytes"] < 1e9
-        assert got["fits"] == (got["hbm_bytes"] <= hw["hbm_bytes"] and got["host_bytes"] <= hw["host_bytes"])
+        assert got["fits"] == (got["hbm_bytes"] <= hw["hbm_bytes"] and got["host_bytes"] <= hw["host_bytes"] and
+                               got["disk_bytes"] <= hw["disk_bytes"])
 
 
 PLAN_CASES = [  # shape, prompt, gen, max rows, device GB, pinned GB
@@ -57,6 +59,7 @@ PLAN_CASES = [  # shape, prompt, gen, max rows, device GB, pinned GB
     ("opt-175b", 512, 32, 256, 90, 270),
     ("opt-175b", 2000, 32, 64, 60, 270),     # long prompts: some caches stay in HBM
     ("opt-175b", 2000, 32, 64, 100, 270),
+    ("opt-175b", 512, 32, 256, 60, 20),      # little pinned memory: the streamed images go to disk
 ]
 
 
@@ -71,13 +74,14 @@ def test_plan_matches_oracle(name, prompt_len, gen_len, max_rows, hbm_gb, host_g
     run, est = tod.plan_decode(shape, prompt_len, gen_len, max_rows, hw)
     ref_run, ref_est = costmodel.plan(shape, prompt_len, gen_len, max_rows, hw)
     for key in ("gpu_batch", "batches_per_block", "weight_tier", "hbm_layers", "host_layers", "prompt_len",
-                "gen_len", "group", "n_blocks", "kv_host_layers"):
+                "gen_len", "group", "n_blocks", "kv_host_layers", "weights_on_disk"):
         assert run[key] == ref_run[key], (key, run, ref_run)
     assert est["tokens_per_s"] == pytest.approx(ref_est["tokens_per_s"], rel=1e-12)
     assert est["fits"] == 1
     print(f"{name} prompt {prompt_len} rows <= {max_rows} hbm {hbm_gb} GB host {host_gb} GB -> tier "
           f"{run['weight_tier']} b {run['gpu_batch']} K {run['batches_per_block']} resident {run['hbm_layers']} "
-          f"host-KV layers {run['kv_host_layers']}: {est['tokens_per_s']:.1f} tokens/s")
+          f"host-KV layers {run['kv_host_layers']} on disk {run['weights_on_disk']}: "
+          f"{est['tokens_per_s']:.1f} tokens/s")
 
 
 @pytest.mark.parametrize("name,prompt_len,gen_len,max_rows,hbm_gb,host_gb", [

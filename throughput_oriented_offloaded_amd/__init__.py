@@ -12,13 +12,14 @@ from ._lib import (TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM, TOD_W_HOST_INT4_STREA
                    attn_cache_export, attn_cache_fill, attn_cache_free, attn_decode_step, decode_block, default_hw,
                    dequantize_groupwise, estimate_decode, export_kv, export_weight, free_model, init_model,
                    last_error, linear_f16, linear_w4, plan_decode, prefill, profile_kernels, profile_read,
-                   quantize_groupwise, set_decode_graph, set_decode_position, set_global_weights, set_layer_weights)
+                   quantize_groupwise, set_decode_graph, set_decode_position, set_global_weights, set_layer_weights,
+                   set_weight_file)
 
 __all__ = ["Model", "TodError", "init_model", "set_global_weights", "set_layer_weights", "prefill",
            "decode_block", "set_decode_position", "set_decode_graph", "quantize_groupwise", "dequantize_groupwise",
            "free_model", "last_error", "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create",
            "attn_cache_fill", "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels",
-           "profile_read", "default_hw", "estimate_decode", "plan_decode",
+           "profile_read", "default_hw", "estimate_decode", "plan_decode", "set_weight_file",
            "TOD_W_HBM_INT4", "TOD_W_HOST_FP16_STREAM", "TOD_W_HOST_INT4_STREAM"]
 
 
@@ -28,14 +29,17 @@ class Model:
     shape: object with n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos.
     run:   dict with gpu_batch, batches_per_block, prompt_len, gen_len,
            optional weight_tier (0 int4 in HBM, 1 fp16 or 2 int4 streamed from pinned host),
-           n_blocks, host_layers and hbm_layers.
+           n_blocks, host_layers, hbm_layers, kv_host_layers and weights_on_disk.
+    weight_file: path of the image file when run["weights_on_disk"] is set.
     """
 
-    def __init__(self, shape, run: dict):
+    def __init__(self, shape, run: dict, weight_file: str | None = None):
         self.shape = shape
         self.run = dict(run)
         self.rows = run["gpu_batch"] * run["batches_per_block"]
         self.handle = init_model(shape, self.run)
+        if weight_file is not None:
+            set_weight_file(self.handle, weight_file)
 
     def set_global_weights(self, tok_emb, pos_emb, lnf_g, lnf_b):
         set_global_weights(self.handle, tok_emb, pos_emb, lnf_g, lnf_b)

@@ -27,7 +27,7 @@ EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", 
             "last_error",
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
             "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read",
-            "default_hw", "estimate_decode", "plan_decode")
+            "default_hw", "estimate_decode", "plan_decode", "set_weight_file")
 KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
                 "argmax", "embed")
 
@@ -48,17 +48,18 @@ class RunConfig(ctypes.Structure):
     _fields_ = [("gpu_batch", ctypes.c_int32), ("batches_per_block", ctypes.c_int32),
                 ("prompt_len", ctypes.c_int32), ("gen_len", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("weight_tier", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("host_layers", ctypes.c_int32),
-                ("hbm_layers", ctypes.c_int32), ("kv_host_layers", ctypes.c_int32)]
+                ("hbm_layers", ctypes.c_int32), ("kv_host_layers", ctypes.c_int32),
+                ("weights_on_disk", ctypes.c_int32)]
 
 
 class HW(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in ("attn_gbs", "mem_gbs", "link_gbs", "int4_tflops", "fp16_tflops",
-                                                 "launch_us", "hbm_bytes", "host_bytes")]
+                                                 "launch_us", "hbm_bytes", "host_bytes", "disk_gbs", "disk_bytes")]
 
 
 class Estimate(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in ("step_s", "tokens_per_s", "compute_s", "link_s", "hbm_bytes",
-                                                 "host_bytes", "workspace_bytes")] + [("fits", ctypes.c_int32)]
+                                                 "host_bytes", "workspace_bytes", "disk_bytes")] + [("fits", ctypes.c_int32)]
 
 
 @functools.lru_cache(maxsize=None)
@@ -92,6 +93,7 @@ def lib() -> ctypes.CDLL:
         "profile_read": [vp, i32, vp, vp],
         "estimate_decode": [vp, vp, vp, vp],
         "plan_decode": [vp, i32, i32, i32, vp, vp, vp],
+        "set_weight_file": [vp, ctypes.c_char_p],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -143,11 +145,12 @@ def _host16(a: np.ndarray) -> np.ndarray:
 def init_model(cfg, run, stream=None) -> ctypes.c_void_p:
     """cfg: synth.ModelShape-like (n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos);
     run: dict with gpu_batch, batches_per_block, prompt_len, gen_len, and optional group, weight_tier,
-    n_blocks, host_layers, hbm_layers, kv_host_layers."""
+    n_blocks, host_layers, hbm_layers, kv_host_layers, weights_on_disk."""
     mc = ModelConfig(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.max_pos)
     rc_ = RunConfig(run["gpu_batch"], run["batches_per_block"], run["prompt_len"], run["gen_len"],
                     run.get("group", 64), run.get("weight_tier", 0), run.get("n_blocks", 1),
-                    run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0))
+                    run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0),
+                    run.get("weights_on_disk", 0))
     h = ctypes.c_void_p()
     _check("init_model", lib().init_model(ctypes.byref(mc), ctypes.byref(rc_), _stream(stream), ctypes.byref(h)))
     return h
@@ -156,6 +159,10 @@ def init_model(cfg, run, stream=None) -> ctypes.c_void_p:
 def set_global_weights(m, tok_emb: np.ndarray, pos_emb: np.ndarray, lnf_g: np.ndarray, lnf_b: np.ndarray):
     arrs = [_host16(x) for x in (tok_emb, pos_emb, lnf_g, lnf_b)]
     _check("set_global_weights", lib().set_global_weights(m, *[a.ctypes.data for a in arrs]))
+
+
+def set_weight_file(m, path: str):
+    _check("set_weight_file", lib().set_weight_file(m, os.fsencode(path)))
 
 
 def set_layer_weights(m, layer: int, tensors):
@@ -289,7 +296,8 @@ def _model_config(cfg) -> ModelConfig:
 def _run_config(run: dict) -> RunConfig:
     return RunConfig(run["gpu_batch"], run["batches_per_block"], run["prompt_len"], run["gen_len"],
                      run.get("group", 64), run.get("weight_tier", 0), run.get("n_blocks", 1),
-                     run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0))
+                     run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0),
+                     run.get("weights_on_disk", 0))
 
 
 def estimate_decode(cfg, run: dict, hw: dict | None = None) -> dict:

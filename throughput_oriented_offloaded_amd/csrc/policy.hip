@@ -29,7 +29,9 @@
 //    (d + d/8) bytes, over the same link. When no weights stream, the first
 //    two host-KV copies (one per slot) can start as soon as the previous pass
 //    frees their slots and overlap the L - kv_host layers before them; the
-//    link idles for max(0, (L - kv_host) * t_layer - min(2, kv_host) * t_kv).
+//    link idles for max(0, (L - kv_host) * t_layer - min(2, kv_host) * t_kv);
+//  * with the images on disk, a streamed layer's copy takes the longer of its
+//    disk read and its link copy (the two overlap across layers).
 // The footprint mirrors init_model's allocations. The search takes, for each
 // candidate, the fewest host-KV layers that make it fit.
 #include <cmath>
@@ -56,12 +58,14 @@ bool valid(const tod_model_config *c, const tod_run_config *r)
            c->vocab > 0 && r->gpu_batch > 0 && r->batches_per_block > 0 && r->prompt_len > 0 && r->gen_len > 0 &&
            r->n_blocks > 0 && r->weight_tier >= TOD_W_HBM_INT4 && r->weight_tier <= TOD_W_HOST_INT4_STREAM &&
            r->hbm_layers >= 0 && r->hbm_layers <= c->n_layers && r->host_layers >= 0 && r->kv_host_layers >= 0 &&
-           r->kv_host_layers <= c->n_layers &&
+           r->kv_host_layers <= c->n_layers && (r->weights_on_disk == 0 || r->weights_on_disk == 1) &&
+           (r->weights_on_disk == 0 || r->weight_tier != TOD_W_HBM_INT4) &&
            (r->weight_tier != TOD_W_HBM_INT4 || (r->hbm_layers == 0 && r->host_layers == 0));
 }
 
 // Device and pinned-host bytes init_model allocates for this configuration.
-void footprint(const tod_model_config *c, const tod_run_config *r, double *hbm, double *host, double *wsb)
+void footprint(const tod_model_config *c, const tod_run_config *r, double *hbm, double *host, double *wsb,
+               double *disk_b)
 {
     const Shape s{(double)c->n_layers, (double)c->hidden, (double)c->n_heads, (double)c->head_dim,
                   (double)c->ffn, (double)c->vocab, (double)c->max_pos};
@@ -108,7 +112,11 @@ void footprint(const tod_model_config *c, const tod_run_config *r, double *hbm, 
     if (!streamed)
         dev += 4.0 + M * 4.0;
     *hbm = dev;
-    *host = (streamed ? P * img : 0.0) + r->n_blocks * (double)KVH * kv_layer;
+    // pinned: the owned images (or, with the images on disk, two staging images) and host caches
+    const double stride = std::ceil(img / 4096.0) * 4096.0;
+    const bool on_disk = streamed && r->weights_on_disk;
+    *host = (streamed ? (on_disk ? 2.0 * stride : P * img) : 0.0) + r->n_blocks * (double)KVH * kv_layer;
+    *disk_b = on_disk ? P * stride : 0.0;
 }
 
 // Bytes of one block-layer's KV cache (codes and params of K and V).
@@ -157,7 +165,12 @@ void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw
     if (streamed) {
         const int R = r->hbm_layers;
         S = c->n_layers - R;
-        const double t_copy = weights_per_layer(s) * wbpe / (hw->link_gbs * 1e9);
+        const double img = weights_per_layer(s) * wbpe;
+        const double t_link_img = img / (hw->link_gbs * 1e9);
+        // from disk, reads and link copies of consecutive layers overlap: the slower sets the pace
+        const double t_copy = r->weights_on_disk && img / (hw->disk_gbs * 1e9) > t_link_img
+                                  ? img / (hw->disk_gbs * 1e9)
+                                  : t_link_img;
         t_link = S * t_copy;
         if (S > 0) {
             const double overlap = (S < 2 ? S : 2) * t_copy;
@@ -194,6 +207,8 @@ void default_hw(tod_hw *hw)
     hw->launch_us = 4.0;      // per kernel inside a replayed decode graph
     hw->hbm_bytes = 280e9;    // device memory a model may use
     hw->host_bytes = 270e9;   // pinned host memory a process may hold
+    hw->disk_gbs = 7.4;       // reads of the weight file (one image per read)
+    hw->disk_bytes = 80e9;    // free space for the weight file
 }
 
 int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out)
@@ -201,11 +216,12 @@ int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, cons
     if (!out || !hw || !valid(cfg, run))
         return TOD_EINVAL;
     if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
-          hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0))
+          hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0))
         return TOD_EINVAL;
     step_model(cfg, run, hw, out);
-    footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes);
-    out->fits = out->hbm_bytes <= hw->hbm_bytes && out->host_bytes <= hw->host_bytes;
+    footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes, &out->disk_bytes);
+    out->fits = out->hbm_bytes <= hw->hbm_bytes && out->host_bytes <= hw->host_bytes &&
+                out->disk_bytes <= hw->disk_bytes;
     return TOD_OK;
 }
 
@@ -220,6 +236,7 @@ int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int ma
     while (b_top * 2 <= max_rows)
         b_top *= 2;
     for (int tier = TOD_W_HBM_INT4; tier <= TOD_W_HOST_INT4_STREAM; tier++)
+        for (int disk = 0; disk <= (tier == TOD_W_HBM_INT4 ? 0 : 1); disk++)
         for (int b = b_top; b >= 1; b /= 2)
             for (int K = 1; b * K <= max_rows; K *= 2) {
                 const int r_max = tier == TOD_W_HBM_INT4 ? 0 : cfg->n_layers;
@@ -235,6 +252,7 @@ int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int ma
                     r.host_layers = 0;
                     r.hbm_layers = R;
                     r.kv_host_layers = 0;
+                    r.weights_on_disk = disk;
                     int rc = estimate_decode(cfg, &r, hw, &cur);
                     if (rc)
                         return rc;
@@ -257,7 +275,8 @@ int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int ma
                                 return rc;
                         }
                     }
-                    // strictly better only: ties keep the earlier (lower tier, larger b, then smaller K, R)
+                    // strictly better only: ties keep the earlier (lower tier, pinned before disk,
+                    // larger b, then smaller K, R)
                     if (cur.fits && (!found || cur.tokens_per_s > est->tokens_per_s)) {
                         *best = r;
                         *est = cur;

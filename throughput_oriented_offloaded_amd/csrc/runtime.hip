@@ -13,11 +13,16 @@
 // abstract, static overlap of transfer and compute): fp16 weights live in
 // pinned host memory; a copy stream brings layer l+1 into one of two HBM
 // slots while the compute stream works on layer l; events order slot reuse.
+#include <atomic>
+#include <cerrno>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <string>
 #include <vector>
+
+#include <fcntl.h>
+#include <unistd.h>
 
 #include "../../include/tod.h"
 #include "common.hpp"
@@ -100,6 +105,17 @@ struct tod_model {
     int kv_host = 0;
     KvView kvslot[2] = {};
     hipEvent_t ev_kv_loaded[2] = {}, ev_kv_free[2] = {};
+    // disk tier: the streamed layers' images live in a file; an I/O stream reads each
+    // into one of two pinned staging buffers, from which the copy stream moves it into the
+    // HBM slot. Direct I/O cannot target pinned buffers, so reads go through the page
+    // cache, and every image is dropped from it after each write and read.
+    bool on_disk = false;
+    int fd = -1;
+    int64_t image_stride = 0; // layer_bytes rounded up to the 4 KiB I/O alignment
+    uint8_t *staging[2] = {};
+    hipStream_t io = nullptr;
+    hipEvent_t ev_staged[2] = {}, ev_staging_free[2] = {};
+    std::atomic<int> io_errno{0};
     std::vector<int> prefilled, decoded;
     // captured decode steps (HBM tier): one graph per block, replayed on gstream;
     // the step reads its position from gpos and its token ids from gids (the
@@ -325,9 +341,59 @@ int image_layer(const tod_model *m, int l)
 
 // Host tiers: enqueue the copy of streamed layer l into its slot (streamed
 // layers alternate between the two) on the copy stream.
+// Disk tier: one read of a layer image into a staging buffer, run on the I/O
+// stream by the HIP runtime's callback thread.
+struct ImageRead {
+    tod_model *m;
+    int sl;
+    int64_t offset;
+};
+
+void read_image(void *arg)
+{
+    ImageRead *job = static_cast<ImageRead *>(arg);
+    tod_model *m = job->m;
+    uint8_t *dst = m->staging[job->sl];
+    int64_t done = 0;
+    while (done < m->image_stride) {
+        const ssize_t n = pread(m->fd, dst + done, (size_t)(m->image_stride - done), job->offset + done);
+        if (n < 0 && errno == EINTR)
+            continue;
+        if (n <= 0) {
+            int expected = 0;
+            m->io_errno.compare_exchange_strong(expected, n < 0 ? errno : EIO);
+            break;
+        }
+        done += n;
+    }
+    (void)posix_fadvise(m->fd, job->offset, m->image_stride, POSIX_FADV_DONTNEED);
+    delete job;
+}
+
+// Byte offset of layer l's image in the weight file (images of the streamed layers that
+// own one, packed from the first streamed layer on).
+int64_t image_offset(const tod_model *m, int l) { return (int64_t)(image_layer(m, l) - m->hbm_layers) * m->image_stride; }
+
 int stream_layer(tod_model *m, int l)
 {
     const int sl = (l - m->hbm_layers) & 1;
+    if (m->on_disk) {
+        // stage on the I/O stream once the previous copy out of this staging buffer is done
+        HIPCHK(hipStreamWaitEvent(m->io, m->ev_staging_free[sl], 0));
+        ImageRead *job = new ImageRead{m, sl, image_offset(m, l)};
+        const hipError_t e = hipLaunchHostFunc(m->io, read_image, job);
+        if (e != hipSuccess) {
+            delete job;
+            HIPCHK(e);
+        }
+        HIPCHK(hipEventRecord(m->ev_staged[sl], m->io));
+        HIPCHK(hipStreamWaitEvent(m->copy, m->ev_free[sl], 0));
+        HIPCHK(hipStreamWaitEvent(m->copy, m->ev_staged[sl], 0));
+        HIPCHK(hipMemcpyAsync(m->slot[sl], m->staging[sl], (size_t)m->layer_bytes, hipMemcpyHostToDevice, m->copy));
+        HIPCHK(hipEventRecord(m->ev_staging_free[sl], m->copy));
+        HIPCHK(hipEventRecord(m->ev_loaded[sl], m->copy));
+        return TOD_OK;
+    }
     HIPCHK(hipStreamWaitEvent(m->copy, m->ev_free[sl], 0));
     HIPCHK(hipMemcpyAsync(m->slot[sl], m->layers[image_layer(m, l)].host, (size_t)m->layer_bytes,
                           hipMemcpyHostToDevice, m->copy));
@@ -418,6 +484,8 @@ int check_ready(tod_model *m, int block)
         return fail(TOD_ESTATE, "block %d out of range [0, %d)", block, m->run.n_blocks);
     if (!m->glob_loaded)
         return fail(TOD_ESTATE, "global weights not set");
+    if (const int e = m->io_errno.load())
+        return fail(TOD_EHIP, "a weight file read failed: %s", strerror(e));
     for (int l = 0; l < m->cfg.n_layers; l++)
         if (!m->layers[l].loaded)
             return fail(TOD_ESTATE, "layer %d weights not set", l);
@@ -484,9 +552,17 @@ int free_model(tod_model *m)
             (void)hipEventDestroy(m->ev_kv_loaded[i]);
         if (m->ev_kv_free[i])
             (void)hipEventDestroy(m->ev_kv_free[i]);
+        if (m->ev_staged[i])
+            (void)hipEventDestroy(m->ev_staged[i]);
+        if (m->ev_staging_free[i])
+            (void)hipEventDestroy(m->ev_staging_free[i]);
     }
     if (m->copy)
         (void)hipStreamDestroy(m->copy);
+    if (m->io)
+        (void)hipStreamDestroy(m->io);
+    if (m->fd >= 0)
+        (void)close(m->fd);
     for (hipGraphExec_t e : m->gexec)
         if (e)
             (void)hipGraphExecDestroy(e);
@@ -564,6 +640,10 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     if (r.kv_host_layers < 0 || r.kv_host_layers > L)
         return fail(TOD_EINVAL, "kv_host_layers (%d) must be in [0, n_layers]", r.kv_host_layers);
     m->kv_host = r.kv_host_layers;
+    if (r.weights_on_disk && !host)
+        return fail(TOD_EINVAL, "weights_on_disk applies to the host tiers only");
+    m->on_disk = r.weights_on_disk != 0;
+    m->image_stride = (m->layer_bytes + 4095) / 4096 * 4096;
     const int n_streamed = host ? L - m->hbm_layers : 0;
     m->host_layers = r.host_layers > 0 && r.host_layers < n_streamed ? r.host_layers : n_streamed;
 
@@ -584,7 +664,7 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         ALLOC(S_.ln2_b, (size_t)h * 2);
         if (host && l < m->hbm_layers)
             ALLOC(S_.dev, (size_t)m->layer_bytes);
-        if (host && l >= m->hbm_layers && l < m->hbm_layers + m->host_layers) {
+        if (host && !m->on_disk && l >= m->hbm_layers && l < m->hbm_layers + m->host_layers) {
             void *p = nullptr;
             hipError_t e = hipHostMalloc(&p, (size_t)m->layer_bytes, hipHostMallocDefault);
             if (e != hipSuccess) {
@@ -685,6 +765,22 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
             HIPCHK(hipEventCreateWithFlags(&m->ev_kv_free[i], hipEventDisableTiming));
         }
     }
+    if (m->on_disk) { // two pinned staging images, the I/O stream and its events
+        for (int i = 0; i < 2; i++) {
+            void *p = nullptr;
+            hipError_t e = hipHostMalloc(&p, (size_t)m->image_stride, hipHostMallocDefault);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(TOD_ENOMEM, "hipHostMalloc(%lld bytes) for a staging image failed: %s",
+                            (long long)m->image_stride, hipGetErrorString(e));
+            }
+            m->host_allocs.push_back(p);
+            m->staging[i] = static_cast<uint8_t *>(p);
+            HIPCHK(hipEventCreateWithFlags(&m->ev_staged[i], hipEventDisableTiming));
+            HIPCHK(hipEventCreateWithFlags(&m->ev_staging_free[i], hipEventDisableTiming));
+        }
+        HIPCHK(hipStreamCreateWithFlags(&m->io, hipStreamNonBlocking));
+    }
     if (m->int4) { // quantization staging for the HBM and int4 host tiers
         const int64_t big = (int64_t)(f > 3 * h ? f : 3 * h) * h;
         ALLOC(m->stage, (size_t)big * 2);
@@ -739,12 +835,55 @@ int set_global_weights(tod_model *m, const uint16_t *tok, const uint16_t *pos, c
     return TOD_OK;
 }
 
+// Disk tier: synchronous whole-image transfers between staging buffer 0 and the file;
+// written images are synced and dropped from the page cache.
+static int image_io(tod_model *m, int layer, bool write)
+{
+    uint8_t *buf = m->staging[0];
+    const int64_t off = image_offset(m, layer);
+    int64_t done = 0;
+    while (done < m->image_stride) {
+        const ssize_t n = write ? pwrite(m->fd, buf + done, (size_t)(m->image_stride - done), off + done)
+                                : pread(m->fd, buf + done, (size_t)(m->image_stride - done), off + done);
+        if (n < 0 && errno == EINTR)
+            continue;
+        if (n <= 0)
+            return fail(TOD_EHIP, "weight file %s of layer %d failed: %s", write ? "write" : "read", layer,
+                        n < 0 ? strerror(errno) : "short transfer");
+        done += n;
+    }
+    if (write && fdatasync(m->fd) != 0)
+        return fail(TOD_EHIP, "weight file sync failed: %s", strerror(errno));
+    (void)posix_fadvise(m->fd, off, m->image_stride, POSIX_FADV_DONTNEED); // keep it out of RAM
+    return TOD_OK;
+}
+
+int set_weight_file(tod_model *m, const char *path)
+{
+    if (!m || !path)
+        return fail(TOD_EINVAL, "null argument");
+    if (!m->on_disk)
+        return fail(TOD_ESTATE, "the model was not created with weights_on_disk");
+    if (m->fd >= 0)
+        return fail(TOD_ESTATE, "the weight file is already set");
+    for (const LayerStore &L : m->layers)
+        if (L.loaded)
+            return fail(TOD_ESTATE, "set_weight_file must come before set_layer_weights");
+    const int fd = open(path, O_RDWR | O_CREAT | O_TRUNC, 0600);
+    if (fd < 0)
+        return fail(TOD_EINVAL, "cannot open %s: %s", path, strerror(errno));
+    m->fd = fd;
+    return TOD_OK;
+}
+
 int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
 {
     if (!m || !t)
         return fail(TOD_EINVAL, "null argument");
     if (layer < 0 || layer >= m->cfg.n_layers)
         return fail(TOD_EINVAL, "layer %d out of range", layer);
+    if (m->on_disk && m->fd < 0)
+        return fail(TOD_ESTATE, "set_weight_file must come before set_layer_weights");
     for (int i = 0; i < TOD_LAYER_TENSORS; i++)
         if (!t[i])
             return fail(TOD_EINVAL, "tensor %d of layer %d is null", i, layer);
@@ -774,14 +913,18 @@ int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
     if (m->streamed && !resident && image_layer(m, layer) != layer) {
         // this streamed layer reuses the pinned image of an earlier one
     } else if (!m->int4) {
+        uint8_t *image = m->on_disk ? m->staging[0] : L.host; // the disk tier stages, then writes
         for (const Part &p : parts) {
             const int64_t off = m->mat_off[p.mat] + ((int64_t)p.row0 * p.cols) * 2;
             const size_t bytes = (size_t)p.rows * p.cols * 2;
             if (resident)
                 HIPCHK(hipMemcpy(L.dev + off, t[p.tensor], bytes, hipMemcpyHostToDevice));
             else
-                memcpy(L.host + off, t[p.tensor], bytes);
+                memcpy(image + off, t[p.tensor], bytes);
         }
+        int rc;
+        if (m->on_disk && !resident && (rc = image_io(m, layer, true)))
+            return rc;
     } else {
         // quantize in HBM; on the int4 host tier a resident layer's image is
         // built in place, a streamed one's in slot 0 (idle outside a pass) and
@@ -801,8 +944,13 @@ int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
                                     const_cast<uint32_t *>(dst.wp) + nb0 * KG * 32, nullptr));
         }
         HIPCHK(hipDeviceSynchronize());
-        if (m->streamed && !resident)
-            HIPCHK(hipMemcpy(L.host, m->slot[0], (size_t)m->layer_bytes, hipMemcpyDeviceToHost));
+        if (m->streamed && !resident) {
+            HIPCHK(hipMemcpy(m->on_disk ? m->staging[0] : L.host, m->slot[0], (size_t)m->layer_bytes,
+                             hipMemcpyDeviceToHost));
+            int rc;
+            if (m->on_disk && (rc = image_io(m, layer, true)))
+                return rc;
+        }
     }
     L.loaded = true;
     return TOD_OK;
@@ -1018,7 +1166,11 @@ int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t
             return fail(TOD_ESTATE, "layer %d (whose image layer %d streams) weights not set", src, layer);
         HIPCHK(hipDeviceSynchronize());
         m->prefetched = false; // slot 0 is overwritten here
-        HIPCHK(hipMemcpy(m->slot[0], m->layers[src].host, (size_t)m->layer_bytes, hipMemcpyHostToDevice));
+        int rc;
+        if (m->on_disk && (rc = image_io(m, layer, false)))
+            return rc;
+        HIPCHK(hipMemcpy(m->slot[0], m->on_disk ? m->staging[0] : m->layers[src].host, (size_t)m->layer_bytes,
+                         hipMemcpyHostToDevice));
         slot = m->slot[0];
     }
     const int h = m->cfg.hidden, f = m->cfg.ffn;
