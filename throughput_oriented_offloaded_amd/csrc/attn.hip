@@ -11,8 +11,8 @@
 // positions with its own online softmax (details at k_attn_decode); nothing
 // is shared between wavefronts, so there are no workgroup barriers. K and V
 // codes share the canonical per-position layout.
-// Prefill (causal, all prompt positions) uses a tiled variant: 64 queries per
-// workgroup, K/V tiles of 64 positions dequantized into LDS, online softmax.
+// Prefill (causal, all prompt positions) uses a tiled MFMA variant: 64 queries
+// per workgroup, K/V tiles of 64 positions dequantized into LDS, online softmax.
 #include "common.hpp"
 
 namespace {
@@ -237,7 +237,21 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: 64 queries x (sequence, head) per workgroup, causal.
+// Prefill: 64 queries of one (sequence, head) per workgroup, causal, on MFMA.
+//
+// Four wavefronts take 16 queries each. Per tile of 64 keys, K is dequantized
+// into LDS row-major and V transposed (fp16 values, each rounded once, as the
+// cache defines them). Scores are computed transposed, S^T = K . Q^T, with
+// v_mfma_f32_16x16x32_f16: lane l ends up with keys 4*(l/16)+i (i < 4) of
+// each 16-key block for query l % 16. Those registers are directly the B
+// operand of O^T += V^T . P^T once the reduction index (keys) is permuted the
+// same way on both operands: within a 32-key step lane group g holds keys
+// 4g..4g+3 of the first 16-key block and 4g..4g+3 of the second, and reads
+// the matching V^T columns. Softmax is online per query (max and sum across
+// the four lanes of a query by lane shuffles); P, scaled by 2^12 so that both
+// parts stay normal fp16 numbers, is split into an fp16 high part and an fp16
+// remainder, each through its own MFMA, so the weights keep fp32-level
+// precision; the scale comes off exactly at the end. Accumulation is fp32.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict__ q, int64_t q_stride,
@@ -245,120 +259,134 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
                                                       int len, KvView kv)
 {
     constexpr int CB = D / 2, G = D / 64;
-    constexpr int DP = D + 2; // padded LDS row (halves)
-    constexpr int DPV = 32;   // dims per thread in the PV product
-    __shared__ half_t sq[64 * DP];
-    __shared__ half_t sk[64 * DP];
-    __shared__ half_t sv[64 * DP];
-    __shared__ float sp[64 * 65];
+    constexpr int KS = D / 32;      // 32-dim MFMA steps of the score product
+    constexpr int DB = D / 16;      // 16-dim output blocks
+    constexpr int KP = D + 8;       // K row pitch (halves)
+    constexpr int VP = 64 + 8;      // V^T row pitch (halves)
+    __shared__ __attribute__((aligned(16))) half_t sk[64 * KP];
+    __shared__ __attribute__((aligned(16))) half_t svt[D * VP];
 
     const int qtiles = (len + 63) / 64;
     const int qt = blockIdx.x % qtiles;
     const int sh = blockIdx.x / qtiles;
     const int head = sh % kv.heads, s = sh / kv.heads;
-    const int seq = seq0 + s;
-    const int tid = threadIdx.x;
-    const int q0 = qt * 64;
-    const size_t slab = kv_slab(kv, seq, head);
+    const size_t slab = kv_slab(kv, seq0 + s, head);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, g = lane >> 4;
+    const int qpos = qt * 64 + wave * 16 + col; // this lane's query
+    const bool qlive = qpos < len;
 
-    // load Q tile (rows beyond len are zero)
-    for (int i = tid; i < 64 * D; i += 256) {
-        const int r = i / D, dd = i % D;
-        const int pos = q0 + r;
-        sq[r * DP + dd] = pos < len ? __builtin_bit_cast(half_t, q[((int64_t)s * len + pos) * q_stride +
-                                                                   (int64_t)head * D + dd])
-                                    : (half_t)0.0f;
-    }
-    const int myq = tid >> 2, sub = tid & 3; // 4 threads per query
-    const int qpos = q0 + myq;
-    float m_run = -INFINITY, l_run = 0.0f;
-    float o[DPV * D / 128];
-    constexpr int NO = DPV * D / 128; // D=128: 32 dims per thread; D=64: 16
+    // Q^T fragments (B operand): dims 32k + 8g .. +8 of query qpos (zeros past len)
+    half8_t qf[KS];
+    {
+        const uint16_t *qp = q + ((int64_t)s * len + (qlive ? qpos : 0)) * q_stride + (int64_t)head * D;
 #pragma unroll
-    for (int e = 0; e < NO; e++)
-        o[e] = 0.0f;
-    const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    const int last_key = min(len, q0 + 64); // keys [0, last_key)
+        for (int k = 0; k < KS; k++) {
+            const uint4_t w = qlive ? *reinterpret_cast<const uint4_t *>(qp + 32 * k + 8 * g) : (uint4_t){0, 0, 0, 0};
+            qf[k] = __builtin_bit_cast(half8_t, w);
+        }
+    }
+    const float scale = 1.0f / sqrtf((float)D);
+    float4_t acc[DB];
+#pragma unroll
+    for (int e = 0; e < DB; e++)
+        acc[e] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, l_part = 0.0f; // l_part: this lane's share of the query's sum
+
+    const int last_key = min(len, qt * 64 + 64);
     for (int k0 = 0; k0 < last_key; k0 += 64) {
         __syncthreads();
-        // dequantize K and V tiles (positions k0..k0+63) into LDS
-        for (int i = tid; i < 64 * CB; i += 256) {
-            const int r = i / CB, byte = i % CB, pos = k0 + r;
-            half_t k_lo = (half_t)0.0f, k_hi = (half_t)0.0f, v_lo = (half_t)0.0f, v_hi = (half_t)0.0f;
+        // dequantize keys k0..k0+63: each thread takes one 32-bit code word (8 dims) of K and of V
+        for (int i = tid; i < 64 * (CB / 4); i += 256) {
+            const int r = i / (CB / 4), wd = i % (CB / 4), pos = k0 + r;
+            half8_t kh = {}, vh = {};
             if (pos < len) {
-                const int gi = byte / 32;
-                const uint8_t kb = kv.kc[(slab * kv.cap + pos) * CB + byte];
-                const uint8_t vb = kv.vc[(slab * kv.cap + pos) * CB + byte];
-                const uint32_t kp = kv.kp[(slab * kv.cap + pos) * G + gi];
-                const uint32_t vp = kv.vp[(slab * kv.cap + pos) * G + gi];
-                const half_t ks = __builtin_bit_cast(half_t, (uint16_t)(kp & 0xffff));
-                const half_t kz = __builtin_bit_cast(half_t, (uint16_t)(kp >> 16));
-                const half_t vs = __builtin_bit_cast(half_t, (uint16_t)(vp & 0xffff));
-                const half_t vz = __builtin_bit_cast(half_t, (uint16_t)(vp >> 16));
-                k_lo = __builtin_fmaf16((half_t)(float)(kb & 15), ks, kz);
-                k_hi = __builtin_fmaf16((half_t)(float)(kb >> 4), ks, kz);
-                v_lo = __builtin_fmaf16((half_t)(float)(vb & 15), vs, vz);
-                v_hi = __builtin_fmaf16((half_t)(float)(vb >> 4), vs, vz);
+                const size_t at = slab * kv.cap + pos;
+                const uint32_t kw = *reinterpret_cast<const uint32_t *>(kv.kc + at * CB + 4 * wd);
+                const uint32_t vw = *reinterpret_cast<const uint32_t *>(kv.vc + at * CB + 4 * wd);
+                const uint32_t kpw = kv.kp[at * G + wd / 8], vpw = kv.vp[at * G + wd / 8];
+                const half_t ks = __builtin_bit_cast(half_t, (uint16_t)(kpw & 0xffff));
+                const half_t kz = __builtin_bit_cast(half_t, (uint16_t)(kpw >> 16));
+                const half_t vs = __builtin_bit_cast(half_t, (uint16_t)(vpw & 0xffff));
+                const half_t vz = __builtin_bit_cast(half_t, (uint16_t)(vpw >> 16));
+#pragma unroll
+                for (int e = 0; e < 8; e++) { // canonical: nibble e of the word is dim 8 * wd + e
+                    kh[e] = __builtin_fmaf16((half_t)(float)((kw >> (4 * e)) & 15u), ks, kz);
+                    vh[e] = __builtin_fmaf16((half_t)(float)((vw >> (4 * e)) & 15u), vs, vz);
+                }
             }
-            sk[r * DP + 2 * byte] = k_lo;
-            sk[r * DP + 2 * byte + 1] = k_hi;
-            sv[r * DP + 2 * byte] = v_lo;
-            sv[r * DP + 2 * byte + 1] = v_hi;
+            *reinterpret_cast<half8_t *>(&sk[r * KP + 8 * wd]) = kh;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+                svt[(8 * wd + e) * VP + r] = vh[e];
         }
         __syncthreads();
-        // scores for keys k0 + sub + 4*i
-        float sc[16];
+
+        // S^T for the four 16-key blocks: lane holds keys k0 + 16b + 4g + i for query qpos
+        float sc[4][4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const int kr = sub + 4 * i;
-            const int kpos = k0 + kr;
-            float acc = 0.0f;
-            for (int dd = 0; dd < D; dd += 2) {
-                const half2_t a = *reinterpret_cast<const half2_t *>(&sq[myq * DP + dd]);
-                const half2_t b = *reinterpret_cast<const half2_t *>(&sk[kr * DP + dd]);
-                acc = __builtin_amdgcn_fdot2(a, b, acc, false);
+        for (int b = 0; b < 4; b++) {
+            float4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < KS; k++) {
+                const half8_t kf = *reinterpret_cast<const half8_t *>(&sk[(16 * b + col) * KP + 32 * k + 8 * g]);
+                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[k], c, 0, 0, 0);
             }
-            acc *= inv_sqrt_d;
-            sc[i] = (kpos <= qpos && kpos < len) ? acc : -INFINITY;
-            tmax = fmaxf(tmax, sc[i]);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int kpos = k0 + 16 * b + 4 * g + i;
+                sc[b][i] = (kpos <= qpos && kpos < len) ? c[i] * scale : -INFINITY;
+                tmax = fmaxf(tmax, sc[b][i]);
+            }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m_run, tmax);
         const float corr = m_new == -INFINITY ? 1.0f : __expf(m_run - m_new);
-        float psum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-            const float p = sc[i] == -INFINITY ? 0.0f : __expf(sc[i] - m_new);
-            sp[myq * 65 + sub + 4 * i] = p;
-            psum += p;
-        }
-        psum += __shfl_xor(psum, 1, 64);
-        psum += __shfl_xor(psum, 2, 64);
-        l_run = l_run * corr + psum;
         m_run = m_new;
+        l_part *= corr;
 #pragma unroll
-        for (int e = 0; e < NO; e++)
-            o[e] *= corr;
-        __syncthreads();
-        // o[q][d] += sum_k p[q][k] v[k][d], dims sub*NO .. +NO
-        for (int kr = 0; kr < 64; kr++) {
-            const float p = sp[myq * 65 + kr];
+        for (int e = 0; e < DB; e++)
+            acc[e] *= corr;
+
+        // P^T operands per 32-key step t: blocks 2t and 2t+1, split into fp16 high and low parts
 #pragma unroll
-            for (int e = 0; e < NO; e += 2) {
-                const half2_t v2 = *reinterpret_cast<const half2_t *>(&sv[kr * DP + sub * NO + e]);
-                o[e] += p * (float)v2[0];
-                o[e + 1] += p * (float)v2[1];
+        for (int t = 0; t < 2; t++) {
+            half8_t ph, pl;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const float sv = sc[2 * t + j / 4][j % 4];
+                const float p = sv == -INFINITY ? 0.0f : __expf(sv - m_new);
+                l_part += p;
+                const float ps = p * 4096.0f; // exact
+                const half_t hi = (half_t)ps;
+                ph[j] = hi;
+                pl[j] = (half_t)(ps - (float)hi);
+            }
+#pragma unroll
+            for (int e = 0; e < DB; e++) {
+                const half_t *vr = &svt[(16 * e + col) * VP + 32 * t + 4 * g];
+                const uint2 v0 = *reinterpret_cast<const uint2 *>(vr);
+                const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16);
+                const half8_t vf = __builtin_bit_cast(half8_t, (uint4_t){v0.x, v0.y, v1.x, v1.y});
+                acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, acc[e], 0, 0, 0);
+                acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[e], 0, 0, 0);
             }
         }
     }
-    if (qpos < len) {
-        const float inv = 1.0f / l_run;
-        uint16_t *op = out + ((int64_t)s * len + qpos) * out_stride + (int64_t)head * D + sub * NO;
+    float l_sum = l_part + __shfl_xor(l_part, 16, 64);
+    l_sum += __shfl_xor(l_sum, 32, 64);
+    if (qlive) {
+        const float inv = 1.0f / l_sum * (1.0f / 4096.0f); // the P scale, exactly
+        uint16_t *op = out + ((int64_t)s * len + qpos) * out_stride + (int64_t)head * D;
 #pragma unroll
-        for (int e = 0; e < NO; e++)
-            op[e] = f2h(o[e] * inv);
+        for (int e = 0; e < DB; e++) { // O^T rows 16e + 4g + i of this query
+            uint2 w;
+            w.x = (uint32_t)f2h(acc[e][0] * inv) | ((uint32_t)f2h(acc[e][1] * inv) << 16);
+            w.y = (uint32_t)f2h(acc[e][2] * inv) | ((uint32_t)f2h(acc[e][3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(op + 16 * e + 4 * g) = w;
+        }
     }
 }
 
