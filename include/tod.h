@@ -43,6 +43,8 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+/* the library is built with hidden visibility: these declarations are its only exports */
+#pragma GCC visibility push(default)
 
 #define TOD_OK 0
 #define TOD_EINVAL (-1) /* bad argument: null pointer, shape or size mismatch, group != 64 */
@@ -373,6 +375,7 @@ int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, cons
 int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int max_rows, const tod_hw *hw,
                 tod_run_config *best, tod_estimate *est);
 
+#pragma GCC visibility pop
 #ifdef __cplusplus
 }
 #endif

@@ -60,3 +60,14 @@ def test_binding_structs_match_header(cname, pyname):
     py = getattr(_lib, pyname)
     ctypes_of = {"int32_t": ctypes.c_int32, "double": ctypes.c_double}
     assert [(f, t) for f, t in py._fields_] == [(f, ctypes_of[c]) for f, c in _struct_fields(cname)]
+
+
+def test_library_exports_only_the_declared_functions():
+    """Built with hidden visibility: the exported functions are exactly the header's."""
+    import shutil
+    import subprocess
+    if not shutil.which("nm"):
+        pytest.skip("nm is not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[2] for line in out.splitlines() if len(line.split()) == 3 and line.split()[1] == "T"}
+    assert exported == set(_declared())

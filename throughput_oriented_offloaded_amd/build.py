@@ -14,7 +14,7 @@ SOURCES = ("quant.hip", "gemm.hip", "attn.hip", "misc.hip", "runtime.hip", "poli
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden",
     # packed fp32 math stays off; fp32 division and sqrt are correctly rounded
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
