@@ -128,7 +128,8 @@ def cost_model_check(tod, shape, run, measured_ms):
     """The library's cost model (estimate_decode, default measured rates) for this run beside the
     measured step time."""
     est = tod.estimate_decode(shape, run)
-    return {"predicted_ms_per_step": est["step_s"] * 1e3, "measured_over_predicted": measured_ms / (est["step_s"] * 1e3),
+    return {"predicted_ms_per_step": est["step_s"] * 1e3,
+            "measured_over_predicted": measured_ms / (est["step_s"] * 1e3),
             "predicted_hbm_gb": est["hbm_bytes"] / 1e9, "predicted_host_gb": est["host_bytes"] / 1e9}
 
 
@@ -236,7 +237,8 @@ def host_tier_bench(args, w, tod, synth, torch):
                    + (" in a file on disk, read into 2 pinned staging buffers" if on_disk else
                       " in pinned host memory") + ", 2 HBM layer slots, copies on a side stream"},
         "roofline": ({"bound": "link", "achieved": link_gbs, "peak": h2d, "unit": "GB/s", "frac": link_gbs / h2d,
-                      "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"} if not on_disk else
+                      "traffic": None, "kernel": "hipMemcpyAsync pinned -> HBM (one layer per copy)"}
+                     if not on_disk else
                      {"bound": "disk", "achieved": link_gbs, "peak": min(disk, h2d), "unit": "GB/s",
                       "frac": link_gbs / min(disk, h2d), "traffic": None,
                       "kernel": "pread -> pinned staging -> hipMemcpyAsync -> HBM, one layer per read"}),
@@ -383,7 +385,8 @@ def copy_probe(mib):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed decode steps (default 31; fp16 host tier 2, int4 host tier 6)")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed decode steps (default 31; fp16 host tier 2, int4 host tier 6)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed decode steps first (default 2; host tiers 1)")
     ap.add_argument("--workload", default="opt-30b",
                     help="opt-125m | opt-6.7b | opt-30b (default) | opt-175b (fp16 host tier) | "

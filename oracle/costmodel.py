@@ -240,7 +240,8 @@ def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
                             continue
                         run["kv_host_layers"] = max(1, need)
                         device, pinned = footprint(shape, run)
-                    if device > hw["hbm_bytes"] or pinned > hw["host_bytes"] or disk_bytes(shape, run) > hw["disk_bytes"]:
+                    if (device > hw["hbm_bytes"] or pinned > hw["host_bytes"]
+                            or disk_bytes(shape, run) > hw["disk_bytes"]):
                         continue
                     est = decode_step(shape, run, hw)
                     if best is None or est["tokens_per_s"] > best[1]["tokens_per_s"]:

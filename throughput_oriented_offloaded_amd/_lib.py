@@ -59,7 +59,8 @@ class HW(ctypes.Structure):
 
 class Estimate(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in ("step_s", "tokens_per_s", "compute_s", "link_s", "hbm_bytes",
-                                                 "host_bytes", "workspace_bytes", "disk_bytes")] + [("fits", ctypes.c_int32)]
+                                                 "host_bytes", "workspace_bytes", "disk_bytes")]
+    _fields_ += [("fits", ctypes.c_int32)]
 
 
 @functools.lru_cache(maxsize=None)

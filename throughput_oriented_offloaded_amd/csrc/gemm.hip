@@ -259,7 +259,7 @@ template <int BM_> struct W4 {
     static constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
     static constexpr int S = 3;                         // ring stages
     static constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
-    static constexpr int LPS = AL + 2;                  // loads per wave per stage: A chunks, one code block, one param block
+    static constexpr int LPS = AL + 2;                  // loads per wave per stage: A chunks, codes, params
     static_assert(BM % 64 == 0 && (BM / 8) % WAVES == 0, "A chunks split evenly over the waves");
 };
 
@@ -550,7 +550,8 @@ __global__ void __launch_bounds__(256) k_splitk_reduce_ln(GemmArgs g, int splits
         if (g.bias && g.epi != EPI_NONE)
             bias = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g.bias + 8 * c));
         if (g.epi == EPI_BIAS_RES)
-            res = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g.residual + (int64_t)row * g.ldc + 8 * c));
+            res = __builtin_bit_cast(half8_t,
+                                     *reinterpret_cast<const uint4_t *>(g.residual + (int64_t)row * g.ldc + 8 * c));
         half8_t o;
 #pragma unroll
         for (int e = 0; e < 8; e++) {

@@ -148,8 +148,8 @@ hipError_t launch_embed(const int32_t *ids, int rows, int rows_per_seq, int pos0
     const int64_t n = (int64_t)rows * h;
     if (n == 0)
         return hipSuccess;
-    hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, rows, rows_per_seq, pos0, dpos,
-                       tok, vocab, posemb, h, out);
+    hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, rows, rows_per_seq, pos0,
+                       dpos, tok, vocab, posemb, h, out);
     return hipGetLastError();
 }
 

@@ -127,7 +127,10 @@ double kv_layer_bytes(const tod_model_config *c, const tod_run_config *r)
     return slabs * cap * (c->head_dim + c->head_dim / 8.0);
 }
 
-double kernel_time(double work_s, const tod_hw *hw) { return work_s > hw->launch_us * 1e-6 ? work_s : hw->launch_us * 1e-6; }
+double kernel_time(double work_s, const tod_hw *hw)
+{
+    return work_s > hw->launch_us * 1e-6 ? work_s : hw->launch_us * 1e-6;
+}
 
 void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw *hw, tod_estimate *e)
 {

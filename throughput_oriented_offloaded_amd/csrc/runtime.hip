@@ -372,7 +372,10 @@ void read_image(void *arg)
 
 // Byte offset of layer l's image in the weight file (images of the streamed layers that
 // own one, packed from the first streamed layer on).
-int64_t image_offset(const tod_model *m, int l) { return (int64_t)(image_layer(m, l) - m->hbm_layers) * m->image_stride; }
+int64_t image_offset(const tod_model *m, int l)
+{
+    return (int64_t)(image_layer(m, l) - m->hbm_layers) * m->image_stride;
+}
 
 int stream_layer(tod_model *m, int l)
 {
@@ -1007,12 +1010,13 @@ static int decode_step(tod_model *m, int block, const int32_t *in, int pos, cons
     // comes out of the GEMM before it (the last one is the head's LN_f)
     // host-KV layers load the pos positions cached before this step (the graph path,
     // whose position lives on the device, is not taken when there are any)
-    int rc = stack_pass(m, st, block, pos, [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
+    auto layer = [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
         const bool last = l + 1 == L;
         const uint16_t *ng = last ? m->lnf_g : m->layers[l + 1].ln1_g;
         const uint16_t *nb = last ? m->lnf_b : m->layers[l + 1].ln1_b;
         return layer_pass(m, l, kv, m->hid, Mr, false, 0, 1, pos, dpos, wslot, st, l > 0, ng, nb, mirror);
-    });
+    };
+    int rc = stack_pass(m, st, block, pos, layer);
     if (rc)
         return rc;
     if ((rc = head_pass(m, m->hid, Mr, logits, out, st, true)))
