@@ -124,8 +124,8 @@ typedef struct {
  * stream, from which the copy stream moves it into the HBM slot; reads of one
  * layer overlap the copy of the previous one. Direct I/O cannot target pinned
  * memory, so the reads are buffered, and each image is dropped from the page
- * cache after it is written and after every read: each pass reads the disk. Results are identical to the pinned
- * tiers. A failed read makes the next prefill / decode_block return TOD_EHIP
+ * cache after it is written and after every read: each pass reads the disk.
+ * Results are identical to the pinned tiers. A failed read makes the next prefill / decode_block return TOD_EHIP
  * (the outputs of the pass it happened in are undefined). The library keeps
  * the file open until free_model and never deletes it.
  * Errors: TOD_EINVAL (null argument, cannot open), TOD_ESTATE (not a disk-tier
@@ -138,8 +138,10 @@ int set_weight_file(tod_model *m, const char *path);
  * Weights are supplied afterwards with set_global_weights / set_layer_weights.
  * FlexGen guide, "2. The Zig-Zag Block Schedule" (a block of K micro-batches
  * shares each weight load) and "1. Three-Tier Storage Hierarchy" (weight tier).
- * Errors: TOD_EINVAL on an invalid shape, TOD_ENOMEM if HBM or pinned host
- * memory runs out, TOD_EHIP otherwise. *out is NULL on error.
+ * Errors: TOD_EINVAL on an invalid shape (also when gpu_batch *
+ * batches_per_block or gpu_batch * prompt_len exceeds 2^24 rows), TOD_ENOMEM
+ * if HBM or pinned host memory runs out, TOD_EHIP otherwise. *out is NULL on
+ * error.
  */
 int init_model(const tod_model_config *cfg, const tod_run_config *run, void *stream, tod_model **out);
 

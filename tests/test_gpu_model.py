@@ -529,6 +529,22 @@ def test_state_errors():
     m.close()
 
 
+@pytest.mark.parametrize("bad", [dict(group=32), dict(gpu_batch=0), dict(weight_tier=7), dict(gen_len=4000),
+                                 dict(hbm_layers=1), dict(kv_host_layers=2), dict(weights_on_disk=1),
+                                 dict(gpu_batch=1 << 13, batches_per_block=1 << 12),
+                                 dict(gpu_batch=1 << 14, prompt_len=2044)])
+def test_invalid_run_config_is_rejected(bad):
+    """init_model rejects each invalid run field with TOD_EINVAL before allocating anything."""
+    torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_125M.replace(n_layers=1)
+    run = dict(gpu_batch=2, batches_per_block=1, prompt_len=4, gen_len=3)
+    run.update(bad)
+    with pytest.raises(tod.TodError) as e:
+        tod.Model(shape, run)
+    assert e.value.code == -1, tod.last_error()
+
+
 @pytest.mark.parametrize("tier,resident", [(0, 0), (1, 1), (2, 2)])
 def test_footprint_matches_device_allocation(tier, resident):
     """The cost model's device footprint of a run configuration (estimate_decode) against the device

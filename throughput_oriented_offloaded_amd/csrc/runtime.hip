@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -339,8 +340,6 @@ int image_layer(const tod_model *m, int l)
     return l < R + m->host_layers ? l : R + (l - R) % m->host_layers;
 }
 
-// Host tiers: enqueue the copy of streamed layer l into its slot (streamed
-// layers alternate between the two) on the copy stream.
 // Disk tier: one read of a layer image into a staging buffer, run on the I/O
 // stream by the HIP runtime's callback thread.
 struct ImageRead {
@@ -377,13 +376,18 @@ int64_t image_offset(const tod_model *m, int l)
     return (int64_t)(image_layer(m, l) - m->hbm_layers) * m->image_stride;
 }
 
+// Host tiers: enqueue the copy of streamed layer l into its slot (streamed
+// layers alternate between the two) on the copy stream; on the disk tier the
+// image is first read into the slot's staging buffer on the I/O stream.
 int stream_layer(tod_model *m, int l)
 {
     const int sl = (l - m->hbm_layers) & 1;
     if (m->on_disk) {
         // stage on the I/O stream once the previous copy out of this staging buffer is done
         HIPCHK(hipStreamWaitEvent(m->io, m->ev_staging_free[sl], 0));
-        ImageRead *job = new ImageRead{m, sl, image_offset(m, l)};
+        ImageRead *job = new (std::nothrow) ImageRead{m, sl, image_offset(m, l)};
+        if (!job)
+            return fail(TOD_ENOMEM, "no memory for an image read");
         const hipError_t e = hipLaunchHostFunc(m->io, read_image, job);
         if (e != hipSuccess) {
             delete job;
@@ -605,8 +609,10 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM &&
         r.weight_tier != TOD_W_HOST_INT4_STREAM)
         return fail(TOD_EINVAL, "unknown weight tier %d", r.weight_tier);
-    if (r.prompt_len + r.gen_len - 1 > c.max_pos)
+    if ((int64_t)r.prompt_len + r.gen_len - 1 > c.max_pos)
         return fail(TOD_EINVAL, "prompt_len + gen_len - 1 exceeds max_pos");
+    if ((int64_t)r.gpu_batch * r.batches_per_block > (1 << 24) || (int64_t)r.gpu_batch * r.prompt_len > (1 << 24))
+        return fail(TOD_EINVAL, "gpu_batch * batches_per_block and gpu_batch * prompt_len must be at most 2^24");
     m->cfg = c;
     m->run = r;
     m->M = r.gpu_batch * r.batches_per_block;
@@ -813,7 +819,9 @@ int init_model(const tod_model_config *cfg, const tod_run_config *run, void *str
     *out = nullptr;
     if (!cfg || !run)
         return fail(TOD_EINVAL, "null config");
-    tod_model *m = new tod_model();
+    tod_model *m = new (std::nothrow) tod_model();
+    if (!m)
+        return fail(TOD_ENOMEM, "no memory for the model");
     const int rc = init_model_impl(cfg, run, m);
     if (rc) {
         const std::string msg = g_err;
@@ -1344,7 +1352,9 @@ int attn_cache_create(int batch, int heads, int head_dim, int cap, tod_attn_cach
     *out = nullptr;
     if (batch <= 0 || heads <= 0 || cap <= 0 || (head_dim != 64 && head_dim != 128))
         return fail(TOD_EINVAL, "bad attention cache shape");
-    tod_attn_cache *c = new tod_attn_cache();
+    tod_attn_cache *c = new (std::nothrow) tod_attn_cache();
+    if (!c)
+        return fail(TOD_ENOMEM, "no memory for the attention cache");
     const int capp = (cap + 63) / 64 * 64;
     size_t kc_b, kp_b;
     kv_bytes((size_t)batch * heads, head_dim, capp, &kc_b, &kp_b);
