@@ -547,7 +547,7 @@ def main():
                 "unit": "TFLOP/s", "frac": d["frac"], "traffic": None, "kernel": f"k_gemm ({dom})"}
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC.replace("OPT-30B", "OPT-" + w.name[4:].replace("b", "B")),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -325,14 +325,24 @@ int attn_cache_free(tod_attn_cache *c);
  *
  * tod_hw: attn_gbs = decode-attention read rate, mem_gbs = streaming rate of
  * the other row-wise kernels and weight reads, link_gbs = pinned -> HBM copy
- * rate (GB/s); int4_tflops / fp16_tflops = GEMM rates by weight type; launch_us
- * = floor per kernel; hbm_bytes / host_bytes = capacities the model may use;
- * disk_gbs / disk_bytes = read rate and free space of the weight file's disk.
- * default_hw fills the figures measured on MI355X for this library.
+ * rate (GB/s); int4_tflops = steady rate of the pipelined int4 GEMM (more than
+ * 128 rows) while every CU holds one of its workgroups, and gemm_wg_us = the
+ * fixed time each wave of its workgroups adds (pipeline fill, epilogue);
+ * fp16_tflops = rate of the register-staged GEMM (fp16 weights, and int4 at
+ * 128 rows or fewer); launch_us = floor per kernel; hbm_bytes / host_bytes =
+ * capacities the model may use; disk_gbs / disk_bytes = read rate and free
+ * space of the weight file's disk. default_hw fills the figures measured on
+ * MI355X for this library.
  *
  * estimate_decode prices one decode step of the block `run` describes at the
- * average decode context (prompt_len + gen_len / 2): per layer, each GEMM takes
- * the larger of flops / rate and weight bytes / mem_gbs (at least launch_us),
+ * average decode context (prompt_len + gen_len / 2): per layer, each GEMM runs
+ * the library's own tile plan: a pipelined int4 GEMM takes ceil(workgroups /
+ * 256) waves of (K-groups per workgroup * tile rows / 256 * t_g + gemm_wg_us),
+ * where t_g = 256 * 2 * 256 * 256 * 64 / int4_tflops is one K-group of a full
+ * 256 x 256 tile on every CU, plus, when its K loop is split, its fp32
+ * partials written and read back at mem_gbs; a register-staged GEMM takes
+ * the larger of flops / fp16_tflops and weight bytes / mem_gbs (each GEMM at
+ * least launch_us),
  * attention M * heads * (ctx * (d + d/8) + 4d) bytes / attn_gbs, the KV append
  * M * heads * (4d + d + d/8) bytes / mem_gbs; plus embedding, one LayerNorm, the
  * fp16 LM head and the argmax. On the host tiers the L - hbm_layers streamed
@@ -350,7 +360,8 @@ int attn_cache_free(tod_attn_cache *c);
  * gets the device and pinned-host bytes init_model would allocate (the device
  * figure includes workspace_bytes, the GEMMs' split-K partials), and fits =
  * both within the capacities. Errors: TOD_EINVAL on a null pointer, a run
- * configuration init_model would reject, or a non-positive rate.
+ * configuration init_model would reject, a non-positive rate or a negative
+ * gemm_wg_us.
  *
  * plan_decode searches weight tier (0, 1, 2), GPU batch b and batches per
  * block K (powers of two, b * K <= max_rows) and, on the host tiers,
@@ -361,12 +372,13 @@ int attn_cache_free(tod_attn_cache *c);
  * is kept). A candidate whose device footprint exceeds the capacity gets the
  * fewest host-KV layers (run.kv_host_layers) that make it fit, if any. Host
  * tiers are tried with pinned images first and then with images on disk
- * (run.weights_on_disk), within disk_bytes. *best is a complete run configuration (group 64, one
- * block, host_layers 0) and *est its estimate. TOD_ENOMEM if nothing fits.
+ * (run.weights_on_disk), within disk_bytes. *best is a complete run
+ * configuration (group 64, one block, host_layers 0) and *est its estimate.
+ * TOD_ENOMEM if nothing fits.
  */
 typedef struct {
     double attn_gbs, mem_gbs, link_gbs, int4_tflops, fp16_tflops, launch_us, hbm_bytes, host_bytes, disk_gbs,
-        disk_bytes;
+        disk_bytes, gemm_wg_us;
 } tod_hw;
 typedef struct {
     double step_s, tokens_per_s, compute_s, link_s, hbm_bytes, host_bytes, workspace_bytes, disk_bytes;

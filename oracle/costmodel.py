@@ -27,8 +27,12 @@ placement choices that the FlexLLMGen overview ("A 175B-parameter model on
 one GPU, if you can wait": caveats) leaves to manual flags. It is written
 from that definition, term by term, for the parity tests of the library's
 own cost model. With free compute and an all-streamed fp16 model it reduces
-to the simulator's formula (pinned against the printed figures). The device
-footprint here leaves out the library's split-K workspace, a GEMM-plan
+to the simulator's formula (pinned against the printed figures). Each GEMM
+is priced on the tile plan the library's GEMM takes for its shape
+(``gemm_plan``, the planner's rule restated): how many workgroups it
+launches, how many K-groups each runs, and whether split-K partials go
+through memory. A flat GEMM rate misses small-batch GEMMs by up to 2x, since
+their K loops split 4 to 16 ways. The device footprint here leaves out the library's split-K workspace, a GEMM-plan
 detail of a few tens of MB; the parity tests keep capacities far from every
 candidate's footprint so that the omission cannot change a fit decision.
 """
@@ -89,20 +93,67 @@ def _kernel(seconds: float, hw: dict) -> float:
     return max(seconds, hw["launch_us"] * 1e-6)
 
 
+CUS = 256  # MI355X compute units: one workgroup of the pipelined int4 GEMM each
+
+
+def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
+    """The tile plan of the library's pipelined int4 GEMM, restated from its rule (None when the
+    register-staged kernel runs: fp16 weights, or 128 rows or fewer).
+
+    Tiles are 256 outputs wide and 256 or 192 rows tall. The K loop (K-groups of 64) is split in
+    powers of two while the tiles times the splits stay below 160 workgroups and each split keeps
+    at least 8 K-groups. Of the two tile heights the one with the fewer waves of 256 workgroups x
+    tile rows x K-groups per workgroup is taken, 256 on a tie."""
+    if not (int4 and rows > 128):
+        return None
+    groups = n_in // 64
+    best = None
+    for tile_rows in (256, 192):
+        tiles = -(-rows // tile_rows) * -(-n_out // 256)
+        splits = 1
+        while tiles * splits < 160 and groups // (splits * 2) >= 8:
+            splits *= 2
+        per_split = -(-groups // splits)
+        splits = -(-groups // per_split)
+        workgroups = tiles * splits
+        cost = -(-workgroups // CUS) * tile_rows * per_split
+        if best is None or cost < best["cost"]:
+            best = dict(cost=cost, tile_rows=tile_rows, splits=splits, groups_per_split=per_split,
+                        workgroups=workgroups)
+    return best
+
+
+def gemm_time(rows: int, n_out: int, n_in: int, int4: bool, hw: dict) -> float:
+    """Seconds for one GEMM. The pipelined kernel runs its workgroups in waves of one per CU: a wave
+    costs its K-groups per workgroup times one K-group of a 256 x 256 tile at the steady int4 rate
+    (scaled by the tile's rows), plus the fixed cost per wave; a split K loop adds its fp32 partials,
+    written and read back at the streaming rate. The register-staged kernel costs the larger of
+    its flops at the fp16 GEMM rate and its weight bytes at the streaming rate."""
+    mem = hw["mem_gbs"] * 1e9
+    plan = gemm_plan(rows, n_out, n_in, int4)
+    if plan is not None:
+        group = CUS * 2.0 * 256 * 256 * 64 / (hw["int4_tflops"] * 1e12)
+        waves = -(-plan["workgroups"] // CUS)
+        seconds = waves * (plan["groups_per_split"] * plan["tile_rows"] / 256 * group + hw["gemm_wg_us"] * 1e-6)
+        if plan["splits"] > 1:
+            seconds += 2.0 * plan["splits"] * rows * n_out * 4.0 / mem
+    else:
+        weight_bytes_ = n_out * n_in * (0.5 + 4.0 / 64 if int4 else 2.0)
+        seconds = max(2.0 * rows * n_out * n_in / (hw["fp16_tflops"] * 1e12), weight_bytes_ / mem)
+    return _kernel(seconds, hw)
+
+
 def decode_step(shape, run: dict, hw: dict) -> dict:
     """Seconds per decode step at the average decode context, and tokens/s."""
     tier = run.get("weight_tier", TIER_HBM_INT4)
     rows = run["gpu_batch"] * run["batches_per_block"]
     h, f, d, heads, vocab = shape.hidden, shape.ffn, shape.head_dim, shape.n_heads, shape.vocab
     mem = hw["mem_gbs"] * 1e9
-    gemm_rate = (hw["fp16_tflops"] if tier == TIER_HOST_FP16 else hw["int4_tflops"]) * 1e12
     context = run["prompt_len"] + run["gen_len"] / 2.0
 
     layer = 0.0
     for n_out, n_in in ((3 * h, h), (h, h), (f, h), (h, f)):
-        flops = 2.0 * rows * n_out * n_in
-        weight_bytes_ = n_out * n_in * _bytes_per_weight(tier)
-        layer += _kernel(max(flops / gemm_rate, weight_bytes_ / mem), hw)
+        layer += gemm_time(rows, n_out, n_in, tier != TIER_HOST_FP16, hw)
     per_position = 2 * (d / 2 + 4 * (d / 64))          # K and V: codes + (scale, zero) per group
     attention_bytes = rows * heads * (context * per_position + 4 * d)   # cache, plus q and out in fp16
     layer += _kernel(attention_bytes / (hw["attn_gbs"] * 1e9), hw)
@@ -110,7 +161,7 @@ def decode_step(shape, run: dict, hw: dict) -> dict:
 
     head = _kernel(rows * h * 4.0 / mem, hw)            # embedding: two table rows in, one row out
     head += _kernel(rows * h * 4.0 / mem, hw)           # the first layer's LayerNorm
-    head += _kernel(max(2.0 * rows * vocab * h / (hw["fp16_tflops"] * 1e12), vocab * h * 2.0 / mem), hw)
+    head += gemm_time(rows, vocab, h, False, hw)            # LM head: fp16 tied embedding
     head += _kernel(rows * vocab * 2.0 / mem, hw)       # argmax over the fp16 logits
     compute = shape.n_layers * layer + head
 

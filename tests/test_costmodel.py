@@ -56,9 +56,9 @@ class _Shape:
 
 
 FREE = dict(attn_gbs=1e12, mem_gbs=1e12, link_gbs=16.0, int4_tflops=1e12, fp16_tflops=1e12, launch_us=0.0,
-            hbm_bytes=1e15, host_bytes=1e15, disk_gbs=1e12, disk_bytes=1e15)
-MI355X = dict(attn_gbs=6250.0, mem_gbs=7100.0, link_gbs=57.2, int4_tflops=930.0, fp16_tflops=410.0,
-              launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9, disk_gbs=7.4, disk_bytes=80e9)
+            hbm_bytes=1e15, host_bytes=1e15, disk_gbs=1e12, disk_bytes=1e15, gemm_wg_us=0.0)
+MI355X = dict(attn_gbs=6250.0, mem_gbs=7100.0, link_gbs=57.2, int4_tflops=1340.0, fp16_tflops=410.0,
+              launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9, disk_gbs=7.4, disk_bytes=80e9, gemm_wg_us=25.0)
 
 
 def test_free_compute_reduces_to_the_printed_simulator():
@@ -130,3 +130,51 @@ def test_images_on_disk():
     assert costmodel.footprint(shape, run)[1] == pytest.approx(2 * aligned, rel=1e-12)
     assert costmodel.disk_bytes(shape, run) == pytest.approx(8 * aligned, rel=1e-12)
     assert costmodel.disk_bytes(shape, dict(run, weights_on_disk=0)) == 0.0
+
+
+def test_gemm_plan_splits_and_tile_heights():
+    """The planner rule at the decode shapes: QKV of OPT-30B fills one wave with 192-row tiles,
+    fc1 with 256-row ones; the out-projection's 56 tiles split K four ways (224 workgroups);
+    at 256 rows the OPT-6.7B GEMMs split 4 to 16 ways; 128 rows take the register-staged kernel."""
+    p = costmodel.gemm_plan(512, 21504, 7168, True)
+    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (192, 1, 252)
+    p = costmodel.gemm_plan(512, 28672, 7168, True)
+    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 1, 224, 112)
+    p = costmodel.gemm_plan(512, 7168, 7168, True)
+    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 4, 224, 28)
+    assert [costmodel.gemm_plan(256, n, k, True)["splits"]
+            for n, k in ((12288, 4096), (4096, 4096), (16384, 4096), (4096, 16384))] == [4, 8, 4, 16]
+    assert costmodel.gemm_plan(128, 4096, 4096, True) is None
+    assert costmodel.gemm_plan(512, 4096, 4096, False) is None
+
+
+def test_gemm_in_whole_waves_of_full_tiles_runs_at_the_steady_rate():
+    """With no fixed cost, a GEMM whose 256 x 256 tiles fill whole waves of 256 workgroups, unsplit,
+    takes exactly its flops over the steady int4 rate (one and two waves)."""
+    hw = dict(MI355X, gemm_wg_us=0.0, launch_us=0.0)
+    for rows in (512, 1024):
+        t = costmodel.gemm_time(rows, 32768, 4096, True, hw)
+        assert t == pytest.approx(2.0 * rows * 32768 * 4096 / 1340e12, rel=1e-12)
+
+
+def test_gemm_fixed_cost_counts_once_per_wave():
+    hw = dict(MI355X, int4_tflops=1e30, launch_us=0.0, gemm_wg_us=25.0)
+    assert costmodel.gemm_time(512, 32768, 4096, True, hw) == pytest.approx(25e-6, rel=1e-9)
+    assert costmodel.gemm_time(1024, 32768, 4096, True, hw) == pytest.approx(50e-6, rel=1e-9)
+
+
+def test_split_gemm_pays_its_partials_twice():
+    """With free compute, a GEMM whose K loop is split costs its fp32 partials (splits x rows x N)
+    written once and read once at the streaming rate; an unsplit one costs nothing."""
+    hw = dict(MI355X, int4_tflops=1e30, launch_us=0.0, gemm_wg_us=0.0)
+    assert costmodel.gemm_time(512, 7168, 7168, True, hw) == pytest.approx(2 * 4 * 512 * 7168 * 4 / 7100e9,
+                                                                           rel=1e-12)
+    assert costmodel.gemm_time(512, 28672, 7168, True, hw) < 1e-12
+
+
+def test_small_and_fp16_gemms_are_the_larger_of_flops_and_weight_bytes():
+    hw = dict(MI355X, launch_us=0.0)
+    flops = 2.0 * 128 * 4096 * 4096
+    assert costmodel.gemm_time(128, 4096, 4096, True, hw) == pytest.approx(
+        max(flops / 410e12, 4096 * 4096 * 0.5625 / 7100e9), rel=1e-12)
+    assert costmodel.gemm_time(8, 4096, 4096, False, hw) == pytest.approx(4096 * 4096 * 2.0 / 7100e9, rel=1e-12)

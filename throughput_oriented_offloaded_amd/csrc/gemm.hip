@@ -679,6 +679,19 @@ size_t gemm_workspace_bytes(int M, int N, int K, bool int4)
     return p.tm.splits > 1 ? (size_t)p.tm.splits * M * N * sizeof(float) : 0;
 }
 
+GemmPlanInfo gemm_plan_info(int M, int N, int K, bool int4)
+{
+    const Plan p = plan_gemm(M, N, K, int4);
+    GemmPlanInfo i;
+    i.pipelined = p.pipelined;
+    i.bm = p.bm;
+    i.bn = p.bn;
+    i.splits = p.tm.splits;
+    i.groups_per_split = p.tm.groups_per_split;
+    i.workgroups = p.tm.total;
+    return i;
+}
+
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
 {
     if (g.M <= 0 || g.N <= 0)

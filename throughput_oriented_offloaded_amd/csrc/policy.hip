@@ -12,9 +12,18 @@
 // pinned-host capacities.
 //
 // Step model at the average decode context c = prompt_len + gen_len / 2:
-//  * each int4 GEMM (or fp16 on the fp16 host tier) costs the larger of its
-//    flops at the GEMM rate and its weight bytes at the streaming rate, and at
-//    least one kernel's launch floor;
+//  * each GEMM is priced on the tile plan the library launches for it. The
+//    pipelined int4 kernel (more than 128 rows) runs its workgroups in waves
+//    of one per CU; a wave costs its K-groups per workgroup times the time of
+//    one K-group (the steady int4 rate, scaled by the tile's rows) plus a fixed
+//    cost for pipeline fill and epilogue, and a split K loop adds its fp32
+//    partials, written once and read once at the streaming rate. Fitted to the
+//    measured decode GEMMs at 512 rows (OPT-30B) and 256 rows (OPT-6.7B), this
+//    is within about 15% on each of them, where one flat rate misses the
+//    256-row GEMMs by up to 2x (their K loops split 4 to 16 ways). The
+//    register-staged kernel (fp16 weights; int4 at 128 rows or fewer) costs
+//    the larger of its flops at the fp16 GEMM rate and its weight bytes at the
+//    streaming rate. Every kernel costs at least one launch floor;
 //  * decode attention moves M * heads * (c * (d + d/8) + 4d) bytes at the
 //    attention rate; the KV append reads 4d and writes d + d/8 bytes per
 //    (row, head); one LayerNorm per step (the others are fused); the LM head is
@@ -132,6 +141,27 @@ double kernel_time(double work_s, const tod_hw *hw)
     return work_s > hw->launch_us * 1e-6 ? work_s : hw->launch_us * 1e-6;
 }
 
+constexpr double kCUs = 256.0; // MI355X compute units; one pipelined GEMM workgroup each
+
+// One GEMM of M rows, N outputs and K inputs on the tile plan launch_gemm takes.
+double gemm_time(int M, int N, int K, bool int4, const tod_hw *hw)
+{
+    const GemmPlanInfo p = gemm_plan_info(M, N, K, int4);
+    const double mem = hw->mem_gbs * 1e9;
+    double t;
+    if (p.pipelined) {
+        const double t_group = kCUs * 2.0 * 256.0 * 256.0 * 64.0 / (hw->int4_tflops * 1e12);
+        const double waves = std::ceil(p.workgroups / kCUs);
+        t = waves * (p.groups_per_split * (p.bm / 256.0) * t_group + hw->gemm_wg_us * 1e-6);
+        if (p.splits > 1)
+            t += 2.0 * p.splits * (double)M * N * 4.0 / mem;
+    } else {
+        const double flop = 2.0 * M * (double)N * K, wb = (double)N * K * (int4 ? 0.5625 : 2.0);
+        t = flop / (hw->fp16_tflops * 1e12) > wb / mem ? flop / (hw->fp16_tflops * 1e12) : wb / mem;
+    }
+    return kernel_time(t, hw);
+}
+
 void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw *hw, tod_estimate *e)
 {
     const Shape s{(double)c->n_layers, (double)c->hidden, (double)c->n_heads, (double)c->head_dim,
@@ -141,26 +171,20 @@ void step_model(const tod_model_config *c, const tod_run_config *r, const tod_hw
     const double M = (double)r->gpu_batch * r->batches_per_block;
     const double h = s.h, f = s.f, d = s.d;
     const double wbpe = tier == TOD_W_HOST_FP16_STREAM ? 2.0 : 0.5625; // weight bytes per element
-    const double rate = (tier == TOD_W_HOST_FP16_STREAM ? hw->fp16_tflops : hw->int4_tflops) * 1e12;
     const double mem = hw->mem_gbs * 1e9;
     const double ctx = r->prompt_len + r->gen_len / 2.0;
     // one layer
-    const double nk[4][2] = {{3.0 * h, h}, {h, h}, {f, h}, {h, f}};
+    const int Mi = r->gpu_batch * r->batches_per_block, hi = c->hidden, fi = c->ffn;
+    const int nk[4][2] = {{3 * hi, hi}, {hi, hi}, {fi, hi}, {hi, fi}};
     double t_layer = 0.0;
-    for (const auto &g : nk) {
-        const double flop = 2.0 * M * g[0] * g[1], wb = g[0] * g[1] * wbpe;
-        const double t = flop / rate > wb / mem ? flop / rate : wb / mem;
-        t_layer += kernel_time(t, hw);
-    }
+    for (const auto &g : nk)
+        t_layer += gemm_time(Mi, g[0], g[1], tier != TOD_W_HOST_FP16_STREAM, hw);
     const double kvpos = d + d / 8.0; // K and V codes and params per (head, position)
     t_layer += kernel_time(M * s.H * (ctx * kvpos + 4.0 * d) / (hw->attn_gbs * 1e9), hw);
     t_layer += kernel_time(M * s.H * (4.0 * d + kvpos) / mem, hw);
     // head: embedding, the first LayerNorm, LM head GEMM, argmax
     double t_head = kernel_time(M * h * 2.0 * 2.0 / mem, hw) + kernel_time(M * h * 4.0 / mem, hw);
-    const double lm_flop = 2.0 * M * s.V * h, lm_w = s.V * h * 2.0;
-    t_head += kernel_time(lm_flop / (hw->fp16_tflops * 1e12) > lm_w / mem ? lm_flop / (hw->fp16_tflops * 1e12)
-                                                                            : lm_w / mem,
-                          hw);
+    t_head += gemm_time(Mi, c->vocab, hi, false, hw);
     t_head += kernel_time(M * s.V * 2.0 / mem, hw);
     const double t_comp = s.L * t_layer + t_head;
     double t_link = 0.0, idle = 0.0;
@@ -205,13 +229,14 @@ void default_hw(tod_hw *hw)
     hw->attn_gbs = 6250.0;    // decode attention, int4 cache, OPT-30B shape
     hw->mem_gbs = 7100.0;     // streaming reads with nontemporal 16-byte loads
     hw->link_gbs = 57.2;      // one pinned -> HBM copy of a layer image
-    hw->int4_tflops = 930.0;  // fused int4 GEMMs at 512 rows, real data
+    hw->int4_tflops = 1340.0; // pipelined int4 GEMMs, steady rate with every CU busy (fitted)
     hw->fp16_tflops = 410.0;  // fp16-weight GEMM (LM head)
     hw->launch_us = 4.0;      // per kernel inside a replayed decode graph
     hw->hbm_bytes = 280e9;    // device memory a model may use
     hw->host_bytes = 270e9;   // pinned host memory a process may hold
     hw->disk_gbs = 7.4;       // reads of the weight file (one image per read)
     hw->disk_bytes = 80e9;    // free space for the weight file
+    hw->gemm_wg_us = 25.0;    // fixed cost per wave of pipelined GEMM workgroups (fitted)
 }
 
 int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out)
@@ -219,7 +244,7 @@ int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, cons
     if (!out || !hw || !valid(cfg, run))
         return TOD_EINVAL;
     if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
-          hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0))
+          hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0 && hw->gemm_wg_us >= 0.0))
         return TOD_EINVAL;
     step_model(cfg, run, hw, out);
     footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes, &out->disk_bytes);
