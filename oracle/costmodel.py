@@ -97,18 +97,18 @@ CUS = 256  # MI355X compute units: one workgroup of the pipelined int4 GEMM each
 
 
 def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
-    """The tile plan of the library's pipelined int4 GEMM, restated from its rule (None when the
-    register-staged kernel runs: fp16 weights, or 128 rows or fewer).
+    """The tile plan of the library's pipelined GEMM, restated from its rule (None when the
+    register-staged kernel runs: 128 rows or fewer, or fp16 weights whose N is not a multiple of 32).
 
-    Tiles are 256 outputs wide and 256 or 192 rows tall. The K loop (K-groups of 64) is split in
-    powers of two while the tiles times the splits stay below 160 workgroups and each split keeps
-    at least 8 K-groups. Of the two tile heights the one with the fewer waves of 256 workgroups x
-    tile rows x K-groups per workgroup is taken, 256 on a tie."""
-    if not (int4 and rows > 128):
+    Tiles are 256 outputs wide and 256 or 192 rows tall (fp16 weights: 256 only). The K loop
+    (K-groups of 64) is split in powers of two while the tiles times the splits stay below 160
+    workgroups and each split keeps at least 8 K-groups. Of the two tile heights the one with the
+    fewer waves of 256 workgroups x tile rows x K-groups per workgroup is taken, 256 on a tie."""
+    if rows <= 128 or (not int4 and n_out % 32):
         return None
     groups = n_in // 64
     best = None
-    for tile_rows in (256, 192):
+    for tile_rows in ((256, 192) if int4 else (256,)):
         tiles = -(-rows // tile_rows) * -(-n_out // 256)
         splits = 1
         while tiles * splits < 160 and groups // (splits * 2) >= 8:
@@ -125,21 +125,23 @@ def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
 
 def gemm_time(rows: int, n_out: int, n_in: int, int4: bool, hw: dict) -> float:
     """Seconds for one GEMM. The pipelined kernel runs its workgroups in waves of one per CU: a wave
-    costs its K-groups per workgroup times one K-group of a 256 x 256 tile at the steady int4 rate
-    (scaled by the tile's rows), plus the fixed cost per wave; a split K loop adds its fp32 partials,
-    written and read back at the streaming rate. The register-staged kernel costs the larger of
-    its flops at the fp16 GEMM rate and its weight bytes at the streaming rate."""
+    costs its K-groups per workgroup times one K-group of a 256 x 256 tile at the steady int4 or
+    fp16 rate (scaled by the tile's rows), plus the fixed cost per wave; a split K loop adds its
+    fp32 partials, written and read back at the streaming rate. The register-staged kernel costs
+    the same fixed cost plus its weight bytes and its flops, each at that kernel's own rate."""
     mem = hw["mem_gbs"] * 1e9
     plan = gemm_plan(rows, n_out, n_in, int4)
     if plan is not None:
-        group = CUS * 2.0 * 256 * 256 * 64 / (hw["int4_tflops"] * 1e12)
+        rate = hw["int4_tflops"] if int4 else hw["fp16_tflops"]
+        group = CUS * 2.0 * 256 * 256 * 64 / (rate * 1e12)
         waves = -(-plan["workgroups"] // CUS)
         seconds = waves * (plan["groups_per_split"] * plan["tile_rows"] / 256 * group + hw["gemm_wg_us"] * 1e-6)
         if plan["splits"] > 1:
             seconds += 2.0 * plan["splits"] * rows * n_out * 4.0 / mem
     else:
         weight_bytes_ = n_out * n_in * (0.5 + 4.0 / 64 if int4 else 2.0)
-        seconds = max(2.0 * rows * n_out * n_in / (hw["fp16_tflops"] * 1e12), weight_bytes_ / mem)
+        seconds = (hw["gemm_wg_us"] * 1e-6 + weight_bytes_ / (hw["staged_gbs"] * 1e9)
+                   + 2.0 * rows * n_out * n_in / (hw["staged_tflops"] * 1e12))
     return _kernel(seconds, hw)
 
 

@@ -56,9 +56,11 @@ class _Shape:
 
 
 FREE = dict(attn_gbs=1e12, mem_gbs=1e12, link_gbs=16.0, int4_tflops=1e12, fp16_tflops=1e12, launch_us=0.0,
-            hbm_bytes=1e15, host_bytes=1e15, disk_gbs=1e12, disk_bytes=1e15, gemm_wg_us=0.0)
-MI355X = dict(attn_gbs=6250.0, mem_gbs=7100.0, link_gbs=57.2, int4_tflops=1340.0, fp16_tflops=410.0,
-              launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9, disk_gbs=7.4, disk_bytes=80e9, gemm_wg_us=25.0)
+            hbm_bytes=1e15, host_bytes=1e15, disk_gbs=1e12, disk_bytes=1e15, gemm_wg_us=0.0, staged_tflops=1e12,
+            staged_gbs=1e12)
+MI355X = dict(attn_gbs=6250.0, mem_gbs=7100.0, link_gbs=57.2, int4_tflops=1340.0, fp16_tflops=1400.0,
+              launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9, disk_gbs=7.4, disk_bytes=80e9, gemm_wg_us=25.0,
+              staged_tflops=1700.0, staged_gbs=3230.0)
 
 
 def test_free_compute_reduces_to_the_printed_simulator():
@@ -145,7 +147,9 @@ def test_gemm_plan_splits_and_tile_heights():
     assert [costmodel.gemm_plan(256, n, k, True)["splits"]
             for n, k in ((12288, 4096), (4096, 4096), (16384, 4096), (4096, 16384))] == [4, 8, 4, 16]
     assert costmodel.gemm_plan(128, 4096, 4096, True) is None
-    assert costmodel.gemm_plan(512, 4096, 4096, False) is None
+    p = costmodel.gemm_plan(512, 50272, 7168, False)  # the fp16 LM head: 256-row tiles, two waves
+    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (256, 1, 394)
+    assert costmodel.gemm_plan(512, 50200, 7168, False) is None  # N not a multiple of 32
 
 
 def test_gemm_in_whole_waves_of_full_tiles_runs_at_the_steady_rate():
@@ -172,9 +176,18 @@ def test_split_gemm_pays_its_partials_twice():
     assert costmodel.gemm_time(512, 28672, 7168, True, hw) < 1e-12
 
 
-def test_small_and_fp16_gemms_are_the_larger_of_flops_and_weight_bytes():
+def test_register_staged_gemm_limits():
+    """At 128 rows or fewer: with free flops and no fixed cost a GEMM is its weight bytes at the
+    kernel's read rate (int4 codes and params, or fp16); each added row adds exactly its flops."""
+    hw = dict(MI355X, launch_us=0.0, gemm_wg_us=0.0, staged_tflops=1e30)
+    assert costmodel.gemm_time(128, 4096, 4096, True, hw) == pytest.approx(4096 * 4096 * 0.5625 / 3230e9, rel=1e-12)
+    assert costmodel.gemm_time(8, 4096, 4096, False, hw) == pytest.approx(4096 * 4096 * 2.0 / 3230e9, rel=1e-12)
     hw = dict(MI355X, launch_us=0.0)
-    flops = 2.0 * 128 * 4096 * 4096
-    assert costmodel.gemm_time(128, 4096, 4096, True, hw) == pytest.approx(
-        max(flops / 410e12, 4096 * 4096 * 0.5625 / 7100e9), rel=1e-12)
-    assert costmodel.gemm_time(8, 4096, 4096, False, hw) == pytest.approx(4096 * 4096 * 2.0 / 7100e9, rel=1e-12)
+    step = costmodel.gemm_time(65, 4096, 4096, True, hw) - costmodel.gemm_time(64, 4096, 4096, True, hw)
+    assert step == pytest.approx(2.0 * 4096 * 4096 / 1700e12, rel=1e-9)
+
+
+def test_fp16_gemm_in_whole_waves_runs_at_the_fp16_steady_rate():
+    hw = dict(MI355X, gemm_wg_us=0.0, launch_us=0.0)
+    assert costmodel.gemm_time(512, 32768, 4096, False, hw) == pytest.approx(2.0 * 512 * 32768 * 4096 / 1400e12,
+                                                                             rel=1e-12)

@@ -78,6 +78,34 @@ def test_linear_residual_in_place():
     assert ulps(to_np16(hd), ref).max() <= 2
 
 
+F16_CASES = [  # rows, in, out, epilogue: above 128 rows with out % 32 == 0 the pipelined kernel runs
+    (129, 256, 160, "res"), (300, 1280, 480, "relu"), (257, 4096, 288, "bias"), (640, 2048, 1056, "res"),
+    (512, 3072, 768, "none"), (300, 512, 200, "bias"), (100, 768, 768, "res"),
+]
+
+
+@pytest.mark.parametrize("rows,k,n,epi", F16_CASES)
+def test_linear_f16_matches_oracle(rows, k, n, epi):
+    """fp16-weight GEMM with ragged M and N tiles, split K and every epilogue; out = 200 is not a
+    multiple of 32 and 100 rows stay at 128 or fewer, so those take the register-staged kernel."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    print(f"linear_f16 rows={rows} in={k} out={n} {epi}", flush=True)
+    seed = rows * 11 + k + n
+    w = synth.normal_f16(seed, 0, (n, k), 0.0, 0.02)
+    a = synth.normal_f16(seed, 1, (rows, k), 0.0, 1.0)
+    bias = synth.normal_f16(seed, 2, (n,), 0.0, 0.1) if epi != "none" else None
+    res = synth.normal_f16(seed, 3, (rows, n), 0.0, 1.0) if epi == "res" else None
+    y = torch.empty((rows, n), dtype=torch.float16, device="cuda")
+    tod.linear_f16(to_dev(a, torch), to_dev(w, torch), y, bias=to_dev(bias, torch) if bias is not None else None,
+                   residual=to_dev(res, torch) if res is not None else None, relu=epi == "relu")
+    torch.cuda.synchronize()
+    ref = oracle.linear_f16(a, w, bias=bias, residual=res, relu=epi == "relu")
+    u = ulps(to_np16(y), ref)
+    assert u.max() <= 2, f"max {u.max()} ulp"
+    assert (u == 0).mean() > 0.99
+
+
 @pytest.mark.parametrize("rows", [8, 100, 512])
 def test_lm_head_fp16_ragged_vocab(rows):
     """fp16 weights with N = 50272 (not a multiple of the tile), as in the tied LM head."""

@@ -13,7 +13,10 @@
 //    prefill path): 256 x 256 or 192 x 256 tiles, eight wavefronts (two per
 //    SIMD), activations, codes and params fed through a 3-stage LDS ring by
 //    direct-to-LDS loads; described at the kernel body (gemm_w4_body).
-//  * k_gemm (M <= 128, and fp16 weights: LM head, host tier): 256-thread
+//    k_gemm_f16_256 is the same body on fp16 weights (LM head and fp16 host
+//    tier above 128 rows): the weight tile is staged like the activation
+//    tile, in a 2-stage ring.
+//  * k_gemm (M <= 128, and fp16 weights of narrow N): 256-thread
 //    workgroups as a 2x2 grid of wavefronts, each owning a (BM/2) x (BN/2)
 //    output tile; the activation tile (BM x 64, one quantization group of K)
 //    is double-buffered in LDS with 16-byte chunks XOR-swizzled by row, and
@@ -239,7 +242,7 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 }
 
 // ---------------------------------------------------------------------------
-// int4 GEMM for M > 128: BM x 256 workgroup tiles (BM = 256, or 192 where
+// Pipelined GEMM for M > 128 (int4, or fp16 weights): BM x 256 workgroup tiles (BM = 256, or 192 where
 // that fills more of the chip), eight wavefronts (two per SIMD) as a 2 x 4
 // grid of BM/2 x 64 wave tiles, fed through a 3-stage LDS ring
 // that direct-to-LDS loads (global_load_lds_dwordx4) fill two K-groups ahead
@@ -248,18 +251,23 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 // run while the other's MFMAs issue. Stage synchronisation is an explicit
 // vmcnt wait on the wave's own loads plus a workgroup barrier.
 // ---------------------------------------------------------------------------
-template <int BM_> struct W4 {
+// F16: fp16 weights W[N][K] instead of int4 codes. W's tile (BN rows x 64 fp16)
+// has the layout of the A tile and the MFMA B fragment is read exactly as an A
+// fragment; both tiles need 64 KiB per stage, so the ring has two stages.
+template <int BM_, bool F16 = false> struct W4 {
     static constexpr int BM = BM_, BN = 256, WAVES = 8;
     static constexpr int RB = BM / 2;                   // rows per wave (2 wave rows)
     static constexpr int MB = RB / 32;                  // 32-row blocks per wave
     static constexpr int NB = 2;                        // 32-column blocks per wave (4 wave columns)
     static constexpr int A_BYTES = BM * 128;            // BM rows x 64 fp16, 16-byte chunks swizzled by row
-    static constexpr int W_BYTES = (BN / 32) * 1024;    // per column block: 64 lanes x 16 B of codes
-    static constexpr int P_BYTES = (BN / 32) * 256;     // per column block: 64 x (scale, zero), lanes 32..63 repeat
+    // int4: per column block 64 lanes x 16 B of codes; fp16: BN rows x 64 fp16 like A
+    static constexpr int W_BYTES = F16 ? BN * 128 : (BN / 32) * 1024;
+    static constexpr int P_BYTES = F16 ? 0 : (BN / 32) * 256; // per column block: 64 x (scale, zero)
     static constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
-    static constexpr int S = 3;                         // ring stages
+    static constexpr int S = F16 ? 2 : 3;               // ring stages
     static constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
-    static constexpr int LPS = AL + 2;                  // loads per wave per stage: A chunks, codes, params
+    static constexpr int WL = F16 ? (BN / 8) / WAVES : 0; // fp16: 1 KiB W chunks per wave per stage
+    static constexpr int LPS = AL + (F16 ? WL : 2);     // loads per wave per stage: A chunks, W chunks or codes and params
     static_assert(BM % 64 == 0 && (BM / 8) % WAVES == 0, "A chunks split evenly over the waves");
 };
 
@@ -286,12 +294,13 @@ __device__ __forceinline__ void wait_vm_loads(int younger)
         __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
-template <int BM_>
+template <int BM_, bool F16>
 __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &tm)
 {
-    using C = W4<BM_>;
+    using C = W4<BM_, F16>;
     constexpr int BM = C::BM, BN = C::BN, WAVES = C::WAVES, RB = C::RB, MB = C::MB, NB = C::NB;
     constexpr int A_BYTES = C::A_BYTES, W_BYTES = C::W_BYTES, STAGE = C::STAGE, S = C::S, AL = C::AL;
+    constexpr int WL = C::WL;
     __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE];
 
     const int tile = xcd_tile(blockIdx.x, tm.total);
@@ -327,6 +336,18 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
     const uint8_t *a_tile = reinterpret_cast<const uint8_t *>(g.a + (int64_t)m0 * g.lda);
     const uint8_t *wc8 = reinterpret_cast<const uint8_t *>(g.wc);
     const uint8_t *wp8 = reinterpret_cast<const uint8_t *>(g.wp);
+    // fp16 weights: W-tile rows as A-tile rows (clamped: rows past N feed discarded columns)
+    uint32_t w_off[WL > 0 ? WL : 1];
+    const uint8_t *w_tile = nullptr;
+    if constexpr (F16) {
+#pragma unroll
+        for (int i = 0; i < WL; i++) {
+            const int row = 8 * (wv + WAVES * i) + (lane >> 3);
+            const int n = min(n0 + row, g.N - 1);
+            w_off[i] = (uint32_t)((n - n0) * g.K + a_pos(row, lane & 7) * 8) * 2u;
+        }
+        w_tile = reinterpret_cast<const uint8_t *>(g.wf + (int64_t)n0 * g.K);
+    }
 
     auto issue = [&](int buf, int grp) {
         uint8_t *base = smem + buf * STAGE;
@@ -334,11 +355,19 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
 #pragma unroll
         for (int i = 0; i < AL; i++)
             __builtin_amdgcn_global_load_lds(ag + a_off[i], (lds_void *)(base + (wv + WAVES * i) * 1024), 16, 0, 0);
-        const int64_t blk = (int64_t)nbw * KG + grp;
-        __builtin_amdgcn_global_load_lds(wc8 + blk * 1024 + lane * 16, (lds_void *)(base + A_BYTES + wv * 1024), 16,
-                                         0, 0);
-        __builtin_amdgcn_global_load_lds(wp8 + blk * 128 + (lane & 31) * 4,
-                                         (lds_void *)(base + A_BYTES + W_BYTES + wv * 256), 4, 0, 0);
+        if constexpr (F16) {
+            const uint8_t *wg = w_tile + grp * (KG_ELEMS * 2);
+#pragma unroll
+            for (int i = 0; i < WL; i++)
+                __builtin_amdgcn_global_load_lds(wg + w_off[i], (lds_void *)(base + A_BYTES + (wv + WAVES * i) * 1024),
+                                                 16, 0, 0);
+        } else {
+            const int64_t blk = (int64_t)nbw * KG + grp;
+            __builtin_amdgcn_global_load_lds(wc8 + blk * 1024 + lane * 16, (lds_void *)(base + A_BYTES + wv * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(wp8 + blk * 128 + (lane & 31) * 4,
+                                             (lds_void *)(base + A_BYTES + W_BYTES + wv * 256), 4, 0, 0);
+        }
     };
 
     float16_t acc[MB][NB];
@@ -363,18 +392,31 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
         const uint8_t *base = smem + (it % S) * STAGE;
         uint4_t bw[NB];
         half2_t s2[NB], z2[NB];
+        if constexpr (!F16) {
 #pragma unroll
-        for (int j = 0; j < NB; j++) {
-            const int cb = wn * NB + j;
-            bw[j] = *reinterpret_cast<const uint4_t *>(base + A_BYTES + cb * 1024 + lane * 16);
-            const uint32_t bp =
-                *reinterpret_cast<const uint32_t *>(base + A_BYTES + W_BYTES + cb * 256 + (lane & 31) * 4);
-            s2[j] = __builtin_bit_cast(half2_t, (bp & 0xffffu) * 0x10001u);
-            z2[j] = __builtin_bit_cast(half2_t, (bp >> 16) * 0x10001u);
+            for (int j = 0; j < NB; j++) {
+                const int cb = wn * NB + j;
+                bw[j] = *reinterpret_cast<const uint4_t *>(base + A_BYTES + cb * 1024 + lane * 16);
+                const uint32_t bp =
+                    *reinterpret_cast<const uint32_t *>(base + A_BYTES + W_BYTES + cb * 256 + (lane & 31) * 4);
+                s2[j] = __builtin_bit_cast(half2_t, (bp & 0xffffu) * 0x10001u);
+                z2[j] = __builtin_bit_cast(half2_t, (bp >> 16) * 0x10001u);
+            }
         }
-        // Four K-steps of 16: the A operands of step t+1 (LDS) and its dequantized
-        // weights are produced before the MFMAs of step t; the other wave on the
-        // SIMD fills the gaps.
+        // B operand of column block j at K-step t: dequantized codes, or the fp16
+        // W-tile fragment read like an A fragment
+        auto b_frag = [&](int j, int t) -> half8_t {
+            if constexpr (F16) {
+                const int row = (wn * NB + j) * 32 + (lane & 31);
+                return *reinterpret_cast<const half8_t *>(base + A_BYTES + row * 128 +
+                                                          (a_pos(row, 2 * t + (lane >> 5)) << 4));
+            } else {
+                return dequant_word(bw[j][t], s2[j], z2[j]);
+            }
+        };
+        // Four K-steps of 16: the A operands of step t+1 (LDS) and its B operands
+        // are produced before the MFMAs of step t; the other wave on the SIMD
+        // fills the gaps.
         half8_t a_cur[MB], a_nxt[MB], b_cur[NB], b_nxt[NB];
 #pragma unroll
         for (int i = 0; i < MB; i++) {
@@ -383,7 +425,7 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
         }
 #pragma unroll
         for (int j = 0; j < NB; j++)
-            b_cur[j] = dequant_word(bw[j][0], s2[j], z2[j]);
+            b_cur[j] = b_frag(j, 0);
 #pragma unroll
         for (int t = 0; t < 4; t++) {
             if (t < 3) {
@@ -395,7 +437,7 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
                 }
 #pragma unroll
                 for (int j = 0; j < NB; j++)
-                    b_nxt[j] = dequant_word(bw[j][t + 1], s2[j], z2[j]);
+                    b_nxt[j] = b_frag(j, t + 1);
             }
 #pragma unroll
             for (int i = 0; i < MB; i++)
@@ -493,8 +535,9 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
     }
 }
 
-__global__ void __launch_bounds__(512, 1) k_gemm_w4_256(GemmArgs g, TileMap tm) { gemm_w4_body<256>(g, tm); }
-__global__ void __launch_bounds__(512, 1) k_gemm_w4_192(GemmArgs g, TileMap tm) { gemm_w4_body<192>(g, tm); }
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_256(GemmArgs g, TileMap tm) { gemm_w4_body<256, false>(g, tm); }
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_192(GemmArgs g, TileMap tm) { gemm_w4_body<192, false>(g, tm); }
+__global__ void __launch_bounds__(512, 1) k_gemm_f16_256(GemmArgs g, TileMap tm) { gemm_w4_body<256, true>(g, tm); }
 
 __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
 {
@@ -578,12 +621,16 @@ struct Plan {
 
 // Tuning overrides (read once): TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" selects the
 // register-staged kernel for every M > 64; TOD_GEMM_SPLIT = workgroup count below which the
-// K loop is split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined kernel's tile height to 256 | 192.
+// K loop is split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined int4 kernel's tile height to 256 | 192;
+// TOD_GEMM_F16PIPE = 0 keeps fp16 weights on the register-staged kernel.
 struct Tuning {
     int bm = 0, bn = 0, split_fill = -1;
     int bm192 = -1; // pipelined tile height: -1 cost model, 0 always 256, 1 always 192
+    bool f16_pipe = true; // fp16 weights on the pipelined kernel above 128 rows
     Tuning()
     {
+        if (const char *t = getenv("TOD_GEMM_F16PIPE"))
+            f16_pipe = atoi(t) != 0;
         if (const char *t = getenv("TOD_GEMM_BM192"))
             bm192 = atoi(t) > 0 ? 1 : atoi(t) == 0 ? 0 : -1;
         if (const char *t = getenv("TOD_GEMM_TILE")) {
@@ -632,8 +679,12 @@ Plan plan_gemm(int M, int N, int K, bool int4)
 {
     Plan p;
     const Tuning &tu = tuning();
-    p.pipelined = int4 && M > 128 && !tu.bm;
-    if (p.pipelined) {
+    p.pipelined = M > 128 && !tu.bm && (int4 || (tu.f16_pipe && N % 32 == 0));
+    if (p.pipelined && !int4) {
+        // fp16 weights: 256 x 256 tiles only
+        p.bm = 256;
+        p.bn = 256;
+    } else if (p.pipelined) {
         // 256 x 256 tiles halve the activation re-reads per MFMA against 256 x 128,
         // at the price of fewer workgroups; narrow N is split along K instead.
         // 192-row tiles are taken where their extra workgroups finish the GEMM
@@ -708,7 +759,9 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         p.tm.total = p.tm.mt * p.tm.nt;
     }
     const dim3 grid(p.tm.total), block(256);
-    if (p.pipelined && p.bm == 192)
+    if (p.pipelined && !int4)
+        hipLaunchKernelGGL(k_gemm_f16_256, grid, dim3(64 * W4<256, true>::WAVES), 0, st, g, p.tm);
+    else if (p.pipelined && p.bm == 192)
         hipLaunchKernelGGL(k_gemm_w4_192, grid, dim3(64 * W4<192>::WAVES), 0, st, g, p.tm);
     else if (p.pipelined)
         hipLaunchKernelGGL(k_gemm_w4_256, grid, dim3(64 * W4<256>::WAVES), 0, st, g, p.tm);
