@@ -326,11 +326,12 @@ int attn_cache_free(tod_attn_cache *c);
  * tod_hw: attn_gbs = decode-attention read rate, mem_gbs = streaming rate of
  * the other row-wise kernels and weight reads, link_gbs = pinned -> HBM copy
  * rate (GB/s); int4_tflops / fp16_tflops = steady rates of the pipelined GEMM
- * (more than 128 rows) on int4 / fp16 weights while every CU holds one of its
+ * on int4 / fp16 weights while every CU holds one of its
  * workgroups, and gemm_wg_us = the fixed time each wave of its workgroups adds
- * (pipeline fill, epilogue); staged_gbs / staged_tflops = the register-staged
- * GEMM's effective weight-read rate and flop rate (128 rows or fewer, or fp16
- * weights whose N is not a multiple of 32); launch_us = floor per kernel;
+ * (pipeline fill, epilogue); staged_us / staged_gbs / staged_tflops = the
+ * register-staged GEMM's fixed time, effective weight-read rate and flop rate
+ * (small GEMMs of 128 rows or fewer, fp16 weights whose N is not a multiple
+ * of 32); launch_us = floor per kernel;
  * hbm_bytes / host_bytes =
  * capacities the model may use; disk_gbs / disk_bytes = read rate and free
  * space of the weight file's disk. default_hw fills the figures measured on
@@ -341,9 +342,10 @@ int attn_cache_free(tod_attn_cache *c);
  * the library's own tile plan: a pipelined GEMM takes ceil(workgroups / 256)
  * waves of (K-groups per workgroup * tile rows / 256 * t_g + gemm_wg_us),
  * where t_g = 256 * 2 * 256 * 256 * 64 / (int4_tflops or fp16_tflops) is one
- * K-group of a full 256 x 256 tile on every CU, plus, when its K loop is
- * split, its fp32 partials written and read back at mem_gbs; a
- * register-staged GEMM takes gemm_wg_us + weight bytes / staged_gbs + flops /
+ * K-group of a full 256 x 256 tile on every CU, at least weight bytes /
+ * mem_gbs + gemm_wg_us, plus, when its K loop is split, its fp32 partials
+ * written and read back at mem_gbs; a
+ * register-staged GEMM takes staged_us + weight bytes / staged_gbs + flops /
  * staged_tflops (each GEMM at least launch_us),
  * attention M * heads * (ctx * (d + d/8) + 4d) bytes / attn_gbs, the KV append
  * M * heads * (4d + d + d/8) bytes / mem_gbs; plus embedding, one LayerNorm, the
@@ -380,7 +382,7 @@ int attn_cache_free(tod_attn_cache *c);
  */
 typedef struct {
     double attn_gbs, mem_gbs, link_gbs, int4_tflops, fp16_tflops, launch_us, hbm_bytes, host_bytes, disk_gbs,
-        disk_bytes, gemm_wg_us, staged_tflops, staged_gbs;
+        disk_bytes, gemm_wg_us, staged_tflops, staged_gbs, staged_us;
 } tod_hw;
 typedef struct {
     double step_s, tokens_per_s, compute_s, link_s, hbm_bytes, host_bytes, workspace_bytes, disk_bytes;

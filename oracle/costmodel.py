@@ -98,17 +98,24 @@ CUS = 256  # MI355X compute units: one workgroup of the pipelined int4 GEMM each
 
 def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
     """The tile plan of the library's pipelined GEMM, restated from its rule (None when the
-    register-staged kernel runs: 128 rows or fewer, or fp16 weights whose N is not a multiple of 32).
+    register-staged kernel runs: fp16 weights whose N is not a multiple of 32, or int4 weights at
+    128 rows or fewer whose pipelined plan would launch fewer than 128 workgroups).
 
-    Tiles are 256 outputs wide and 256 or 192 rows tall (fp16 weights: 256 only). The K loop
-    (K-groups of 64) is split in powers of two while the tiles times the splits stay below 160
-    workgroups and each split keeps at least 8 K-groups. Of the two tile heights the one with the
-    fewer waves of 256 workgroups x tile rows x K-groups per workgroup is taken, 256 on a tie."""
-    if rows <= 128 or (not int4 and n_out % 32):
+    Tiles are 256 outputs wide. int4 tiles are 256 or 192 rows tall above 128 rows and 128 or 64
+    rows at 128 rows or fewer; fp16 tiles are 256 rows tall above 128 rows and 64 below. The K
+    loop (K-groups of 64) is split in powers of two while the tiles times the splits stay below
+    160 workgroups and each split keeps at least 8 K-groups. Of the two tile heights the one
+    with the fewer waves of 256 workgroups x tile rows x K-groups per workgroup is taken, the
+    taller on a tie."""
+    if not int4 and n_out % 32:
         return None
+    if int4:
+        heights = (256, 192) if rows > 128 else (128, 64)
+    else:
+        heights = (256,) if rows > 128 else (64,)
     groups = n_in // 64
     best = None
-    for tile_rows in ((256, 192) if int4 else (256,)):
+    for tile_rows in heights:
         tiles = -(-rows // tile_rows) * -(-n_out // 256)
         splits = 1
         while tiles * splits < 160 and groups // (splits * 2) >= 8:
@@ -120,27 +127,32 @@ def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
         if best is None or cost < best["cost"]:
             best = dict(cost=cost, tile_rows=tile_rows, splits=splits, groups_per_split=per_split,
                         workgroups=workgroups)
+    if int4 and rows <= 128 and best["workgroups"] < 128:
+        return None
     return best
 
 
 def gemm_time(rows: int, n_out: int, n_in: int, int4: bool, hw: dict) -> float:
     """Seconds for one GEMM. The pipelined kernel runs its workgroups in waves of one per CU: a wave
     costs its K-groups per workgroup times one K-group of a 256 x 256 tile at the steady int4 or
-    fp16 rate (scaled by the tile's rows), plus the fixed cost per wave; a split K loop adds its
-    fp32 partials, written and read back at the streaming rate. The register-staged kernel costs
-    the same fixed cost plus its weight bytes and its flops, each at that kernel's own rate."""
+    fp16 rate (scaled by the tile's rows), plus the fixed cost per wave, and no less than its weight
+    bytes at the streaming rate plus that fixed cost; a split K loop adds its fp32 partials,
+    written and read back at the streaming rate. The register-staged kernel costs its own fixed
+    time plus its weight bytes and its flops, each at that kernel's own rate."""
     mem = hw["mem_gbs"] * 1e9
     plan = gemm_plan(rows, n_out, n_in, int4)
+    weight_bytes_ = n_out * n_in * (0.5 + 4.0 / 64 if int4 else 2.0)
     if plan is not None:
         rate = hw["int4_tflops"] if int4 else hw["fp16_tflops"]
         group = CUS * 2.0 * 256 * 256 * 64 / (rate * 1e12)
         waves = -(-plan["workgroups"] // CUS)
         seconds = waves * (plan["groups_per_split"] * plan["tile_rows"] / 256 * group + hw["gemm_wg_us"] * 1e-6)
+        # no faster than its weight stream (an fp16 GEMM of few rows is bound there)
+        seconds = max(seconds, weight_bytes_ / mem + hw["gemm_wg_us"] * 1e-6)
         if plan["splits"] > 1:
             seconds += 2.0 * plan["splits"] * rows * n_out * 4.0 / mem
     else:
-        weight_bytes_ = n_out * n_in * (0.5 + 4.0 / 64 if int4 else 2.0)
-        seconds = (hw["gemm_wg_us"] * 1e-6 + weight_bytes_ / (hw["staged_gbs"] * 1e9)
+        seconds = (hw["staged_us"] * 1e-6 + weight_bytes_ / (hw["staged_gbs"] * 1e9)
                    + 2.0 * rows * n_out * n_in / (hw["staged_tflops"] * 1e12))
     return _kernel(seconds, hw)
 

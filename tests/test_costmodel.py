@@ -57,10 +57,10 @@ class _Shape:
 
 FREE = dict(attn_gbs=1e12, mem_gbs=1e12, link_gbs=16.0, int4_tflops=1e12, fp16_tflops=1e12, launch_us=0.0,
             hbm_bytes=1e15, host_bytes=1e15, disk_gbs=1e12, disk_bytes=1e15, gemm_wg_us=0.0, staged_tflops=1e12,
-            staged_gbs=1e12)
+            staged_gbs=1e12, staged_us=0.0)
 MI355X = dict(attn_gbs=6250.0, mem_gbs=7100.0, link_gbs=57.2, int4_tflops=1340.0, fp16_tflops=1400.0,
               launch_us=4.0, hbm_bytes=280e9, host_bytes=270e9, disk_gbs=7.4, disk_bytes=80e9, gemm_wg_us=25.0,
-              staged_tflops=1700.0, staged_gbs=3230.0)
+              staged_tflops=1700.0, staged_gbs=3230.0, staged_us=10.0)
 
 
 def test_free_compute_reduces_to_the_printed_simulator():
@@ -137,7 +137,8 @@ def test_images_on_disk():
 def test_gemm_plan_splits_and_tile_heights():
     """The planner rule at the decode shapes: QKV of OPT-30B fills one wave with 192-row tiles,
     fc1 with 256-row ones; the out-projection's 56 tiles split K four ways (224 workgroups);
-    at 256 rows the OPT-6.7B GEMMs split 4 to 16 ways; 128 rows take the register-staged kernel."""
+    at 256 rows the OPT-6.7B GEMMs split 4 to 16 ways; at 128 rows or fewer int4 GEMMs take
+    128- or 64-row tiles (the taller on a tie), fp16 ones 64-row tiles."""
     p = costmodel.gemm_plan(512, 21504, 7168, True)
     assert (p["tile_rows"], p["splits"], p["workgroups"]) == (192, 1, 252)
     p = costmodel.gemm_plan(512, 28672, 7168, True)
@@ -146,7 +147,14 @@ def test_gemm_plan_splits_and_tile_heights():
     assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 4, 224, 28)
     assert [costmodel.gemm_plan(256, n, k, True)["splits"]
             for n, k in ((12288, 4096), (4096, 4096), (16384, 4096), (4096, 16384))] == [4, 8, 4, 16]
-    assert costmodel.gemm_plan(128, 4096, 4096, True) is None
+    p = costmodel.gemm_plan(128, 4096, 4096, True)
+    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (64, 8, 256)
+    # OPT-125m's GEMMs at 8 rows would give 3 to 12 workgroups: register-staged
+    assert all(costmodel.gemm_plan(8, n, k, True) is None for n, k in ((2304, 768), (768, 768), (3072, 768),
+                                                                        (768, 3072)))
+    assert [costmodel.gemm_plan(r, 28672, 7168, True)["tile_rows"] for r in (8, 64, 128)] == [64, 64, 128]
+    p = costmodel.gemm_plan(8, 50272, 7168, False)
+    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (64, 1, 197)
     p = costmodel.gemm_plan(512, 50272, 7168, False)  # the fp16 LM head: 256-row tiles, two waves
     assert (p["tile_rows"], p["splits"], p["workgroups"]) == (256, 1, 394)
     assert costmodel.gemm_plan(512, 50200, 7168, False) is None  # N not a multiple of 32
@@ -162,29 +170,39 @@ def test_gemm_in_whole_waves_of_full_tiles_runs_at_the_steady_rate():
 
 
 def test_gemm_fixed_cost_counts_once_per_wave():
-    hw = dict(MI355X, int4_tflops=1e30, launch_us=0.0, gemm_wg_us=25.0)
+    hw = dict(MI355X, int4_tflops=1e30, mem_gbs=1e30, launch_us=0.0, gemm_wg_us=25.0)
     assert costmodel.gemm_time(512, 32768, 4096, True, hw) == pytest.approx(25e-6, rel=1e-9)
     assert costmodel.gemm_time(1024, 32768, 4096, True, hw) == pytest.approx(50e-6, rel=1e-9)
 
 
 def test_split_gemm_pays_its_partials_twice():
-    """With free compute, a GEMM whose K loop is split costs its fp32 partials (splits x rows x N)
-    written once and read once at the streaming rate; an unsplit one costs nothing."""
+    """With free compute and no fixed cost, a GEMM costs its weight stream, and a GEMM whose K loop
+    is split also its fp32 partials (splits x rows x N) written once and read once, all at the
+    streaming rate."""
     hw = dict(MI355X, int4_tflops=1e30, launch_us=0.0, gemm_wg_us=0.0)
-    assert costmodel.gemm_time(512, 7168, 7168, True, hw) == pytest.approx(2 * 4 * 512 * 7168 * 4 / 7100e9,
-                                                                           rel=1e-12)
-    assert costmodel.gemm_time(512, 28672, 7168, True, hw) < 1e-12
+    weights = 7168 * 7168 * 0.5625 / 7100e9
+    assert costmodel.gemm_time(512, 7168, 7168, True, hw) == pytest.approx(
+        weights + 2 * 4 * 512 * 7168 * 4 / 7100e9, rel=1e-12)
+    assert costmodel.gemm_time(512, 28672, 7168, True, hw) == pytest.approx(4 * weights, rel=1e-12)
 
 
 def test_register_staged_gemm_limits():
-    """At 128 rows or fewer: with free flops and no fixed cost a GEMM is its weight bytes at the
-    kernel's read rate (int4 codes and params, or fp16); each added row adds exactly its flops."""
-    hw = dict(MI355X, launch_us=0.0, gemm_wg_us=0.0, staged_tflops=1e30)
-    assert costmodel.gemm_time(128, 4096, 4096, True, hw) == pytest.approx(4096 * 4096 * 0.5625 / 3230e9, rel=1e-12)
-    assert costmodel.gemm_time(8, 4096, 4096, False, hw) == pytest.approx(4096 * 4096 * 2.0 / 3230e9, rel=1e-12)
+    """fp16 weights whose N is not a multiple of 32: with free flops and no fixed cost a GEMM is its
+    weight bytes at the kernel's read rate; each added row adds exactly its flops."""
+    hw = dict(MI355X, launch_us=0.0, staged_us=0.0, staged_tflops=1e30)
+    assert costmodel.gemm_plan(128, 4004, 4096, False) is None
+    assert costmodel.gemm_time(128, 4004, 4096, False, hw) == pytest.approx(4004 * 4096 * 2.0 / 3230e9, rel=1e-12)
     hw = dict(MI355X, launch_us=0.0)
-    step = costmodel.gemm_time(65, 4096, 4096, True, hw) - costmodel.gemm_time(64, 4096, 4096, True, hw)
-    assert step == pytest.approx(2.0 * 4096 * 4096 / 1700e12, rel=1e-9)
+    step = costmodel.gemm_time(65, 4004, 4096, False, hw) - costmodel.gemm_time(64, 4004, 4096, False, hw)
+    assert step == pytest.approx(2.0 * 4004 * 4096 / 1700e12, rel=1e-9)
+
+
+def test_pipelined_gemm_is_no_faster_than_its_weight_stream():
+    """With free flops, the fp16 LM head of OPT-30B at 8 rows (one wave, unsplit) costs its weights
+    read once at the streaming rate plus the fixed cost."""
+    hw = dict(MI355X, launch_us=0.0, fp16_tflops=1e30)
+    assert costmodel.gemm_time(8, 50272, 7168, False, hw) == pytest.approx(50272 * 7168 * 2.0 / 7100e9 + 25e-6,
+                                                                           rel=1e-12)
 
 
 def test_fp16_gemm_in_whole_waves_runs_at_the_fp16_steady_rate():

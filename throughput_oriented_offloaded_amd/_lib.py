@@ -55,7 +55,7 @@ class RunConfig(ctypes.Structure):
 class HW(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in ("attn_gbs", "mem_gbs", "link_gbs", "int4_tflops", "fp16_tflops",
                                                  "launch_us", "hbm_bytes", "host_bytes", "disk_gbs", "disk_bytes",
-                                                 "gemm_wg_us", "staged_tflops", "staged_gbs")]
+                                                 "gemm_wg_us", "staged_tflops", "staged_gbs", "staged_us")]
 
 
 class Estimate(ctypes.Structure):

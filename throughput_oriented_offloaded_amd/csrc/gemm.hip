@@ -9,20 +9,24 @@
 // "2. The Zig-Zag Block Schedule").
 //
 // gfx950 design (two kernels, fp32 accumulation in v_mfma_f32_32x32x16_f16):
-//  * k_gemm_w4_256 / k_gemm_w4_192 (int4 weights, M > 128; the decode and
-//    prefill path): 256 x 256 or 192 x 256 tiles, eight wavefronts (two per
+//  * k_gemm_w4_256 / k_gemm_w4_192 (int4 weights; the decode and prefill
+//    path above 128 rows): 256 x 256 or 192 x 256 tiles, eight wavefronts (two per
 //    SIMD), activations, codes and params fed through a 3-stage LDS ring by
 //    direct-to-LDS loads; described at the kernel body (gemm_w4_body).
-//    k_gemm_f16_256 is the same body on fp16 weights (LM head and fp16 host
-//    tier above 128 rows): the weight tile is staged like the activation
-//    tile, in a 2-stage ring.
-//  * k_gemm (M <= 128, and fp16 weights of narrow N): 256-thread
+//    k_gemm_f16_256 is the same body on fp16 weights (LM head, fp16 host
+//    tier): the weight tile is staged like the activation tile, in a 2-stage
+//    ring.
+//    At 128 rows or fewer the same bodies run on 128- or 64-row tiles (int4)
+//    and 64-row tiles (fp16), two workgroups per CU where LDS allows.
+//  * k_gemm (small GEMMs of 128 rows or fewer that would give the pipelined
+//    kernel fewer than 128 workgroups; fp16 weights whose N is not a
+//    multiple of 32): 256-thread
 //    workgroups as a 2x2 grid of wavefronts, each owning a (BM/2) x (BN/2)
-//    output tile; the activation tile (BM x 64, one quantization group of K)
-//    is double-buffered in LDS with 16-byte chunks XOR-swizzled by row, and
-//    weights go from HBM straight to registers: the int4 store is pre-tiled so
-//    that one 16-byte load per lane brings exactly the 32 nibbles that lane
-//    feeds to four MFMA K-steps as its B operand.
+//    output tile; the activation tile (BM x 64, one K-group) is
+//    double-buffered in LDS with 16-byte chunks XOR-swizzled by row, and
+//    weights go from HBM straight to registers.
+//  * The int4 store is pre-tiled so that one 16-byte load brings exactly the
+//    32 nibbles a lane feeds to four MFMA K-steps as its B operand.
 //  * Dequantization (dequant_word): masked nibbles become exact fp16 codes by
 //    one fp8 -> fp16 convert per pair, then one v_pk_fma_f16 with (scale,
 //    zero) rounds once, so each weight equals fp16(zero + c*scale).
@@ -254,7 +258,7 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 // F16: fp16 weights W[N][K] instead of int4 codes. W's tile (BN rows x 64 fp16)
 // has the layout of the A tile and the MFMA B fragment is read exactly as an A
 // fragment; both tiles need 64 KiB per stage, so the ring has two stages.
-template <int BM_, bool F16 = false> struct W4 {
+template <int BM_, bool F16 = false, int S_ = 0> struct W4 {
     static constexpr int BM = BM_, BN = 256, WAVES = 8;
     static constexpr int RB = BM / 2;                   // rows per wave (2 wave rows)
     static constexpr int MB = RB / 32;                  // 32-row blocks per wave
@@ -264,7 +268,7 @@ template <int BM_, bool F16 = false> struct W4 {
     static constexpr int W_BYTES = F16 ? BN * 128 : (BN / 32) * 1024;
     static constexpr int P_BYTES = F16 ? 0 : (BN / 32) * 256; // per column block: 64 x (scale, zero)
     static constexpr int STAGE = A_BYTES + W_BYTES + P_BYTES;
-    static constexpr int S = F16 ? 2 : 3;               // ring stages
+    static constexpr int S = S_ ? S_ : F16 ? 2 : 3;     // ring stages
     static constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
     static constexpr int WL = F16 ? (BN / 8) / WAVES : 0; // fp16: 1 KiB W chunks per wave per stage
     static constexpr int LPS = AL + (F16 ? WL : 2);     // loads per wave per stage: A chunks, W chunks or codes and params
@@ -280,24 +284,31 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int a_pos(int row, int ch) { return ch ^ ((row ^ (row >> 3)) & 7); }
 
 // Wait until at most `younger` stages' worth (LPS loads each) of this wave's
-// vector-memory loads are outstanding (younger is 0 or 1 with three stages).
-template <int LPS_>
-__device__ __forceinline__ void wait_vm_loads(int younger)
+// vector-memory loads are outstanding (0 <= younger <= S - 2).
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt()
 {
     // s_waitcnt simm16 on gfx9: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
-    constexpr int n1 = LPS_;
-    constexpr int e1 = (n1 & 15) | ((n1 >> 4) << 14) | (7 << 4) | (15 << 8);
-    static_assert(n1 < 64, "vmcnt holds 6 bits");
-    if (younger >= 1)
-        __builtin_amdgcn_s_waitcnt(e1);
-    else
-        __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+    static_assert(N_ < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N_ & 15) | ((N_ >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BM_, bool F16>
+template <int LPS_, int S_>
+__device__ __forceinline__ void wait_vm_loads(int younger)
+{
+    static_assert(S_ >= 2 && S_ <= 4, "two to four ring stages");
+    if (S_ == 4 && younger >= 2)
+        wait_vmcnt<(S_ == 4 ? 2 * LPS_ : 0)>();
+    else if (S_ >= 3 && younger >= 1)
+        wait_vmcnt<(S_ >= 3 ? LPS_ : 0)>();
+    else
+        wait_vmcnt<0>();
+}
+
+template <int BM_, bool F16, int S_ = 0>
 __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &tm)
 {
-    using C = W4<BM_, F16>;
+    using C = W4<BM_, F16, S_>;
     constexpr int BM = C::BM, BN = C::BN, WAVES = C::WAVES, RB = C::RB, MB = C::MB, NB = C::NB;
     constexpr int A_BYTES = C::A_BYTES, W_BYTES = C::W_BYTES, STAGE = C::STAGE, S = C::S, AL = C::AL;
     constexpr int WL = C::WL;
@@ -385,7 +396,7 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
             issue(s_, g0 + s_);
 
     for (int it = 0; it < nst; it++) {
-        wait_vm_loads<C::LPS>(min(S - 2, nst - 1 - it));
+        wait_vm_loads<C::LPS, S>(min(S - 2, nst - 1 - it));
         __builtin_amdgcn_s_barrier();
         if (it + S - 1 < nst)
             issue((it + S - 1) % S, g0 + it + S - 1);
@@ -538,6 +549,11 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
 __global__ void __launch_bounds__(512, 1) k_gemm_w4_256(GemmArgs g, TileMap tm) { gemm_w4_body<256, false>(g, tm); }
 __global__ void __launch_bounds__(512, 1) k_gemm_w4_192(GemmArgs g, TileMap tm) { gemm_w4_body<192, false>(g, tm); }
 __global__ void __launch_bounds__(512, 1) k_gemm_f16_256(GemmArgs g, TileMap tm) { gemm_w4_body<256, true>(g, tm); }
+// 128 rows or fewer: short tiles, two workgroups per CU where LDS and registers allow
+__global__ void __launch_bounds__(512, 2) k_gemm_w4_128(GemmArgs g, TileMap tm) { gemm_w4_body<128, false>(g, tm); }
+__global__ void __launch_bounds__(512, 2) k_gemm_w4_64(GemmArgs g, TileMap tm) { gemm_w4_body<64, false>(g, tm); }
+// fp16, 128 rows or fewer: bound by the weight stream, so a third stage in flight pays
+__global__ void __launch_bounds__(512, 1) k_gemm_f16_64(GemmArgs g, TileMap tm) { gemm_w4_body<64, true, 3>(g, tm); }
 
 __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
 {
@@ -619,16 +635,20 @@ struct Plan {
     TileMap tm;
 };
 
-// Tuning overrides (read once): TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" selects the
-// register-staged kernel for every M > 64; TOD_GEMM_SPLIT = workgroup count below which the
-// K loop is split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined int4 kernel's tile height to 256 | 192;
-// TOD_GEMM_F16PIPE = 0 keeps fp16 weights on the register-staged kernel.
+// Tuning overrides (read once): TOD_GEMM_SPLIT = workgroup count below which the K loop is
+// split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined int4 tile height above 128 rows to 256 | 192;
+// TOD_GEMM_SMALL_BM = 64 | 128 pins it at 128 rows or fewer; TOD_GEMM_F16PIPE = 0 keeps fp16
+// weights on the register-staged kernel; TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" puts
+// every GEMM on it with that tile for M > 64.
 struct Tuning {
     int bm = 0, bn = 0, split_fill = -1;
     int bm192 = -1; // pipelined tile height: -1 cost model, 0 always 256, 1 always 192
-    bool f16_pipe = true; // fp16 weights on the pipelined kernel above 128 rows
+    bool f16_pipe = true;   // fp16 weights on the pipelined kernel
+    int small_bm = 0;       // pin the int4 tile height at 128 rows or fewer (64 or 128)
     Tuning()
     {
+        if (const char *t = getenv("TOD_GEMM_SMALL_BM"))
+            small_bm = atoi(t) == 64 || atoi(t) == 128 ? atoi(t) : 0;
         if (const char *t = getenv("TOD_GEMM_F16PIPE"))
             f16_pipe = atoi(t) != 0;
         if (const char *t = getenv("TOD_GEMM_BM192"))
@@ -679,41 +699,49 @@ Plan plan_gemm(int M, int N, int K, bool int4)
 {
     Plan p;
     const Tuning &tu = tuning();
-    p.pipelined = M > 128 && !tu.bm && (int4 || (tu.f16_pipe && N % 32 == 0));
-    if (p.pipelined && !int4) {
-        // fp16 weights: 256 x 256 tiles only
-        p.bm = 256;
+    // the pipelined kernel unless fp16 N is not a multiple of 32 (or a tuning override)
+    p.pipelined = !tu.bm && (int4 || (tu.f16_pipe && N % 32 == 0));
+    if (p.pipelined) {
+        // Above 128 rows, 256 x 256 tiles halve the activation re-reads per MFMA against
+        // 256 x 128, at the price of fewer workgroups; narrow N is split along K instead.
+        // 192-row tiles are taken where their extra workgroups finish the GEMM sooner: the
+        // cost is waves of workgroups x rows x K-groups per workgroup (one 256-CU wave of
+        // 192-row tiles takes 3/4 of one of 256-row tiles). At 128 rows or fewer the
+        // same cost picks 128- or 64-row tiles: there the weight stream, which the ring
+        // keeps two K-groups deep, sets the pace. fp16 weights: 256- or 64-row tiles.
         p.bn = 256;
-    } else if (p.pipelined) {
-        // 256 x 256 tiles halve the activation re-reads per MFMA against 256 x 128,
-        // at the price of fewer workgroups; narrow N is split along K instead.
-        // 192-row tiles are taken where their extra workgroups finish the GEMM
-        // sooner: the cost is waves of workgroups x rows x K-groups per workgroup
-        // (one 256-CU wave of 192-row tiles takes 3/4 of one of 256-row tiles).
-        p.bn = 256;
         p.bm = 256;
-        if (tu.bm192 != 0) {
-            long best = -1;
-            for (int bm : {256, 192}) {
-                const Plan q = split_plan(M, N, K, bm, 256, true);
-                const long waves = (q.tm.total + 255) / 256;
-                const long cost = waves * bm * q.tm.groups_per_split;
-                if ((tu.bm192 < 0 && (best < 0 || cost < best)) || (tu.bm192 > 0 && bm == 192)) {
-                    best = cost;
-                    p.bm = bm;
-                }
+        int cand[2] = {256, 192};
+        if (!int4)
+            cand[0] = cand[1] = M > 128 ? 256 : 64;
+        else if (M <= 128) {
+            cand[0] = tu.small_bm ? tu.small_bm : 128;
+            cand[1] = tu.small_bm ? tu.small_bm : 64;
+        } else if (tu.bm192 >= 0) {
+            cand[0] = cand[1] = tu.bm192 ? 192 : 256;
+        }
+        long best = -1;
+        int wgs = 0;
+        for (int bm : cand) {
+            const Plan q = split_plan(M, N, K, bm, 256, true);
+            const long waves = (q.tm.total + 255) / 256;
+            const long cost = waves * bm * q.tm.groups_per_split;
+            if (best < 0 || cost < best) {
+                best = cost;
+                p.bm = bm;
+                wgs = q.tm.total;
             }
         }
-    } else if (M <= 64) {
-        // 128 x 128 tiles keep a wave at ~150 registers, so three workgroups share a
-        // CU and hide each other's load latency.
-        p.bm = 64;
-        p.bn = 64;
-    } else {
-        p.bm = 128;
-        p.bn = 128;
+        // a small GEMM at 128 rows or fewer whose 256-wide tiles would leave most CUs idle
+        // (fewer than 128 workgroups) runs on the register-staged kernel's 64-wide tiles
+        if (int4 && M <= 128 && wgs < 128)
+            p.pipelined = false;
     }
-    if (tu.bm && M > 64) {
+    if (!p.pipelined) {
+        // register-staged kernel: 64 x 64 tiles for a few rows, 128 x 128 above
+        p.bm = p.bn = M <= 64 ? 64 : 128;
+    }
+    if (!p.pipelined && tu.bm && M > 64) {
         p.bm = tu.bm;
         p.bn = tu.bn;
     }
@@ -759,12 +787,19 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         p.tm.total = p.tm.mt * p.tm.nt;
     }
     const dim3 grid(p.tm.total), block(256);
-    if (p.pipelined && !int4)
-        hipLaunchKernelGGL(k_gemm_f16_256, grid, dim3(64 * W4<256, true>::WAVES), 0, st, g, p.tm);
+    const dim3 wg8(64 * W4<256>::WAVES); // every pipelined kernel runs eight wavefronts
+    if (p.pipelined && !int4 && p.bm == 64)
+        hipLaunchKernelGGL(k_gemm_f16_64, grid, wg8, 0, st, g, p.tm);
+    else if (p.pipelined && !int4)
+        hipLaunchKernelGGL(k_gemm_f16_256, grid, wg8, 0, st, g, p.tm);
+    else if (p.pipelined && p.bm == 64)
+        hipLaunchKernelGGL(k_gemm_w4_64, grid, wg8, 0, st, g, p.tm);
+    else if (p.pipelined && p.bm == 128)
+        hipLaunchKernelGGL(k_gemm_w4_128, grid, wg8, 0, st, g, p.tm);
     else if (p.pipelined && p.bm == 192)
-        hipLaunchKernelGGL(k_gemm_w4_192, grid, dim3(64 * W4<192>::WAVES), 0, st, g, p.tm);
+        hipLaunchKernelGGL(k_gemm_w4_192, grid, wg8, 0, st, g, p.tm);
     else if (p.pipelined)
-        hipLaunchKernelGGL(k_gemm_w4_256, grid, dim3(64 * W4<256>::WAVES), 0, st, g, p.tm);
+        hipLaunchKernelGGL(k_gemm_w4_256, grid, wg8, 0, st, g, p.tm);
     else {
 #define TOD_GEMM_CASE(BM_, BN_, MINW_)                                                               \
     if (p.bm == BM_ && p.bn == BN_) {                                                                \

@@ -13,19 +13,21 @@
 //
 // Step model at the average decode context c = prompt_len + gen_len / 2:
 //  * each GEMM is priced on the tile plan the library launches for it. The
-//    pipelined kernel (more than 128 rows) runs its workgroups in waves of one
-//    per CU; a wave costs its K-groups per workgroup times the time of one
-//    K-group (the steady int4 or fp16 rate, scaled by the tile's rows) plus a fixed
+//    pipelined kernel (int4 weights; fp16 weights of N a multiple of 32) runs
+//    its workgroups in waves of one per CU; a wave costs its K-groups per
+//    workgroup times the time of one K-group (the steady int4 or fp16 rate,
+//    scaled by the tile's rows) plus a fixed
 //    cost for pipeline fill and epilogue, and a split K loop adds its fp32
-//    partials, written once and read once at the streaming rate. Fitted to the
+//    partials, written once and read once at the streaming rate; no GEMM is
+//    faster than its weight bytes at the streaming rate plus the fixed cost
+//    (the fp16 LM head at a few rows is bound there). Fitted to the
 //    measured decode GEMMs at 512 rows (OPT-30B) and 256 rows (OPT-6.7B), this
 //    is within about 15% on each of them, where one flat rate misses the
 //    256-row GEMMs by up to 2x (their K loops split 4 to 16 ways). The
-//    register-staged kernel (128 rows or fewer; fp16 weights of N not a
-//    multiple of 32) costs the same fixed cost plus its weight bytes and its
-//    flops at that kernel's own effective rates (fitted at 64 and 128 rows:
-//    it reads weights at well under HBM bandwidth). Every kernel costs at
-//    least one launch floor;
+//    register-staged kernel (small GEMMs of 128 rows or fewer; fp16 weights of
+//    N not a multiple of 32) costs its own fixed time plus its weight bytes
+//    and its flops at that kernel's effective rates (it reads weights at well
+//    under HBM bandwidth). Every kernel costs at least one launch floor;
 //  * decode attention moves M * heads * (c * (d + d/8) + 4d) bytes at the
 //    attention rate; the KV append reads 4d and writes d + d/8 bytes per
 //    (row, head); one LayerNorm per step (the others are fused); the LM head is
@@ -151,16 +153,19 @@ double gemm_time(int M, int N, int K, bool int4, const tod_hw *hw)
     const GemmPlanInfo p = gemm_plan_info(M, N, K, int4);
     const double mem = hw->mem_gbs * 1e9;
     double t;
+    const double wb = (double)N * K * (int4 ? 0.5625 : 2.0);
     if (p.pipelined) {
         const double rate = (int4 ? hw->int4_tflops : hw->fp16_tflops) * 1e12;
         const double t_group = kCUs * 2.0 * 256.0 * 256.0 * 64.0 / rate;
         const double waves = std::ceil(p.workgroups / kCUs);
         t = waves * (p.groups_per_split * (p.bm / 256.0) * t_group + hw->gemm_wg_us * 1e-6);
+        const double t_read = wb / mem + hw->gemm_wg_us * 1e-6; // few rows: the weight stream
+        t = t > t_read ? t : t_read;
         if (p.splits > 1)
             t += 2.0 * p.splits * (double)M * N * 4.0 / mem;
     } else {
-        const double flop = 2.0 * M * (double)N * K, wb = (double)N * K * (int4 ? 0.5625 : 2.0);
-        t = hw->gemm_wg_us * 1e-6 + wb / (hw->staged_gbs * 1e9) + flop / (hw->staged_tflops * 1e12);
+        const double flop = 2.0 * M * (double)N * K;
+        t = hw->staged_us * 1e-6 + wb / (hw->staged_gbs * 1e9) + flop / (hw->staged_tflops * 1e12);
     }
     return kernel_time(t, hw);
 }
@@ -242,6 +247,7 @@ void default_hw(tod_hw *hw)
     hw->gemm_wg_us = 25.0;    // fixed cost per wave of pipelined GEMM workgroups (fitted)
     hw->staged_tflops = 1700.0; // register-staged GEMM (<= 128 rows): flops, fitted
     hw->staged_gbs = 3230.0;   // register-staged GEMM: weight bytes, fitted
+    hw->staged_us = 10.0;      // register-staged GEMM: fixed time (OPT-125m GEMMs at 8 rows)
 }
 
 int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out)
@@ -250,7 +256,7 @@ int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, cons
         return TOD_EINVAL;
     if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
           hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0 && hw->gemm_wg_us >= 0.0 &&
-          hw->staged_tflops > 0.0 && hw->staged_gbs > 0.0))
+          hw->staged_tflops > 0.0 && hw->staged_gbs > 0.0 && hw->staged_us >= 0.0))
         return TOD_EINVAL;
     step_model(cfg, run, hw, out);
     footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes, &out->disk_bytes);
