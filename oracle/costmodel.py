@@ -101,16 +101,18 @@ def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
     register-staged kernel runs: fp16 weights whose N is not a multiple of 32, or int4 weights at
     128 rows or fewer whose pipelined plan would launch fewer than 128 workgroups).
 
-    Tiles are 256 outputs wide. int4 tiles are 256 or 192 rows tall above 128 rows and 128 or 64
-    rows at 128 rows or fewer; fp16 tiles are 256 rows tall above 128 rows and 64 below. The K
-    loop (K-groups of 64) is split in powers of two while the tiles times the splits stay below
-    160 workgroups and each split keeps at least 8 K-groups. Of the two tile heights the one
-    with the fewer waves of 256 workgroups x tile rows x K-groups per workgroup is taken, the
-    taller on a tie."""
+    Tiles are 256 outputs wide. int4 tiles are 256, 192 or 128 rows tall above 128 rows and 128
+    or 64 rows at 128 rows or fewer; fp16 tiles are 256 rows tall above 128 rows and 64 below.
+    The K loop (K-groups of 64) is split in powers of two while the tiles times the splits stay
+    below 160 workgroups and each split keeps at least 8 K-groups. Of the tile heights the one
+    with the least predicted time is taken, the earlier listed on a tie, where that time counts
+    1.6 us per K-group of a 256 x 256 tile (times rows / 256 and an efficiency loss of 1.1 at 128
+    rows and 1.5 at 64) per wave of 256 workgroups, 25 us per wave of resident workgroups (two
+    per CU at 128 rows or fewer), and split-K partials written and read at 7.1 TB/s."""
     if not int4 and n_out % 32:
         return None
     if int4:
-        heights = (256, 192) if rows > 128 else (128, 64)
+        heights = (256, 192, 128) if rows > 128 else (128, 64)
     else:
         heights = (256,) if rows > 128 else (64,)
     groups = n_in // 64
@@ -123,7 +125,12 @@ def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
         per_split = -(-groups // splits)
         splits = -(-groups // per_split)
         workgroups = tiles * splits
-        cost = -(-workgroups // CUS) * tile_rows * per_split
+        loss = 1.5 if tile_rows <= 64 else 1.1 if tile_rows <= 128 else 1.0
+        slots = 2 * CUS if tile_rows <= 128 else CUS
+        cost = (-(-workgroups // CUS) * per_split * (tile_rows / 256.0) * 1.6 * loss
+                + -(-workgroups // slots) * 25.0)
+        if splits > 1:
+            cost += 2.0 * splits * rows * n_out * 4.0 / 7.1e6
         if best is None or cost < best["cost"]:
             best = dict(cost=cost, tile_rows=tile_rows, splits=splits, groups_per_split=per_split,
                         workgroups=workgroups)
@@ -145,8 +152,11 @@ def gemm_time(rows: int, n_out: int, n_in: int, int4: bool, hw: dict) -> float:
     if plan is not None:
         rate = hw["int4_tflops"] if int4 else hw["fp16_tflops"]
         group = CUS * 2.0 * 256 * 256 * 64 / (rate * 1e12)
-        waves = -(-plan["workgroups"] // CUS)
-        seconds = waves * (plan["groups_per_split"] * plan["tile_rows"] / 256 * group + hw["gemm_wg_us"] * 1e-6)
+        rows_ = plan["tile_rows"]
+        loss = 1.0 if not int4 else 1.5 if rows_ <= 64 else 1.1 if rows_ <= 128 else 1.0
+        slots = 2 * CUS if int4 and rows_ <= 128 else CUS
+        seconds = (-(-plan["workgroups"] // CUS) * plan["groups_per_split"] * (rows_ / 256) * loss * group
+                   + -(-plan["workgroups"] // slots) * hw["gemm_wg_us"] * 1e-6)
         # no faster than its weight stream (an fp16 GEMM of few rows is bound there)
         seconds = max(seconds, weight_bytes_ / mem + hw["gemm_wg_us"] * 1e-6)
         if plan["splits"] > 1:

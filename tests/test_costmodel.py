@@ -136,17 +136,20 @@ def test_images_on_disk():
 
 def test_gemm_plan_splits_and_tile_heights():
     """The planner rule at the decode shapes: QKV of OPT-30B fills one wave with 192-row tiles,
-    fc1 with 256-row ones; the out-projection's 56 tiles split K four ways (224 workgroups);
-    at 256 rows the OPT-6.7B GEMMs split 4 to 16 ways; at 128 rows or fewer int4 GEMMs take
-    128- or 64-row tiles (the taller on a tie), fp16 ones 64-row tiles."""
+    fc1 with 256-row ones and fc2 splits their 56 tiles' K four ways; the out-projection takes
+    112 tiles of 128 rows split twice (half the partials of 256-row tiles split four ways); at
+    256 rows the OPT-6.7B GEMMs take 128-row tiles split 2 or 8 ways; at 128 rows or fewer int4
+    GEMMs take 128- or 64-row tiles, fp16 ones 64-row tiles."""
     p = costmodel.gemm_plan(512, 21504, 7168, True)
     assert (p["tile_rows"], p["splits"], p["workgroups"]) == (192, 1, 252)
     p = costmodel.gemm_plan(512, 28672, 7168, True)
     assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 1, 224, 112)
+    p = costmodel.gemm_plan(512, 7168, 28672, True)
+    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 4, 224, 112)
     p = costmodel.gemm_plan(512, 7168, 7168, True)
-    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 4, 224, 28)
-    assert [costmodel.gemm_plan(256, n, k, True)["splits"]
-            for n, k in ((12288, 4096), (4096, 4096), (16384, 4096), (4096, 16384))] == [4, 8, 4, 16]
+    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (128, 2, 224, 56)
+    assert [(p["tile_rows"], p["splits"]) for p in (costmodel.gemm_plan(256, n, k, True) for n, k in
+            ((12288, 4096), (4096, 4096), (16384, 4096), (4096, 16384)))] == [(128, 2), (128, 8), (128, 2), (128, 8)]
     p = costmodel.gemm_plan(128, 4096, 4096, True)
     assert (p["tile_rows"], p["splits"], p["workgroups"]) == (64, 8, 256)
     # OPT-125m's GEMMs at 8 rows would give 3 to 12 workgroups: register-staged
@@ -180,10 +183,10 @@ def test_split_gemm_pays_its_partials_twice():
     is split also its fp32 partials (splits x rows x N) written once and read once, all at the
     streaming rate."""
     hw = dict(MI355X, int4_tflops=1e30, launch_us=0.0, gemm_wg_us=0.0)
-    weights = 7168 * 7168 * 0.5625 / 7100e9
-    assert costmodel.gemm_time(512, 7168, 7168, True, hw) == pytest.approx(
+    weights = 7168 * 28672 * 0.5625 / 7100e9  # fc2 of OPT-30B at 512 rows: K split four ways
+    assert costmodel.gemm_time(512, 7168, 28672, True, hw) == pytest.approx(
         weights + 2 * 4 * 512 * 7168 * 4 / 7100e9, rel=1e-12)
-    assert costmodel.gemm_time(512, 28672, 7168, True, hw) == pytest.approx(4 * weights, rel=1e-12)
+    assert costmodel.gemm_time(512, 28672, 7168, True, hw) == pytest.approx(weights, rel=1e-12)
 
 
 def test_register_staged_gemm_limits():

@@ -636,8 +636,9 @@ struct Plan {
 };
 
 // Tuning overrides (read once): TOD_GEMM_SPLIT = workgroup count below which the K loop is
-// split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined int4 tile height above 128 rows to 256 | 192;
-// TOD_GEMM_SMALL_BM = 64 | 128 pins it at 128 rows or fewer; TOD_GEMM_F16PIPE = 0 keeps fp16
+// split; TOD_GEMM_BM192 = 0 | 1 pins the pipelined int4 tile height above 128 rows to 256 | 192
+// and TOD_GEMM_BIG_BM = 128 | 192 | 256 to any of them; TOD_GEMM_SMALL_BM = 64 | 128 pins it at
+// 128 rows or fewer; TOD_GEMM_F16PIPE = 0 keeps fp16
 // weights on the register-staged kernel; TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" puts
 // every GEMM on it with that tile for M > 64.
 struct Tuning {
@@ -645,6 +646,7 @@ struct Tuning {
     int bm192 = -1; // pipelined tile height: -1 cost model, 0 always 256, 1 always 192
     bool f16_pipe = true;   // fp16 weights on the pipelined kernel
     int small_bm = 0;       // pin the int4 tile height at 128 rows or fewer (64 or 128)
+    int big_bm = 0;         // pin the int4 tile height above 128 rows (128, 192 or 256)
     Tuning()
     {
         if (const char *t = getenv("TOD_GEMM_SMALL_BM"))
@@ -653,6 +655,8 @@ struct Tuning {
             f16_pipe = atoi(t) != 0;
         if (const char *t = getenv("TOD_GEMM_BM192"))
             bm192 = atoi(t) > 0 ? 1 : atoi(t) == 0 ? 0 : -1;
+        if (const char *t = getenv("TOD_GEMM_BIG_BM"))
+            big_bm = atoi(t) == 128 || atoi(t) == 192 || atoi(t) == 256 ? atoi(t) : 0;
         if (const char *t = getenv("TOD_GEMM_TILE")) {
             int a = 0, b = 0;
             if (sscanf(t, "%dx%d", &a, &b) == 2 &&
@@ -695,6 +699,23 @@ Plan split_plan(int M, int N, int K, int bm, int bn, bool pipelined)
     return p;
 }
 
+// Predicted microseconds of a pipelined GEMM plan, used only to rank tile heights (the
+// library's cost model prices launches with its own rates). Fitted on MI355X decode GEMMs:
+// one K-group of a 256 x 256 tile takes 1.6 us while every CU runs one such workgroup, a
+// K-group of a shorter tile takes its share of that times the tile's efficiency loss (128
+// rows 1.1, 64 rows 1.5), each wave of resident workgroups (two per CU at 128 rows or fewer)
+// adds 25 us of fill and epilogue, and split-K partials are written and read at 7.1 TB/s.
+double pipelined_plan_us(const TileMap &tm, int bm, int M, int N)
+{
+    const double eff = bm <= 64 ? 1.5 : bm <= 128 ? 1.1 : 1.0;
+    const int slots = bm <= 128 ? 512 : 256;
+    double t = (double)((tm.total + 255) / 256) * tm.groups_per_split * (bm / 256.0) * 1.6 * eff +
+               (double)((tm.total + slots - 1) / slots) * 25.0;
+    if (tm.splits > 1)
+        t += 2.0 * tm.splits * (double)M * N * 4.0 / 7.1e6;
+    return t;
+}
+
 Plan plan_gemm(int M, int N, int K, bool int4)
 {
     Plan p;
@@ -702,32 +723,39 @@ Plan plan_gemm(int M, int N, int K, bool int4)
     // the pipelined kernel unless fp16 N is not a multiple of 32 (or a tuning override)
     p.pipelined = !tu.bm && (int4 || (tu.f16_pipe && N % 32 == 0));
     if (p.pipelined) {
-        // Above 128 rows, 256 x 256 tiles halve the activation re-reads per MFMA against
-        // 256 x 128, at the price of fewer workgroups; narrow N is split along K instead.
-        // 192-row tiles are taken where their extra workgroups finish the GEMM sooner: the
-        // cost is waves of workgroups x rows x K-groups per workgroup (one 256-CU wave of
-        // 192-row tiles takes 3/4 of one of 256-row tiles). At 128 rows or fewer the
-        // same cost picks 128- or 64-row tiles: there the weight stream, which the ring
-        // keeps two K-groups deep, sets the pace. fp16 weights: 256- or 64-row tiles.
+        // Tile height by predicted time (pipelined_plan_us): 256, 192 or 128 rows above
+        // 128 rows, 128 or 64 at 128 rows or fewer; fp16 weights: 256 or 64 rows. Narrow N
+        // is split along K instead of shrinking the tile below 256 columns.
         p.bn = 256;
         p.bm = 256;
-        int cand[2] = {256, 192};
-        if (!int4)
-            cand[0] = cand[1] = M > 128 ? 256 : 64;
-        else if (M <= 128) {
-            cand[0] = tu.small_bm ? tu.small_bm : 128;
-            cand[1] = tu.small_bm ? tu.small_bm : 64;
+        int cand[3] = {256, 192, 128};
+        int nc = 3;
+        if (!int4) {
+            cand[0] = M > 128 ? 256 : 64;
+            nc = 1;
+        } else if (M <= 128) {
+            cand[0] = 128;
+            cand[1] = 64;
+            nc = 2;
+            if (tu.small_bm) {
+                cand[0] = tu.small_bm;
+                nc = 1;
+            }
+        } else if (tu.big_bm) {
+            cand[0] = tu.big_bm;
+            nc = 1;
         } else if (tu.bm192 >= 0) {
-            cand[0] = cand[1] = tu.bm192 ? 192 : 256;
+            cand[0] = tu.bm192 ? 192 : 256;
+            nc = 1;
         }
-        long best = -1;
+        double best = -1.0;
         int wgs = 0;
-        for (int bm : cand) {
+        for (int c = 0; c < nc; c++) {
+            const int bm = cand[c];
             const Plan q = split_plan(M, N, K, bm, 256, true);
-            const long waves = (q.tm.total + 255) / 256;
-            const long cost = waves * bm * q.tm.groups_per_split;
-            if (best < 0 || cost < best) {
-                best = cost;
+            const double t = pipelined_plan_us(q.tm, bm, M, N);
+            if (best < 0.0 || t < best) {
+                best = t;
                 p.bm = bm;
                 wgs = q.tm.total;
             }

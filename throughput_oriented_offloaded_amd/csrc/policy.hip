@@ -16,7 +16,9 @@
 //    pipelined kernel (int4 weights; fp16 weights of N a multiple of 32) runs
 //    its workgroups in waves of one per CU; a wave costs its K-groups per
 //    workgroup times the time of one K-group (the steady int4 or fp16 rate,
-//    scaled by the tile's rows) plus a fixed
+//    scaled by the tile's rows, and for 128- and 64-row int4 tiles by their
+//    efficiency loss of 1.1 and 1.5; those sit two per CU and share one fixed
+//    cost per pair) plus a fixed
 //    cost for pipeline fill and epilogue, and a split K loop adds its fp32
 //    partials, written once and read once at the streaming rate; no GEMM is
 //    faster than its weight bytes at the streaming rate plus the fixed cost
@@ -157,8 +159,11 @@ double gemm_time(int M, int N, int K, bool int4, const tod_hw *hw)
     if (p.pipelined) {
         const double rate = (int4 ? hw->int4_tflops : hw->fp16_tflops) * 1e12;
         const double t_group = kCUs * 2.0 * 256.0 * 256.0 * 64.0 / rate;
-        const double waves = std::ceil(p.workgroups / kCUs);
-        t = waves * (p.groups_per_split * (p.bm / 256.0) * t_group + hw->gemm_wg_us * 1e-6);
+        // shorter int4 tiles lose some efficiency per flop and sit two per CU
+        const double eff = !int4 ? 1.0 : p.bm <= 64 ? 1.5 : p.bm <= 128 ? 1.1 : 1.0;
+        const double slots = int4 && p.bm <= 128 ? 2.0 * kCUs : kCUs;
+        t = std::ceil(p.workgroups / kCUs) * p.groups_per_split * (p.bm / 256.0) * eff * t_group +
+            std::ceil(p.workgroups / slots) * hw->gemm_wg_us * 1e-6;
         const double t_read = wb / mem + hw->gemm_wg_us * 1e-6; // few rows: the weight stream
         t = t > t_read ? t : t_read;
         if (p.splits > 1)
