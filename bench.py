@@ -397,7 +397,8 @@ def main():
                     help="HBM-weight workloads: trailing layers whose KV cache lives in pinned host memory "
                          "(default 0; not the headline configuration)")
     ap.add_argument("--weight-file", default="",
-                    help="host tiers only: keep the streamed images in this file (created; O_DIRECT reads)")
+                    help="host tiers only: keep the streamed images in this file (created or truncated; buffered "
+                         "reads, each image dropped from the page cache after use)")
     ap.add_argument("--hbm-layers", type=int, default=0,
                     help="host tiers only: leading layers whose weights stay resident in HBM (default 0)")
     ap.add_argument("--host-layers", type=int, default=8,
