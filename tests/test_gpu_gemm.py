@@ -61,6 +61,38 @@ def test_linear_w4_matches_oracle(rows, k, n, epi):
     assert (u == 0).mean() > 0.99
 
 
+SHORT_CASES = [  # rows, in, out, epilogue: 128 rows or fewer on the pipelined kernel's 64- and 128-row tiles
+    (8, 2048, 32768, "relu"), (64, 1024, 20480, "bias"), (100, 2048, 16384, "res"), (128, 1024, 32768, "none"),
+    (37, 4096, 16384, "res"), (128, 7168, 7168, "bias"),
+]
+
+
+@pytest.mark.parametrize("rows,k,n,epi", SHORT_CASES)
+def test_linear_w4_short_tiles(rows, k, n, epi):
+    """Few rows and wide N: 64- or 128-row tiles (ragged M at 37 and 100 rows), with and without a
+    split K loop; the oracle checks the first, middle and last rows."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    print(f"linear_w4 short rows={rows} in={k} out={n} {epi}", flush=True)
+    seed = rows * 13 + k + n
+    w = synth.normal_f16(seed, 0, (n, k), 0.0, 0.02)
+    a = synth.normal_f16(seed, 1, (rows, k), 0.0, 1.0)
+    bias = synth.normal_f16(seed, 2, (n,), 0.0, 0.1) if epi != "none" else None
+    res = synth.normal_f16(seed, 3, (rows, n), 0.0, 1.0) if epi == "res" else None
+    codes, scale, zero = _gpu_codes(w, torch)
+    y = torch.empty((rows, n), dtype=torch.float16, device="cuda")
+    tod.linear_w4(to_dev(a, torch), codes, scale, zero, n, y, bias=to_dev(bias, torch) if bias is not None else None,
+                  residual=to_dev(res, torch) if res is not None else None, relu=epi == "relu")
+    torch.cuda.synchronize()
+    sample = np.unique(np.array([0, rows // 2, rows - 1]))
+    oc, os_, oz = oracle.quantize_groupwise(w)
+    ref = oracle.linear_w4(a[sample], oc, os_, oz, n, bias=bias, residual=res[sample] if res is not None else None,
+                           relu=epi == "relu")
+    u = ulps(to_np16(y)[sample], ref)
+    assert u.max() <= 2, f"max {u.max()} ulp"
+    assert (u == 0).mean() > 0.99
+
+
 def test_linear_residual_in_place():
     """The decode path adds the residual into the same buffer it writes."""
     torch = torch_cuda()
