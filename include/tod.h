@@ -288,7 +288,7 @@ int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t 
               const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
               void *stream);
 
-/* linear_f16: as linear_w4 with fp16 weights d_w [out][in] (the LM head's and the host tier's path). */
+/* linear_f16: as linear_w4 with fp16 weights d_w [out][in] (the LM head's and the fp16 host tier's GEMM). */
 int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_t *d_w, const uint16_t *d_bias,
                const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream);
 

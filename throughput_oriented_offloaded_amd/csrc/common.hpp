@@ -274,7 +274,7 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
 size_t gemm_workspace_bytes(int M, int N, int K, bool int4);
 // The tile plan launch_gemm uses for this shape (with the workspace it asks for):
-// the pipelined int4 kernel or the register-staged one, tile, K splits, K-groups
+// the pipelined kernel or the register-staged one, tile, K splits, K-groups
 // of 64 per workgroup and workgroups launched.
 struct GemmPlanInfo {
     bool pipelined;

@@ -9,15 +9,15 @@
 // "2. The Zig-Zag Block Schedule").
 //
 // gfx950 design (two kernels, fp32 accumulation in v_mfma_f32_32x32x16_f16):
-//  * k_gemm_w4_256 / k_gemm_w4_192 (int4 weights; the decode and prefill
-//    path above 128 rows): 256 x 256 or 192 x 256 tiles, eight wavefronts (two per
-//    SIMD), activations, codes and params fed through a 3-stage LDS ring by
+//  * k_gemm_w4_256 / _192 / _128 (int4 weights; the decode and prefill path
+//    above 128 rows): 256-, 192- or 128-row x 256 tiles, eight wavefronts,
+//    activations, codes and params fed through a 3-stage LDS ring by
 //    direct-to-LDS loads; described at the kernel body (gemm_w4_body).
 //    k_gemm_f16_256 is the same body on fp16 weights (LM head, fp16 host
 //    tier): the weight tile is staged like the activation tile, in a 2-stage
 //    ring.
-//    At 128 rows or fewer the same bodies run on 128- or 64-row tiles (int4)
-//    and 64-row tiles (fp16), two workgroups per CU where LDS allows.
+//    At 128 rows or fewer the same bodies run on 128- or 64-row tiles (int4,
+//    two workgroups per CU) and 64-row tiles (fp16).
 //  * k_gemm (small GEMMs of 128 rows or fewer that would give the pipelined
 //    kernel fewer than 128 workgroups; fp16 weights whose N is not a
 //    multiple of 32): 256-thread
@@ -246,18 +246,20 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined GEMM for M > 128 (int4, or fp16 weights): BM x 256 workgroup tiles (BM = 256, or 192 where
-// that fills more of the chip), eight wavefronts (two per SIMD) as a 2 x 4
-// grid of BM/2 x 64 wave tiles, fed through a 3-stage LDS ring
-// that direct-to-LDS loads (global_load_lds_dwordx4) fill two K-groups ahead
-// of the MFMAs, so the weight stream's HBM latency is covered without staging
-// registers. With two waves per SIMD one wave's LDS reads and dequantization
-// run while the other's MFMAs issue. Stage synchronisation is an explicit
-// vmcnt wait on the wave's own loads plus a workgroup barrier.
+// Pipelined GEMM (int4 weights, and fp16 weights whose N is a multiple of 32):
+// BM x 256 workgroup tiles (BM = 256, 192, 128 or 64, chosen by plan_gemm),
+// eight wavefronts as a 2 x 4 grid of BM/2 x 64 wave tiles, fed through an LDS
+// ring (S stages) that direct-to-LDS loads (global_load_lds_dwordx4) fill
+// S - 1 K-groups ahead of the MFMAs, so the weight stream's HBM latency is
+// covered without staging registers. With two waves per SIMD one wave's LDS
+// reads and dequantization run while the other's MFMAs issue. Stage
+// synchronisation is an explicit vmcnt wait on the wave's own loads plus a
+// workgroup barrier.
 // ---------------------------------------------------------------------------
 // F16: fp16 weights W[N][K] instead of int4 codes. W's tile (BN rows x 64 fp16)
 // has the layout of the A tile and the MFMA B fragment is read exactly as an A
-// fragment; both tiles need 64 KiB per stage, so the ring has two stages.
+// fragment; at 256 rows both tiles need 64 KiB per stage, so that ring has two
+// stages (the 64-row tile keeps three).
 template <int BM_, bool F16 = false, int S_ = 0> struct W4 {
     static constexpr int BM = BM_, BN = 256, WAVES = 8;
     static constexpr int RB = BM / 2;                   // rows per wave (2 wave rows)
