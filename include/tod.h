@@ -10,10 +10,13 @@
  *   - group-wise 4-bit weights and a group-wise 4-bit KV cache, dequantized
  *     on the fly for fp16 compute
  *       (FlexGen guide, "3. Group-Wise 4-Bit Quantization for Weights and KV Cache");
- *   - optionally, fp16 weights held in pinned host memory and streamed into
- *     HBM layer by layer, overlapped with compute
+ *   - optionally, weights (fp16 or the int4 image) held in pinned host memory
+ *     or in a file on disk and streamed into HBM layer by layer, overlapped
+ *     with compute, with a chosen number of leading layers kept resident, and
+ *     the KV caches of trailing layers in pinned host memory
  *       (FlexGen guide, "1. Three-Tier Storage Hierarchy"; TightLLM abstract,
- *        on overlapping transfer with computation).
+ *        on overlapping transfer with computation);
+ *   - a cost model of the decode step and a search over these placements.
  *
  * Conventions for every entry point:
  *   - Return 0 on success, a negative TOD_E* code on error; never abort and
@@ -26,6 +29,9 @@
  *     Calls that take a stream are asynchronous on it; init_model,
  *     set_global_weights, set_layer_weights and free_model synchronize.
  *   - A kernel fault surfaces as TOD_EHIP at the next synchronizing call.
+ *   - One model (or attention cache) handle is used by one thread at a time;
+ *     distinct handles are independent. Besides the per-thread error message
+ *     the library keeps no global state (tuning variables are read once).
  *
  * Group-wise int4 format (canonical, as exchanged through this ABI): a tensor
  * of n elements is cut into n/64 contiguous groups. Per group: zero = group
