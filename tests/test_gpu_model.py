@@ -225,6 +225,50 @@ def test_host_kv_tier_gives_identical_bits(tier):
 
 
 @pytest.mark.parametrize("tier", [1, 2])
+def test_interleaved_blocks_on_host_tiers(tier):
+    """Two blocks prefilled, then decoded in alternating slices of steps, on a host tier with the
+    first layer resident and the last two layers' KV caches on the host: the same tokens and
+    logits, bit for bit, as each block generated on its own with every layer streamed and all
+    caches in HBM. Covers the cross-pass prefetch and the per-block host caches when passes of
+    different blocks alternate."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.OPT_125M.replace(n_layers=4)
+    s, g, b, K = 16, 7, 2, 2
+    rows, V = b * K, shape.vocab
+    prompts = [to_dev(synth.prompt_ids(rows, s, V, seed=11 + blk), torch) for blk in range(2)]
+    base = dict(gpu_batch=b, batches_per_block=K, prompt_len=s, gen_len=g, weight_tier=tier, n_blocks=2)
+
+    def run(cfg, schedule):
+        m, _ = build_gpu_model(shape, dict(base, **cfg))
+        first = [torch.empty(rows, dtype=torch.int32, device="cuda") for _ in range(2)]
+        toks = [torch.empty((g - 1, rows), dtype=torch.int32, device="cuda") for _ in range(2)]
+        logits = [torch.empty((g - 1, rows, V), dtype=torch.float16, device="cuda") for _ in range(2)]
+        head = [torch.empty((rows, V), dtype=torch.float16, device="cuda") for _ in range(2)]
+        done = [None, None]
+        for blk, n in schedule:
+            if done[blk] is None:
+                tod.prefill(m.handle, blk, prompts[blk], first[blk], head[blk])
+                done[blk] = 0
+            if n == 0:
+                continue
+            j = done[blk]
+            ids = first[blk] if j == 0 else toks[blk][j - 1]
+            tod.decode_block(m.handle, blk, n, ids, toks[blk][j:j + n], logits[blk][j:j + n])
+            done[blk] = j + n
+        torch.cuda.synchronize()
+        out = [x.cpu() for blk in range(2) for x in (first[blk], toks[blk])]
+        out += [x.cpu().view(torch.int16) for blk in range(2) for x in (head[blk], logits[blk])]
+        m.close()
+        return out
+
+    ref = run(dict(), [(0, 0), (0, g - 1), (1, 0), (1, g - 1)])
+    got = run(dict(hbm_layers=1, kv_host_layers=2), [(0, 0), (1, 0), (0, 2), (1, 3), (0, 4), (1, 3)])
+    print(f"tier {tier}: interleaved blocks, tokens equal {torch.equal(ref[1], got[1])}", flush=True)
+    assert all(torch.equal(x, y) for x, y in zip(ref, got))
+
+
+@pytest.mark.parametrize("tier", [1, 2])
 def test_weights_on_disk_give_identical_bits(tier, tmp_path):
     """Streamed images read back from a file (4 layers: one resident, two owned images, layer 3
     streaming layer 1's): identical tokens, logits and (int4) exported weights to pinned images."""
