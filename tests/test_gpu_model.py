@@ -453,27 +453,29 @@ def test_full_size_opt30b_kv_codes_sampled():
     assert rates[1] >= calib["layer1_fp32_agreement"] - 0.02
 
 
-@pytest.mark.parametrize("name,gpu_batch", [("opt-6.7b", 0), ("opt-30b", 0), ("opt-30b", 8)])
+@pytest.mark.parametrize("name,gpu_batch", [("opt-6.7b", 0), ("opt-30b", 0), ("opt-30b", 8), ("opt-175b", 0)])
 def test_reduced_depth_full_width(name, gpu_batch):
     """Real hidden/FFN widths and the real block rows (M = K * b), 2 layers, prompt 16,
-    4 generated tokens; the oracle recomputes two sampled sequences (row 0 of batch 0
-    and the last row of batch K-1) on its own. gpu_batch 8 gives OPT-30B a 64-row block,
-    whose GEMMs run on the short pipelined tiles."""
+    4 generated tokens, on the workload's own weight tier (OPT-175B: fp16 streamed from pinned
+    host memory); the oracle recomputes two sampled sequences (row 0 of batch 0 and the last
+    row of batch K-1) on its own. gpu_batch 8 gives OPT-30B a 64-row block, whose GEMMs run on
+    the short pipelined tiles."""
     torch = torch_cuda()
     w = synth.WORKLOADS[name]
     shape = w.shape.replace(n_layers=2)
     s, g = 16, 4
     b = gpu_batch or w.gpu_batch
     rows_total = b * w.batches_per_block
-    run = dict(gpu_batch=b, batches_per_block=w.batches_per_block, prompt_len=s, gen_len=g)
-    print(f"{name}: 2 layers, {rows_total} rows", flush=True)
+    run = dict(gpu_batch=b, batches_per_block=w.batches_per_block, prompt_len=s, gen_len=g, weight_tier=w.weight_tier)
+    print(f"{name}: 2 layers, {rows_total} rows, weight tier {w.weight_tier}", flush=True)
     m, glob = build_gpu_model(shape, run)
     prompts = synth.prompt_ids(rows_total, s, shape.vocab)
     toks, logits = m.generate(to_dev(prompts, torch), g, return_logits=True)
     torch.cuda.synchronize()
     gt = toks.cpu().numpy()
     rows = np.array([0, rows_total - 1])
-    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full")) for l in range(shape.n_layers)]
+    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full"), int4_weights=w.weight_tier != 1)
+              for l in range(shape.n_layers)]
     ot, ol, _ = oracle.generate(shape, layers, glob, prompts[rows], g, 1, oracle.SCHED_ZIGZAG)
     max_bar, mean_bar = fp32_bars(shape, layers, glob, prompts[rows], g, 1, ot, ol)
     compare(gt[rows], to_np16(logits[:, rows, :]), ot, ol, f"{name} rows {rows.tolist()}", max_bar, mean_bar)
