@@ -145,9 +145,9 @@ int set_weight_file(tod_model *m, const char *path);
  * FlexGen guide, "2. The Zig-Zag Block Schedule" (a block of K micro-batches
  * shares each weight load) and "1. Three-Tier Storage Hierarchy" (weight tier).
  * Errors: TOD_EINVAL on an invalid shape (also when gpu_batch *
- * batches_per_block or gpu_batch * prompt_len exceeds 2^24 rows), TOD_ENOMEM
- * if HBM or pinned host memory runs out, TOD_EHIP otherwise. *out is NULL on
- * error.
+ * batches_per_block or gpu_batch * prompt_len exceeds 2^24 rows), found before
+ * any allocation or device call; TOD_ENOMEM if HBM or pinned host memory runs
+ * out, TOD_EHIP otherwise. *out is NULL on error.
  */
 int init_model(const tod_model_config *cfg, const tod_run_config *run, void *stream, tod_model **out);
 
@@ -288,7 +288,12 @@ int export_kv(tod_model *m, int layer, int block, int row, int head, int t0, int
  * [, ReLU]) with W given in the canonical int4 format (device). The library
  * repacks W into its GEMM layout in scratch memory it owns, then runs the same
  * fused dequant+MFMA GEMM as the decode path. relu: 0/1. bias and residual
- * are nullable. Used to test the GEMM at full shapes.
+ * are nullable. Used to test the GEMM at full shapes. Synchronizes stream
+ * before returning (the scratch memory is freed). Errors, all before any
+ * device work: TOD_EINVAL for a null a, y, codes (scale, zero) or d_w, rows
+ * outside [0, 2^31), in not a positive multiple of 64, out <= 0, an int4 out
+ * not a multiple of 32, or relu with a residual; TOD_ENOMEM when the scratch
+ * memory cannot be allocated.
  */
 int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes, const uint16_t *d_scale,
               const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
@@ -374,7 +379,8 @@ int attn_cache_free(tod_attn_cache *c);
  * gemm_wg_us.
  *
  * plan_decode searches weight tier (0, 1, 2), GPU batch b and batches per
- * block K (powers of two, b * K <= max_rows) and, on the host tiers,
+ * block K (powers of two, b * K <= max_rows, b * K and b * prompt_len at
+ * most 2^24 as init_model requires) and, on the host tiers,
  * hbm_layers (0..n_layers), for the most decode tokens per second among the
  * configurations that fit; ties keep the earliest in the order lower tier,
  * larger b, smaller K, smaller hbm_layers (decode cost depends on b * K only;
@@ -384,6 +390,8 @@ int attn_cache_free(tod_attn_cache *c);
  * tiers are tried with pinned images first and then with images on disk
  * (run.weights_on_disk), within disk_bytes. *best is a complete run
  * configuration (group 64, one block, host_layers 0) and *est its estimate.
+ * TOD_EINVAL for null pointers, non-positive lengths or max_rows, or a model
+ * configuration or prompt_len + gen_len that init_model would reject;
  * TOD_ENOMEM if nothing fits.
  */
 typedef struct {

@@ -93,6 +93,7 @@ def _kernel(seconds: float, hw: dict) -> float:
     return max(seconds, hw["launch_us"] * 1e-6)
 
 
+ROW_CAP = 1 << 24  # the library's limit on a block's rows and on a prefill's rows
 CUS = 256  # MI355X compute units: one workgroup of the pipelined int4 GEMM each
 
 
@@ -285,13 +286,15 @@ def _cache_bytes(shape, run: dict) -> float:
 
 
 def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
-    """Most decode tokens/s over tier, GPU batch b, batches per block K (powers of two, b * K <= max_rows)
+    """Most decode tokens/s over tier, GPU batch b, batches per block K (powers of two, b * K <= max_rows,
+    b * K and b * prompt_len at most ROW_CAP)
     and resident layers, among configurations whose footprint fits hw's capacities. Ties keep the first
     found in the order: tier ascending (pinned images before images on disk), b descending, K
     ascending, resident layers ascending (the step
     depends on b * K only, and the largest b gives prefill its largest batches). Returns (run, estimate)
     or None."""
     best = None
+    max_rows = min(max_rows, ROW_CAP)
     top = 1
     while top * 2 <= max_rows:
         top *= 2
@@ -300,7 +303,7 @@ def plan(shape, prompt_len: int, gen_len: int, max_rows: int, hw: dict):
         b = top
         while b >= 1:
             k = 1
-            while b * k <= max_rows:
+            while b * k <= max_rows and b * prompt_len <= ROW_CAP:
                 for resident in range(0, (shape.n_layers if tier != TIER_HBM_INT4 else 0) + 1):
                     run = dict(gpu_batch=b, batches_per_block=k, prompt_len=prompt_len, gen_len=gen_len,
                                group=64, weight_tier=tier, n_blocks=1, host_layers=0, hbm_layers=resident,

@@ -148,11 +148,7 @@ def init_model(cfg, run, stream=None) -> ctypes.c_void_p:
     """cfg: synth.ModelShape-like (n_layers, hidden, n_heads, head_dim, ffn, vocab, max_pos);
     run: dict with gpu_batch, batches_per_block, prompt_len, gen_len, and optional group, weight_tier,
     n_blocks, host_layers, hbm_layers, kv_host_layers, weights_on_disk."""
-    mc = ModelConfig(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.ffn, cfg.vocab, cfg.max_pos)
-    rc_ = RunConfig(run["gpu_batch"], run["batches_per_block"], run["prompt_len"], run["gen_len"],
-                    run.get("group", 64), run.get("weight_tier", 0), run.get("n_blocks", 1),
-                    run.get("host_layers", 0), run.get("hbm_layers", 0), run.get("kv_host_layers", 0),
-                    run.get("weights_on_disk", 0))
+    mc, rc_ = _model_config(cfg), _run_config(run)
     h = ctypes.c_void_p()
     _check("init_model", lib().init_model(ctypes.byref(mc), ctypes.byref(rc_), _stream(stream), ctypes.byref(h)))
     return h

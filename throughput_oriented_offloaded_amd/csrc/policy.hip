@@ -51,6 +51,7 @@
 // candidate, the fewest host-KV layers that make it fit.
 #include <cmath>
 
+#include "api.hpp"
 #include "common.hpp"
 #include "tod.h"
 
@@ -65,17 +66,6 @@ double weights_per_layer(const Shape &s) { return 4.0 * s.h * s.h + 2.0 * s.h * 
 double image_bytes(const Shape &s, int tier)
 {
     return weights_per_layer(s) * (tier == TOD_W_HOST_FP16_STREAM ? 2.0 : 0.5625);
-}
-
-bool valid(const tod_model_config *c, const tod_run_config *r)
-{
-    return c && r && c->n_layers > 0 && c->hidden > 0 && c->n_heads > 0 && c->head_dim > 0 && c->ffn > 0 &&
-           c->vocab > 0 && r->gpu_batch > 0 && r->batches_per_block > 0 && r->prompt_len > 0 && r->gen_len > 0 &&
-           r->n_blocks > 0 && r->weight_tier >= TOD_W_HBM_INT4 && r->weight_tier <= TOD_W_HOST_INT4_STREAM &&
-           r->hbm_layers >= 0 && r->hbm_layers <= c->n_layers && r->host_layers >= 0 && r->kv_host_layers >= 0 &&
-           r->kv_host_layers <= c->n_layers && (r->weights_on_disk == 0 || r->weights_on_disk == 1) &&
-           (r->weights_on_disk == 0 || r->weight_tier != TOD_W_HBM_INT4) &&
-           (r->weight_tier != TOD_W_HBM_INT4 || (r->hbm_layers == 0 && r->host_layers == 0));
 }
 
 // Device and pinned-host bytes init_model allocates for this configuration.
@@ -257,12 +247,14 @@ void default_hw(tod_hw *hw)
 
 int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out)
 {
-    if (!out || !hw || !valid(cfg, run))
-        return TOD_EINVAL;
+    if (!out || !hw)
+        return fail(TOD_EINVAL, "null argument");
+    if (int rc = check_config(cfg, run))
+        return rc;
     if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
           hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0 && hw->gemm_wg_us >= 0.0 &&
           hw->staged_tflops > 0.0 && hw->staged_gbs > 0.0 && hw->staged_us >= 0.0))
-        return TOD_EINVAL;
+        return fail(TOD_EINVAL, "hardware rates must be positive and fixed costs non-negative");
     step_model(cfg, run, hw, out);
     footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes, &out->disk_bytes);
     out->fits = out->hbm_bytes <= hw->hbm_bytes && out->host_bytes <= hw->host_bytes &&
@@ -274,16 +266,19 @@ int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int ma
                 tod_run_config *best, tod_estimate *est)
 {
     if (!cfg || !hw || !best || !est || prompt_len <= 0 || gen_len <= 0 || max_rows <= 0)
-        return TOD_EINVAL;
+        return fail(TOD_EINVAL, "bad plan_decode arguments");
     bool found = false;
     tod_estimate cur{};
+    const int64_t row_cap = 1 << 24; // init_model's limit on block rows and on prefill rows
+    if (max_rows > row_cap)
+        max_rows = (int)row_cap;
     int b_top = 1;
     while (b_top * 2 <= max_rows)
         b_top *= 2;
     for (int tier = TOD_W_HBM_INT4; tier <= TOD_W_HOST_INT4_STREAM; tier++)
         for (int disk = 0; disk <= (tier == TOD_W_HBM_INT4 ? 0 : 1); disk++)
         for (int b = b_top; b >= 1; b /= 2)
-            for (int K = 1; b * K <= max_rows; K *= 2) {
+            for (int K = 1; b * K <= max_rows && (int64_t)b * prompt_len <= row_cap; K *= 2) {
                 const int r_max = tier == TOD_W_HBM_INT4 ? 0 : cfg->n_layers;
                 for (int R = 0; R <= r_max; R++) {
                     tod_run_config r{};
@@ -329,5 +324,5 @@ int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int ma
                     }
                 }
             }
-    return found ? TOD_OK : TOD_ENOMEM;
+    return found ? TOD_OK : fail(TOD_ENOMEM, "no configuration fits the capacities");
 }

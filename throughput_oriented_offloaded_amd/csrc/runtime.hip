@@ -26,11 +26,12 @@
 #include <unistd.h>
 
 #include "../../include/tod.h"
+#include "api.hpp"
 #include "common.hpp"
 
 namespace {
-
 thread_local std::string g_err;
+} // namespace
 
 int fail(int code, const char *fmt, ...)
 {
@@ -42,6 +43,8 @@ int fail(int code, const char *fmt, ...)
     g_err = buf;
     return code;
 }
+
+namespace {
 
 #define HIPCHK(expr)                                                                          \
     do {                                                                                      \
@@ -534,6 +537,48 @@ int head_pass(tod_model *m, const uint16_t *hrows, int rows, uint16_t *logits, i
 
 } // namespace
 
+// The rules init_model applies to its configurations (estimate_decode applies them too).
+int check_config(const tod_model_config *cfg, const tod_run_config *run)
+{
+    if (!cfg || !run)
+        return fail(TOD_EINVAL, "null config");
+    const tod_model_config &c = *cfg;
+    const tod_run_config &r = *run;
+    if (c.n_layers <= 0 || c.hidden <= 0 || c.n_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 || c.vocab <= 0 ||
+        c.max_pos <= 0)
+        return fail(TOD_EINVAL, "model config fields must be positive");
+    if (c.hidden != c.n_heads * c.head_dim)
+        return fail(TOD_EINVAL, "hidden (%d) != n_heads * head_dim (%d)", c.hidden, c.n_heads * c.head_dim);
+    if (c.head_dim % 64 || c.hidden % 64 || c.ffn % 64 || (c.head_dim != 64 && c.head_dim != 128))
+        return fail(TOD_EINVAL, "head_dim must be 64 or 128; hidden and ffn multiples of 64");
+    if (c.hidden > 16384)
+        return fail(TOD_EINVAL, "hidden (%d) above 16384", c.hidden);
+    if (r.group != TOD_GROUP)
+        return fail(TOD_EINVAL, "group must be 64 (got %d)", r.group);
+    if (r.gpu_batch <= 0 || r.batches_per_block <= 0 || r.prompt_len <= 0 || r.gen_len <= 0 || r.n_blocks <= 0)
+        return fail(TOD_EINVAL, "run config fields must be positive");
+    if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM &&
+        r.weight_tier != TOD_W_HOST_INT4_STREAM)
+        return fail(TOD_EINVAL, "unknown weight tier %d", r.weight_tier);
+    if ((int64_t)r.prompt_len + r.gen_len - 1 > c.max_pos)
+        return fail(TOD_EINVAL, "prompt_len + gen_len - 1 exceeds max_pos");
+    if ((int64_t)r.gpu_batch * r.batches_per_block > (1 << 24) || (int64_t)r.gpu_batch * r.prompt_len > (1 << 24))
+        return fail(TOD_EINVAL, "gpu_batch * batches_per_block and gpu_batch * prompt_len must be at most 2^24");
+    const bool host = r.weight_tier != TOD_W_HBM_INT4;
+    if (r.host_layers < 0 || (r.host_layers && !host))
+        return fail(TOD_EINVAL, "host_layers (%d) applies to the host tiers only and must be >= 0", r.host_layers);
+    if (r.hbm_layers < 0 || r.hbm_layers > c.n_layers || (r.hbm_layers && !host))
+        return fail(TOD_EINVAL, "hbm_layers (%d) applies to the host tiers only and must be in [0, n_layers]",
+                    r.hbm_layers);
+    if (r.kv_host_layers < 0 || r.kv_host_layers > c.n_layers)
+        return fail(TOD_EINVAL, "kv_host_layers (%d) must be in [0, n_layers]", r.kv_host_layers);
+    if (r.weights_on_disk != 0 && r.weights_on_disk != 1)
+        return fail(TOD_EINVAL, "weights_on_disk must be 0 or 1 (got %d)", r.weights_on_disk);
+    if (r.weights_on_disk && !host)
+        return fail(TOD_EINVAL, "weights_on_disk applies to the host tiers only");
+    return TOD_OK;
+}
+
 // ===========================================================================
 // C ABI
 // ===========================================================================
@@ -592,27 +637,7 @@ int free_model(tod_model *m)
 static int init_model_impl(const tod_model_config *cfg, const tod_run_config *run, tod_model *m)
 {
     const tod_model_config &c = *cfg;
-    const tod_run_config &r = *run;
-    if (c.n_layers <= 0 || c.hidden <= 0 || c.n_heads <= 0 || c.head_dim <= 0 || c.ffn <= 0 || c.vocab <= 0 ||
-        c.max_pos <= 0)
-        return fail(TOD_EINVAL, "model config fields must be positive");
-    if (c.hidden != c.n_heads * c.head_dim)
-        return fail(TOD_EINVAL, "hidden (%d) != n_heads * head_dim (%d)", c.hidden, c.n_heads * c.head_dim);
-    if (c.head_dim % 64 || c.hidden % 64 || c.ffn % 64 || (c.head_dim != 64 && c.head_dim != 128))
-        return fail(TOD_EINVAL, "head_dim must be 64 or 128; hidden and ffn multiples of 64");
-    if (c.hidden > 16384)
-        return fail(TOD_EINVAL, "hidden (%d) above 16384", c.hidden);
-    if (r.group != TOD_GROUP)
-        return fail(TOD_EINVAL, "group must be 64 (got %d)", r.group);
-    if (r.gpu_batch <= 0 || r.batches_per_block <= 0 || r.prompt_len <= 0 || r.gen_len <= 0 || r.n_blocks <= 0)
-        return fail(TOD_EINVAL, "run config fields must be positive");
-    if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM &&
-        r.weight_tier != TOD_W_HOST_INT4_STREAM)
-        return fail(TOD_EINVAL, "unknown weight tier %d", r.weight_tier);
-    if ((int64_t)r.prompt_len + r.gen_len - 1 > c.max_pos)
-        return fail(TOD_EINVAL, "prompt_len + gen_len - 1 exceeds max_pos");
-    if ((int64_t)r.gpu_batch * r.batches_per_block > (1 << 24) || (int64_t)r.gpu_batch * r.prompt_len > (1 << 24))
-        return fail(TOD_EINVAL, "gpu_batch * batches_per_block and gpu_batch * prompt_len must be at most 2^24");
+    const tod_run_config &r = *run; // checked by init_model
     m->cfg = c;
     m->run = r;
     m->M = r.gpu_batch * r.batches_per_block;
@@ -640,17 +665,8 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
     m->layer_bytes = off;
     m->layers.resize(L);
     const bool host = m->streamed;
-    if (r.host_layers < 0 || (r.host_layers && !host))
-        return fail(TOD_EINVAL, "host_layers (%d) applies to the host tiers only and must be >= 0", r.host_layers);
-    if (r.hbm_layers < 0 || r.hbm_layers > L || (r.hbm_layers && !host))
-        return fail(TOD_EINVAL, "hbm_layers (%d) applies to the host tiers only and must be in [0, n_layers]",
-                    r.hbm_layers);
     m->hbm_layers = host ? r.hbm_layers : 0;
-    if (r.kv_host_layers < 0 || r.kv_host_layers > L)
-        return fail(TOD_EINVAL, "kv_host_layers (%d) must be in [0, n_layers]", r.kv_host_layers);
     m->kv_host = r.kv_host_layers;
-    if (r.weights_on_disk && !host)
-        return fail(TOD_EINVAL, "weights_on_disk applies to the host tiers only");
     m->on_disk = r.weights_on_disk != 0;
     m->image_stride = (m->layer_bytes + 4095) / 4096 * 4096;
     const int n_streamed = host ? L - m->hbm_layers : 0;
@@ -817,8 +833,8 @@ int init_model(const tod_model_config *cfg, const tod_run_config *run, void *str
     if (!out)
         return fail(TOD_EINVAL, "null out pointer");
     *out = nullptr;
-    if (!cfg || !run)
-        return fail(TOD_EINVAL, "null config");
+    if (int rc = check_config(cfg, run)) // before any allocation or device call
+        return rc;
     tod_model *m = new (std::nothrow) tod_model();
     if (!m)
         return fail(TOD_ENOMEM, "no memory for the model");
@@ -976,7 +992,6 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
         return fail(TOD_EINVAL, "null ids");
     const hipStream_t st = S(stream);
     const int b = m->run.gpu_batch, K = m->run.batches_per_block, s = m->run.prompt_len, h = m->cfg.hidden;
-    const int L = m->cfg.n_layers;
     const int64_t brow = (int64_t)b * s; // rows of one batch
     for (int k = 0; k < K; k++) {
         ProfScope ps(m, TOD_K_EMBED, st);
@@ -1228,6 +1243,10 @@ static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, con
     const bool int4 = d_codes != nullptr;
     if (int4 && (out % 32 || !d_scale || !d_zero))
         return fail(TOD_EINVAL, "int4 linear needs out %% 32 == 0 and scale/zero");
+    if (!int4 && !d_w)
+        return fail(TOD_EINVAL, "null weights");
+    if (relu && d_residual)
+        return fail(TOD_EINVAL, "relu with residual is not an epilogue of this library");
     const hipStream_t st = S(stream);
     std::vector<void *> tmp;
     auto cleanup = [&]() {
@@ -1263,8 +1282,6 @@ static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, con
         g.wc = tc;
         g.wp = tp;
     } else {
-        if (!d_w)
-            return fail(TOD_EINVAL, "null weights");
         g.wf = d_w;
     }
     g.bias = d_bias;
@@ -1275,10 +1292,6 @@ static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, con
     g.N = out;
     g.K = in;
     g.epi = relu ? EPI_BIAS_RELU : (d_residual ? EPI_BIAS_RES : (d_bias ? EPI_BIAS : EPI_NONE));
-    if (relu && d_residual) {
-        cleanup();
-        return fail(TOD_EINVAL, "relu with residual is not an epilogue of this library");
-    }
     g.ws_bytes = gemm_workspace_bytes((int)rows, out, in, int4);
     g.ws = static_cast<float *>(talloc(g.ws_bytes));
     if (g.ws_bytes && !g.ws) {
