@@ -412,7 +412,7 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (see the design notes on "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (see the design notes on "
               "sharding); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

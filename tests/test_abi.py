@@ -18,7 +18,7 @@ def _declared():
     return sorted(set(names))
 
 
-def test_header_declares_the_north_star_calls():
+def test_header_declares_the_core_calls():
     names = _declared()
     for n in ("init_model", "prefill", "decode_block", "quantize_groupwise"):
         assert n in names

@@ -6,7 +6,7 @@
 // on one GPU, if you can wait": what it does; caveats) places tensors across
 // the memory hierarchy with a policy that is tuned by hand through flags, an
 // automatic optimiser being future work. Here the step is priced from the
-// measured rates of this build's kernels and of the host link, and the search
+// measured rates of the library's kernels and of the host link, and the search
 // enumerates the run-configuration choices the library offers (weight tier,
 // resident layers, GPU batch and batches per block) under the device and
 // pinned-host capacities.
