@@ -20,8 +20,10 @@
  *
  * Conventions for every entry point:
  *   - Return 0 on success, a negative TOD_E* code on error; never abort and
- *     never throw. last_error() returns a message for the calling thread's
- *     last failing call.
+ *     never throw: a host allocation that fails inside the library (a C++
+ *     exception) is caught at the entry point and returned as TOD_ENOMEM.
+ *     last_error() returns a message for the calling thread's last failing
+ *     call.
  *   - Pointers named d_* are caller-owned device (HBM) memory; h_* are
  *     caller-owned host memory. Sizes are element counts unless stated.
  *   - fp16 tensors are passed as uint16_t bit patterns (IEEE binary16).
@@ -59,6 +61,7 @@ extern "C" {
 #define TOD_ESTATE (-4) /* call out of order: decode before prefill, context full, block out of range */
 
 #define TOD_GROUP 64
+#define TOD_MAX_BLOCKS 4096 /* most blocks (each with its own KV cache) one model holds */
 
 /* Where a model's six decoder matrices per layer live. */
 #define TOD_W_HBM_INT4 0         /* int4 group-64 in HBM, quantized at load */
@@ -87,8 +90,9 @@ typedef struct {
 /* One block = batches_per_block (K) GPU batches of gpu_batch sequences each;
  * its K*gpu_batch rows are row k*gpu_batch + i for batch k. Every sequence
  * has prompt_len prompt tokens and at most gen_len generated tokens, so the
- * KV cache holds prompt_len + gen_len - 1 positions. n_blocks blocks are
- * resident at once (each has its own KV cache). group must be 64.
+ * KV cache holds prompt_len + gen_len - 1 positions. n_blocks blocks (1 ..
+ * TOD_MAX_BLOCKS) are resident at once (each has its own KV cache). group
+ * must be 64.
  * hbm_layers (host tiers only; 0..n_layers, default 0): layers 0..hbm_layers-1
  * keep their weight image (the bytes a streamed layer would copy) resident in
  * HBM and never cross the host link; the remaining layers stream. This is the

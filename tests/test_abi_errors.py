@@ -109,6 +109,7 @@ BAD_CONFIGS = [  # (what, model-shape changes, run changes)
     ("group 32", {}, dict(group=32)),
     ("zero gpu_batch", {}, dict(gpu_batch=0)),
     ("zero blocks", {}, dict(n_blocks=0)),
+    ("blocks above TOD_MAX_BLOCKS", {}, dict(n_blocks=4097)),
     ("unknown tier", {}, dict(weight_tier=7)),
     ("past max_pos", {}, dict(gen_len=4000)),
     ("resident layers on the HBM tier", {}, dict(hbm_layers=1)),

@@ -247,82 +247,86 @@ void default_hw(tod_hw *hw)
 
 int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out)
 {
-    if (!out || !hw)
-        return fail(TOD_EINVAL, "null argument");
-    if (int rc = check_config(cfg, run))
-        return rc;
-    if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
-          hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0 && hw->gemm_wg_us >= 0.0 &&
-          hw->staged_tflops > 0.0 && hw->staged_gbs > 0.0 && hw->staged_us >= 0.0))
-        return fail(TOD_EINVAL, "hardware rates must be positive and fixed costs non-negative");
-    step_model(cfg, run, hw, out);
-    footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes, &out->disk_bytes);
-    out->fits = out->hbm_bytes <= hw->hbm_bytes && out->host_bytes <= hw->host_bytes &&
-                out->disk_bytes <= hw->disk_bytes;
-    return TOD_OK;
+    return guard("estimate_decode", [&]() -> int {
+        if (!out || !hw)
+            return fail(TOD_EINVAL, "null argument");
+        if (int rc = check_config(cfg, run))
+            return rc;
+        if (!(hw->attn_gbs > 0.0 && hw->mem_gbs > 0.0 && hw->link_gbs > 0.0 && hw->int4_tflops > 0.0 &&
+              hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 && hw->disk_gbs > 0.0 && hw->gemm_wg_us >= 0.0 &&
+              hw->staged_tflops > 0.0 && hw->staged_gbs > 0.0 && hw->staged_us >= 0.0))
+            return fail(TOD_EINVAL, "hardware rates must be positive and fixed costs non-negative");
+        step_model(cfg, run, hw, out);
+        footprint(cfg, run, &out->hbm_bytes, &out->host_bytes, &out->workspace_bytes, &out->disk_bytes);
+        out->fits = out->hbm_bytes <= hw->hbm_bytes && out->host_bytes <= hw->host_bytes &&
+                    out->disk_bytes <= hw->disk_bytes;
+        return TOD_OK;
+    });
 }
 
 int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int max_rows, const tod_hw *hw,
                 tod_run_config *best, tod_estimate *est)
 {
-    if (!cfg || !hw || !best || !est || prompt_len <= 0 || gen_len <= 0 || max_rows <= 0)
-        return fail(TOD_EINVAL, "bad plan_decode arguments");
-    bool found = false;
-    tod_estimate cur{};
-    const int64_t row_cap = 1 << 24; // init_model's limit on block rows and on prefill rows
-    if (max_rows > row_cap)
-        max_rows = (int)row_cap;
-    int b_top = 1;
-    while (b_top * 2 <= max_rows)
-        b_top *= 2;
-    for (int tier = TOD_W_HBM_INT4; tier <= TOD_W_HOST_INT4_STREAM; tier++)
-        for (int disk = 0; disk <= (tier == TOD_W_HBM_INT4 ? 0 : 1); disk++)
-        for (int b = b_top; b >= 1; b /= 2)
-            for (int K = 1; b * K <= max_rows && (int64_t)b * prompt_len <= row_cap; K *= 2) {
-                const int r_max = tier == TOD_W_HBM_INT4 ? 0 : cfg->n_layers;
-                for (int R = 0; R <= r_max; R++) {
-                    tod_run_config r{};
-                    r.gpu_batch = b;
-                    r.batches_per_block = K;
-                    r.prompt_len = prompt_len;
-                    r.gen_len = gen_len;
-                    r.group = 64;
-                    r.weight_tier = tier;
-                    r.n_blocks = 1;
-                    r.host_layers = 0;
-                    r.hbm_layers = R;
-                    r.kv_host_layers = 0;
-                    r.weights_on_disk = disk;
-                    int rc = estimate_decode(cfg, &r, hw, &cur);
-                    if (rc)
-                        return rc;
-                    if (cur.hbm_bytes > hw->hbm_bytes) {
-                        // the fewest host-KV layers that bring the device footprint within the
-                        // capacity: each moves one layer's cache out, the first also adds two
-                        // slots. Counted without the split-K workspace, then raised while the
-                        // workspace still keeps it from fitting.
-                        const double kv_layer = kv_layer_bytes(cfg, &r);
-                        const double need = std::ceil((cur.hbm_bytes - cur.workspace_bytes + 2.0 * kv_layer -
-                                                       hw->hbm_bytes) / kv_layer);
-                        if (need > cfg->n_layers)
-                            continue;
-                        r.kv_host_layers = need < 1.0 ? 1 : (int)need;
-                        if ((rc = estimate_decode(cfg, &r, hw, &cur)))
+    return guard("plan_decode", [&]() -> int {
+        if (!cfg || !hw || !best || !est || prompt_len <= 0 || gen_len <= 0 || max_rows <= 0)
+            return fail(TOD_EINVAL, "bad plan_decode arguments");
+        bool found = false;
+        tod_estimate cur{};
+        const int64_t row_cap = 1 << 24; // init_model's limit on block rows and on prefill rows
+        if (max_rows > row_cap)
+            max_rows = (int)row_cap;
+        int b_top = 1;
+        while (b_top * 2 <= max_rows)
+            b_top *= 2;
+        for (int tier = TOD_W_HBM_INT4; tier <= TOD_W_HOST_INT4_STREAM; tier++)
+            for (int disk = 0; disk <= (tier == TOD_W_HBM_INT4 ? 0 : 1); disk++)
+            for (int b = b_top; b >= 1; b /= 2)
+                for (int K = 1; b * K <= max_rows && (int64_t)b * prompt_len <= row_cap; K *= 2) {
+                    const int r_max = tier == TOD_W_HBM_INT4 ? 0 : cfg->n_layers;
+                    for (int R = 0; R <= r_max; R++) {
+                        tod_run_config r{};
+                        r.gpu_batch = b;
+                        r.batches_per_block = K;
+                        r.prompt_len = prompt_len;
+                        r.gen_len = gen_len;
+                        r.group = 64;
+                        r.weight_tier = tier;
+                        r.n_blocks = 1;
+                        r.host_layers = 0;
+                        r.hbm_layers = R;
+                        r.kv_host_layers = 0;
+                        r.weights_on_disk = disk;
+                        int rc = estimate_decode(cfg, &r, hw, &cur);
+                        if (rc)
                             return rc;
-                        while (cur.hbm_bytes > hw->hbm_bytes && r.kv_host_layers < cfg->n_layers) {
-                            r.kv_host_layers++;
+                        if (cur.hbm_bytes > hw->hbm_bytes) {
+                            // the fewest host-KV layers that bring the device footprint within the
+                            // capacity: each moves one layer's cache out, the first also adds two
+                            // slots. Counted without the split-K workspace, then raised while the
+                            // workspace still keeps it from fitting.
+                            const double kv_layer = kv_layer_bytes(cfg, &r);
+                            const double need = std::ceil((cur.hbm_bytes - cur.workspace_bytes + 2.0 * kv_layer -
+                                                           hw->hbm_bytes) / kv_layer);
+                            if (need > cfg->n_layers)
+                                continue;
+                            r.kv_host_layers = need < 1.0 ? 1 : (int)need;
                             if ((rc = estimate_decode(cfg, &r, hw, &cur)))
                                 return rc;
+                            while (cur.hbm_bytes > hw->hbm_bytes && r.kv_host_layers < cfg->n_layers) {
+                                r.kv_host_layers++;
+                                if ((rc = estimate_decode(cfg, &r, hw, &cur)))
+                                    return rc;
+                            }
+                        }
+                        // strictly better only: ties keep the earlier (lower tier, pinned before disk,
+                        // larger b, then smaller K, R)
+                        if (cur.fits && (!found || cur.tokens_per_s > est->tokens_per_s)) {
+                            *best = r;
+                            *est = cur;
+                            found = true;
                         }
                     }
-                    // strictly better only: ties keep the earlier (lower tier, pinned before disk,
-                    // larger b, then smaller K, R)
-                    if (cur.fits && (!found || cur.tokens_per_s > est->tokens_per_s)) {
-                        *best = r;
-                        *est = cur;
-                        found = true;
-                    }
                 }
-            }
-    return found ? TOD_OK : fail(TOD_ENOMEM, "no configuration fits the capacities");
+        return found ? TOD_OK : fail(TOD_ENOMEM, "no configuration fits the capacities");
+    });
 }

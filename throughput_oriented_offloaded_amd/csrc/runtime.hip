@@ -19,7 +19,6 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
-#include <string>
 #include <vector>
 
 #include <fcntl.h>
@@ -30,17 +29,17 @@
 #include "common.hpp"
 
 namespace {
-thread_local std::string g_err;
+thread_local char g_err[512];
 } // namespace
 
 int fail(int code, const char *fmt, ...)
 {
-    char buf[512];
+    char buf[sizeof g_err]; // the arguments may point into g_err itself
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    g_err = buf;
+    memcpy(g_err, buf, sizeof g_err);
     return code;
 }
 
@@ -226,18 +225,30 @@ struct ProfScope {
             }
         }
     }
+    // Never throws: the event lists have room reserved by profile_kernels, and an event that
+    // cannot be kept is destroyed instead (its launch then goes untimed).
     ~ProfScope()
     {
         if (!a)
             return;
         hipEvent_t b = pooled_event(m);
-        if (b && hipEventRecord(b, st) == hipSuccess) {
-            m->pend.push_back({kind, a, b});
-        } else {
+        const bool recorded = b && hipEventRecord(b, st) == hipSuccess;
+        if (!recorded)
             (void)hipGetLastError();
+        try {
+            if (recorded) {
+                m->pend.push_back({kind, a, b});
+                return;
+            }
             m->ev_pool.push_back(a);
+            a = nullptr;
             if (b)
                 m->ev_pool.push_back(b);
+        } catch (...) {
+            if (a)
+                (void)hipEventDestroy(a);
+            if (b)
+                (void)hipEventDestroy(b);
         }
     }
 };
@@ -557,6 +568,8 @@ int check_config(const tod_model_config *cfg, const tod_run_config *run)
         return fail(TOD_EINVAL, "group must be 64 (got %d)", r.group);
     if (r.gpu_batch <= 0 || r.batches_per_block <= 0 || r.prompt_len <= 0 || r.gen_len <= 0 || r.n_blocks <= 0)
         return fail(TOD_EINVAL, "run config fields must be positive");
+    if (r.n_blocks > TOD_MAX_BLOCKS)
+        return fail(TOD_EINVAL, "n_blocks (%d) above %d", r.n_blocks, TOD_MAX_BLOCKS);
     if (r.weight_tier != TOD_W_HBM_INT4 && r.weight_tier != TOD_W_HOST_FP16_STREAM &&
         r.weight_tier != TOD_W_HOST_INT4_STREAM)
         return fail(TOD_EINVAL, "unknown weight tier %d", r.weight_tier);
@@ -584,54 +597,56 @@ int check_config(const tod_model_config *cfg, const tod_run_config *run)
 // ===========================================================================
 extern "C" {
 
-const char *last_error(void) { return g_err.c_str(); }
+const char *last_error(void) { return g_err; }
 
 int free_model(tod_model *m)
 {
-    if (!m)
+    return guard("free_model", [&]() -> int {
+        if (!m)
+            return TOD_OK;
+        (void)hipDeviceSynchronize();
+        for (void *p : m->dev_allocs)
+            (void)hipFree(p);
+        for (void *p : m->host_allocs)
+            (void)hipHostFree(p);
+        for (int i = 0; i < 2; i++) {
+            if (m->ev_loaded[i])
+                (void)hipEventDestroy(m->ev_loaded[i]);
+            if (m->ev_free[i])
+                (void)hipEventDestroy(m->ev_free[i]);
+            if (m->ev_kv_loaded[i])
+                (void)hipEventDestroy(m->ev_kv_loaded[i]);
+            if (m->ev_kv_free[i])
+                (void)hipEventDestroy(m->ev_kv_free[i]);
+            if (m->ev_staged[i])
+                (void)hipEventDestroy(m->ev_staged[i]);
+            if (m->ev_staging_free[i])
+                (void)hipEventDestroy(m->ev_staging_free[i]);
+        }
+        if (m->copy)
+            (void)hipStreamDestroy(m->copy);
+        if (m->io)
+            (void)hipStreamDestroy(m->io);
+        if (m->fd >= 0)
+            (void)close(m->fd);
+        for (hipGraphExec_t e : m->gexec)
+            if (e)
+                (void)hipGraphExecDestroy(e);
+        if (m->gstream)
+            (void)hipStreamDestroy(m->gstream);
+        if (m->gev_in)
+            (void)hipEventDestroy(m->gev_in);
+        if (m->gev_out)
+            (void)hipEventDestroy(m->gev_out);
+        for (auto &p : m->pend) {
+            (void)hipEventDestroy(p.a);
+            (void)hipEventDestroy(p.b);
+        }
+        for (hipEvent_t e : m->ev_pool)
+            (void)hipEventDestroy(e);
+        delete m;
         return TOD_OK;
-    (void)hipDeviceSynchronize();
-    for (void *p : m->dev_allocs)
-        (void)hipFree(p);
-    for (void *p : m->host_allocs)
-        (void)hipHostFree(p);
-    for (int i = 0; i < 2; i++) {
-        if (m->ev_loaded[i])
-            (void)hipEventDestroy(m->ev_loaded[i]);
-        if (m->ev_free[i])
-            (void)hipEventDestroy(m->ev_free[i]);
-        if (m->ev_kv_loaded[i])
-            (void)hipEventDestroy(m->ev_kv_loaded[i]);
-        if (m->ev_kv_free[i])
-            (void)hipEventDestroy(m->ev_kv_free[i]);
-        if (m->ev_staged[i])
-            (void)hipEventDestroy(m->ev_staged[i]);
-        if (m->ev_staging_free[i])
-            (void)hipEventDestroy(m->ev_staging_free[i]);
-    }
-    if (m->copy)
-        (void)hipStreamDestroy(m->copy);
-    if (m->io)
-        (void)hipStreamDestroy(m->io);
-    if (m->fd >= 0)
-        (void)close(m->fd);
-    for (hipGraphExec_t e : m->gexec)
-        if (e)
-            (void)hipGraphExecDestroy(e);
-    if (m->gstream)
-        (void)hipStreamDestroy(m->gstream);
-    if (m->gev_in)
-        (void)hipEventDestroy(m->gev_in);
-    if (m->gev_out)
-        (void)hipEventDestroy(m->gev_out);
-    for (auto &p : m->pend) {
-        (void)hipEventDestroy(p.a);
-        (void)hipEventDestroy(p.b);
-    }
-    for (hipEvent_t e : m->ev_pool)
-        (void)hipEventDestroy(e);
-    delete m;
-    return TOD_OK;
+    });
 }
 
 static int init_model_impl(const tod_model_config *cfg, const tod_run_config *run, tod_model *m)
@@ -829,37 +844,42 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
 
 int init_model(const tod_model_config *cfg, const tod_run_config *run, void *stream, tod_model **out)
 {
-    (void)stream;
-    if (!out)
-        return fail(TOD_EINVAL, "null out pointer");
-    *out = nullptr;
-    if (int rc = check_config(cfg, run)) // before any allocation or device call
-        return rc;
-    tod_model *m = new (std::nothrow) tod_model();
-    if (!m)
-        return fail(TOD_ENOMEM, "no memory for the model");
-    const int rc = init_model_impl(cfg, run, m);
-    if (rc) {
-        const std::string msg = g_err;
-        free_model(m);
-        g_err = msg;
-        return rc;
-    }
-    *out = m;
-    return TOD_OK;
+    return guard("init_model", [&]() -> int {
+        (void)stream;
+        if (!out)
+            return fail(TOD_EINVAL, "null out pointer");
+        *out = nullptr;
+        if (int rc = check_config(cfg, run)) // before any allocation or device call
+            return rc;
+        tod_model *m = new (std::nothrow) tod_model();
+        if (!m)
+            return fail(TOD_ENOMEM, "no memory for the model");
+        const int rc = init_model_impl(cfg, run, m);
+        if (rc) {
+            char msg[sizeof g_err];
+            memcpy(msg, g_err, sizeof msg);
+            free_model(m);
+            memcpy(g_err, msg, sizeof msg);
+            return rc;
+        }
+        *out = m;
+        return TOD_OK;
+    });
 }
 
 int set_global_weights(tod_model *m, const uint16_t *tok, const uint16_t *pos, const uint16_t *g, const uint16_t *b)
 {
-    if (!m || !tok || !pos || !g || !b)
-        return fail(TOD_EINVAL, "null argument");
-    const int h = m->cfg.hidden;
-    HIPCHK(hipMemcpy(m->tok_emb, tok, (size_t)m->cfg.vocab * h * 2, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(m->pos_emb, pos, (size_t)(m->cfg.max_pos + 2) * h * 2, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(m->lnf_g, g, (size_t)h * 2, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(m->lnf_b, b, (size_t)h * 2, hipMemcpyHostToDevice));
-    m->glob_loaded = true;
-    return TOD_OK;
+    return guard("set_global_weights", [&]() -> int {
+        if (!m || !tok || !pos || !g || !b)
+            return fail(TOD_EINVAL, "null argument");
+        const int h = m->cfg.hidden;
+        HIPCHK(hipMemcpy(m->tok_emb, tok, (size_t)m->cfg.vocab * h * 2, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(m->pos_emb, pos, (size_t)(m->cfg.max_pos + 2) * h * 2, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(m->lnf_g, g, (size_t)h * 2, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(m->lnf_b, b, (size_t)h * 2, hipMemcpyHostToDevice));
+        m->glob_loaded = true;
+        return TOD_OK;
+    });
 }
 
 // Disk tier: synchronous whole-image transfers between staging buffer 0 and the file;
@@ -887,135 +907,141 @@ static int image_io(tod_model *m, int layer, bool write)
 
 int set_weight_file(tod_model *m, const char *path)
 {
-    if (!m || !path)
-        return fail(TOD_EINVAL, "null argument");
-    if (!m->on_disk)
-        return fail(TOD_ESTATE, "the model was not created with weights_on_disk");
-    if (m->fd >= 0)
-        return fail(TOD_ESTATE, "the weight file is already set");
-    for (const LayerStore &L : m->layers)
-        if (L.loaded)
-            return fail(TOD_ESTATE, "set_weight_file must come before set_layer_weights");
-    const int fd = open(path, O_RDWR | O_CREAT | O_TRUNC, 0600);
-    if (fd < 0)
-        return fail(TOD_EINVAL, "cannot open %s: %s", path, strerror(errno));
-    m->fd = fd;
-    return TOD_OK;
+    return guard("set_weight_file", [&]() -> int {
+        if (!m || !path)
+            return fail(TOD_EINVAL, "null argument");
+        if (!m->on_disk)
+            return fail(TOD_ESTATE, "the model was not created with weights_on_disk");
+        if (m->fd >= 0)
+            return fail(TOD_ESTATE, "the weight file is already set");
+        for (const LayerStore &L : m->layers)
+            if (L.loaded)
+                return fail(TOD_ESTATE, "set_weight_file must come before set_layer_weights");
+        const int fd = open(path, O_RDWR | O_CREAT | O_TRUNC, 0600);
+        if (fd < 0)
+            return fail(TOD_EINVAL, "cannot open %s: %s", path, strerror(errno));
+        m->fd = fd;
+        return TOD_OK;
+    });
 }
 
 int set_layer_weights(tod_model *m, int layer, const uint16_t *const *t)
 {
-    if (!m || !t)
-        return fail(TOD_EINVAL, "null argument");
-    if (layer < 0 || layer >= m->cfg.n_layers)
-        return fail(TOD_EINVAL, "layer %d out of range", layer);
-    if (m->on_disk && m->fd < 0)
-        return fail(TOD_ESTATE, "set_weight_file must come before set_layer_weights");
-    for (int i = 0; i < TOD_LAYER_TENSORS; i++)
-        if (!t[i])
-            return fail(TOD_EINVAL, "tensor %d of layer %d is null", i, layer);
-    LayerStore &L = m->layers[layer];
-    const int h = m->cfg.hidden, f = m->cfg.ffn;
-    const size_t hb = (size_t)h * 2;
-    HIPCHK(hipMemcpy(L.ln1_g, t[TOD_LN1_G], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.ln1_b, t[TOD_LN1_B], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.ln2_g, t[TOD_LN2_G], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.ln2_b, t[TOD_LN2_B], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.bias[MAT_QKV], t[TOD_Q_B], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.bias[MAT_QKV] + h, t[TOD_K_B], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.bias[MAT_QKV] + 2 * h, t[TOD_V_B], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.bias[MAT_O], t[TOD_O_B], hb, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.bias[MAT_FC1], t[TOD_FC1_B], (size_t)f * 2, hipMemcpyHostToDevice));
-    HIPCHK(hipMemcpy(L.bias[MAT_FC2], t[TOD_FC2_B], hb, hipMemcpyHostToDevice));
-    // the six matrices: (source tensor, gemm matrix, row offset inside it, rows, cols)
-    struct Part {
-        int tensor, mat, row0, rows, cols;
-    } parts[6] = {{TOD_Q_W, MAT_QKV, 0, h, h},   {TOD_K_W, MAT_QKV, h, h, h}, {TOD_V_W, MAT_QKV, 2 * h, h, h},
-                  {TOD_O_W, MAT_O, 0, h, h},     {TOD_FC1_W, MAT_FC1, 0, f, h}, {TOD_FC2_W, MAT_FC2, 0, h, f}};
-    const bool resident = m->streamed && layer < m->hbm_layers;
-    if (m->streamed) { // slot 0 serves as scratch below and an image may change: drop the prefetch
-        HIPCHK(hipDeviceSynchronize());
-        m->prefetched = false;
-    }
-    if (m->streamed && !resident && image_layer(m, layer) != layer) {
-        // this streamed layer reuses the pinned image of an earlier one
-    } else if (!m->int4) {
-        uint8_t *image = m->on_disk ? m->staging[0] : L.host; // the disk tier stages, then writes
-        for (const Part &p : parts) {
-            const int64_t off = m->mat_off[p.mat] + ((int64_t)p.row0 * p.cols) * 2;
-            const size_t bytes = (size_t)p.rows * p.cols * 2;
-            if (resident)
-                HIPCHK(hipMemcpy(L.dev + off, t[p.tensor], bytes, hipMemcpyHostToDevice));
-            else
-                memcpy(image + off, t[p.tensor], bytes);
+    return guard("set_layer_weights", [&]() -> int {
+        if (!m || !t)
+            return fail(TOD_EINVAL, "null argument");
+        if (layer < 0 || layer >= m->cfg.n_layers)
+            return fail(TOD_EINVAL, "layer %d out of range", layer);
+        if (m->on_disk && m->fd < 0)
+            return fail(TOD_ESTATE, "set_weight_file must come before set_layer_weights");
+        for (int i = 0; i < TOD_LAYER_TENSORS; i++)
+            if (!t[i])
+                return fail(TOD_EINVAL, "tensor %d of layer %d is null", i, layer);
+        LayerStore &L = m->layers[layer];
+        const int h = m->cfg.hidden, f = m->cfg.ffn;
+        const size_t hb = (size_t)h * 2;
+        HIPCHK(hipMemcpy(L.ln1_g, t[TOD_LN1_G], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.ln1_b, t[TOD_LN1_B], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.ln2_g, t[TOD_LN2_G], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.ln2_b, t[TOD_LN2_B], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.bias[MAT_QKV], t[TOD_Q_B], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.bias[MAT_QKV] + h, t[TOD_K_B], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.bias[MAT_QKV] + 2 * h, t[TOD_V_B], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.bias[MAT_O], t[TOD_O_B], hb, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.bias[MAT_FC1], t[TOD_FC1_B], (size_t)f * 2, hipMemcpyHostToDevice));
+        HIPCHK(hipMemcpy(L.bias[MAT_FC2], t[TOD_FC2_B], hb, hipMemcpyHostToDevice));
+        // the six matrices: (source tensor, gemm matrix, row offset inside it, rows, cols)
+        struct Part {
+            int tensor, mat, row0, rows, cols;
+        } parts[6] = {{TOD_Q_W, MAT_QKV, 0, h, h},   {TOD_K_W, MAT_QKV, h, h, h}, {TOD_V_W, MAT_QKV, 2 * h, h, h},
+                      {TOD_O_W, MAT_O, 0, h, h},     {TOD_FC1_W, MAT_FC1, 0, f, h}, {TOD_FC2_W, MAT_FC2, 0, h, f}};
+        const bool resident = m->streamed && layer < m->hbm_layers;
+        if (m->streamed) { // slot 0 serves as scratch below and an image may change: drop the prefetch
+            HIPCHK(hipDeviceSynchronize());
+            m->prefetched = false;
         }
-        int rc;
-        if (m->on_disk && !resident && (rc = image_io(m, layer, true)))
-            return rc;
-    } else {
-        // quantize in HBM; on the int4 host tier a resident layer's image is
-        // built in place, a streamed one's in slot 0 (idle outside a pass) and
-        // then copied to its pinned buffer
-        const uint8_t *image = !m->streamed ? nullptr : resident ? L.dev : m->slot[0];
-        HIPCHK(hipDeviceSynchronize());
-        for (const Part &p : parts) {
-            const int64_t n = (int64_t)p.rows * p.cols;
-            const int KG = p.cols / 64;
-            HIPCHK(hipMemcpy(m->stage, t[p.tensor], (size_t)n * 2, hipMemcpyHostToDevice));
-            HIPCHK(launch_quantize_groupwise(m->stage, n, m->stage_codes, m->stage_scale, m->stage_zero, nullptr));
-            const int64_t nb0 = p.row0 / 32;
-            GemmArgs dst{};
-            weights_of(m, L, p.mat, image, dst);
-            HIPCHK(launch_repack_w4(m->stage_codes, m->stage_scale, m->stage_zero, p.rows, p.cols,
-                                    const_cast<uint32_t *>(dst.wc) + nb0 * KG * 256,
-                                    const_cast<uint32_t *>(dst.wp) + nb0 * KG * 32, nullptr));
-        }
-        HIPCHK(hipDeviceSynchronize());
-        if (m->streamed && !resident) {
-            HIPCHK(hipMemcpy(m->on_disk ? m->staging[0] : L.host, m->slot[0], (size_t)m->layer_bytes,
-                             hipMemcpyDeviceToHost));
+        if (m->streamed && !resident && image_layer(m, layer) != layer) {
+            // this streamed layer reuses the pinned image of an earlier one
+        } else if (!m->int4) {
+            uint8_t *image = m->on_disk ? m->staging[0] : L.host; // the disk tier stages, then writes
+            for (const Part &p : parts) {
+                const int64_t off = m->mat_off[p.mat] + ((int64_t)p.row0 * p.cols) * 2;
+                const size_t bytes = (size_t)p.rows * p.cols * 2;
+                if (resident)
+                    HIPCHK(hipMemcpy(L.dev + off, t[p.tensor], bytes, hipMemcpyHostToDevice));
+                else
+                    memcpy(image + off, t[p.tensor], bytes);
+            }
             int rc;
-            if (m->on_disk && (rc = image_io(m, layer, true)))
+            if (m->on_disk && !resident && (rc = image_io(m, layer, true)))
                 return rc;
+        } else {
+            // quantize in HBM; on the int4 host tier a resident layer's image is
+            // built in place, a streamed one's in slot 0 (idle outside a pass) and
+            // then copied to its pinned buffer
+            const uint8_t *image = !m->streamed ? nullptr : resident ? L.dev : m->slot[0];
+            HIPCHK(hipDeviceSynchronize());
+            for (const Part &p : parts) {
+                const int64_t n = (int64_t)p.rows * p.cols;
+                const int KG = p.cols / 64;
+                HIPCHK(hipMemcpy(m->stage, t[p.tensor], (size_t)n * 2, hipMemcpyHostToDevice));
+                HIPCHK(launch_quantize_groupwise(m->stage, n, m->stage_codes, m->stage_scale, m->stage_zero, nullptr));
+                const int64_t nb0 = p.row0 / 32;
+                GemmArgs dst{};
+                weights_of(m, L, p.mat, image, dst);
+                HIPCHK(launch_repack_w4(m->stage_codes, m->stage_scale, m->stage_zero, p.rows, p.cols,
+                                        const_cast<uint32_t *>(dst.wc) + nb0 * KG * 256,
+                                        const_cast<uint32_t *>(dst.wp) + nb0 * KG * 32, nullptr));
+            }
+            HIPCHK(hipDeviceSynchronize());
+            if (m->streamed && !resident) {
+                HIPCHK(hipMemcpy(m->on_disk ? m->staging[0] : L.host, m->slot[0], (size_t)m->layer_bytes,
+                                 hipMemcpyDeviceToHost));
+                int rc;
+                if (m->on_disk && (rc = image_io(m, layer, true)))
+                    return rc;
+            }
         }
-    }
-    L.loaded = true;
-    return TOD_OK;
+        L.loaded = true;
+        return TOD_OK;
+    });
 }
 
 int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint16_t *d_logits, void *stream)
 {
-    int rc = check_ready(m, block);
-    if (rc)
-        return rc;
-    if (!d_ids || !d_next)
-        return fail(TOD_EINVAL, "null ids");
-    const hipStream_t st = S(stream);
-    const int b = m->run.gpu_batch, K = m->run.batches_per_block, s = m->run.prompt_len, h = m->cfg.hidden;
-    const int64_t brow = (int64_t)b * s; // rows of one batch
-    for (int k = 0; k < K; k++) {
-        ProfScope ps(m, TOD_K_EMBED, st);
-        HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, nullptr, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
-                                m->hid + k * brow * h, st));
-    }
-    rc = stack_pass(m, st, block, 0, [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
-        for (int kk = 0; kk < K; kk++) {
-            const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
-            const int r = layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, nullptr, wslot,
-                                     st, false, nullptr, nullptr, mirror);
-            if (r)
-                return r;
+    return guard("prefill", [&]() -> int {
+        int rc = check_ready(m, block);
+        if (rc)
+            return rc;
+        if (!d_ids || !d_next)
+            return fail(TOD_EINVAL, "null ids");
+        const hipStream_t st = S(stream);
+        const int b = m->run.gpu_batch, K = m->run.batches_per_block, s = m->run.prompt_len, h = m->cfg.hidden;
+        const int64_t brow = (int64_t)b * s; // rows of one batch
+        for (int k = 0; k < K; k++) {
+            ProfScope ps(m, TOD_K_EMBED, st);
+            HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, nullptr, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
+                                    m->hid + k * brow * h, st));
         }
+        rc = stack_pass(m, st, block, 0, [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
+            for (int kk = 0; kk < K; kk++) {
+                const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
+                const int r = layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, nullptr, wslot,
+                                         st, false, nullptr, nullptr, mirror);
+                if (r)
+                    return r;
+            }
+            return TOD_OK;
+        });
+        if (rc)
+            return rc;
+        HIPCHK(launch_gather_rows(m->hid + (int64_t)(s - 1) * h, (int64_t)s * h, m->M, h, m->last, st));
+        if ((rc = head_pass(m, m->last, m->M, d_logits ? d_logits : m->logits, d_next, st)))
+            return rc;
+        m->prefilled[block] = 1;
+        m->decoded[block] = 0;
         return TOD_OK;
     });
-    if (rc)
-        return rc;
-    HIPCHK(launch_gather_rows(m->hid + (int64_t)(s - 1) * h, (int64_t)s * h, m->M, h, m->last, st));
-    if ((rc = head_pass(m, m->last, m->M, d_logits ? d_logits : m->logits, d_next, st)))
-        return rc;
-    m->prefilled[block] = 1;
-    m->decoded[block] = 0;
-    return TOD_OK;
 }
 
 // One decode step of a block: embed the ids at `pos`, every layer, head and argmax
@@ -1080,156 +1106,170 @@ static bool capture_step(tod_model *m, int block)
 int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, int32_t *d_ids_out,
                  uint16_t *d_logits, void *stream)
 {
-    int rc = check_ready(m, block);
-    if (rc)
-        return rc;
-    if (!d_ids_in || !d_ids_out || n_steps < 0)
-        return fail(TOD_EINVAL, "bad decode arguments");
-    if (!m->prefilled[block])
-        return fail(TOD_ESTATE, "decode_block before prefill on block %d", block);
-    if (m->decoded[block] + n_steps > m->run.gen_len - 1)
-        return fail(TOD_ESTATE, "decode would exceed gen_len - 1 = %d steps (done %d, asked %d)",
-                    m->run.gen_len - 1, m->decoded[block], n_steps);
-    const hipStream_t st = S(stream);
-    const int Mr = m->M, V = m->cfg.vocab;
-    const bool graph = n_steps > 0 && m->graphs_on && !m->prof_mask && m->gstream &&
-                       m->run.weight_tier == TOD_W_HBM_INT4 && m->kv_host == 0 && !m->gfail[block] &&
-                       (m->gexec[block] || capture_step(m, block) || (m->gfail[block] = 1, false));
-    if (graph) {
-        // replay on the model's stream, ordered after and before the caller's
-        HIPCHK(hipEventRecord(m->gev_in, st));
-        HIPCHK(hipStreamWaitEvent(m->gstream, m->gev_in, 0));
-        HIPCHK(hipMemcpyAsync(m->gids, d_ids_in, (size_t)Mr * 4, hipMemcpyDeviceToDevice, m->gstream));
-        HIPCHK(launch_set_int(m->gpos, m->run.prompt_len + m->decoded[block], m->gstream));
+    return guard("decode_block", [&]() -> int {
+        int rc = check_ready(m, block);
+        if (rc)
+            return rc;
+        if (!d_ids_in || !d_ids_out || n_steps < 0)
+            return fail(TOD_EINVAL, "bad decode arguments");
+        if (!m->prefilled[block])
+            return fail(TOD_ESTATE, "decode_block before prefill on block %d", block);
+        if (m->decoded[block] + n_steps > m->run.gen_len - 1)
+            return fail(TOD_ESTATE, "decode would exceed gen_len - 1 = %d steps (done %d, asked %d)",
+                        m->run.gen_len - 1, m->decoded[block], n_steps);
+        const hipStream_t st = S(stream);
+        const int Mr = m->M, V = m->cfg.vocab;
+        const bool graph = n_steps > 0 && m->graphs_on && !m->prof_mask && m->gstream &&
+                           m->run.weight_tier == TOD_W_HBM_INT4 && m->kv_host == 0 && !m->gfail[block] &&
+                           (m->gexec[block] || capture_step(m, block) || (m->gfail[block] = 1, false));
+        if (graph) {
+            // replay on the model's stream, ordered after and before the caller's
+            HIPCHK(hipEventRecord(m->gev_in, st));
+            HIPCHK(hipStreamWaitEvent(m->gstream, m->gev_in, 0));
+            HIPCHK(hipMemcpyAsync(m->gids, d_ids_in, (size_t)Mr * 4, hipMemcpyDeviceToDevice, m->gstream));
+            HIPCHK(launch_set_int(m->gpos, m->run.prompt_len + m->decoded[block], m->gstream));
+            for (int j = 0; j < n_steps; j++) {
+                HIPCHK(hipGraphLaunch(m->gexec[block], m->gstream));
+                HIPCHK(hipMemcpyAsync(d_ids_out + (int64_t)j * Mr, m->gids, (size_t)Mr * 4, hipMemcpyDeviceToDevice,
+                                      m->gstream));
+                if (d_logits)
+                    HIPCHK(hipMemcpyAsync(d_logits + (int64_t)j * Mr * V, m->logits, (size_t)Mr * V * 2,
+                                          hipMemcpyDeviceToDevice, m->gstream));
+                m->decoded[block]++;
+            }
+            HIPCHK(hipEventRecord(m->gev_out, m->gstream));
+            HIPCHK(hipStreamWaitEvent(st, m->gev_out, 0));
+            return TOD_OK;
+        }
         for (int j = 0; j < n_steps; j++) {
-            HIPCHK(hipGraphLaunch(m->gexec[block], m->gstream));
-            HIPCHK(hipMemcpyAsync(d_ids_out + (int64_t)j * Mr, m->gids, (size_t)Mr * 4, hipMemcpyDeviceToDevice,
-                                  m->gstream));
-            if (d_logits)
-                HIPCHK(hipMemcpyAsync(d_logits + (int64_t)j * Mr * V, m->logits, (size_t)Mr * V * 2,
-                                      hipMemcpyDeviceToDevice, m->gstream));
+            const int pos = m->run.prompt_len + m->decoded[block];
+            const int32_t *in = j == 0 ? d_ids_in : d_ids_out + (int64_t)(j - 1) * Mr;
+            uint16_t *lg = d_logits ? d_logits + (int64_t)j * Mr * V : m->logits;
+            if ((rc = decode_step(m, block, in, pos, nullptr, lg, d_ids_out + (int64_t)j * Mr, st)))
+                return rc;
             m->decoded[block]++;
         }
-        HIPCHK(hipEventRecord(m->gev_out, m->gstream));
-        HIPCHK(hipStreamWaitEvent(st, m->gev_out, 0));
         return TOD_OK;
-    }
-    for (int j = 0; j < n_steps; j++) {
-        const int pos = m->run.prompt_len + m->decoded[block];
-        const int32_t *in = j == 0 ? d_ids_in : d_ids_out + (int64_t)(j - 1) * Mr;
-        uint16_t *lg = d_logits ? d_logits + (int64_t)j * Mr * V : m->logits;
-        if ((rc = decode_step(m, block, in, pos, nullptr, lg, d_ids_out + (int64_t)j * Mr, st)))
-            return rc;
-        m->decoded[block]++;
-    }
-    return TOD_OK;
+    });
 }
 
 int set_decode_graph(tod_model *m, int enable)
 {
-    if (!m)
-        return fail(TOD_EINVAL, "null model");
-    m->graphs_on = enable != 0;
-    return TOD_OK;
+    return guard("set_decode_graph", [&]() -> int {
+        if (!m)
+            return fail(TOD_EINVAL, "null model");
+        m->graphs_on = enable != 0;
+        return TOD_OK;
+    });
 }
 
 int set_decode_position(tod_model *m, int block, int steps)
 {
-    if (!m)
-        return fail(TOD_EINVAL, "null model");
-    if (block < 0 || block >= m->run.n_blocks)
-        return fail(TOD_ESTATE, "block %d out of range", block);
-    if (!m->prefilled[block])
-        return fail(TOD_ESTATE, "block %d has not been prefilled", block);
-    if (steps < 0 || steps > m->run.gen_len - 1)
-        return fail(TOD_EINVAL, "steps %d outside [0, %d]", steps, m->run.gen_len - 1);
-    m->decoded[block] = steps;
-    return TOD_OK;
+    return guard("set_decode_position", [&]() -> int {
+        if (!m)
+            return fail(TOD_EINVAL, "null model");
+        if (block < 0 || block >= m->run.n_blocks)
+            return fail(TOD_ESTATE, "block %d out of range", block);
+        if (!m->prefilled[block])
+            return fail(TOD_ESTATE, "block %d has not been prefilled", block);
+        if (steps < 0 || steps > m->run.gen_len - 1)
+            return fail(TOD_EINVAL, "steps %d outside [0, %d]", steps, m->run.gen_len - 1);
+        m->decoded[block] = steps;
+        return TOD_OK;
+    });
 }
 
 int quantize_groupwise(const uint16_t *d_x, int64_t n, int group, uint8_t *d_codes, uint16_t *d_scale,
                        uint16_t *d_zero, void *stream)
 {
-    if (group != TOD_GROUP)
-        return fail(TOD_EINVAL, "group must be 64 (got %d)", group);
-    if (n < 0 || n % group)
-        return fail(TOD_EINVAL, "n (%lld) must be a non-negative multiple of %d", (long long)n, group);
-    if (n && (!d_x || !d_codes || !d_scale || !d_zero))
-        return fail(TOD_EINVAL, "null pointer");
-    HIPCHK(launch_quantize_groupwise(d_x, n, d_codes, d_scale, d_zero, S(stream)));
-    return TOD_OK;
+    return guard("quantize_groupwise", [&]() -> int {
+        if (group != TOD_GROUP)
+            return fail(TOD_EINVAL, "group must be 64 (got %d)", group);
+        if (n < 0 || n % group)
+            return fail(TOD_EINVAL, "n (%lld) must be a non-negative multiple of %d", (long long)n, group);
+        if (n && (!d_x || !d_codes || !d_scale || !d_zero))
+            return fail(TOD_EINVAL, "null pointer");
+        HIPCHK(launch_quantize_groupwise(d_x, n, d_codes, d_scale, d_zero, S(stream)));
+        return TOD_OK;
+    });
 }
 
 int dequantize_groupwise(const uint8_t *d_codes, const uint16_t *d_scale, const uint16_t *d_zero, int64_t n,
                          int group, uint16_t *d_out, void *stream)
 {
-    if (group != TOD_GROUP)
-        return fail(TOD_EINVAL, "group must be 64 (got %d)", group);
-    if (n < 0 || n % group)
-        return fail(TOD_EINVAL, "n must be a non-negative multiple of 64");
-    if (n && (!d_codes || !d_scale || !d_zero || !d_out))
-        return fail(TOD_EINVAL, "null pointer");
-    HIPCHK(launch_dequantize_groupwise(d_codes, d_scale, d_zero, n, d_out, S(stream)));
-    return TOD_OK;
+    return guard("dequantize_groupwise", [&]() -> int {
+        if (group != TOD_GROUP)
+            return fail(TOD_EINVAL, "group must be 64 (got %d)", group);
+        if (n < 0 || n % group)
+            return fail(TOD_EINVAL, "n must be a non-negative multiple of 64");
+        if (n && (!d_codes || !d_scale || !d_zero || !d_out))
+            return fail(TOD_EINVAL, "null pointer");
+        HIPCHK(launch_dequantize_groupwise(d_codes, d_scale, d_zero, n, d_out, S(stream)));
+        return TOD_OK;
+    });
 }
 
 int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t *d_scale, uint16_t *d_zero,
                   void *stream)
 {
-    if (!m || !d_codes || !d_scale || !d_zero)
-        return fail(TOD_EINVAL, "null argument");
-    if (layer < 0 || layer >= m->cfg.n_layers || which < TOD_MAT_Q || which > TOD_MAT_FC2)
-        return fail(TOD_EINVAL, "layer or matrix id out of range");
-    if (!m->int4)
-        return fail(TOD_ESTATE, "the fp16 host tier keeps fp16 weights");
-    if (!m->layers[layer].loaded)
-        return fail(TOD_ESTATE, "layer %d weights not set", layer);
-    const uint8_t *slot = nullptr;
-    if (m->streamed && layer < m->hbm_layers) {
-        slot = m->layers[layer].dev;
-    } else if (m->streamed) { // bring the layer's pinned image into slot 0 (idle outside a pass)
-        const int src = image_layer(m, layer);
-        if (!m->layers[src].loaded)
-            return fail(TOD_ESTATE, "layer %d (whose image layer %d streams) weights not set", src, layer);
-        HIPCHK(hipDeviceSynchronize());
-        m->prefetched = false; // slot 0 is overwritten here
-        int rc;
-        if (m->on_disk && (rc = image_io(m, layer, false)))
-            return rc;
-        HIPCHK(hipMemcpy(m->slot[0], m->on_disk ? m->staging[0] : m->layers[src].host, (size_t)m->layer_bytes,
-                         hipMemcpyHostToDevice));
-        slot = m->slot[0];
-    }
-    const int h = m->cfg.hidden, f = m->cfg.ffn;
-    int mat, row0 = 0, rows = h, cols = h;
-    switch (which) {
-    case TOD_MAT_Q: mat = MAT_QKV; break;
-    case TOD_MAT_K: mat = MAT_QKV; row0 = h; break;
-    case TOD_MAT_V: mat = MAT_QKV; row0 = 2 * h; break;
-    case TOD_MAT_O: mat = MAT_O; break;
-    case TOD_MAT_FC1: mat = MAT_FC1; rows = f; break;
-    default: mat = MAT_FC2; cols = f; break;
-    }
-    const int KG = cols / 64;
-    const int64_t nb0 = row0 / 32;
-    GemmArgs src{};
-    weights_of(m, m->layers[layer], mat, slot, src);
-    HIPCHK(launch_unpack_w4(src.wc + nb0 * KG * 256, src.wp + nb0 * KG * 32, rows, cols, d_codes, d_scale, d_zero,
-                            S(stream)));
-    return TOD_OK;
+    return guard("export_weight", [&]() -> int {
+        if (!m || !d_codes || !d_scale || !d_zero)
+            return fail(TOD_EINVAL, "null argument");
+        if (layer < 0 || layer >= m->cfg.n_layers || which < TOD_MAT_Q || which > TOD_MAT_FC2)
+            return fail(TOD_EINVAL, "layer or matrix id out of range");
+        if (!m->int4)
+            return fail(TOD_ESTATE, "the fp16 host tier keeps fp16 weights");
+        if (!m->layers[layer].loaded)
+            return fail(TOD_ESTATE, "layer %d weights not set", layer);
+        const uint8_t *slot = nullptr;
+        if (m->streamed && layer < m->hbm_layers) {
+            slot = m->layers[layer].dev;
+        } else if (m->streamed) { // bring the layer's pinned image into slot 0 (idle outside a pass)
+            const int src = image_layer(m, layer);
+            if (!m->layers[src].loaded)
+                return fail(TOD_ESTATE, "layer %d (whose image layer %d streams) weights not set", src, layer);
+            HIPCHK(hipDeviceSynchronize());
+            m->prefetched = false; // slot 0 is overwritten here
+            int rc;
+            if (m->on_disk && (rc = image_io(m, layer, false)))
+                return rc;
+            HIPCHK(hipMemcpy(m->slot[0], m->on_disk ? m->staging[0] : m->layers[src].host, (size_t)m->layer_bytes,
+                             hipMemcpyHostToDevice));
+            slot = m->slot[0];
+        }
+        const int h = m->cfg.hidden, f = m->cfg.ffn;
+        int mat, row0 = 0, rows = h, cols = h;
+        switch (which) {
+        case TOD_MAT_Q: mat = MAT_QKV; break;
+        case TOD_MAT_K: mat = MAT_QKV; row0 = h; break;
+        case TOD_MAT_V: mat = MAT_QKV; row0 = 2 * h; break;
+        case TOD_MAT_O: mat = MAT_O; break;
+        case TOD_MAT_FC1: mat = MAT_FC1; rows = f; break;
+        default: mat = MAT_FC2; cols = f; break;
+        }
+        const int KG = cols / 64;
+        const int64_t nb0 = row0 / 32;
+        GemmArgs src{};
+        weights_of(m, m->layers[layer], mat, slot, src);
+        HIPCHK(launch_unpack_w4(src.wc + nb0 * KG * 256, src.wp + nb0 * KG * 32, rows, cols, d_codes, d_scale, d_zero,
+                                S(stream)));
+        return TOD_OK;
+    });
 }
 
 int export_kv(tod_model *m, int layer, int block, int row, int head, int t0, int t1, uint8_t *d_kc, uint16_t *d_ks,
               uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream)
 {
-    if (!m || !d_kc || !d_ks || !d_kz || !d_vc || !d_vs || !d_vz)
-        return fail(TOD_EINVAL, "null argument");
-    if (layer < 0 || layer >= m->cfg.n_layers || block < 0 || block >= m->run.n_blocks || row < 0 || row >= m->M ||
-        head < 0 || head >= m->cfg.n_heads || t0 < 0 || t1 > m->cap || t0 > t1)
-        return fail(TOD_EINVAL, "export_kv index out of range");
-    HIPCHK(launch_kv_export(m->kv[(size_t)block * m->cfg.n_layers + layer], row, head, t0, t1, d_kc, d_ks, d_kz, d_vc,
-                            d_vs, d_vz, S(stream)));
-    return TOD_OK;
+    return guard("export_kv", [&]() -> int {
+        if (!m || !d_kc || !d_ks || !d_kz || !d_vc || !d_vs || !d_vz)
+            return fail(TOD_EINVAL, "null argument");
+        if (layer < 0 || layer >= m->cfg.n_layers || block < 0 || block >= m->run.n_blocks || row < 0 || row >= m->M ||
+            head < 0 || head >= m->cfg.n_heads || t0 < 0 || t1 > m->cap || t0 > t1)
+            return fail(TOD_EINVAL, "export_kv index out of range");
+        HIPCHK(launch_kv_export(m->kv[(size_t)block * m->cfg.n_layers + layer], row, head, t0, t1, d_kc, d_ks, d_kz, d_vc,
+                                d_vs, d_vz, S(stream)));
+        return TOD_OK;
+    });
 }
 
 static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
@@ -1309,139 +1349,161 @@ int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t 
               const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
               void *stream)
 {
-    if (!d_codes)
-        return fail(TOD_EINVAL, "null codes");
-    return linear_common(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y, stream);
+    return guard("linear_w4", [&]() -> int {
+        if (!d_codes)
+            return fail(TOD_EINVAL, "null codes");
+        return linear_common(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y, stream);
+    });
 }
 
 int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_t *d_w, const uint16_t *d_bias,
                const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
 {
-    return linear_common(d_a, rows, in, out, nullptr, nullptr, nullptr, d_w, d_bias, d_residual, relu, d_y, stream);
+    return guard("linear_f16", [&]() -> int {
+        return linear_common(d_a, rows, in, out, nullptr, nullptr, nullptr, d_w, d_bias, d_residual, relu, d_y, stream);
+    });
 }
 
 int profile_kernels(tod_model *m, unsigned mask)
 {
-    if (!m)
-        return fail(TOD_EINVAL, "null model");
-    double ms;
-    int64_t n;
-    int rc = profile_read(m, 0, &ms, &n); // drain pending events
-    if (rc)
-        return rc;
-    m->prof_mask = mask;
-    for (int k = 0; k < TOD_K_COUNT; k++) {
-        m->prof_ms[k] = 0.0;
-        m->prof_n[k] = 0;
-    }
-    return TOD_OK;
+    return guard("profile_kernels", [&]() -> int {
+        if (!m)
+            return fail(TOD_EINVAL, "null model");
+        double ms;
+        int64_t n;
+        int rc = profile_read(m, 0, &ms, &n); // drain pending events
+        if (rc)
+            return rc;
+        m->prof_mask = mask;
+        if (mask) { // room for the launches of a few decode steps, so timing rarely grows the lists
+            m->pend.reserve(1 << 14);
+            m->ev_pool.reserve(1 << 15);
+        }
+        for (int k = 0; k < TOD_K_COUNT; k++) {
+            m->prof_ms[k] = 0.0;
+            m->prof_n[k] = 0;
+        }
+        return TOD_OK;
+    });
 }
 
 int profile_read(tod_model *m, int kind, double *total_ms, int64_t *launches)
 {
-    if (!m || !total_ms || !launches || kind < 0 || kind >= TOD_K_COUNT)
-        return fail(TOD_EINVAL, "bad profile_read arguments");
-    for (auto &p : m->pend) {
-        HIPCHK(hipEventSynchronize(p.b));
-        float ms = 0.0f;
-        HIPCHK(hipEventElapsedTime(&ms, p.a, p.b));
-        m->prof_ms[p.kind] += ms;
-        m->prof_n[p.kind]++;
-        m->ev_pool.push_back(p.a);
-        m->ev_pool.push_back(p.b);
-    }
-    m->pend.clear();
-    *total_ms = m->prof_ms[kind];
-    *launches = m->prof_n[kind];
-    return TOD_OK;
+    return guard("profile_read", [&]() -> int {
+        if (!m || !total_ms || !launches || kind < 0 || kind >= TOD_K_COUNT)
+            return fail(TOD_EINVAL, "bad profile_read arguments");
+        for (auto &p : m->pend) {
+            HIPCHK(hipEventSynchronize(p.b));
+            float ms = 0.0f;
+            HIPCHK(hipEventElapsedTime(&ms, p.a, p.b));
+            m->prof_ms[p.kind] += ms;
+            m->prof_n[p.kind]++;
+            m->ev_pool.push_back(p.a);
+            m->ev_pool.push_back(p.b);
+        }
+        m->pend.clear();
+        *total_ms = m->prof_ms[kind];
+        *launches = m->prof_n[kind];
+        return TOD_OK;
+    });
 }
 
 inline bool misaligned16(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 
 int attn_cache_create(int batch, int heads, int head_dim, int cap, tod_attn_cache **out)
 {
-    if (!out)
-        return fail(TOD_EINVAL, "null out pointer");
-    *out = nullptr;
-    if (batch <= 0 || heads <= 0 || cap <= 0 || (head_dim != 64 && head_dim != 128))
-        return fail(TOD_EINVAL, "bad attention cache shape");
-    tod_attn_cache *c = new (std::nothrow) tod_attn_cache();
-    if (!c)
-        return fail(TOD_ENOMEM, "no memory for the attention cache");
-    const int capp = (cap + 63) / 64 * 64;
-    size_t kc_b, kp_b;
-    kv_bytes((size_t)batch * heads, head_dim, capp, &kc_b, &kp_b);
-    void *p[4] = {};
-    const size_t sz[4] = {kc_b, kp_b, kc_b, kp_b};
-    for (int i = 0; i < 4; i++) {
-        if (hipMalloc(&p[i], sz[i]) != hipSuccess) {
-            (void)hipGetLastError();
-            for (void *q : c->allocs)
-                (void)hipFree(q);
-            delete c;
-            return fail(TOD_ENOMEM, "hipMalloc of %zu bytes for the attention cache failed", sz[i]);
+    return guard("attn_cache_create", [&]() -> int {
+        if (!out)
+            return fail(TOD_EINVAL, "null out pointer");
+        *out = nullptr;
+        if (batch <= 0 || heads <= 0 || cap <= 0 || (head_dim != 64 && head_dim != 128))
+            return fail(TOD_EINVAL, "bad attention cache shape");
+        tod_attn_cache *c = new (std::nothrow) tod_attn_cache();
+        if (!c)
+            return fail(TOD_ENOMEM, "no memory for the attention cache");
+        const int capp = (cap + 63) / 64 * 64;
+        size_t kc_b, kp_b;
+        kv_bytes((size_t)batch * heads, head_dim, capp, &kc_b, &kp_b);
+        void *p[4] = {};
+        const size_t sz[4] = {kc_b, kp_b, kc_b, kp_b};
+        for (int i = 0; i < 4; i++) {
+            if (hipMalloc(&p[i], sz[i]) != hipSuccess) {
+                (void)hipGetLastError();
+                for (void *q : c->allocs)
+                    (void)hipFree(q);
+                delete c;
+                return fail(TOD_ENOMEM, "hipMalloc of %zu bytes for the attention cache failed", sz[i]);
+            }
+            c->allocs.push_back(p[i]);
         }
-        c->allocs.push_back(p[i]);
-    }
-    c->kv = make_kv_view(static_cast<uint8_t *>(p[0]), static_cast<uint32_t *>(p[1]), static_cast<uint8_t *>(p[2]),
-                         static_cast<uint32_t *>(p[3]), heads, head_dim, capp);
-    c->batch = batch;
-    *out = c;
-    return TOD_OK;
+        c->kv = make_kv_view(static_cast<uint8_t *>(p[0]), static_cast<uint32_t *>(p[1]), static_cast<uint8_t *>(p[2]),
+                             static_cast<uint32_t *>(p[3]), heads, head_dim, capp);
+        c->batch = batch;
+        *out = c;
+        return TOD_OK;
+    });
 }
 
 int attn_cache_fill(tod_attn_cache *c, const uint16_t *d_k, const uint16_t *d_v, int t0, int n, void *stream)
 {
-    if (!c || !d_k || !d_v || t0 < 0 || n < 0 || t0 + n > c->kv.cap)
-        return fail(TOD_EINVAL, "bad attention cache fill");
-    if (misaligned16(d_k) || misaligned16(d_v))
-        return fail(TOD_EINVAL, "K/V buffers must be 16-byte aligned");
-    // time-major input [n][batch][heads][d]: row r = (sequence r / n, position t0 + r % n)
-    const int d = c->kv.head_dim, H = c->kv.heads;
-    const SrcMap src = {(int64_t)H * d, (int64_t)c->batch * H * d, d};
-    const RowMap map = {0, n, t0, nullptr};
-    HIPCHK(launch_kv_append(d_k, d_v, src, c->batch * n, map, c->kv, S(stream)));
-    return TOD_OK;
+    return guard("attn_cache_fill", [&]() -> int {
+        if (!c || !d_k || !d_v || t0 < 0 || n < 0 || t0 + n > c->kv.cap)
+            return fail(TOD_EINVAL, "bad attention cache fill");
+        if (misaligned16(d_k) || misaligned16(d_v))
+            return fail(TOD_EINVAL, "K/V buffers must be 16-byte aligned");
+        // time-major input [n][batch][heads][d]: row r = (sequence r / n, position t0 + r % n)
+        const int d = c->kv.head_dim, H = c->kv.heads;
+        const SrcMap src = {(int64_t)H * d, (int64_t)c->batch * H * d, d};
+        const RowMap map = {0, n, t0, nullptr};
+        HIPCHK(launch_kv_append(d_k, d_v, src, c->batch * n, map, c->kv, S(stream)));
+        return TOD_OK;
+    });
 }
 
 int attn_decode_step(tod_attn_cache *c, int pos, const uint16_t *d_q, const uint16_t *d_k_new,
                      const uint16_t *d_v_new, uint16_t *d_out, void *stream)
 {
-    if (!c || !d_q || !d_k_new || !d_v_new || !d_out)
-        return fail(TOD_EINVAL, "null argument");
-    if (pos < 0 || pos >= c->kv.cap)
-        return fail(TOD_ESTATE, "position %d outside the cache (capacity %d)", pos, c->kv.cap);
-    if (misaligned16(d_q) || misaligned16(d_k_new) || misaligned16(d_v_new) || misaligned16(d_out))
-        return fail(TOD_EINVAL, "q, k, v and out buffers must be 16-byte aligned");
-    const int d = c->kv.head_dim, H = c->kv.heads;
-    const SrcMap src = {(int64_t)H * d, 0, d};
-    const RowMap map = {0, 1, pos, nullptr};
-    HIPCHK(launch_kv_append(d_k_new, d_v_new, src, c->batch, map, c->kv, S(stream)));
-    HIPCHK(launch_attn_decode(d_q, (int64_t)H * d, d_out, (int64_t)H * d, c->batch, 0, pos + 1, nullptr, c->kv,
-                              S(stream)));
-    return TOD_OK;
+    return guard("attn_decode_step", [&]() -> int {
+        if (!c || !d_q || !d_k_new || !d_v_new || !d_out)
+            return fail(TOD_EINVAL, "null argument");
+        if (pos < 0 || pos >= c->kv.cap)
+            return fail(TOD_ESTATE, "position %d outside the cache (capacity %d)", pos, c->kv.cap);
+        if (misaligned16(d_q) || misaligned16(d_k_new) || misaligned16(d_v_new) || misaligned16(d_out))
+            return fail(TOD_EINVAL, "q, k, v and out buffers must be 16-byte aligned");
+        const int d = c->kv.head_dim, H = c->kv.heads;
+        const SrcMap src = {(int64_t)H * d, 0, d};
+        const RowMap map = {0, 1, pos, nullptr};
+        HIPCHK(launch_kv_append(d_k_new, d_v_new, src, c->batch, map, c->kv, S(stream)));
+        HIPCHK(launch_attn_decode(d_q, (int64_t)H * d, d_out, (int64_t)H * d, c->batch, 0, pos + 1, nullptr, c->kv,
+                                  S(stream)));
+        return TOD_OK;
+    });
 }
 
 int attn_cache_export(tod_attn_cache *c, int seq, int head, int t0, int t1, uint8_t *d_kc, uint16_t *d_ks,
                       uint16_t *d_kz, uint8_t *d_vc, uint16_t *d_vs, uint16_t *d_vz, void *stream)
 {
-    if (!c || !d_kc || !d_ks || !d_kz || !d_vc || !d_vs || !d_vz)
-        return fail(TOD_EINVAL, "null argument");
-    if (seq < 0 || seq >= c->batch || head < 0 || head >= c->kv.heads || t0 < 0 || t1 > c->kv.cap || t0 > t1)
-        return fail(TOD_EINVAL, "export index out of range");
-    HIPCHK(launch_kv_export(c->kv, seq, head, t0, t1, d_kc, d_ks, d_kz, d_vc, d_vs, d_vz, S(stream)));
-    return TOD_OK;
+    return guard("attn_cache_export", [&]() -> int {
+        if (!c || !d_kc || !d_ks || !d_kz || !d_vc || !d_vs || !d_vz)
+            return fail(TOD_EINVAL, "null argument");
+        if (seq < 0 || seq >= c->batch || head < 0 || head >= c->kv.heads || t0 < 0 || t1 > c->kv.cap || t0 > t1)
+            return fail(TOD_EINVAL, "export index out of range");
+        HIPCHK(launch_kv_export(c->kv, seq, head, t0, t1, d_kc, d_ks, d_kz, d_vc, d_vs, d_vz, S(stream)));
+        return TOD_OK;
+    });
 }
 
 int attn_cache_free(tod_attn_cache *c)
 {
-    if (!c)
+    return guard("attn_cache_free", [&]() -> int {
+        if (!c)
+            return TOD_OK;
+        (void)hipDeviceSynchronize();
+        for (void *p : c->allocs)
+            (void)hipFree(p);
+        delete c;
         return TOD_OK;
-    (void)hipDeviceSynchronize();
-    for (void *p : c->allocs)
-        (void)hipFree(p);
-    delete c;
-    return TOD_OK;
+    });
 }
 
 } // extern "C"
