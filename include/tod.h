@@ -280,6 +280,25 @@ int export_weight(tod_model *m, int layer, int which, uint8_t *d_codes, uint16_t
                   void *stream);
 
 /*
+ * set_layer_tap: test hook that exposes one layer's input and output. From the
+ * next prefill (phase 0) or decode_block (phase 1) on, every pass of that phase
+ * over layer `layer` copies hidden rows [row0, row0 + n_rows) of the pass into
+ * d_in (before the layer) and d_out (after it), each fp16 [n_rows][hidden]
+ * device memory owned by the caller and kept alive while the tap is set (either
+ * may be NULL). The hidden rows are the residual stream between layers (before
+ * the layer's own LayerNorm): in decode row r is row r of the block; in
+ * prefill row r is position r % prompt_len of block row r / prompt_len. The
+ * copies run on the pass's stream. n_rows == 0 removes the tap. While any
+ * decode tap is set decode steps are launched one by one (no decode graph).
+ * Used to check a layer against a reference given exactly the inputs it saw
+ * (FlexGen guide, "3. Group-Wise 4-Bit Quantization": the layer computes in
+ * fp16 on dequantized weights and cache). Errors: TOD_EINVAL (phase not 0/1,
+ * layer out of range, rows outside the pass, n_rows > 0 with both buffers NULL).
+ */
+int set_layer_tap(tod_model *m, int phase, int layer, int64_t row0, int64_t n_rows, uint16_t *d_in,
+                  uint16_t *d_out);
+
+/*
  * export_kv: copy positions [t0, t1) of (layer, block, row, head) out of the
  * KV cache in the canonical per-position format (device buffers): K codes
  * [t1-t0][head_dim/2], K scale/zero [t1-t0][head_dim/64], same for V.

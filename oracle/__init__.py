@@ -71,6 +71,9 @@ def _lib() -> ctypes.CDLL:
         "o_head": ([vp, vp, vp, vp, vp, i32, vp, vp], None),
         "o_generate": ([vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, vp, vp], i32),
         "o_set_fp32_accumulation": ([i32], None),
+        "o_set_exact_v": ([i32], None),
+        "o_kv_load": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+        "o_layer_forward_given_kv": ([vp, vp, i32, i32, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -109,6 +112,19 @@ class fp32_accumulation:
 
     def __exit__(self, *exc):
         _lib().o_set_fp32_accumulation(0)
+        return False
+
+
+class exact_v:
+    """Context manager: attention reads each cached V element as the exact real zero + c * scale
+    instead of its fp16 rounding (the same attention with that one rounding left out)."""
+
+    def __enter__(self):
+        _lib().o_set_exact_v(1)
+        return self
+
+    def __exit__(self, *exc):
+        _lib().o_set_exact_v(0)
         return False
 
 
@@ -264,6 +280,17 @@ class Layer:
             raise ValueError(f"oracle layer forward failed ({rc})")
         return hid.view(np.float16)
 
+    def forward_given_kv(self, cache: "KVCache", pos0: int, hidden: np.ndarray):
+        """The layer at positions pos0.. against the cache as given (positions 0..pos0+n-1
+        already loaded): (hidden out fp16 [n][h], the layer's own k and v fp16 [n][h])."""
+        hid = np.array(_h(hidden), dtype=np.uint16, copy=True).reshape(-1, self.shape.hidden)
+        k = np.empty_like(hid)
+        v = np.empty_like(hid)
+        rc = _lib().o_layer_forward_given_kv(self._ptr, cache._ptr, pos0, hid.shape[0], _p(hid), _p(k), _p(v))
+        if rc != 0:
+            raise ValueError(f"oracle layer forward (given cache) failed ({rc})")
+        return hid.view(np.float16), k.view(np.float16), v.view(np.float16)
+
     def close(self):
         if self._ptr:
             _lib().o_layer_free(self._ptr)
@@ -298,6 +325,17 @@ class KVCache:
         if rc != 0:
             raise ValueError("oracle kv export: bad range")
         return kc, ks.view(np.float16), kz.view(np.float16), vc, vs.view(np.float16), vz.view(np.float16)
+
+    def load(self, head: int, t0: int, kc, ks, kz, vc, vs, vz):
+        """Store positions t0.. of one head from the canonical format (inverse of export)."""
+        kc = np.ascontiguousarray(kc, dtype=np.uint8)
+        vc = np.ascontiguousarray(vc, dtype=np.uint8)
+        n = kc.shape[0]
+        arr = [_h(np.ascontiguousarray(x)) for x in (ks, kz, vs, vz)]
+        rc = _lib().o_kv_load(self._ptr, head, t0, t0 + n, _p(kc), _p(arr[0]), _p(arr[1]), _p(vc), _p(arr[2]),
+                              _p(arr[3]))
+        if rc != 0:
+            raise ValueError("oracle kv load: bad range")
 
     def close(self):
         if self._ptr:

@@ -196,6 +196,24 @@ static inline double acc_add(double acc, double term)
     return g_acc32 ? (double)(float)r : r;
 }
 
+/*
+ * Value of a cached V element in attention. The pages compute attention in
+ * fp16 on dequantized values, so by default each V element is the fp16 value
+ * fp16_rn(zero + c * scale). With o_set_exact_v(1) it is instead the exact
+ * real zero + c * scale (never rounded): the same attention with that one
+ * rounding left out. Both readings give one result up to half an fp16 ulp of
+ * the largest |v| (the output is a weighted mean of the values); the second
+ * one isolates what accumulation order and precision alone change.
+ */
+static int g_exact_v = 0;
+
+void o_set_exact_v(int on) { g_exact_v = on != 0; }
+
+static inline double v_value(int c, uint16_t scale, uint16_t zero)
+{
+    return g_exact_v ? o_half_to_double(zero) + (double)c * o_half_to_double(scale) : dequant(c, scale, zero);
+}
+
 /* LayerNorm over h features: biased variance, eps 1e-5, one rounding. */
 void o_layernorm(const uint16_t *x, int64_t rows, int h, const uint16_t *gain,
                  const uint16_t *shift, uint16_t *y)
@@ -289,6 +307,7 @@ int o_linear_f16(const uint16_t *a, int64_t rows, int in, int out, const uint16_
  * and values dequantized (the cache is int4; compute on fp16 values):
  *   score_t = (sum_i q_i * k_t,i) / sqrt(d),  w_t = exp(score_t - max_t score)
  *   out_i   = fp16_rn(sum_t w_t * v_t,i / sum_t w_t)
+ * (v_t,i as chosen by o_set_exact_v: the fp16 dequantized value by default).
  * Cache layout for the head: codes [T][d/2], scale/zero [T][d/group].
  */
 void o_attend(int d, int group, int T, const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
@@ -315,7 +334,7 @@ void o_attend(int d, int group, int T, const uint16_t *q, const uint8_t *kc, con
     for (int i = 0; i < d; i++) {
         double acc = 0.0;
         for (int t = 0; t < T; t++)
-            acc = acc_add(acc, score[t] * dequant(code_at(vc + (int64_t)t * (d / 2), i),
+            acc = acc_add(acc, score[t] * v_value(code_at(vc + (int64_t)t * (d / 2), i),
                                                   vs[(int64_t)t * ng + i / group], vz[(int64_t)t * ng + i / group]));
         out[i] = o_double_to_half(acc / den);
     }
@@ -492,6 +511,70 @@ int o_kv_export(const o_kv *c, int head, int t0, int t1, uint8_t *kc, uint16_t *
     memcpy(kz, c->kz + base * ng, sizeof(uint16_t) * (size_t)(n * ng));
     memcpy(vs, c->vs + base * ng, sizeof(uint16_t) * (size_t)(n * ng));
     memcpy(vz, c->vz + base * ng, sizeof(uint16_t) * (size_t)(n * ng));
+    return 0;
+}
+
+/* Store positions [t0, t1) of one head from the canonical per-position format
+ * (the inverse of o_kv_export): codes [t1-t0][d/2], params [t1-t0][d/group]. */
+int o_kv_load(o_kv *c, int head, int t0, int t1, const uint8_t *kc, const uint16_t *ks, const uint16_t *kz,
+              const uint8_t *vc, const uint16_t *vs, const uint16_t *vz)
+{
+    const int d = c->dm.head_dim, ng = d / c->dm.group;
+    if (head < 0 || head >= c->dm.n_heads || t0 < 0 || t1 > c->cap || t0 > t1)
+        return -1;
+    const int64_t base = (int64_t)head * c->cap + t0, n = t1 - t0;
+    memcpy(c->kc + base * (d / 2), kc, (size_t)(n * (d / 2)));
+    memcpy(c->vc + base * (d / 2), vc, (size_t)(n * (d / 2)));
+    memcpy(c->ks + base * ng, ks, sizeof(uint16_t) * (size_t)(n * ng));
+    memcpy(c->kz + base * ng, kz, sizeof(uint16_t) * (size_t)(n * ng));
+    memcpy(c->vs + base * ng, vs, sizeof(uint16_t) * (size_t)(n * ng));
+    memcpy(c->vz + base * ng, vz, sizeof(uint16_t) * (size_t)(n * ng));
+    return 0;
+}
+
+/*
+ * The layer of o_layer_forward for positions pos0..pos0+n-1 of one sequence,
+ * except that the K/V cache is taken as given: positions 0..pos0+n-1 must
+ * already hold codes (o_kv_load). The layer's own k and v for these positions
+ * (fp16 [n][h], before quantization) go to k_out / v_out (nullable) and are
+ * not stored. With a cache that o_layer_forward itself filled this equals
+ * o_layer_forward; with another implementation's cache it checks that
+ * implementation's layer on the inputs it actually saw.
+ */
+int o_layer_forward_given_kv(const o_layer *L, const o_kv *c, int pos0, int n, uint16_t *hidden, uint16_t *k_out,
+                             uint16_t *v_out)
+{
+    const int h = L->dm.hidden, H = L->dm.n_heads, d = L->dm.head_dim, f = L->dm.ffn, G = L->dm.group;
+    if (pos0 < 0 || pos0 + n > c->cap || n <= 0)
+        return -4;
+    uint16_t *a = malloc(sizeof(uint16_t) * (size_t)n * h);
+    uint16_t *q = malloc(sizeof(uint16_t) * (size_t)n * h);
+    uint16_t *k = malloc(sizeof(uint16_t) * (size_t)n * h);
+    uint16_t *v = malloc(sizeof(uint16_t) * (size_t)n * h);
+    uint16_t *o = malloc(sizeof(uint16_t) * (size_t)n * h);
+    uint16_t *u = malloc(sizeof(uint16_t) * (size_t)n * f);
+    o_layernorm(hidden, n, h, L->ln1_g, L->ln1_b, a);
+    linear_rows(a, n, h, h, L->w[W_Q], L->bias[W_Q], NULL, 0, q);
+    linear_rows(a, n, h, h, L->w[W_K], L->bias[W_K], NULL, 0, k);
+    linear_rows(a, n, h, h, L->w[W_V], L->bias[W_V], NULL, 0, v);
+    if (k_out)
+        memcpy(k_out, k, sizeof(uint16_t) * (size_t)n * h);
+    if (v_out)
+        memcpy(v_out, v, sizeof(uint16_t) * (size_t)n * h);
+    const int ng = d / G;
+#pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int t = 0; t < n; t++)
+        for (int hd = 0; hd < H; hd++) {
+            const int64_t base = (int64_t)hd * c->cap;
+            o_attend(d, G, pos0 + t + 1, q + (int64_t)t * h + (int64_t)hd * d, c->kc + base * (d / 2),
+                     c->ks + base * ng, c->kz + base * ng, c->vc + base * (d / 2), c->vs + base * ng,
+                     c->vz + base * ng, o + (int64_t)t * h + (int64_t)hd * d);
+        }
+    linear_rows(o, n, h, h, L->w[W_O], L->bias[W_O], hidden, 0, hidden);
+    o_layernorm(hidden, n, h, L->ln2_g, L->ln2_b, a);
+    linear_rows(a, n, h, f, L->w[W_FC1], L->bias[W_FC1], NULL, 1, u);
+    linear_rows(u, n, f, h, L->w[W_FC2], L->bias[W_FC2], hidden, 0, hidden);
+    free(a); free(q); free(k); free(v); free(o); free(u);
     return 0;
 }
 

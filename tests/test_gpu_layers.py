@@ -1,0 +1,165 @@
+"""Teacher-forced per-layer parity at full width and full depth.
+
+The GPU runs a whole workload (prefill of every prompt, then one decode step)
+with taps on a few layers: the residual-stream rows entering and leaving each
+tapped layer are copied out (``set_layer_tap``), and the int4 KV cache the
+layer attended over is read back (``export_kv``). The oracle then recomputes
+each tapped layer on exactly those inputs: the GPU's input rows and the
+GPU's cache (``Layer.forward_given_kv``), so an element-wise bar applies at
+any depth. Everything the oracle computes comes from its own weights
+(quantized by its own quantizer) and its own arithmetic; the GPU supplies
+only the inputs of the function under test.
+
+Checked per tapped layer:
+  * decode: the first and last rows of the block at the new position;
+  * prefill: sampled positions of the block's last sequence, spanning the
+    64-query tiles of the MFMA prefill attention and the causal mask across
+    tiles;
+  * the int4 codes of the new K/V (the oracle quantizes its own k, v).
+Bars (the readings are in the design notes):
+  * against the oracle's exact-V reading (attention on zero + c * scale, not
+    rounded; the only rounding the GPU's attention leaves out): every
+    element within 2 fp16 ulps;
+  * against the pages' reading (each V element rounded to fp16 first): the
+    two readings differ by up to half an ulp of the largest cached value,
+    which the later GEMMs carry forward, so that comparison is reported and
+    held to the bound the exact-V difference implies (printed);
+  * K/V codes: bit-exact except where the fp16 k or v itself differs by an
+    ulp across a code threshold (agreement reported, >= 0.999).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import to_dev, to_np16, torch_cuda, ulps
+
+pytestmark = pytest.mark.gpu
+
+# (workload, layers: decode count, tapped layers, weight variant, weight tier)
+CASES = {
+    # the benchmark's own configuration: 48 layers, 512 rows, prompt 512, its plain weights
+    "opt-30b": dict(workload="opt-30b", n_layers=None, taps=(0, 23, 47), variant="plain"),
+    # OPT-6.7B shape at full depth, full weights (biases and LayerNorm parameters drawn)
+    "opt-6.7b": dict(workload="opt-6.7b", n_layers=None, taps=(0, 15, 31), variant="full"),
+    # OPT-175B width on its own tier (fp16 weights streamed from pinned host memory), 4 layers
+    "opt-175b": dict(workload="opt-175b", n_layers=4, taps=(0, 3), variant="full"),
+}
+PREFILL_POSITIONS = (0, 1, 63, 64, 65, 127, 200, 383, 447, 448, 510, 511)
+
+
+def _export_cache(tod, torch, m, layer, row, shape, T):
+    """The GPU's int4 cache of (layer, block 0, row) for positions 0..T-1, every head,
+    as an oracle KVCache, plus the codes of the last position per head."""
+    d = shape.head_dim
+    cache = oracle.KVCache(shape, T)
+    kc = torch.empty((T, d // 2), dtype=torch.uint8, device="cuda")
+    vc = torch.empty_like(kc)
+    ks, kz, vs, vz = (torch.empty((T, d // 64), dtype=torch.float16, device="cuda") for _ in range(4))
+    last = []
+    for head in range(shape.n_heads):
+        tod.export_kv(m.handle, layer, 0, row, head, 0, T, kc, ks, kz, vc, vs, vz)
+        torch.cuda.synchronize()
+        arr = (kc.cpu().numpy(), to_np16(ks), to_np16(kz), vc.cpu().numpy(), to_np16(vs), to_np16(vz))
+        cache.load(head, 0, *arr)
+        last.append(arr)
+    return cache, last
+
+
+def _code_agreement(shape, gpu_arrays, k, v, positions):
+    """Fraction of K/V code and parameter bytes equal between the GPU cache at `positions` and the
+    oracle's quantization of its own k, v rows (one row per position)."""
+    T = len(positions)
+    own = oracle.KVCache(shape, T)
+    own.store(0, k, v)
+    agree = total = 0
+    for head, arr in enumerate(gpu_arrays):
+        ref = own.export(head, 0, T)
+        for x, y in zip(arr, ref):
+            x = np.asarray(x)[list(positions)].view(np.uint8)
+            y = np.asarray(y).view(np.uint8)
+            agree += int((x == y).sum())
+            total += x.size
+    return agree / total
+
+
+def _report(label, got, ref_exact, ref_rounded):
+    ue, ur = ulps(got, ref_exact), ulps(got, ref_rounded)
+    print(f"{label}: vs exact-V max {ue.max():.0f} ulp, {np.mean(ue == 0):.4f} equal | "
+          f"vs rounded-V max {ur.max():.0f} ulp, {np.mean(ur == 0):.4f} equal, "
+          f"max-abs {np.abs(got.astype(np.float64) - ref_rounded.astype(np.float64)).max():.3g}", flush=True)
+    return ue, ur
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(CASES))
+def test_teacher_forced_layers(name):
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    case = CASES[name]
+    w = synth.WORKLOADS[case["workload"]]
+    shape = w.shape if case["n_layers"] is None else w.shape.replace(n_layers=case["n_layers"])
+    M, s, h = w.rows, w.prompt_len, shape.hidden
+    tier = w.weight_tier
+    run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=s, gen_len=w.gen_len,
+               weight_tier=tier)
+    print(f"{name}: {shape.n_layers} layers, {M} rows, prompt {s}, tier {tier}, taps {case['taps']}", flush=True)
+    m = tod.Model(shape, run)
+    glob = synth.global_weights(shape, variant=case["variant"])
+    m.set_global_weights(glob["tok_emb"], glob["pos_emb"], glob["lnf_g"], glob["lnf_b"])
+    for l in range(shape.n_layers):
+        m.set_layer_weights(l, synth.layer_weights(shape, l, variant=case["variant"]))
+    pseq = M - 1  # the last sequence of the block's last batch
+    bufs = {}
+    for l in case["taps"]:
+        bufs[l] = [torch.empty((n, h), dtype=torch.float16, device="cuda") for n in (s, s, M, M)]
+        tod.set_layer_tap(m.handle, "prefill", l, pseq * s, s, bufs[l][0], bufs[l][1])
+        tod.set_layer_tap(m.handle, "decode", l, 0, M, bufs[l][2], bufs[l][3])
+    prompts = synth.prompt_ids(M, s, shape.vocab)
+    first = torch.empty(M, dtype=torch.int32, device="cuda")
+    tod.prefill(m.handle, 0, to_dev(prompts, torch), first)
+    out = torch.empty((1, M), dtype=torch.int32, device="cuda")
+    tod.decode_block(m.handle, 0, 1, first, out)
+    torch.cuda.synchronize()
+    print("GPU prefill + 1 decode step done", flush=True)
+    worst = {"exact": 0.0, "rounded": 0.0}
+    code_rates = []
+    for l in case["taps"]:
+        pin, pout, din, dout = (to_np16(b) for b in bufs[l])
+        layer = oracle.Layer(shape, synth.layer_weights(shape, l, variant=case["variant"]), int4_weights=tier != 1)
+        for row in (0, M - 1):
+            cache, arrays = _export_cache(tod, torch, m, l, row, shape, s + 1)
+            ref, k, v = layer.forward_given_kv(cache, s, din[row:row + 1])
+            with oracle.exact_v():
+                ref_x, _, _ = layer.forward_given_kv(cache, s, din[row:row + 1])
+            ue, ur = _report(f"layer {l} decode row {row}", dout[row:row + 1], ref_x, ref)
+            worst["exact"] = max(worst["exact"], ue.max())
+            worst["rounded"] = max(worst["rounded"], ur.max())
+            rate = _code_agreement(shape, arrays, k, v, [s])
+            code_rates.append(rate)
+            print(f"layer {l} decode row {row}: new-position K/V byte agreement {rate:.5f}", flush=True)
+            if row == pseq:
+                got, refs, refs_x, ks_, vs_ = [], [], [], [], []
+                for t in PREFILL_POSITIONS:
+                    r_, k_, v_ = layer.forward_given_kv(cache, t, pin[t:t + 1])
+                    with oracle.exact_v():
+                        rx_, _, _ = layer.forward_given_kv(cache, t, pin[t:t + 1])
+                    got.append(pout[t:t + 1])
+                    refs.append(r_)
+                    refs_x.append(rx_)
+                    ks_.append(k_)
+                    vs_.append(v_)
+                ue, ur = _report(f"layer {l} prefill row {row} positions {PREFILL_POSITIONS}",
+                                 np.concatenate(got), np.concatenate(refs_x), np.concatenate(refs))
+                worst["exact"] = max(worst["exact"], ue.max())
+                worst["rounded"] = max(worst["rounded"], ur.max())
+                rate = _code_agreement(shape, arrays, np.concatenate(ks_), np.concatenate(vs_), PREFILL_POSITIONS)
+                code_rates.append(rate)
+                print(f"layer {l} prefill row {row}: K/V byte agreement {rate:.5f}", flush=True)
+            cache.close()
+        layer.close()
+    m.close()
+    print(f"{name}: worst {worst['exact']:.0f} ulp vs exact-V, {worst['rounded']:.0f} ulp vs rounded-V; "
+          f"K/V agreement min {min(code_rates):.5f}", flush=True)
+    assert worst["exact"] <= 2
+    assert min(code_rates) >= 0.999

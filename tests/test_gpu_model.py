@@ -74,28 +74,56 @@ def fp32_bars(shape, layers, glob, prompts, g, K, ref_tokens, ref_logits):
     return max(LOGIT_MAX_ABS, 2.0 * d.max()), max(LOGIT_MEAN_ABS, 1.5 * d.mean())
 
 
-@pytest.mark.parametrize("tier", [0, 1, 2])
-def test_opt125m_full_generation(tier):
-    """OPT-125m shape, 4 x 2 batches, prompt 32, 8 generated tokens: every logit checked."""
+# (weight tier, placement fields): the three tiers as they are, then every placement path --
+# leading layers resident while the rest stream, trailing layers' KV caches in pinned host memory,
+# streamed images read from a file -- each against the same free-running oracle
+PLACEMENTS = [
+    (0, {}), (1, {}), (2, {}),
+    (0, dict(kv_host_layers=6)),
+    (1, dict(hbm_layers=6)), (1, dict(kv_host_layers=6)), (1, dict(weights_on_disk=1, hbm_layers=3)),
+    (2, dict(hbm_layers=6, kv_host_layers=6)), (2, dict(weights_on_disk=1)),
+]
+_C1_ORACLE = {}
+
+
+def _c1_oracle(shape, glob, prompts, w, int4):
+    """The oracle's free-running C1 generation and its fp32-drift bars, once per weight precision."""
+    if int4 not in _C1_ORACLE:
+        layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full"), int4_weights=int4)
+                  for l in range(shape.n_layers)]
+        ot, ol, loads = oracle.generate(shape, layers, glob, prompts, w.gen_len, w.batches_per_block,
+                                        oracle.SCHED_ZIGZAG)
+        bars = fp32_bars(shape, layers, glob, prompts, w.gen_len, w.batches_per_block, ot, ol)
+        _C1_ORACLE[int4] = (layers, ot, ol, loads, bars)
+    return _C1_ORACLE[int4]
+
+
+@pytest.mark.parametrize("tier,placement", PLACEMENTS,
+                         ids=[f"tier{t}" + "".join(f"-{k}{v}" for k, v in p.items()) for t, p in PLACEMENTS])
+def test_opt125m_full_generation(tier, placement, tmp_path):
+    """OPT-125m shape, 4 x 2 batches, prompt 32, 8 generated tokens: every logit checked against
+    the free-running oracle, on each weight tier and each placement of weights and KV cache."""
     torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
     w = synth.WORKLOADS["opt-125m"]
     shape = w.shape
     run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=w.prompt_len,
-               gen_len=w.gen_len, weight_tier=tier)
-    m, glob = build_gpu_model(shape, run)
+               gen_len=w.gen_len, weight_tier=tier, **placement)
+    print(f"opt-125m tier {tier} placement {placement}", flush=True)
+    m = tod.Model(shape, run, weight_file=str(tmp_path / "images.bin") if placement.get("weights_on_disk") else None)
+    glob = synth.global_weights(shape, variant="full")
+    m.set_global_weights(glob["tok_emb"], glob["pos_emb"], glob["lnf_g"], glob["lnf_b"])
+    for l in range(shape.n_layers):
+        m.set_layer_weights(l, synth.layer_weights(shape, l, variant="full"))
     prompts = synth.prompt_ids(w.rows, w.prompt_len, shape.vocab)
     toks, logits = m.generate(to_dev(prompts, torch), w.gen_len, return_logits=True)
     torch.cuda.synchronize()
     gt = toks.cpu().numpy()
     gl = to_np16(logits)
-    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full"), int4_weights=tier != 1)
-              for l in range(shape.n_layers)]
-    ot, ol, loads = oracle.generate(shape, layers, glob, prompts, w.gen_len, w.batches_per_block,
-                                    oracle.SCHED_ZIGZAG)
+    layers, ot, ol, loads, (max_bar, mean_bar) = _c1_oracle(shape, glob, prompts, w, tier != 1)
     assert loads == w.gen_len * shape.n_layers
     print(f"token agreement with the oracle: {np.mean(gt == ot):.4f}", flush=True)
-    max_bar, mean_bar = fp32_bars(shape, layers, glob, prompts, w.gen_len, w.batches_per_block, ot, ol)
-    compare(gt, gl, ot, ol, f"opt-125m tier {tier}", max_bar, mean_bar)
+    compare(gt, gl, ot, ol, f"opt-125m tier {tier} {placement}", max_bar, mean_bar)
     if tier != 1:
         import throughput_oriented_offloaded_amd as tod
         for l in (0, shape.n_layers - 1):
@@ -347,6 +375,24 @@ def test_opt125m_shallow_meets_stated_bar(n_layers):
     layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full")) for l in range(n_layers)]
     ot, ol, _ = oracle.generate(shape, layers, glob, prompts, g, K, oracle.SCHED_ZIGZAG)
     compare(toks.cpu().numpy(), to_np16(logits), ot, ol, f"opt-125m depth {n_layers}")
+    m.close()
+
+
+@pytest.mark.parametrize("prompt_len", [130, 200])
+def test_opt125m_long_prompt_meets_stated_bar(prompt_len):
+    """Prompts of 130 and 200 tokens: prefill attention runs 3 and 4 query tiles of 64, the last
+    one ragged, with earlier key tiles unmasked and the online softmax rescaled across tiles; at
+    depth 2 the stated logit bar applies as is."""
+    torch = torch_cuda()
+    shape = synth.OPT_125M.replace(n_layers=2)
+    s, g, b, K = prompt_len, 4, 2, 2
+    m, glob = build_gpu_model(shape, dict(gpu_batch=b, batches_per_block=K, prompt_len=s, gen_len=g))
+    prompts = synth.prompt_ids(b * K, s, shape.vocab)
+    toks, logits = m.generate(to_dev(prompts, torch), g, return_logits=True)
+    torch.cuda.synchronize()
+    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full")) for l in range(2)]
+    ot, ol, _ = oracle.generate(shape, layers, glob, prompts, g, K, oracle.SCHED_ZIGZAG)
+    compare(toks.cpu().numpy(), to_np16(logits), ot, ol, f"opt-125m depth 2 prompt {s}")
     m.close()
 
 

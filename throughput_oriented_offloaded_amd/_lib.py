@@ -27,7 +27,7 @@ EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", 
             "last_error",
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
             "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read",
-            "default_hw", "estimate_decode", "plan_decode", "set_weight_file")
+            "default_hw", "estimate_decode", "plan_decode", "set_weight_file", "set_layer_tap")
 KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
                 "argmax", "embed")
 
@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
         "estimate_decode": [vp, vp, vp, vp],
         "plan_decode": [vp, i32, i32, i32, vp, vp, vp],
         "set_weight_file": [vp, ctypes.c_char_p],
+        "set_layer_tap": [vp, i32, i32, i64, i64, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(L, name)
@@ -187,6 +188,12 @@ def set_decode_position(m, block: int, steps: int):
 
 def set_decode_graph(m, enable: bool):
     _check("set_decode_graph", lib().set_decode_graph(m, int(bool(enable))))
+
+
+def set_layer_tap(m, phase: str, layer: int, row0: int = 0, n_rows: int = 0, t_in=None, t_out=None):
+    """phase "prefill" or "decode"; n_rows 0 removes the tap."""
+    ph = {"prefill": 0, "decode": 1}[phase]
+    _check("set_layer_tap", lib().set_layer_tap(m, ph, layer, row0, n_rows, _ptr(t_in), _ptr(t_out)))
 
 
 def free_model(m):

@@ -140,6 +140,14 @@ struct tod_model {
     std::vector<Pending> pend;
     double prof_ms[TOD_K_COUNT] = {};
     int64_t prof_n[TOD_K_COUNT] = {};
+    // test taps (set_layer_tap): per phase (0 prefill, 1 decode) and layer, a range of the
+    // pass's hidden rows copied out before and after the layer
+    struct Tap {
+        int64_t row0 = 0, n = 0;
+        uint16_t *in = nullptr, *out = nullptr;
+    };
+    std::vector<Tap> taps[2];
+    int n_decode_taps = 0;
 };
 
 struct tod_attn_cache {
@@ -343,6 +351,25 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         return rc;
     if ((rc = run_gemm(m, m->ffn, rows, MAT_FC2, L, wslot, h, hd, EPI_BIAS_RES, st, next_g, next_b)))
         return rc;
+    return TOD_OK;
+}
+
+// Test taps: copy the tapped rows that lie among the `rows` hidden rows at h (global rows
+// r0 .. r0 + rows - 1 of the pass) into the tap's `in` buffer (before the layer) or its
+// `out` buffer (after it), on the pass's stream.
+int tap_copy(tod_model *m, int phase, int l, const uint16_t *h, int64_t r0, int64_t rows, bool after,
+             hipStream_t st)
+{
+    if (m->taps[phase].empty())
+        return TOD_OK;
+    const tod_model::Tap &t = m->taps[phase][l];
+    uint16_t *dst = after ? t.out : t.in;
+    const int64_t lo = t.row0 > r0 ? t.row0 : r0, hi = t.row0 + t.n < r0 + rows ? t.row0 + t.n : r0 + rows;
+    if (t.n <= 0 || !dst || lo >= hi)
+        return TOD_OK;
+    const int64_t hd = m->cfg.hidden;
+    HIPCHK(hipMemcpyAsync(dst + (lo - t.row0) * hd, h + (lo - r0) * hd, (size_t)((hi - lo) * hd) * 2,
+                          hipMemcpyDeviceToDevice, st));
     return TOD_OK;
 }
 
@@ -1023,16 +1050,22 @@ int prefill(tod_model *m, int block, const int32_t *d_ids, int32_t *d_next, uint
             HIPCHK(launch_embed(d_ids + k * brow, (int)brow, s, 0, nullptr, m->tok_emb, m->cfg.vocab, m->pos_emb, h,
                                     m->hid + k * brow * h, st));
         }
-        rc = stack_pass(m, st, block, 0, [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
+        auto layer = [&](int l, const uint8_t *wslot, const KvView &kv, const KvView *mirror) -> int {
             for (int kk = 0; kk < K; kk++) {
                 const int k = (l & 1) ? K - 1 - kk : kk; // zig-zag: alternate the batch order per layer
-                const int r = layer_pass(m, l, kv, m->hid + k * brow * h, (int)brow, true, k * b, s, 0, nullptr, wslot,
-                                         st, false, nullptr, nullptr, mirror);
+                uint16_t *hk = m->hid + k * brow * h;
+                int r = tap_copy(m, 0, l, hk, k * brow, brow, false, st);
+                if (!r)
+                    r = layer_pass(m, l, kv, hk, (int)brow, true, k * b, s, 0, nullptr, wslot, st, false, nullptr,
+                                   nullptr, mirror);
+                if (!r)
+                    r = tap_copy(m, 0, l, hk, k * brow, brow, true, st);
                 if (r)
                     return r;
             }
             return TOD_OK;
-        });
+        };
+        rc = stack_pass(m, st, block, 0, layer);
         if (rc)
             return rc;
         HIPCHK(launch_gather_rows(m->hid + (int64_t)(s - 1) * h, (int64_t)s * h, m->M, h, m->last, st));
@@ -1063,7 +1096,12 @@ static int decode_step(tod_model *m, int block, const int32_t *in, int pos, cons
         const bool last = l + 1 == L;
         const uint16_t *ng = last ? m->lnf_g : m->layers[l + 1].ln1_g;
         const uint16_t *nb = last ? m->lnf_b : m->layers[l + 1].ln1_b;
-        return layer_pass(m, l, kv, m->hid, Mr, false, 0, 1, pos, dpos, wslot, st, l > 0, ng, nb, mirror);
+        int r = tap_copy(m, 1, l, m->hid, 0, Mr, false, st);
+        if (!r)
+            r = layer_pass(m, l, kv, m->hid, Mr, false, 0, 1, pos, dpos, wslot, st, l > 0, ng, nb, mirror);
+        if (!r)
+            r = tap_copy(m, 1, l, m->hid, 0, Mr, true, st);
+        return r;
     };
     int rc = stack_pass(m, st, block, pos, layer);
     if (rc)
@@ -1119,7 +1157,7 @@ int decode_block(tod_model *m, int block, int n_steps, const int32_t *d_ids_in, 
                         m->run.gen_len - 1, m->decoded[block], n_steps);
         const hipStream_t st = S(stream);
         const int Mr = m->M, V = m->cfg.vocab;
-        const bool graph = n_steps > 0 && m->graphs_on && !m->prof_mask && m->gstream &&
+        const bool graph = n_steps > 0 && m->graphs_on && !m->prof_mask && !m->n_decode_taps && m->gstream &&
                            m->run.weight_tier == TOD_W_HBM_INT4 && m->kv_host == 0 && !m->gfail[block] &&
                            (m->gexec[block] || capture_step(m, block) || (m->gfail[block] = 1, false));
         if (graph) {
@@ -1159,6 +1197,36 @@ int set_decode_graph(tod_model *m, int enable)
         if (!m)
             return fail(TOD_EINVAL, "null model");
         m->graphs_on = enable != 0;
+        return TOD_OK;
+    });
+}
+
+int set_layer_tap(tod_model *m, int phase, int layer, int64_t row0, int64_t n_rows, uint16_t *d_in,
+                  uint16_t *d_out)
+{
+    return guard("set_layer_tap", [&]() -> int {
+        if (!m)
+            return fail(TOD_EINVAL, "null model");
+        if (phase != 0 && phase != 1)
+            return fail(TOD_EINVAL, "phase must be 0 (prefill) or 1 (decode), got %d", phase);
+        if (layer < 0 || layer >= m->cfg.n_layers)
+            return fail(TOD_EINVAL, "layer %d out of range", layer);
+        const int64_t limit = phase == 0 ? (int64_t)m->M * m->run.prompt_len : (int64_t)m->M;
+        if (n_rows < 0 || row0 < 0 || row0 + n_rows > limit)
+            return fail(TOD_EINVAL, "tap rows [%lld, %lld) outside the pass's %lld rows", (long long)row0,
+                        (long long)(row0 + n_rows), (long long)limit);
+        if (n_rows > 0 && !d_in && !d_out)
+            return fail(TOD_EINVAL, "a tap needs d_in or d_out");
+        std::vector<tod_model::Tap> &taps = m->taps[phase];
+        if (taps.empty())
+            taps.resize(m->cfg.n_layers);
+        tod_model::Tap &t = taps[layer];
+        if (phase == 1)
+            m->n_decode_taps += (n_rows > 0) - (t.n > 0);
+        t.row0 = row0;
+        t.n = n_rows;
+        t.in = d_in;
+        t.out = d_out;
         return TOD_OK;
     });
 }
