@@ -46,6 +46,7 @@
 #ifndef TOD_H
 #define TOD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -427,6 +428,10 @@ typedef struct {
 } tod_estimate;
 void default_hw(tod_hw *hw);
 int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, const tod_hw *hw, tod_estimate *out);
+/* estimate_gemm: the seconds estimate_decode charges one GEMM of rows x out x in (int4 != 0: int4
+ * weights, else fp16), on the tile plan the library launches for that shape. TOD_EINVAL for a shape
+ * the GEMM does not take (in % 64, int4 out % 32, rows outside [1, 2^24]) or invalid rates. */
+int estimate_gemm(int64_t rows, int out, int in, int int4, const tod_hw *hw, double *seconds);
 int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int max_rows, const tod_hw *hw,
                 tod_run_config *best, tod_estimate *est);
 

@@ -19,22 +19,17 @@ Two models are given:
   row-by-row moves K times the bytes.
 
 A third part, ``decode_step`` / ``footprint`` / ``plan``, prices one decode
-step of the library's block schedule from measured rates, and searches the
-run configurations for the most tokens per second under memory capacities.
-It extends the simulator's "time = bytes moved / link rate" with the
-roofline terms of the step (GEMM flops, KV-cache reads) and with the
-placement choices that the FlexLLMGen overview ("A 175B-parameter model on
-one GPU, if you can wait": caveats) leaves to manual flags. It is written
-from that definition, term by term, for the parity tests of the library's
-own cost model. With free compute and an all-streamed fp16 model it reduces
-to the simulator's formula (pinned against the printed figures). Each GEMM
-is priced on the tile plan the library's GEMM takes for its shape
-(``gemm_plan``, the planner's rule restated): how many workgroups it
-launches, how many K-groups each runs, and whether split-K partials go
-through memory. A flat GEMM rate misses small-batch GEMMs by up to 2x, since
-their K loops split 4 to 16 ways. The device footprint here leaves out the library's split-K workspace, a GEMM-plan
-detail of a few tens of MB; the parity tests keep capacities far from every
-candidate's footprint so that the omission cannot change a fit decision.
+step of the block schedule from measured rates, and searches the run
+configurations for the most tokens per second under memory capacities. It
+extends the simulator's "time = bytes moved / link rate" with the roofline
+terms of the step (GEMM flops, KV-cache reads) and with the placement choices
+that the FlexLLMGen overview ("A 175B-parameter model on one GPU, if you can
+wait": caveats) leaves to manual flags. It is written from those terms alone
+and knows nothing of how any implementation tiles its GEMMs: a GEMM costs the
+larger of its flops at the GEMM rate and its weight bytes at the streaming
+rate, plus one fixed cost. With free compute and an all-streamed fp16 model it
+reduces to the simulator's formula (pinned against the printed figures). The
+device footprint here leaves out an implementation's GEMM workspace.
 """
 from __future__ import annotations
 
@@ -93,79 +88,17 @@ def _kernel(seconds: float, hw: dict) -> float:
     return max(seconds, hw["launch_us"] * 1e-6)
 
 
-ROW_CAP = 1 << 24  # the library's limit on a block's rows and on a prefill's rows
-CUS = 256  # MI355X compute units: one workgroup of the pipelined int4 GEMM each
-
-
-def gemm_plan(rows: int, n_out: int, n_in: int, int4: bool):
-    """The tile plan of the library's pipelined GEMM, restated from its rule (None when the
-    register-staged kernel runs: fp16 weights whose N is not a multiple of 32, or int4 weights at
-    128 rows or fewer whose pipelined plan would launch fewer than 128 workgroups).
-
-    Tiles are 256 outputs wide. int4 tiles are 256, 192 or 128 rows tall above 128 rows and 128
-    or 64 rows at 128 rows or fewer; fp16 tiles are 256 rows tall above 128 rows and 64 below.
-    The K loop (K-groups of 64) is split in powers of two while the tiles times the splits stay
-    below 160 workgroups and each split keeps at least 8 K-groups. Of the tile heights the one
-    with the least predicted time is taken, the earlier listed on a tie, where that time counts
-    1.6 us per K-group of a 256 x 256 tile (times rows / 256 and an efficiency loss of 1.1 at 128
-    rows and 1.5 at 64) per wave of 256 workgroups, 25 us per wave of resident workgroups (two
-    per CU at 128 rows or fewer), and split-K partials written and read at 7.1 TB/s."""
-    if not int4 and n_out % 32:
-        return None
-    if int4:
-        heights = (256, 192, 128) if rows > 128 else (128, 64)
-    else:
-        heights = (256,) if rows > 128 else (64,)
-    groups = n_in // 64
-    best = None
-    for tile_rows in heights:
-        tiles = -(-rows // tile_rows) * -(-n_out // 256)
-        splits = 1
-        while tiles * splits < 160 and groups // (splits * 2) >= 8:
-            splits *= 2
-        per_split = -(-groups // splits)
-        splits = -(-groups // per_split)
-        workgroups = tiles * splits
-        loss = 1.5 if tile_rows <= 64 else 1.1 if tile_rows <= 128 else 1.0
-        slots = 2 * CUS if tile_rows <= 128 else CUS
-        cost = (-(-workgroups // CUS) * per_split * (tile_rows / 256.0) * 1.6 * loss
-                + -(-workgroups // slots) * 25.0)
-        if splits > 1:
-            cost += 2.0 * splits * rows * n_out * 4.0 / 7.1e6
-        if best is None or cost < best["cost"]:
-            best = dict(cost=cost, tile_rows=tile_rows, splits=splits, groups_per_split=per_split,
-                        workgroups=workgroups)
-    if int4 and rows <= 128 and best["workgroups"] < 128:
-        return None
-    return best
+ROW_CAP = 1 << 24  # most rows of a block and of one prefill batch
 
 
 def gemm_time(rows: int, n_out: int, n_in: int, int4: bool, hw: dict) -> float:
-    """Seconds for one GEMM. The pipelined kernel runs its workgroups in waves of one per CU: a wave
-    costs its K-groups per workgroup times one K-group of a 256 x 256 tile at the steady int4 or
-    fp16 rate (scaled by the tile's rows), plus the fixed cost per wave, and no less than its weight
-    bytes at the streaming rate plus that fixed cost; a split K loop adds its fp32 partials,
-    written and read back at the streaming rate. The register-staged kernel costs its own fixed
-    time plus its weight bytes and its flops, each at that kernel's own rate."""
-    mem = hw["mem_gbs"] * 1e9
-    plan = gemm_plan(rows, n_out, n_in, int4)
+    """Seconds for one GEMM of rows x n_out x n_in: the larger of its flops 2 * rows * n_out * n_in
+    at the GEMM rate (int4 or fp16 weights) and its weight bytes (0.5625 or 2 per weight) at the
+    streaming rate, plus the fixed cost of one GEMM (gemm_wg_us), and at least one launch."""
+    rate = (hw["int4_tflops"] if int4 else hw["fp16_tflops"]) * 1e12
     weight_bytes_ = n_out * n_in * (0.5 + 4.0 / 64 if int4 else 2.0)
-    if plan is not None:
-        rate = hw["int4_tflops"] if int4 else hw["fp16_tflops"]
-        group = CUS * 2.0 * 256 * 256 * 64 / (rate * 1e12)
-        rows_ = plan["tile_rows"]
-        loss = 1.0 if not int4 else 1.5 if rows_ <= 64 else 1.1 if rows_ <= 128 else 1.0
-        slots = 2 * CUS if int4 and rows_ <= 128 else CUS
-        seconds = (-(-plan["workgroups"] // CUS) * plan["groups_per_split"] * (rows_ / 256) * loss * group
-                   + -(-plan["workgroups"] // slots) * hw["gemm_wg_us"] * 1e-6)
-        # no faster than its weight stream (an fp16 GEMM of few rows is bound there)
-        seconds = max(seconds, weight_bytes_ / mem + hw["gemm_wg_us"] * 1e-6)
-        if plan["splits"] > 1:
-            seconds += 2.0 * plan["splits"] * rows * n_out * 4.0 / mem
-    else:
-        seconds = (hw["staged_us"] * 1e-6 + weight_bytes_ / (hw["staged_gbs"] * 1e9)
-                   + 2.0 * rows * n_out * n_in / (hw["staged_tflops"] * 1e12))
-    return _kernel(seconds, hw)
+    seconds = max(2.0 * rows * n_out * n_in / rate, weight_bytes_ / (hw["mem_gbs"] * 1e9))
+    return _kernel(seconds + hw["gemm_wg_us"] * 1e-6, hw)
 
 
 def decode_step(shape, run: dict, hw: dict) -> dict:

@@ -182,11 +182,13 @@ def test_estimate_and_plan_null_and_rate_arguments(lib):
 
 def test_plan_keeps_within_the_row_limits():
     """With room for anything, the search stops at the library's row limits: b * K and b * prompt_len
-    at most 2^24 (init_model rejects more), the same choice as the oracle's search."""
+    at most 2^24 (init_model rejects more), the same choice as the oracle's search (GEMMs made free,
+    where the two step models agree exactly)."""
     from oracle import costmodel
     from throughput_oriented_offloaded_amd import _lib
     shape = synth.OPT_125M.replace(n_layers=2)
-    hw = dict(_lib.default_hw(), hbm_bytes=1e18, host_bytes=1e18, disk_bytes=1e18)
+    hw = dict(_lib.default_hw(), hbm_bytes=1e18, host_bytes=1e18, disk_bytes=1e18, int4_tflops=1e30,
+              fp16_tflops=1e30, staged_tflops=1e30, staged_gbs=1e30, staged_us=0.0, gemm_wg_us=0.0, mem_gbs=1e30)
     run, est = _lib.plan_decode(shape, 2048, 1, 1 << 15, hw)
     assert run["gpu_batch"] * 2048 <= 1 << 24 and run["gpu_batch"] * run["batches_per_block"] <= 1 << 15
     ref_run, ref_est = costmodel.plan(shape, 2048, 1, 1 << 15, hw)

@@ -1,4 +1,5 @@
 """Pins of the closed-form cost model against the FlexGen guide's printed simulator output."""
+import math
 import os
 
 import pytest
@@ -134,81 +135,31 @@ def test_images_on_disk():
     assert costmodel.disk_bytes(shape, dict(run, weights_on_disk=0)) == 0.0
 
 
-def test_gemm_plan_splits_and_tile_heights():
-    """The planner rule at the decode shapes: QKV of OPT-30B fills one wave with 192-row tiles,
-    fc1 with 256-row ones and fc2 splits their 56 tiles' K four ways; the out-projection takes
-    112 tiles of 128 rows split twice (half the partials of 256-row tiles split four ways); at
-    256 rows the OPT-6.7B GEMMs take 128-row tiles split 2 or 8 ways; at 128 rows or fewer int4
-    GEMMs take 128- or 64-row tiles, fp16 ones 64-row tiles."""
-    p = costmodel.gemm_plan(512, 21504, 7168, True)
-    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (192, 1, 252)
-    p = costmodel.gemm_plan(512, 28672, 7168, True)
-    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 1, 224, 112)
-    p = costmodel.gemm_plan(512, 7168, 28672, True)
-    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (256, 4, 224, 112)
-    p = costmodel.gemm_plan(512, 7168, 7168, True)
-    assert (p["tile_rows"], p["splits"], p["workgroups"], p["groups_per_split"]) == (128, 2, 224, 56)
-    assert [(p["tile_rows"], p["splits"]) for p in (costmodel.gemm_plan(256, n, k, True) for n, k in
-            ((12288, 4096), (4096, 4096), (16384, 4096), (4096, 16384)))] == [(128, 2), (128, 8), (128, 2), (128, 8)]
-    p = costmodel.gemm_plan(128, 4096, 4096, True)
-    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (64, 8, 256)
-    # OPT-125m's GEMMs at 8 rows would give 3 to 12 workgroups: register-staged
-    assert all(costmodel.gemm_plan(8, n, k, True) is None for n, k in ((2304, 768), (768, 768), (3072, 768),
-                                                                        (768, 3072)))
-    assert [costmodel.gemm_plan(r, 28672, 7168, True)["tile_rows"] for r in (8, 64, 128)] == [64, 64, 128]
-    p = costmodel.gemm_plan(8, 50272, 7168, False)
-    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (64, 1, 197)
-    p = costmodel.gemm_plan(512, 50272, 7168, False)  # the fp16 LM head: 256-row tiles, two waves
-    assert (p["tile_rows"], p["splits"], p["workgroups"]) == (256, 1, 394)
-    assert costmodel.gemm_plan(512, 50200, 7168, False) is None  # N not a multiple of 32
-
-
-def test_gemm_in_whole_waves_of_full_tiles_runs_at_the_steady_rate():
-    """With no fixed cost, a GEMM whose 256 x 256 tiles fill whole waves of 256 workgroups, unsplit,
-    takes exactly its flops over the steady int4 rate (one and two waves)."""
-    hw = dict(MI355X, gemm_wg_us=0.0, launch_us=0.0)
-    for rows in (512, 1024):
-        t = costmodel.gemm_time(rows, 32768, 4096, True, hw)
-        assert t == pytest.approx(2.0 * rows * 32768 * 4096 / 1340e12, rel=1e-12)
-
-
-def test_gemm_fixed_cost_counts_once_per_wave():
-    hw = dict(MI355X, int4_tflops=1e30, mem_gbs=1e30, launch_us=0.0, gemm_wg_us=25.0)
-    assert costmodel.gemm_time(512, 32768, 4096, True, hw) == pytest.approx(25e-6, rel=1e-9)
-    assert costmodel.gemm_time(1024, 32768, 4096, True, hw) == pytest.approx(50e-6, rel=1e-9)
-
-
-def test_split_gemm_pays_its_partials_twice():
-    """With free compute and no fixed cost, a GEMM costs its weight stream, and a GEMM whose K loop
-    is split also its fp32 partials (splits x rows x N) written once and read once, all at the
-    streaming rate."""
-    hw = dict(MI355X, int4_tflops=1e30, launch_us=0.0, gemm_wg_us=0.0)
-    weights = 7168 * 28672 * 0.5625 / 7100e9  # fc2 of OPT-30B at 512 rows: K split four ways
-    assert costmodel.gemm_time(512, 7168, 28672, True, hw) == pytest.approx(
-        weights + 2 * 4 * 512 * 7168 * 4 / 7100e9, rel=1e-12)
-    assert costmodel.gemm_time(512, 28672, 7168, True, hw) == pytest.approx(weights, rel=1e-12)
-
-
-def test_register_staged_gemm_limits():
-    """fp16 weights whose N is not a multiple of 32: with free flops and no fixed cost a GEMM is its
-    weight bytes at the kernel's read rate; each added row adds exactly its flops."""
-    hw = dict(MI355X, launch_us=0.0, staged_us=0.0, staged_tflops=1e30)
-    assert costmodel.gemm_plan(128, 4004, 4096, False) is None
-    assert costmodel.gemm_time(128, 4004, 4096, False, hw) == pytest.approx(4004 * 4096 * 2.0 / 3230e9, rel=1e-12)
+def test_gemm_is_the_larger_of_its_flops_and_its_weight_stream():
+    """Closed forms of one GEMM: compute-bound at many rows (flops / rate + the fixed cost), bound by
+    its weight bytes at few rows (bytes / streaming rate + the fixed cost), and the crossover row
+    count where the two terms are equal: rows* = rate x bytes-per-weight / (2 x streaming rate)."""
     hw = dict(MI355X, launch_us=0.0)
-    step = costmodel.gemm_time(65, 4004, 4096, False, hw) - costmodel.gemm_time(64, 4004, 4096, False, hw)
-    assert step == pytest.approx(2.0 * 4004 * 4096 / 1700e12, rel=1e-9)
+    n, k = 28672, 7168
+    assert costmodel.gemm_time(4096, n, k, True, hw) == pytest.approx(2 * 4096 * n * k / 1340e12 + 25e-6, rel=1e-12)
+    assert costmodel.gemm_time(8, n, k, True, hw) == pytest.approx(n * k * 0.5625 / 7100e9 + 25e-6, rel=1e-12)
+    cross = 1340e12 * 0.5625 / (2 * 7100e9)
+    lo, hi = math.floor(cross), math.ceil(cross)
+    assert costmodel.gemm_time(lo, n, k, True, hw) == pytest.approx(n * k * 0.5625 / 7100e9 + 25e-6, rel=1e-12)
+    assert costmodel.gemm_time(hi, n, k, True, hw) == pytest.approx(2 * hi * n * k / 1340e12 + 25e-6, rel=1e-12)
 
 
-def test_pipelined_gemm_is_no_faster_than_its_weight_stream():
-    """With free flops, the fp16 LM head of OPT-30B at 8 rows (one wave, unsplit) costs its weights
-    read once at the streaming rate plus the fixed cost."""
-    hw = dict(MI355X, launch_us=0.0, fp16_tflops=1e30)
-    assert costmodel.gemm_time(8, 50272, 7168, False, hw) == pytest.approx(50272 * 7168 * 2.0 / 7100e9 + 25e-6,
-                                                                           rel=1e-12)
+def test_fp16_weights_use_their_own_rate_and_bytes():
+    hw = dict(MI355X, launch_us=0.0, gemm_wg_us=0.0)
+    assert costmodel.gemm_time(512, 50272, 7168, False, hw) == pytest.approx(2 * 512 * 50272 * 7168 / 1400e12,
+                                                                              rel=1e-12)
+    assert costmodel.gemm_time(8, 50272, 7168, False, hw) == pytest.approx(50272 * 7168 * 2.0 / 7100e9, rel=1e-12)
 
 
-def test_fp16_gemm_in_whole_waves_runs_at_the_fp16_steady_rate():
-    hw = dict(MI355X, gemm_wg_us=0.0, launch_us=0.0)
-    assert costmodel.gemm_time(512, 32768, 4096, False, hw) == pytest.approx(2.0 * 512 * 32768 * 4096 / 1400e12,
-                                                                             rel=1e-12)
+def test_every_kernel_costs_at_least_a_launch():
+    hw = dict(FREE, launch_us=4.0)
+    assert costmodel.gemm_time(1, 64, 64, True, hw) == pytest.approx(4e-6, rel=1e-12)
+    shape = _Shape(2, 64, 1, 64, 256, 100)
+    run = dict(gpu_batch=1, batches_per_block=1, prompt_len=4, gen_len=2)
+    # per layer: 4 GEMMs, attention, KV append; head: embedding, LayerNorm, LM head, argmax
+    assert costmodel.decode_step(shape, run, hw)["step_s"] == pytest.approx((2 * 6 + 4) * 4e-6, rel=1e-12)

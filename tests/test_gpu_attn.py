@@ -15,9 +15,11 @@ below it. That bound is loose by construction, so the outputs are also held
 to the oracle's exact-V reading (the same attention on the exact values
 zero + c*scale, the one rounding the GPU leaves out): there only fp32
 accumulation, the fp32 exp and the output rounding differ, and every element
-must be within 2 fp16 ulps (judged on an absolute floor of 2^-7 near zero),
-with a mean under 0.25 ulp; a loss of a few bits in the offset V accumulation
-fails that. Contexts straddle the kernel's 64-position chunks and its pairs of
+must be within 1 fp16 ulp (judged on an absolute floor of 2^-7 near zero),
+with a mean under 0.05 ulp (measured: at most 1 ulp, mean 0.012 ulp and 97.5%
+bit-equal at 2051 positions); a V accumulation that lost a few bits fails
+that, as the earlier offset form (acc += p*s*(1024 + c)) did at 700 and 2051
+positions. Contexts straddle the kernel's 64-position chunks and its pairs of
 chunks; a scaled query gives sharply peaked softmax weights.
 """
 import numpy as np
@@ -44,8 +46,8 @@ def _spacing16(x):
     return np.spacing(np.abs(np.asarray(x, dtype=np.float64)).astype(np.float16)).astype(np.float64)
 
 
-EXACT_V_MAX_ULP = 2
-EXACT_V_MEAN_ULP = 0.25
+EXACT_V_MAX_ULP = 1
+EXACT_V_MEAN_ULP = 0.05
 
 
 def _check_attention(got, q, ref_cache, label, stats=None):

@@ -32,7 +32,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import to_dev, to_np16, torch_cuda, ulps
+from tests.gpu_util import to_dev, to_np16, torch_cuda
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +46,8 @@ CASES = {
     "opt-175b": dict(workload="opt-175b", n_layers=4, taps=(0, 3), variant="full"),
 }
 PREFILL_POSITIONS = (0, 1, 63, 64, 65, 127, 200, 383, 447, 448, 510, 511)
+ROW_ULP_MAX = 2.0       # every element within 2 fp16 ulps of its row's largest value
+MEAN_ABS_FACTOR = 2.0   # mean error at most twice the fp32-accumulating oracle's drift
 
 
 def _export_cache(tod, torch, m, layer, row, shape, T):
@@ -83,12 +85,33 @@ def _code_agreement(shape, gpu_arrays, k, v, positions):
     return agree / total
 
 
-def _report(label, got, ref_exact, ref_rounded):
-    ue, ur = ulps(got, ref_exact), ulps(got, ref_rounded)
-    print(f"{label}: vs exact-V max {ue.max():.0f} ulp, {np.mean(ue == 0):.4f} equal | "
-          f"vs rounded-V max {ur.max():.0f} ulp, {np.mean(ur == 0):.4f} equal, "
-          f"max-abs {np.abs(got.astype(np.float64) - ref_rounded.astype(np.float64)).max():.3g}", flush=True)
-    return ue, ur
+def _row_ulps(got, ref):
+    """|got - ref| in fp16 ulps of each row's largest |ref|: the scale at which the layer's sums
+    are carried (a row's small elements come out of sums of terms of that size)."""
+    g, r = got.astype(np.float64), ref.astype(np.float64)
+    scale = np.spacing(np.abs(r).max(axis=-1, keepdims=True).astype(np.float16)).astype(np.float64)
+    return np.abs(g - r) / scale
+
+
+class Stats:
+    """Errors of the GPU and of the fp32-accumulating oracle against the fp64 oracle (exact-V)."""
+
+    def __init__(self):
+        self.gpu, self.fp32, self.gpu_abs, self.fp32_abs = [], [], [], []
+
+    def add(self, label, got, ref_x, ref_rounded, ref32):
+        g, f = _row_ulps(got, ref_x), _row_ulps(ref32, ref_x)
+        ga = np.abs(got.astype(np.float64) - ref_x.astype(np.float64))
+        fa = np.abs(ref32.astype(np.float64) - ref_x.astype(np.float64))
+        self.gpu.append(g.reshape(-1))
+        self.fp32.append(f.reshape(-1))
+        self.gpu_abs.append(ga.reshape(-1))
+        self.fp32_abs.append(fa.reshape(-1))
+        ur = _row_ulps(got, ref_rounded)
+        print(f"{label}: GPU vs oracle (exact-V) max {g.max():.2f} / mean {g.mean():.4f} row-ulp, "
+              f"{np.mean(ga == 0):.4f} equal, max-abs {ga.max():.3g} | fp32 oracle max {f.max():.2f} / mean "
+              f"{f.mean():.4f} row-ulp, {np.mean(fa == 0):.4f} equal | GPU vs rounded-V max {ur.max():.2f} row-ulp",
+              flush=True)
 
 
 @pytest.mark.timeout(900)
@@ -122,44 +145,43 @@ def test_teacher_forced_layers(name):
     tod.decode_block(m.handle, 0, 1, first, out)
     torch.cuda.synchronize()
     print("GPU prefill + 1 decode step done", flush=True)
-    worst = {"exact": 0.0, "rounded": 0.0}
+    st = Stats()
     code_rates = []
+
+    def refs(layer, cache, pos, rows):
+        """(fp64 pages' reading, fp64 exact-V, fp32-accumulating exact-V, k, v) of one layer."""
+        r, k, v = layer.forward_given_kv(cache, pos, rows)
+        with oracle.exact_v():
+            rx, _, _ = layer.forward_given_kv(cache, pos, rows)
+            with oracle.fp32_accumulation():
+                r32, _, _ = layer.forward_given_kv(cache, pos, rows)
+        return r, rx, r32, k, v
+
     for l in case["taps"]:
         pin, pout, din, dout = (to_np16(b) for b in bufs[l])
         layer = oracle.Layer(shape, synth.layer_weights(shape, l, variant=case["variant"]), int4_weights=tier != 1)
         for row in (0, M - 1):
             cache, arrays = _export_cache(tod, torch, m, l, row, shape, s + 1)
-            ref, k, v = layer.forward_given_kv(cache, s, din[row:row + 1])
-            with oracle.exact_v():
-                ref_x, _, _ = layer.forward_given_kv(cache, s, din[row:row + 1])
-            ue, ur = _report(f"layer {l} decode row {row}", dout[row:row + 1], ref_x, ref)
-            worst["exact"] = max(worst["exact"], ue.max())
-            worst["rounded"] = max(worst["rounded"], ur.max())
-            rate = _code_agreement(shape, arrays, k, v, [s])
-            code_rates.append(rate)
-            print(f"layer {l} decode row {row}: new-position K/V byte agreement {rate:.5f}", flush=True)
+            r, rx, r32, k, v = refs(layer, cache, s, din[row:row + 1])
+            st.add(f"layer {l} decode row {row}", dout[row:row + 1], rx, r, r32)
+            code_rates.append(_code_agreement(shape, arrays, k, v, [s]))
+            print(f"layer {l} decode row {row}: new-position K/V byte agreement {code_rates[-1]:.5f}", flush=True)
             if row == pseq:
-                got, refs, refs_x, ks_, vs_ = [], [], [], [], []
-                for t in PREFILL_POSITIONS:
-                    r_, k_, v_ = layer.forward_given_kv(cache, t, pin[t:t + 1])
-                    with oracle.exact_v():
-                        rx_, _, _ = layer.forward_given_kv(cache, t, pin[t:t + 1])
-                    got.append(pout[t:t + 1])
-                    refs.append(r_)
-                    refs_x.append(rx_)
-                    ks_.append(k_)
-                    vs_.append(v_)
-                ue, ur = _report(f"layer {l} prefill row {row} positions {PREFILL_POSITIONS}",
-                                 np.concatenate(got), np.concatenate(refs_x), np.concatenate(refs))
-                worst["exact"] = max(worst["exact"], ue.max())
-                worst["rounded"] = max(worst["rounded"], ur.max())
-                rate = _code_agreement(shape, arrays, np.concatenate(ks_), np.concatenate(vs_), PREFILL_POSITIONS)
-                code_rates.append(rate)
-                print(f"layer {l} prefill row {row}: K/V byte agreement {rate:.5f}", flush=True)
+                parts = [refs(layer, cache, t, pin[t:t + 1]) for t in PREFILL_POSITIONS]
+                got = np.concatenate([pout[t:t + 1] for t in PREFILL_POSITIONS])
+                st.add(f"layer {l} prefill row {row} positions {PREFILL_POSITIONS}", got,
+                       np.concatenate([x[1] for x in parts]), np.concatenate([x[0] for x in parts]),
+                       np.concatenate([x[2] for x in parts]))
+                code_rates.append(_code_agreement(shape, arrays, np.concatenate([x[3] for x in parts]),
+                                                  np.concatenate([x[4] for x in parts]), PREFILL_POSITIONS))
+                print(f"layer {l} prefill row {row}: K/V byte agreement {code_rates[-1]:.5f}", flush=True)
             cache.close()
         layer.close()
     m.close()
-    print(f"{name}: worst {worst['exact']:.0f} ulp vs exact-V, {worst['rounded']:.0f} ulp vs rounded-V; "
-          f"K/V agreement min {min(code_rates):.5f}", flush=True)
-    assert worst["exact"] <= 2
+    g, f = np.concatenate(st.gpu), np.concatenate(st.fp32)
+    ga, fa = np.concatenate(st.gpu_abs), np.concatenate(st.fp32_abs)
+    print(f"{name}: GPU max {g.max():.2f} row-ulp, mean-abs {ga.mean():.4g}; fp32 oracle max {f.max():.2f} "
+          f"row-ulp, mean-abs {fa.mean():.4g}; K/V agreement min {min(code_rates):.5f}", flush=True)
+    assert g.max() <= ROW_ULP_MAX
+    assert ga.mean() <= MEAN_ABS_FACTOR * fa.mean()
     assert min(code_rates) >= 0.999

@@ -27,7 +27,8 @@ EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", 
             "last_error",
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
             "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read",
-            "default_hw", "estimate_decode", "plan_decode", "set_weight_file", "set_layer_tap")
+            "default_hw", "estimate_decode", "plan_decode", "set_weight_file", "set_layer_tap",
+            "estimate_gemm")
 KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
                 "argmax", "embed")
 
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
                           "(python -m throughput_oriented_offloaded_amd.build)")
+    # torch ships its own HIP runtime under the same soname as ROCm's; load it first so that this
+    # library binds to the runtime torch uses (two runtimes in one process do not share a device)
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     sig = {
@@ -95,6 +99,7 @@ def lib() -> ctypes.CDLL:
         "profile_read": [vp, i32, vp, vp],
         "estimate_decode": [vp, vp, vp, vp],
         "plan_decode": [vp, i32, i32, i32, vp, vp, vp],
+        "estimate_gemm": [i64, i32, i32, i32, vp, vp],
         "set_weight_file": [vp, ctypes.c_char_p],
         "set_layer_tap": [vp, i32, i32, i64, i64, vp, vp],
     }
@@ -313,6 +318,15 @@ def estimate_decode(cfg, run: dict, hw: dict | None = None) -> dict:
     _check("estimate_decode", lib().estimate_decode(ctypes.byref(mc), ctypes.byref(rc_), ctypes.byref(h),
                                                     ctypes.byref(est)))
     return _struct_dict(est)
+
+
+def estimate_gemm(rows: int, out_features: int, in_features: int, int4: bool, hw: dict | None = None) -> float:
+    """Seconds the cost model charges one GEMM of this shape."""
+    h = HW(**(hw or default_hw()))
+    t = ctypes.c_double()
+    _check("estimate_gemm", lib().estimate_gemm(rows, out_features, in_features, int(int4), ctypes.byref(h),
+                                                ctypes.byref(t)))
+    return t.value
 
 
 def plan_decode(cfg, prompt_len: int, gen_len: int, max_rows: int, hw: dict | None = None):

@@ -17,16 +17,6 @@
 
 namespace {
 
-// fp16 pair from two nibble fields of a word: field value f sits in the low
-// mantissa bits under the exponent of 1024, so the half is 1024 + f exactly.
-// One v_and_or_b32 (the mask in an SGPR, the exponent bits in a VGPR).
-__device__ __forceinline__ half2_t magic_pair(uint32_t x, uint32_t mask)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(0x64006400u));
-    return __builtin_bit_cast(half2_t, r);
-}
-
 // Exact codes of bytes 0,1 (HI = false) or 2,3 (HI = true) of a word whose
 // bytes each hold one 4-bit code: the byte read as fp8 e4m3 is c * 2^-9.
 template <bool HI> __device__ __forceinline__ half2_t code_pair(uint32_t nibbles)
@@ -71,7 +61,7 @@ __device__ __forceinline__ void load_chunk(KvChunk<D / 32> &c, int c0, int slot,
 // State of one wavefront's online softmax; acc holds the lane's 32 dims.
 struct SoftmaxState {
     float acc[32];
-    float m_run, lsum, psum, zsum;
+    float m_run, lsum, zsum;
 };
 
 // Scores of a chunk and its weighted values.
@@ -81,10 +71,11 @@ struct SoftmaxState {
 //    (e0,e2) (e4,e6) (e1,e3) (e5,e7) exactly, and one packed FMA gives the
 //    fp16 key fp16(c * scale + zero), rounded once, i.e. the dequantized cache
 //    entry itself; v_dot2 against the matching query pairs sums q.k in fp32.
-//  * V: the same fields feed fp32 accumulators through mixed-precision FMA,
-//    acc_e += (p * scale) * (1024 + c) (or 1024 + 16c); the offsets and the
-//    zero term are removed once at the end from the running sums of
-//    p * scale and p * zero.
+//  * V: the codes are decoded exactly the same way and feed fp32 accumulators
+//    through mixed-precision FMA, acc_e += (p * scale) * c; the zero term is
+//    added once at the end from the running sum of p * zero. So V enters as
+//    the exact value zero + c * scale (never rounded to fp16), and each
+//    accumulator carries only the code part of the weighted sum.
 template <int D>
 __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, int slot, int ctx,
                                              const half2_t (&qa)[8], const half2_t (&qb)[8], SoftmaxState &st)
@@ -121,7 +112,6 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
         for (int e = 0; e < 32; e++)
             st.acc[e] *= corr;
         st.lsum *= corr;
-        st.psum *= corr;
         st.zsum *= corr;
         st.m_run = mloc;
     }
@@ -131,22 +121,21 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
         const float p = __expf(sc[j] - st.m_run); // 0 past the context
         const float ps = live ? p * h2f((uint16_t)(c.vp[j] & 0xffffu)) : 0.0f;
         st.lsum += p;
-        st.psum += ps;
         st.zsum += live ? p * h2f((uint16_t)(c.vp[j] >> 16)) : 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-            const uint32_t x = c.v[j][w], y = x >> 8;
-            const half2_t a0 = magic_pair(x, 0x000F000Fu), b0 = magic_pair(x, 0x00F000F0u);
-            const half2_t a1 = magic_pair(y, 0x000F000Fu), b1 = magic_pair(y, 0x00F000F0u);
+            const uint32_t x = c.v[j][w], lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+            const half2_t c02 = code_pair<false>(lo), c46 = code_pair<true>(lo);
+            const half2_t c13 = code_pair<false>(hi), c57 = code_pair<true>(hi);
             float *acc = st.acc + 8 * w;
-            acc[0] = fmaf(ps, (float)a0[0], acc[0]);
-            acc[4] = fmaf(ps, (float)a0[1], acc[4]);
-            acc[1] = fmaf(ps, (float)b0[0], acc[1]);
-            acc[5] = fmaf(ps, (float)b0[1], acc[5]);
-            acc[2] = fmaf(ps, (float)a1[0], acc[2]);
-            acc[6] = fmaf(ps, (float)a1[1], acc[6]);
-            acc[3] = fmaf(ps, (float)b1[0], acc[3]);
-            acc[7] = fmaf(ps, (float)b1[1], acc[7]);
+            acc[0] = fmaf(ps, (float)c02[0], acc[0]);
+            acc[2] = fmaf(ps, (float)c02[1], acc[2]);
+            acc[4] = fmaf(ps, (float)c46[0], acc[4]);
+            acc[6] = fmaf(ps, (float)c46[1], acc[6]);
+            acc[1] = fmaf(ps, (float)c13[0], acc[1]);
+            acc[3] = fmaf(ps, (float)c13[1], acc[3]);
+            acc[5] = fmaf(ps, (float)c57[0], acc[5]);
+            acc[7] = fmaf(ps, (float)c57[1], acc[7]);
         }
     }
 }
@@ -196,7 +185,7 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
     for (int e = 0; e < 32; e++)
         st.acc[e] = 0.0f;
     st.m_run = -INFINITY;
-    st.lsum = st.psum = st.zsum = 0.0f;
+    st.lsum = st.zsum = 0.0f;
 
     // chunks in pairs through two register buffers; loads of a chunk index
     // past the context are clamped to its last position (cache hits)
@@ -213,15 +202,12 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
     if (nchunks & 1)
         attend_chunk<D>(ca, c0, slot, ctx, qa, qb, st);
 
-    // remove the field offsets, add the zero term, sum over the wave's positions
+    // add the zero term, sum over the wave's positions
     const float den = reduce_slots<L>(st.lsum, OpAdd());
-    const float off = 1024.0f * st.psum;
     float o[32];
 #pragma unroll
-    for (int e = 0; e < 32; e++) {
-        const float f = (e & 1) ? 0.0625f : 1.0f;
-        o[e] = reduce_slots<L>((st.acc[e] - off) * f + st.zsum, OpAdd());
-    }
+    for (int e = 0; e < 32; e++)
+        o[e] = reduce_slots<L>(st.acc[e] + st.zsum, OpAdd());
     const float inv = 1.0f / den;
     if (slot == 0) {
         uint16_t *op = out + (int64_t)row * out_stride + (int64_t)head * D + pc * 32;

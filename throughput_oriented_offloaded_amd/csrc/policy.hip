@@ -264,6 +264,21 @@ int estimate_decode(const tod_model_config *cfg, const tod_run_config *run, cons
     });
 }
 
+int estimate_gemm(int64_t rows, int out, int in, int int4, const tod_hw *hw, double *seconds)
+{
+    return guard("estimate_gemm", [&]() -> int {
+        if (!hw || !seconds)
+            return fail(TOD_EINVAL, "null argument");
+        if (rows <= 0 || rows > (1 << 24) || out <= 0 || in <= 0 || in % 64 || (int4 && out % 32))
+            return fail(TOD_EINVAL, "bad GEMM shape %lld x %d x %d", (long long)rows, out, in);
+        if (!(hw->mem_gbs > 0.0 && hw->int4_tflops > 0.0 && hw->fp16_tflops > 0.0 && hw->launch_us >= 0.0 &&
+              hw->gemm_wg_us >= 0.0 && hw->staged_tflops > 0.0 && hw->staged_gbs > 0.0 && hw->staged_us >= 0.0))
+            return fail(TOD_EINVAL, "hardware rates must be positive and fixed costs non-negative");
+        *seconds = gemm_time((int)rows, out, in, int4 != 0, hw);
+        return TOD_OK;
+    });
+}
+
 int plan_decode(const tod_model_config *cfg, int prompt_len, int gen_len, int max_rows, const tod_hw *hw,
                 tod_run_config *best, tod_estimate *est)
 {

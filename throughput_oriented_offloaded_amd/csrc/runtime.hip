@@ -1340,9 +1340,10 @@ int export_kv(tod_model *m, int layer, int block, int row, int head, int t0, int
     });
 }
 
-static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
-                         const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_w, const uint16_t *d_bias,
-                         const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
+// Argument rules of the linear entry points (no device work).
+static int check_linear(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
+                        const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_w,
+                        const uint16_t *d_residual, int relu, const uint16_t *d_y)
 {
     if (!d_a || !d_y || rows < 0 || rows > 0x7fffffff || in <= 0 || out <= 0)
         return fail(TOD_EINVAL, "bad linear arguments");
@@ -1355,6 +1356,51 @@ static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, con
         return fail(TOD_EINVAL, "null weights");
     if (relu && d_residual)
         return fail(TOD_EINVAL, "relu with residual is not an epilogue of this library");
+    return TOD_OK;
+}
+
+// The GEMM of a linear call, given device memory for the repacked int4 weights (tc, tp; int4
+// only) and for the split-K partials (ws, gemm_workspace_bytes of the shape).
+static int run_linear(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
+                      const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_w, const uint16_t *d_bias,
+                      const uint16_t *d_residual, int relu, uint16_t *d_y, uint32_t *tc, uint32_t *tp, float *ws,
+                      hipStream_t st)
+{
+    GemmArgs g{};
+    g.a = d_a;
+    g.lda = in;
+    if (d_codes) {
+        hipError_t e = launch_repack_w4(d_codes, d_scale, d_zero, out, in, tc, tp, st);
+        if (e != hipSuccess)
+            return fail(TOD_EHIP, "repack failed: %s", hipGetErrorString(e));
+        g.wc = tc;
+        g.wp = tp;
+    } else {
+        g.wf = d_w;
+    }
+    g.bias = d_bias;
+    g.residual = d_residual;
+    g.y = d_y;
+    g.ldc = out;
+    g.M = (int)rows;
+    g.N = out;
+    g.K = in;
+    g.epi = relu ? EPI_BIAS_RELU : (d_residual ? EPI_BIAS_RES : (d_bias ? EPI_BIAS : EPI_NONE));
+    g.ws_bytes = gemm_workspace_bytes((int)rows, out, in, d_codes != nullptr);
+    g.ws = ws;
+    hipError_t e = launch_gemm(g, st);
+    if (e != hipSuccess)
+        return fail(TOD_EHIP, "gemm failed: %s", hipGetErrorString(e));
+    return TOD_OK;
+}
+
+static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
+                         const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_w, const uint16_t *d_bias,
+                         const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
+{
+    int rc = check_linear(d_a, rows, in, out, d_codes, d_scale, d_zero, d_w, d_residual, relu, d_y);
+    if (rc)
+        return rc;
     const hipStream_t st = S(stream);
     std::vector<void *> tmp;
     auto cleanup = [&]() {
@@ -1371,46 +1417,25 @@ static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, con
         tmp.push_back(p);
         return p;
     };
-    GemmArgs g{};
-    g.a = d_a;
-    g.lda = in;
-    if (int4) {
+    uint32_t *tc = nullptr, *tp = nullptr;
+    if (d_codes) {
         const int64_t n = (int64_t)out * in;
-        uint32_t *tc = static_cast<uint32_t *>(talloc((size_t)n / 2));
-        uint32_t *tp = static_cast<uint32_t *>(talloc((size_t)n / 64 * 4));
+        tc = static_cast<uint32_t *>(talloc((size_t)n / 2));
+        tp = static_cast<uint32_t *>(talloc((size_t)n / 64 * 4));
         if (!tc || !tp) {
             cleanup();
             return fail(TOD_ENOMEM, "no memory for the repacked weights");
         }
-        hipError_t e = launch_repack_w4(d_codes, d_scale, d_zero, out, in, tc, tp, st);
-        if (e != hipSuccess) {
-            cleanup();
-            return fail(TOD_EHIP, "repack failed: %s", hipGetErrorString(e));
-        }
-        g.wc = tc;
-        g.wp = tp;
-    } else {
-        g.wf = d_w;
     }
-    g.bias = d_bias;
-    g.residual = d_residual;
-    g.y = d_y;
-    g.ldc = out;
-    g.M = (int)rows;
-    g.N = out;
-    g.K = in;
-    g.epi = relu ? EPI_BIAS_RELU : (d_residual ? EPI_BIAS_RES : (d_bias ? EPI_BIAS : EPI_NONE));
-    g.ws_bytes = gemm_workspace_bytes((int)rows, out, in, int4);
-    g.ws = static_cast<float *>(talloc(g.ws_bytes));
-    if (g.ws_bytes && !g.ws) {
+    const size_t ws_bytes = gemm_workspace_bytes((int)rows, out, in, d_codes != nullptr);
+    float *ws = static_cast<float *>(talloc(ws_bytes));
+    if (ws_bytes && !ws) {
         cleanup();
         return fail(TOD_ENOMEM, "no memory for the split-K workspace");
     }
-    hipError_t e = launch_gemm(g, st);
+    rc = run_linear(d_a, rows, in, out, d_codes, d_scale, d_zero, d_w, d_bias, d_residual, relu, d_y, tc, tp, ws, st);
     cleanup();
-    if (e != hipSuccess)
-        return fail(TOD_EHIP, "gemm failed: %s", hipGetErrorString(e));
-    return TOD_OK;
+    return rc;
 }
 
 int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes, const uint16_t *d_scale,
