@@ -397,7 +397,8 @@ def test_opt125m_long_prompt_meets_stated_bar(prompt_len):
 
 
 def test_layer0_kv_codes_match_oracle():
-    """Layer 0's K/V depend only on embeddings and one LN + linear: their int4 codes agree."""
+    """Layer 0's K/V depend only on the token ids, the embeddings, one LN and one linear: fed the same
+    ids (the prompt and the GPU's generated tokens), the int4 codes agree."""
     torch = torch_cuda()
     import throughput_oriented_offloaded_amd as tod
     shape = synth.OPT_125M
@@ -408,14 +409,11 @@ def test_layer0_kv_codes_match_oracle():
     toks = m.generate(to_dev(prompts, torch), g)
     torch.cuda.synchronize()
     gt = toks.cpu().numpy()
-    layers = [oracle.Layer(shape, synth.layer_weights(shape, l, variant="full")) for l in range(shape.n_layers)]
-    ot, _, _ = oracle.generate(shape, layers, glob, prompts, g, 2, oracle.SCHED_ZIGZAG, want_logits=False)
-    assert np.array_equal(gt, ot), "token histories differ; the KV comparison needs the same inputs"
-    layer0 = layers[0]
+    layer0 = oracle.Layer(shape, synth.layer_weights(shape, 0, variant="full"))
     T = s + g - 1
     agree = total = 0
     for r in range(4):
-        ids = np.concatenate([prompts[r], ot[r, :g - 1]]).astype(np.int32)
+        ids = np.concatenate([prompts[r], gt[r, :g - 1]]).astype(np.int32)
         hid = oracle.embed(shape, glob["tok_emb"], glob["pos_emb"], ids, np.arange(T, dtype=np.int32))
         cache = oracle.KVCache(shape, T)
         layer0.forward(cache, 0, hid)
