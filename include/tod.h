@@ -323,6 +323,28 @@ int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t 
               const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
               void *stream);
 
+/*
+ * linear_w4_noalloc: linear_w4 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results as linear_w4, but the
+ * repacked weights and the split-K partials live in a fixed scratch array of
+ * TOD_LINEAR_NOALLOC_BYTES that each device holds from its first call until
+ * the process ends; the call allocates and frees nothing and does not
+ * synchronize (it is asynchronous on stream). A call needs out*in/2 and
+ * out*in/16 bytes (each rounded up to 256) plus the GEMM's split-K partials
+ * (0, or splits * rows * out * 4 bytes); a call that needs more fails with
+ * TOD_EINVAL before any device work. Every call on a device shares that
+ * device's scratch: calls on one stream are ordered, but calls that overlap on
+ * one device (other streams or threads) race and their outputs are undefined.
+ * The scratch keeps the last call's contents; no call reads what it did not
+ * write first, so nothing needs clearing. Errors: as linear_w4, plus the
+ * scratch limit above.
+ */
+#define TOD_LINEAR_NOALLOC_BYTES ((size_t)192 << 20)
+int linear_w4_noalloc(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
+                      const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_bias,
+                      const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream);
+
 /* linear_f16: as linear_w4 with fp16 weights d_w [out][in] (the LM head's and the fp16 host tier's GEMM). */
 int linear_f16(const uint16_t *d_a, int64_t rows, int in, int out, const uint16_t *d_w, const uint16_t *d_bias,
                const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream);

@@ -11,16 +11,16 @@ from . import _lib
 from ._lib import (TOD_W_HBM_INT4, TOD_W_HOST_FP16_STREAM, TOD_W_HOST_INT4_STREAM, attn_cache_create,
                    attn_cache_export, attn_cache_fill, attn_cache_free, attn_decode_step, decode_block, default_hw,
                    dequantize_groupwise, estimate_decode, estimate_gemm, export_kv, export_weight, free_model,
-                   init_model, last_error, linear_f16, linear_w4, plan_decode, prefill, profile_kernels,
-                   profile_read, quantize_groupwise, set_decode_graph, set_decode_position, set_global_weights,
-                   set_layer_tap, set_layer_weights, set_weight_file, TodError)
+                   init_model, last_error, linear_f16, linear_w4, linear_w4_noalloc, plan_decode, prefill,
+                   profile_kernels, profile_read, quantize_groupwise, set_decode_graph, set_decode_position,
+                   set_global_weights, set_layer_tap, set_layer_weights, set_weight_file, TodError)
 
 __all__ = ["Model", "TodError", "init_model", "set_global_weights", "set_layer_weights", "prefill", "decode_block",
            "set_decode_position", "set_decode_graph", "quantize_groupwise", "dequantize_groupwise", "free_model",
-           "last_error", "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create",
-           "attn_cache_fill", "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels",
-           "profile_read", "default_hw", "estimate_decode", "estimate_gemm", "plan_decode", "set_weight_file",
-           "set_layer_tap", "TOD_W_HBM_INT4", "TOD_W_HOST_FP16_STREAM", "TOD_W_HOST_INT4_STREAM"]
+           "last_error", "export_weight", "export_kv", "linear_w4", "linear_w4_noalloc", "linear_f16",
+           "attn_cache_create", "attn_cache_fill", "attn_decode_step", "attn_cache_export", "attn_cache_free",
+           "profile_kernels", "profile_read", "default_hw", "estimate_decode", "estimate_gemm", "plan_decode",
+           "set_weight_file", "set_layer_tap", "TOD_W_HBM_INT4", "TOD_W_HOST_FP16_STREAM", "TOD_W_HOST_INT4_STREAM"]
 
 
 class Model:

@@ -28,7 +28,7 @@ EXPORTED = ("init_model", "set_global_weights", "set_layer_weights", "prefill", 
             "export_weight", "export_kv", "linear_w4", "linear_f16", "attn_cache_create", "attn_cache_fill",
             "attn_decode_step", "attn_cache_export", "attn_cache_free", "profile_kernels", "profile_read",
             "default_hw", "estimate_decode", "plan_decode", "set_weight_file", "set_layer_tap",
-            "estimate_gemm")
+            "linear_w4_noalloc", "estimate_gemm")
 KERNEL_KINDS = ("gemm_qkv", "gemm_o", "gemm_fc1", "gemm_fc2", "attn", "kv_append", "layernorm", "lm_head",
                 "argmax", "embed")
 
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
         "export_kv": [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
         "linear_w4": [vp, i64, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp],
         "linear_f16": [vp, i64, i32, i32, vp, vp, vp, i32, vp, vp],
+        "linear_w4_noalloc": [vp, i64, i32, i32, vp, vp, vp, vp, vp, i32, vp, vp],
         "attn_cache_create": [i32, i32, i32, i32, vp],
         "attn_cache_fill": [vp, vp, vp, i32, i32, vp],
         "attn_decode_step": [vp, i32, vp, vp, vp, vp, vp],
@@ -236,6 +237,14 @@ def linear_w4(a, codes, scale, zero, out_features: int, y, bias=None, residual=N
     rows, k = a.shape
     _check("linear_w4", lib().linear_w4(_ptr(a), rows, k, out_features, _ptr(codes), _ptr(scale), _ptr(zero),
                                         _ptr(bias), _ptr(residual), int(relu), _ptr(y), _stream(stream)))
+
+
+def linear_w4_noalloc(a, codes, scale, zero, out_features: int, y, bias=None, residual=None, relu=False,
+                      stream=None):
+    rows, k = a.shape
+    _check("linear_w4_noalloc", lib().linear_w4_noalloc(_ptr(a), rows, k, out_features, _ptr(codes), _ptr(scale),
+                                                        _ptr(zero), _ptr(bias), _ptr(residual), int(relu), _ptr(y),
+                                                        _stream(stream)))
 
 
 def linear_f16(a, w, y, bias=None, residual=None, relu=False, stream=None):

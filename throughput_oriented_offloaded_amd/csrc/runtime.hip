@@ -1438,6 +1438,34 @@ static int linear_common(const uint16_t *d_a, int64_t rows, int in, int out, con
     return rc;
 }
 
+// Scratch of linear_w4_noalloc: the repacked weights and split-K partials of one call, so that
+// the call allocates nothing. In host code `scratch` names a host-side stand-in, not a device
+// address: host code uses only the address scratch_base() looked up for the current device.
+constexpr size_t kNoallocBytes = TOD_LINEAR_NOALLOC_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
+
+// The current device's address of `scratch`: looked up on the device's first call, then kept.
+static int scratch_base(uint8_t **out)
+{
+    static std::atomic<uint8_t *> addr[kMaxDevices];
+    int dev = -1;
+    HIPCHK(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(TOD_EINVAL, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+    uint8_t *p = addr[dev].load();
+    if (!p) {
+        void *q = nullptr;
+        HIPCHK(hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)));
+        p = static_cast<uint8_t *>(q);
+        addr[dev].store(p);
+    }
+    *out = p;
+    return TOD_OK;
+}
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
 int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes, const uint16_t *d_scale,
               const uint16_t *d_zero, const uint16_t *d_bias, const uint16_t *d_residual, int relu, uint16_t *d_y,
               void *stream)
@@ -1446,6 +1474,34 @@ int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t 
         if (!d_codes)
             return fail(TOD_EINVAL, "null codes");
         return linear_common(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y, stream);
+    });
+}
+
+int linear_w4_noalloc(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t *d_codes,
+                      const uint16_t *d_scale, const uint16_t *d_zero, const uint16_t *d_bias,
+                      const uint16_t *d_residual, int relu, uint16_t *d_y, void *stream)
+{
+    return guard("linear_w4_noalloc", [&]() -> int {
+        if (!d_codes)
+            return fail(TOD_EINVAL, "null codes");
+        int rc = check_linear(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_residual, relu, d_y);
+        if (rc)
+            return rc;
+        const size_t n = (size_t)out * in;
+        const size_t codes_b = round256(n / 2), params_b = round256(n / 64 * 4);
+        const size_t ws_b = gemm_workspace_bytes((int)rows, out, in, true);
+        if (codes_b + params_b + ws_b > kNoallocBytes)
+            return fail(TOD_EINVAL,
+                        "linear_w4_noalloc: %d x %d weights at %lld rows need %zu bytes of scratch, above its %zu",
+                        out, in, (long long)rows, codes_b + params_b + ws_b, kNoallocBytes);
+        uint8_t *base = nullptr;
+        if ((rc = scratch_base(&base)))
+            return rc;
+        uint32_t *tc = reinterpret_cast<uint32_t *>(base);
+        uint32_t *tp = reinterpret_cast<uint32_t *>(base + codes_b);
+        float *ws = ws_b ? reinterpret_cast<float *>(base + codes_b + params_b) : nullptr;
+        return run_linear(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y, tc, tp,
+                          ws, S(stream));
     });
 }
 
