@@ -15,9 +15,11 @@ cache and weights are resident in HBM when it starts.
 Prints one JSON line. `value` is decode tokens/s = rows * steps / time.
 `roofline` reports the kernel class with the largest share of the step,
 timed with HIP events on the library's stream over a second pass of the
-same steps (launched one by one; the timed region replays captured graphs).
-`cpu_baseline` times the CPU oracle on a bounded sample (one layer, one
-decode step, one GPU batch of 64 rows, plus the LM head) and extrapolates.
+same steps (launched one by one; the timed region replays captured graphs),
+and beside it (`step_achieved`, `step_frac`) the whole step's algorithmic
+HBM bytes over the step time. `cpu_baseline` times the CPU oracle on a
+bounded sample (one layer and one decode step for every row of the block,
+plus the LM head for those rows) and extrapolates to the stack.
 """
 from __future__ import annotations
 
@@ -299,15 +301,28 @@ def attention_bench(args, tod, synth, torch):
     }
 
 
-def cpu_baseline(w, rows=64, passes=3):
-    """Oracle on one layer x one decode step x `rows` sequences at the average decode
-    context, plus the LM head for those rows, each timed over `passes` repetitions
-    (about 10 s of work on a 16-core host); extrapolated to the whole stack."""
+def cpu_model():
+    """The host CPU's model name (first processor entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, rows=None, passes=1):
+    """The oracle on one layer x one decode step of the whole block (every row, at the average
+    decode context) plus the LM head for those rows (about 30 s on a 16-core host); extrapolated
+    to the whole stack as rows / (layers x t_layer + t_lm)."""
     import numpy as np
 
     import oracle
     import synth
     shape = w.shape
+    rows = rows or w.rows
     ctx = w.prompt_len + (w.gen_len - 1) // 2          # average attended context - 1 cached positions
     layer = oracle.Layer(shape, synth.layer_weights(shape, 0))
     glob = synth.global_weights(shape)
@@ -328,18 +343,21 @@ def cpu_baseline(w, rows=64, passes=3):
     for _ in range(passes):
         oracle.head(shape, glob["lnf_g"], glob["lnf_b"], glob["tok_emb"], hid)
     t_lm = (time.perf_counter() - t0) / passes
+    del caches
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     tps = rows / (shape.n_layers * t_layer + t_lm)
-    return {"value": tps, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"1 of {shape.n_layers} layers x 1 decode step x {rows} sequences at context {ctx + 1} "
-                       f"({t_layer:.2f} s) + LM head for {rows} rows ({t_lm:.2f} s), each the mean of {passes} "
-                       f"timed passes; extrapolated as {rows} / ({shape.n_layers} * t_layer + t_lm)")}
+    return {"value": tps, "unit": "tokens/s", "cores": cores, "cpu": cpu_model(), "kind": "oracle",
+            "sample": (f"1 of {shape.n_layers} layers x 1 decode step x all {rows} sequences of the block at context "
+                       f"{ctx + 1} ({t_layer:.2f} s) + LM head for {rows} rows ({t_lm:.2f} s), {passes} timed "
+                       f"pass(es); extrapolated as {rows} / ({shape.n_layers} * t_layer + t_lm)")}
 
 
 # HBM traffic of the dominant kernel, measured separately with rocprofv3 counters
 # (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the same counters on a plain
-# copy of known size) and kept with the profiles. It is reported only while the
-# kernel's sources are unchanged since the counters were taken.
+# copy of known size) and kept with the profiles as the ratio of measured to
+# algorithmic bytes; a run reports that ratio times its own algorithmic bytes per
+# launch. It is reported only while the kernel's sources are unchanged since the
+# counters were taken.
 TRAFFIC_FILES = {"k_attn_decode<128>": ("profiles/k_attn_decode_opt30b_counters.txt",
                                         ("throughput_oriented_offloaded_amd/csrc/attn.hip",
                                          "throughput_oriented_offloaded_amd/csrc/common.hpp"))}
@@ -354,21 +372,21 @@ def source_digest(paths):
     return h.hexdigest()
 
 
-def measured_traffic(kernel):
-    """Bytes per launch from the counter summary, or None if absent or stale."""
+def measured_traffic(kernel, algorithmic_bytes):
+    """Measured HBM bytes per launch (the recorded ratio times this run's algorithmic bytes), or None
+    if the summary is absent or its kernel sources have changed since."""
     if kernel not in TRAFFIC_FILES:
         return None
     summary, sources = TRAFFIC_FILES[kernel]
     try:
         with open(os.path.join(ROOT, summary)) as f:
-            fields = dict(line.split(":", 1) for line in f if line.startswith(("traffic_bytes_per_launch:",
-                                                                               "source_sha256:")))
+            fields = dict(line.split(":", 1) for line in f if line.startswith(("traffic_ratio:", "source_sha256:")))
     except OSError:
         return None
     if fields.get("source_sha256", "").strip() != source_digest(sources):
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields["traffic_ratio"]) * algorithmic_bytes
     except (KeyError, ValueError):
         return None
 
@@ -383,6 +401,33 @@ def copy_probe(mib):
         torch.bitwise_not(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+
+
+def blas_probe():
+    """fp16 GEMMs of the vendor library (torch.mm, hipBLASLt on ROCm) at the OPT-30B decode shapes and on
+    two large ones: a measured practical ceiling for the int4 GEMMs' rate on this part. Context only: the
+    library never calls it."""
+    import torch
+    torch.manual_seed(0)
+    for m, n, k in ((512, 21504, 7168), (512, 7168, 7168), (512, 28672, 7168), (512, 7168, 28672),
+                    (512, 50272, 7168), (8192, 8192, 8192), (32768, 28672, 7168)):
+        a = torch.randn(m, k, device="cuda", dtype=torch.float16)
+        wt = (torch.randn(n, k, device="cuda", dtype=torch.float16) * 0.02).t().contiguous()
+        reps = 50 if m * n * k < 1e12 else 10
+        for _ in range(5):
+            torch.mm(a, wt)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, wt)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"blas_probe": "torch.mm fp16", "m": m, "n": n, "k": k, "us": us,
+                          "tflops": 2 * m * n * k / us / 1e6}), flush=True)
+        del a, wt
+        torch.cuda.empty_cache()
 
 
 def main():
@@ -410,6 +455,8 @@ def main():
                     help="one decode step per call with a log line each (long profiler runs); not for the metric")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--blas-probe", action="store_true",
+                    help="only time the vendor library's fp16 GEMMs at the decode shapes (a ceiling) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path (see the design notes on "
@@ -420,6 +467,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.blas_probe:
+        blas_probe()
         return
 
     import synth
@@ -537,18 +587,23 @@ def main():
             total = sum((M * kv_bytes_per_position(shape) * c + 2 * M * shape.hidden * 2) * shape.n_layers
                         for c in contexts)
             gbs = total / (ms * 1e-3) / 1e9
-            entry.update(bound="hbm", achieved_gbs=gbs, frac=gbs / HBM_PEAK_GBS)
+            entry.update(bound="hbm", achieved_gbs=gbs, frac=gbs / HBM_PEAK_GBS, bytes_per_launch=total / n)
         kernels[k] = entry
     dom = max((k for k in kernels if "frac" in kernels[k]), key=lambda k: kernels[k]["share"])
     d = kernels[dom]
     if d["bound"] == "hbm":
         kname = f"k_attn_decode<{shape.head_dim}>"
         roof = {"bound": "hbm", "achieved": d["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["frac"], "traffic": measured_traffic(kname) if w.name == "opt-30b" else None,
+                "frac": d["frac"],
+                "traffic": measured_traffic(kname, d["bytes_per_launch"]) if w.name == "opt-30b" else None,
                 "kernel": kname}
     else:
         roof = {"bound": "mfma", "achieved": d["achieved_tflops"], "peak": MFMA_F16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": d["frac"], "traffic": None, "kernel": f"k_gemm ({dom})"}
+    # the whole step against HBM: algorithmic bytes of a step (weights once, the LM head, every cached
+    # K/V read, the appends and the logits) over the step time
+    roof.update(step_achieved=bytes_avg / (ms_per_step * 1e-3) / 1e9, step_frac=hbm_frac,
+                step_unit="GB/s of algorithmic step bytes")
 
     result = {
         "metric": METRIC.replace("OPT-30B", "OPT-" + w.name[4:].replace("b", "B")),

@@ -14,6 +14,10 @@ plan it launches (waves of workgroups, split-K partials). So:
   rates (no tile plan beats its own flops and bytes) and at most 2.2x it at
   the decode shapes (wave quantization, fixed cost per wave, split-K
   partials);
+* with the library's default rates, each recorded measurement on MI355X
+  (profiles/cost_model_measurements.txt: per-GEMM durations and whole decode
+  steps of the OPT-6.7B, OPT-30B and streamed OPT-175B workloads) is within
+  10% of the library's estimate;
 * the search picks the configuration with the most tokens/s among those that
   fit, checked by exhaustive enumeration through the library's own estimate,
   and equals the oracle's search when the GEMMs are free.
@@ -110,6 +114,44 @@ def test_gemm_estimates_bracket_the_roofline():
                 assert roof * (1 - 1e-12) <= lib <= 2.2 * roof, (name, rows, n, k, lib / roof)
                 worst = max(worst, lib / roof)
     print(f"library GEMM estimates are at most {worst:.2f} x the roofline")
+
+
+def _measurements():
+    path = os.path.join(ROOT, "profiles", "cost_model_measurements.txt")
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def test_estimates_match_recorded_measurements():
+    """Per-GEMM average durations (HIP events on the library's stream) and decode step times of
+    recorded benchmark runs, against the library's predictions with its default rates."""
+    tod = _lib()
+    hw = tod.default_hw()
+    checked = 0
+    for rec in _measurements():
+        kind, workload = rec[0], rec[1]
+        w = synth.WORKLOADS[workload]
+        shape = w.shape
+        if kind == "gemm":
+            rows, n, k, int4, measured_us = int(rec[2]), int(rec[3]), int(rec[4]), int(rec[5]), float(rec[6])
+            predicted_us = tod.estimate_gemm(rows, n, k, int4, hw) * 1e6
+        else:  # step: the workload's own run configuration, with the recorded placement
+            hbm_layers, host_layers, prompt_len, measured_us = int(rec[2]), int(rec[3]), int(rec[4]), float(rec[5])
+            run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=prompt_len,
+                       gen_len=w.gen_len, weight_tier=w.weight_tier, hbm_layers=hbm_layers, host_layers=host_layers)
+            predicted_us = tod.estimate_decode(shape, run, hw)["step_s"] * 1e6
+        ratio = measured_us / predicted_us
+        print(f"{' '.join(rec)}: predicted {predicted_us:.1f} us, measured / predicted {ratio:.3f}")
+        assert abs(ratio - 1) <= 0.10, rec
+        checked += 1
+    assert checked >= 10
+
+
 
 
 def _exhaustive_best(tod, shape, prompt_len, gen_len, max_rows, hw):

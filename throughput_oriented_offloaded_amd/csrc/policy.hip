@@ -24,8 +24,9 @@
 //    faster than its weight bytes at the streaming rate plus the fixed cost
 //    (the fp16 LM head at a few rows is bound there). Fitted to the
 //    measured decode GEMMs at 512 rows (OPT-30B) and 256 rows (OPT-6.7B), this
-//    is within about 15% on each of them, where one flat rate misses the
-//    256-row GEMMs by up to 2x (their K loops split 4 to 16 ways). The
+//    is within 8% on each of them (profiles/cost_model_measurements.txt), where
+//    one flat rate misses the 256-row GEMMs by up to 2x (their K loops split 4
+//    to 16 ways). The
 //    register-staged kernel (small GEMMs of 128 rows or fewer; fp16 weights of
 //    N not a multiple of 32) costs its own fixed time plus its weight bytes
 //    and its flops at that kernel's effective rates (it reads weights at well
@@ -229,17 +230,17 @@ void default_hw(tod_hw *hw)
 {
     if (!hw)
         return;
-    hw->attn_gbs = 6250.0;    // decode attention, int4 cache, OPT-30B shape
+    hw->attn_gbs = 6100.0;    // decode attention, int4 cache, OPT-30B shape
     hw->mem_gbs = 7100.0;     // streaming reads with nontemporal 16-byte loads
     hw->link_gbs = 57.2;      // one pinned -> HBM copy of a layer image
-    hw->int4_tflops = 1340.0; // pipelined int4 GEMMs, steady rate with every CU busy (fitted)
-    hw->fp16_tflops = 1400.0; // pipelined fp16-weight GEMMs (LM head), steady rate (fitted)
+    hw->int4_tflops = 1250.0; // pipelined int4 GEMMs, steady rate with every CU busy (fitted)
+    hw->fp16_tflops = 1300.0; // pipelined fp16-weight GEMMs (LM head), steady rate (fitted)
     hw->launch_us = 4.0;      // per kernel inside a replayed decode graph
     hw->hbm_bytes = 280e9;    // device memory a model may use
     hw->host_bytes = 270e9;   // pinned host memory a process may hold
     hw->disk_gbs = 7.4;       // reads of the weight file (one image per read)
     hw->disk_bytes = 80e9;    // free space for the weight file
-    hw->gemm_wg_us = 25.0;    // fixed cost per wave of pipelined GEMM workgroups (fitted)
+    hw->gemm_wg_us = 21.0;    // fixed cost per wave of pipelined GEMM workgroups (fitted)
     hw->staged_tflops = 1700.0; // register-staged GEMM (<= 128 rows): flops, fitted
     hw->staged_gbs = 3230.0;   // register-staged GEMM: weight bytes, fitted
     hw->staged_us = 10.0;      // register-staged GEMM: fixed time (OPT-125m GEMMs at 8 rows)
