@@ -31,8 +31,9 @@
 //    one fp8 -> fp16 convert per pair, then one v_pk_fma_f16 with (scale,
 //    zero) rounds once, so each weight equals fp16(zero + c*scale).
 //  * Workgroup ids are remapped so that each XCD (ids round-robin over 8 XCDs)
-//    gets a contiguous run of tiles, M fastest: workgroups sharing a weight
-//    tile share that XCD's L2.
+//    gets a contiguous run of tiles, ordered in groups of four row tiles
+//    (rows fastest, then columns): the workgroups an XCD runs at once share a
+//    few activation tiles and a few weight tiles in its L2.
 //  * When the tile grid is too small to fill 256 CUs the K loop is split and
 //    fp32 partials are reduced by a second kernel (deterministic order).
 #include <cstdio>
@@ -46,6 +47,7 @@ constexpr int KG_ELEMS = 64; // K elements per main-loop iteration (one quant gr
 
 struct TileMap {
     int mt, nt, splits, groups_per_split, total;
+    int group_m; // row tiles per group of the tile order (tile_coords)
 };
 
 __device__ __forceinline__ int xcd_tile(int b, int total)
@@ -54,6 +56,24 @@ __device__ __forceinline__ int xcd_tile(int b, int total)
     // contiguous range of tile ids.
     const int x = b & 7, k = b >> 3, q = total >> 3, r = total & 7;
     return x * q + (x < r ? x : r) + k;
+}
+
+// Tile id -> (row tile, column tile, K split). Within a split, ids run over groups of
+// tm.group_m row tiles: row fastest inside a group, then column, then the next group.
+// The workgroups an XCD runs at once (consecutive ids) then share a few activation
+// tiles and a few weight tiles in its L2; with every row tile in one group (as in
+// decode) this is plain row-fastest order.
+__device__ __forceinline__ void tile_coords(int tile, const TileMap &tm, int &m_tile, int &n_tile, int &split)
+{
+    const int per_split = tm.mt * tm.nt;
+    split = tile / per_split;
+    const int t = tile - split * per_split;
+    const int per_group = tm.group_m * tm.nt;
+    const int group = t / per_group, first = group * tm.group_m;
+    const int rows = min(tm.mt - first, tm.group_m);
+    const int u = t - group * per_group;
+    m_tile = first + u % rows;
+    n_tile = u / rows;
 }
 
 // Eight weights of one tiled word (nibble slots 0,2,4,6 hold e0..e3 and slots
@@ -87,10 +107,8 @@ __global__ void __launch_bounds__(256, MINW) k_gemm(GemmArgs g, TileMap tm)
     const int tile = xcd_tile(blockIdx.x, tm.total);
     if (tile >= tm.total)
         return;
-    const int m_tile = tile % tm.mt;
-    const int rest = tile / tm.mt;
-    const int n_tile = rest % tm.nt;
-    const int split = rest / tm.nt;
+    int m_tile, n_tile, split;
+    tile_coords(tile, tm, m_tile, n_tile, split);
     const int m0 = m_tile * BM, n0 = n_tile * BN;
     const int KG = g.K / KG_ELEMS;
     const int g0 = split * tm.groups_per_split;
@@ -319,10 +337,8 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
     const int tile = xcd_tile(blockIdx.x, tm.total);
     if (tile >= tm.total)
         return;
-    const int m_tile = tile % tm.mt;
-    const int rest = tile / tm.mt;
-    const int n_tile = rest % tm.nt;
-    const int split = rest / tm.nt;
+    int m_tile, n_tile, split;
+    tile_coords(tile, tm, m_tile, n_tile, split);
     const int m0 = m_tile * BM, n0 = n_tile * BN;
     const int KG = g.K / KG_ELEMS;
     const int g0 = split * tm.groups_per_split;
@@ -642,15 +658,19 @@ struct Plan {
 // and TOD_GEMM_BIG_BM = 128 | 192 | 256 to any of them; TOD_GEMM_SMALL_BM = 64 | 128 pins it at
 // 128 rows or fewer; TOD_GEMM_F16PIPE = 0 keeps fp16
 // weights on the register-staged kernel; TOD_GEMM_TILE = "64x64" | "128x128" | "256x128" puts
-// every GEMM on it with that tile for M > 64.
+// every GEMM on it with that tile for M > 64; TOD_GEMM_GROUP_M = row tiles per group of the
+// tile order (default 4; a large value gives plain row-fastest order).
 struct Tuning {
     int bm = 0, bn = 0, split_fill = -1;
     int bm192 = -1; // pipelined tile height: -1 cost model, 0 always 256, 1 always 192
     bool f16_pipe = true;   // fp16 weights on the pipelined kernel
     int small_bm = 0;       // pin the int4 tile height at 128 rows or fewer (64 or 128)
     int big_bm = 0;         // pin the int4 tile height above 128 rows (128, 192 or 256)
+    int group_m = 4;        // row tiles per group of the tile order
     Tuning()
     {
+        if (const char *t = getenv("TOD_GEMM_GROUP_M"))
+            group_m = atoi(t) >= 1 ? atoi(t) : 4;
         if (const char *t = getenv("TOD_GEMM_SMALL_BM"))
             small_bm = atoi(t) == 64 || atoi(t) == 128 ? atoi(t) : 0;
         if (const char *t = getenv("TOD_GEMM_F16PIPE"))
@@ -690,6 +710,7 @@ Plan split_plan(int M, int N, int K, int bm, int bn, bool pipelined)
     const int KG = K / KG_ELEMS;
     p.tm.mt = (M + bm - 1) / bm;
     p.tm.nt = (N + bn - 1) / bn;
+    p.tm.group_m = tu.group_m;
     const int tiles = p.tm.mt * p.tm.nt;
     const int fill = tu.split_fill >= 0 ? tu.split_fill : (pipelined ? 160 : 384);
     int splits = 1;
