@@ -340,6 +340,59 @@ def test_weights_on_disk_give_identical_bits(tier, tmp_path):
         tod.Model(shape, dict(run, weight_tier=0, hbm_layers=0, host_layers=0, weights_on_disk=1))
 
 
+@pytest.mark.parametrize("kv_host", [0, 1])
+def test_qkv_gemm_append_gives_identical_bits(kv_host):
+    """Decode steps quantize and append each step's K and V in the QKV GEMM's epilogue where its plan
+    allows (int4 weights on the pipelined kernel, K loop not split), instead of a separate append
+    kernel. The same fp16 values go through the same quantizer, so tokens, logits and the cache must
+    equal the separate kernel's bit for bit (TOD_QKV_APPEND=0 at init_model turns the fused path
+    off). OPT-30B width (192-row QKV tiles at 512 rows), 2 layers, 3 decode steps; with kv_host the
+    last layer's cache lives in pinned host memory and the epilogue writes through to it too."""
+    torch = torch_cuda()
+    import throughput_oriented_offloaded_amd as tod
+    shape = synth.WORKLOADS["opt-30b"].shape.replace(n_layers=2)
+    b, K, s, g = 64, 8, 16, 4
+    run = dict(gpu_batch=b, batches_per_block=K, prompt_len=s, gen_len=g, kv_host_layers=kv_host)
+    prompts = to_dev(synth.prompt_ids(b * K, s, shape.vocab), torch)
+    d = shape.head_dim
+    out = {}
+    for label, env in (("separate", "0"), ("fused", None)):
+        if env is None:
+            os.environ.pop("TOD_QKV_APPEND", None)
+        else:
+            os.environ["TOD_QKV_APPEND"] = env
+        try:
+            m, _ = build_gpu_model(shape, run)
+        finally:
+            os.environ.pop("TOD_QKV_APPEND", None)
+        tod.profile_kernels(m.handle, ("kv_append", "gemm_qkv"))   # profiled: steps launched one by one
+        toks_eager, logits_eager = m.generate(prompts, g, return_logits=True)
+        torch.cuda.synchronize()
+        appends = tod.profile_read(m.handle, "kv_append")[1]
+        qkv = tod.profile_read(m.handle, "gemm_qkv")[1]
+        tod.profile_kernels(m.handle, ())                             # unprofiled: captured steps replayed
+        toks, logits = m.generate(prompts, g, return_logits=True)
+        torch.cuda.synchronize()
+        assert torch.equal(toks, toks_eager) and torch.equal(logits.view(torch.int16), logits_eager.view(torch.int16))
+        kv = []
+        for layer, row, head in ((0, 0, 0), (1, b * K - 1, shape.n_heads - 1), (1, 77, 13), (0, 300, 40)):
+            kc = torch.empty((s + g - 1, d // 2), dtype=torch.uint8, device="cuda")
+            vc = torch.empty_like(kc)
+            ks, kz, vs, vz = (torch.empty((s + g - 1, d // 64), dtype=torch.float16, device="cuda")
+                              for _ in range(4))
+            tod.export_kv(m.handle, layer, 0, row, head, 0, s + g - 1, kc, ks, kz, vc, vs, vz)
+            torch.cuda.synchronize()
+            kv.append(b"".join(t.view(torch.uint8).cpu().numpy().tobytes() for t in (kc, ks, kz, vc, vs, vz)))
+        out[label] = (toks.cpu().numpy(), logits.view(torch.int16).cpu().numpy(), kv, appends, qkv)
+        m.close()
+    print(f"kv_host {kv_host}: append launches separate {out['separate'][3]}, fused {out['fused'][3]}; "
+          f"QKV launches {out['separate'][4]} / {out['fused'][4]}", flush=True)
+    assert out["separate"][3] > 0 and out["fused"][3] < out["separate"][3]  # prefill keeps its append kernel
+    assert np.array_equal(out["separate"][0], out["fused"][0])
+    assert np.array_equal(out["separate"][1], out["fused"][1])
+    assert out["separate"][2] == out["fused"][2]
+
+
 def test_int4_host_tier_matches_hbm_tier():
     """The int4 host tier streams the same tiled int4 image the HBM tier keeps
     resident, so prefill + decode give identical bits (tokens and logits) on a

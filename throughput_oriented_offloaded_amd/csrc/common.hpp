@@ -10,6 +10,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t uint4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2_t __attribute__((ext_vector_type(2)));
 
 #define TOD_WAVE 64
 
@@ -212,6 +213,56 @@ struct KvView {
 
 __device__ __forceinline__ size_t kv_slab(const KvView &v, int seq, int head) { return (size_t)seq * v.heads + head; }
 
+// ---------------------------------------------------------------------------
+// The int4 group quantizer (FlexGen guide, "3. Group-Wise 4-Bit Quantization
+// for Weights and KV Cache"): per group, zero = min, scale = fp16(fp32(max -
+// min) / 15), code = nearest grid point with ties to the larger code. Shared
+// by the quantize and KV-append kernels and the QKV GEMM's fused append, so
+// every path produces the same bytes.
+// ---------------------------------------------------------------------------
+// Parameters of one group from its minimum and maximum.
+struct GroupQ {
+    float mn, sf, rcp;
+    uint16_t scale, zero;
+};
+
+__device__ __forceinline__ GroupQ group_quant(float mn, float mx)
+{
+#pragma clang fp contract(off)
+    // -0 and +0 are one value: a zero minimum is stored as +0, a zero range gives scale +0
+    if (mn == 0.0f)
+        mn = fabsf(mn);
+    if (mx == 0.0f)
+        mx = fabsf(mx);
+    const float range = mx - mn;
+    const float s32 = range / 15.0f; // correctly rounded division
+    const half_t s16 = (half_t)s32;  // round to nearest even
+    GroupQ g;
+    g.mn = mn;
+    g.sf = (float)s16;
+    g.rcp = g.sf != 0.0f ? __builtin_amdgcn_rcpf(g.sf) : 0.0f; // estimate only
+    g.scale = __builtin_bit_cast(uint16_t, s16);
+    g.zero = f2h(mn); // exact: mn is one of the fp16 inputs
+    return g;
+}
+
+// Code of x: the number of k in 0..14 with fl32(x - mn) >= (k + 1/2) * scale.
+// In exact arithmetic that count is clamp(floor(d/scale + 1/2), 0, 15) with
+// d = fl32(x - mn) >= 0. The estimate from the approximate reciprocal is off
+// by at most one (d/scale <= 15.01 and the relative error is below 2^-21), and
+// one exact threshold test in each direction settles it: the thresholds are
+// exact in fp32 (an fp16 scale times a 5-bit multiple of 1/2).
+__device__ __forceinline__ int code_of(float x, const GroupQ &g)
+{
+#pragma clang fp contract(off)
+    const float d = x - g.mn;
+    int c = (int)(d * g.rcp + 0.5f);
+    c = c < 0 ? 0 : (c > 15 ? 15 : c);
+    c += (c < 15 && d >= ((float)c + 0.5f) * g.sf) ? 1 : 0;
+    c -= (c > 0 && d < ((float)c - 0.5f) * g.sf) ? 1 : 0;
+    return g.sf == 0.0f ? 0 : c;
+}
+
 // Rows of activations feeding the KV and attention kernels: row r belongs to
 // sequence seq0 + r / rows_per_seq at position pos0 + r % rows_per_seq.
 struct RowMap {
@@ -219,7 +270,9 @@ struct RowMap {
     const int *dpos; // if non-null, pos0 is read from device memory (captured decode steps)
 };
 
-enum Epilogue { EPI_BIAS = 0, EPI_BIAS_RES = 1, EPI_BIAS_RELU = 2, EPI_NONE = 3 };
+// EPI_QKV_APPEND: EPI_BIAS, and the output's K and V columns are quantized into the KV
+// cache instead of being stored (the fields after ln_y in GemmArgs)
+enum Epilogue { EPI_BIAS = 0, EPI_BIAS_RES = 1, EPI_BIAS_RELU = 2, EPI_NONE = 3, EPI_QKV_APPEND = 4 };
 
 // ---------------------------------------------------------------------------
 // Launchers (host side), defined next to their kernels.
@@ -270,6 +323,14 @@ struct GemmArgs {
     // gamma ln_g, beta ln_b; fused into the split-K reduction when there is one
     const uint16_t *ln_g, *ln_b;
     uint16_t *ln_y;
+    // EPI_QKV_APPEND (one decode step; int4 weights on the pipelined kernel, K loop not
+    // split): output columns [kv_col0, kv_col0 + h) are K and the next h are V. Each row's
+    // K and V are quantized in groups of 64 and stored at position *kv_dpos (kv_pos0 when
+    // null) of sequence kv_seq0 + row in kv, and in kv_mirror too when its kc is set; only
+    // the columns before kv_col0 (the query) are written to y.
+    KvView kv, kv_mirror;
+    const int *kv_dpos;
+    int kv_pos0, kv_seq0, kv_col0;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
 size_t gemm_workspace_bytes(int M, int N, int K, bool int4);

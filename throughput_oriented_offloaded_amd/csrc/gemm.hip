@@ -325,7 +325,62 @@ __device__ __forceinline__ void wait_vm_loads(int younger)
         wait_vmcnt<0>();
 }
 
-template <int BM_, bool F16, int S_ = 0>
+// Fused K/V append of the QKV GEMM's epilogue: this lane holds columns gb + c0 .. +15 (a)
+// and gb + 32 + c0 .. +15 (b) of one row, fp16 after the bias; its partner (lane ^ 1) holds
+// the other 32 columns of the 64-column group gb. Quantized exactly as the KV-append
+// kernel does (the same group_quant and code_of on the same fp16 values) and stored in the
+// cache's canonical layout.
+__device__ __forceinline__ void qkv_append(const GemmArgs &g, int grow, int gb, int c0, half8_t a0, half8_t a1,
+                                           half8_t b0, half8_t b1)
+{
+    float x[32];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+        x[e] = (float)a0[e];
+        x[8 + e] = (float)a1[e];
+        x[16 + e] = (float)b0[e];
+        x[24 + e] = (float)b1[e];
+    }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; e++) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+    }
+    mn = fminf(mn, __shfl_xor(mn, 1, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    const GroupQ q = group_quant(mn, mx);
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            word |= (uint32_t)code_of(x[8 * k + e], q) << (4 * e); // byte b: elements 2b, 2b + 1
+        w[k] = word;
+    }
+    const int d = g.kv.head_dim, h = g.kv.heads * d;
+    const int rel = gb - g.kv_col0, isv = rel >= h ? 1 : 0, within = rel - isv * h;
+    const int head = within / d, grp = (within % d) / 64;
+    const int pos = g.kv_dpos ? *g.kv_dpos : g.kv_pos0;
+    const size_t at = kv_slab(g.kv, g.kv_seq0 + grow, head) * g.kv.cap + pos;
+    const size_t cofs = at * (d / 2) + grp * 32 + c0 / 2, pofs = at * (d / 64) + grp;
+    const uint32_t param = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
+    uint8_t *codes = isv ? g.kv.vc : g.kv.kc;
+    *reinterpret_cast<uint2_t *>(codes + cofs) = (uint2_t){w[0], w[1]};
+    *reinterpret_cast<uint2_t *>(codes + cofs + 16) = (uint2_t){w[2], w[3]};
+    if (c0 == 0)
+        (isv ? g.kv.vp : g.kv.kp)[pofs] = param;
+    if (g.kv_mirror.kc) { // the same bytes into the pinned host copy of the cache
+        uint8_t *mc = isv ? g.kv_mirror.vc : g.kv_mirror.kc;
+        *reinterpret_cast<uint2_t *>(mc + cofs) = (uint2_t){w[0], w[1]};
+        *reinterpret_cast<uint2_t *>(mc + cofs + 16) = (uint2_t){w[2], w[3]};
+        if (c0 == 0)
+            (isv ? g.kv_mirror.vp : g.kv_mirror.kp)[pofs] = param;
+    }
+}
+
+template <int BM_, bool F16, int S_ = 0, bool APPEND = false>
 __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &tm)
 {
     using C = W4<BM_, F16, S_>;
@@ -491,6 +546,11 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
     static_assert(WAVES * 32 * SROW * 4 <= S * STAGE, "scratch fits the ring");
     float *scr = reinterpret_cast<float *>(smem) + wave * 32 * SROW;
     const int lr = lane >> 1, c0 = (lane & 1) * 16;
+    // APPEND: the wave's 64 columns are one quantization group of K or V (the QKV
+    // output's K and V start at a multiple of 64); column block 0's values wait here
+    static_assert(!APPEND || NB == 2, "one 64-column group per wave");
+    const bool kv_group = APPEND && n0 + wn * NB * 32 >= g.kv_col0;
+    half8_t hold[APPEND ? MB : 1][2];
 #pragma unroll
     for (int j = 0; j < NB; j++) {
         const int gcol = n0 + (wn * NB + j) * 32 + c0;
@@ -557,6 +617,15 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
                 else
                     o1[e - 8] = (half_t)x;
             }
+            if (kv_group) {
+                if (j == 0) {
+                    hold[i][0] = o0;
+                    hold[i][1] = o1;
+                } else {
+                    qkv_append(g, grow, n0 + wn * NB * 32, c0, hold[i][0], hold[i][1], o0, o1);
+                }
+                continue;
+            }
             uint16_t *yp = g.y + (int64_t)grow * g.ldc + gcol;
             *reinterpret_cast<uint4_t *>(yp) = __builtin_bit_cast(uint4_t, o0);
             *reinterpret_cast<uint4_t *>(yp + 8) = __builtin_bit_cast(uint4_t, o1);
@@ -570,6 +639,23 @@ __global__ void __launch_bounds__(512, 1) k_gemm_f16_256(GemmArgs g, TileMap tm)
 // 128 rows or fewer: short tiles, two workgroups per CU where LDS and registers allow
 __global__ void __launch_bounds__(512, 2) k_gemm_w4_128(GemmArgs g, TileMap tm) { gemm_w4_body<128, false>(g, tm); }
 __global__ void __launch_bounds__(512, 2) k_gemm_w4_64(GemmArgs g, TileMap tm) { gemm_w4_body<64, false>(g, tm); }
+// the QKV GEMM of a decode step with the K/V append in its epilogue (EPI_QKV_APPEND)
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_256a(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<256, false, 0, true>(g, tm);
+}
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_192a(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<192, false, 0, true>(g, tm);
+}
+__global__ void __launch_bounds__(512, 2) k_gemm_w4_128a(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<128, false, 0, true>(g, tm);
+}
+__global__ void __launch_bounds__(512, 2) k_gemm_w4_64a(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<64, false, 0, true>(g, tm);
+}
 // fp16, 128 rows or fewer: bound by the weight stream, so a third stage in flight pays
 __global__ void __launch_bounds__(512, 1) k_gemm_f16_64(GemmArgs g, TileMap tm) { gemm_w4_body<64, true, 3>(g, tm); }
 
@@ -839,6 +925,20 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
     }
     const dim3 grid(p.tm.total), block(256);
     const dim3 wg8(64 * W4<256>::WAVES); // every pipelined kernel runs eight wavefronts
+    if (g.epi == EPI_QKV_APPEND) {
+        // only where the caller checked the plan: int4 weights, pipelined, K loop not split
+        if (!int4 || !p.pipelined || p.tm.splits != 1 || g.kv_col0 % 64 || g.kv.head_dim % 64)
+            return hipErrorInvalidValue;
+        if (p.bm == 64)
+            hipLaunchKernelGGL(k_gemm_w4_64a, grid, wg8, 0, st, g, p.tm);
+        else if (p.bm == 128)
+            hipLaunchKernelGGL(k_gemm_w4_128a, grid, wg8, 0, st, g, p.tm);
+        else if (p.bm == 192)
+            hipLaunchKernelGGL(k_gemm_w4_192a, grid, wg8, 0, st, g, p.tm);
+        else
+            hipLaunchKernelGGL(k_gemm_w4_256a, grid, wg8, 0, st, g, p.tm);
+        return hipGetLastError();
+    }
     if (p.pipelined && !int4 && p.bm == 64)
         hipLaunchKernelGGL(k_gemm_f16_64, grid, wg8, 0, st, g, p.tm);
     else if (p.pipelined && !int4)

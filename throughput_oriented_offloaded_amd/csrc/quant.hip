@@ -16,47 +16,6 @@ namespace {
 
 #pragma clang fp contract(off)
 
-// Parameters of one group from its minimum and maximum.
-struct GroupQ {
-    float mn, sf, rcp;
-    uint16_t scale, zero;
-};
-
-__device__ __forceinline__ GroupQ group_quant(float mn, float mx)
-{
-    // -0 and +0 are one value: a zero minimum is stored as +0, a zero range gives scale +0
-    if (mn == 0.0f)
-        mn = fabsf(mn);
-    if (mx == 0.0f)
-        mx = fabsf(mx);
-    const float range = mx - mn;
-    const float s32 = range / 15.0f; // correctly rounded division
-    const half_t s16 = (half_t)s32;  // round to nearest even
-    GroupQ g;
-    g.mn = mn;
-    g.sf = (float)s16;
-    g.rcp = g.sf != 0.0f ? __builtin_amdgcn_rcpf(g.sf) : 0.0f; // estimate only
-    g.scale = __builtin_bit_cast(uint16_t, s16);
-    g.zero = f2h(mn); // exact: mn is one of the fp16 inputs
-    return g;
-}
-
-// Code of x: the number of k in 0..14 with fl32(x - mn) >= (k + 1/2) * scale.
-// In exact arithmetic that count is clamp(floor(d/scale + 1/2), 0, 15) with
-// d = fl32(x - mn) >= 0. The estimate from the approximate reciprocal is off
-// by at most one (d/scale <= 15.01 and the relative error is below 2^-21), and
-// one exact threshold test in each direction settles it: the thresholds are
-// exact in fp32 (an fp16 scale times a 5-bit multiple of 1/2).
-__device__ __forceinline__ int code_of(float x, const GroupQ &g)
-{
-    const float d = x - g.mn;
-    int c = (int)(d * g.rcp + 0.5f);
-    c = c < 0 ? 0 : (c > 15 ? 15 : c);
-    c += (c < 15 && d >= ((float)c + 0.5f) * g.sf) ? 1 : 0;
-    c -= (c > 0 && d < ((float)c - 0.5f) * g.sf) ? 1 : 0;
-    return g.sf == 0.0f ? 0 : c;
-}
-
 struct QuantLane {
     uint16_t scale, zero;
     int code;

@@ -93,6 +93,9 @@ struct tod_model {
     int32_t *ids = nullptr;
     float *ws = nullptr;
     size_t ws_bytes = 0;
+    // decode steps quantize and append K/V in the QKV GEMM's epilogue (its plan allows
+    // it: int4 weights on the pipelined kernel, K loop not split; TOD_QKV_APPEND=0: never)
+    bool qkv_append = false;
     // load-time staging
     uint16_t *stage = nullptr;
     uint8_t *stage_codes = nullptr;
@@ -278,9 +281,12 @@ void weights_of(const tod_model *m, const LayerStore &L, int mat, const uint8_t 
 
 // ln_g/ln_b (nullable): also write LayerNorm(y) into m->act, fused into the
 // GEMM's split-K reduction when it has one.
+// kv (nullable, EPI_QKV_APPEND): the cache the QKV GEMM appends this step's K/V to, for
+// sequences seq0 + row at position *dpos (pos0 when null), with its host mirror.
 int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint8_t *slot,
              uint16_t *y, int64_t ldc, int epi, hipStream_t st, const uint16_t *ln_g = nullptr,
-             const uint16_t *ln_b = nullptr)
+             const uint16_t *ln_b = nullptr, const KvView *kv = nullptr, const KvView *kv_mirror = nullptr,
+             int seq0 = 0, int pos0 = 0, const int *dpos = nullptr)
 {
     GemmArgs g{};
     g.a = a;
@@ -300,6 +306,15 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
         g.ln_g = ln_g;
         g.ln_b = ln_b;
         g.ln_y = m->act;
+    }
+    if (kv) {
+        g.kv = *kv;
+        if (kv_mirror)
+            g.kv_mirror = *kv_mirror;
+        g.kv_dpos = dpos;
+        g.kv_pos0 = pos0;
+        g.kv_seq0 = seq0;
+        g.kv_col0 = m->cfg.hidden; // q, then k, then v
     }
     ProfScope ps(m, TOD_K_GEMM_QKV + mat, st);
     HIPCHK(launch_gemm(g, st));
@@ -323,8 +338,14 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         ProfScope ps(m, TOD_K_LAYERNORM, st);
         HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
     }
-    if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wslot, m->qkv, 3 * hd, EPI_BIAS, st)))
+    const bool fused = !prefill_mode && m->qkv_append; // K/V appended by the QKV GEMM itself
+    if (fused) {
+        if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wslot, m->qkv, 3 * hd, EPI_QKV_APPEND, st, nullptr, nullptr,
+                           &kv, kv_mirror, seq0, pos, dpos)))
+            return rc;
+    } else if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wslot, m->qkv, 3 * hd, EPI_BIAS, st))) {
         return rc;
+    }
     SrcMap src;
     RowMap map;
     if (prefill_mode) {
@@ -334,7 +355,7 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         src = {3 * hd, 0, m->cfg.head_dim};
         map = {seq0, 1, pos, dpos};
     }
-    {
+    if (!fused) {
         ProfScope ps(m, TOD_K_KV_APPEND, st);
         HIPCHK(launch_kv_append(m->qkv + hd, m->qkv + 2 * hd, src, rows, map, kv, st, kv_mirror));
     }
@@ -817,6 +838,12 @@ static int init_model_impl(const tod_model_config *cfg, const tod_run_config *ru
         ws = b > ws ? b : ws;
     }
     m->ws_bytes = ws;
+    {
+        const GemmPlanInfo qp = gemm_plan_info(m->M, m->n_out[MAT_QKV], m->n_in[MAT_QKV], m->int4);
+        const char *t = getenv("TOD_QKV_APPEND");
+        m->qkv_append = m->int4 && qp.pipelined && qp.splits == 1 && h % 64 == 0 && c.head_dim % 64 == 0 &&
+                        !(t && atoi(t) == 0);
+    }
     ALLOC(m->ws, ws);
 
     if (host && n_streamed > 0) {
