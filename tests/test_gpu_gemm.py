@@ -36,6 +36,9 @@ CASES = [  # rows, in, out, epilogue
     (512, 512, 21504, "bias"), (450, 768, 20384, "res"),
     # 256-row tiles, where 192-row ones would need a second wave (fc1-like width; ragged M and N)
     (500, 512, 28640, "relu"),
+    # more than four row tiles, where tile ids run in groups of four row tiles: two whole groups;
+    # a ragged last group of three (and ragged N); the same with the K loop split eight ways
+    (2000, 512, 1056, "res"), (2600, 768, 800, "relu"), (2600, 4096, 256, "bias"),
 ]
 
 
