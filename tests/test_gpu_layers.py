@@ -25,7 +25,12 @@ Bars (the readings are in the design notes):
     which the later GEMMs carry forward, so that comparison is reported and
     held to the bound the exact-V difference implies (printed);
   * K/V codes: bit-exact except where the fp16 k or v itself differs by an
-    ulp across a code threshold (agreement reported, >= 0.999).
+    ulp. The quantizer is discontinuous: one ulp on a group's largest or
+    smallest value changes its scale and can move every code of the group, up
+    to 36 of the 8064 bytes of a position at OPT-30B width. So each checked
+    set of positions must agree with the oracle's codes at least as well as
+    the fp32-accumulating oracle's codes do on the same inputs, less one
+    group's bytes, and never below 0.99 (agreement of both is reported).
 """
 import numpy as np
 import pytest
@@ -82,6 +87,24 @@ def _code_agreement(shape, gpu_arrays, k, v, positions):
             y = np.asarray(y).view(np.uint8)
             agree += int((x == y).sum())
             total += x.size
+    return agree / total
+
+
+def _oracle_code_agreement(shape, k_a, v_a, k_b, v_b):
+    """Fraction of K/V code and parameter bytes equal between the oracle's quantization of two
+    sets of k, v rows (one row per position)."""
+    T = k_a.shape[0]
+    ca, cb = oracle.KVCache(shape, T), oracle.KVCache(shape, T)
+    ca.store(0, k_a, v_a)
+    cb.store(0, k_b, v_b)
+    agree = total = 0
+    for head in range(shape.n_heads):
+        for x, y in zip(ca.export(head, 0, T), cb.export(head, 0, T)):
+            x, y = np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)
+            agree += int((x == y).sum())
+            total += x.size
+    ca.close()
+    cb.close()
     return agree / total
 
 
@@ -149,39 +172,47 @@ def test_teacher_forced_layers(name):
     code_rates = []
 
     def refs(layer, cache, pos, rows):
-        """(fp64 pages' reading, fp64 exact-V, fp32-accumulating exact-V, k, v) of one layer."""
+        """(fp64 pages' reading, fp64 exact-V, fp32-accumulating exact-V, k, v, and the
+        fp32-accumulating oracle's k, v) of one layer."""
         r, k, v = layer.forward_given_kv(cache, pos, rows)
         with oracle.exact_v():
             rx, _, _ = layer.forward_given_kv(cache, pos, rows)
             with oracle.fp32_accumulation():
-                r32, _, _ = layer.forward_given_kv(cache, pos, rows)
-        return r, rx, r32, k, v
+                r32, k32, v32 = layer.forward_given_kv(cache, pos, rows)
+        return r, rx, r32, k, v, k32, v32
 
     for l in case["taps"]:
         pin, pout, din, dout = (to_np16(b) for b in bufs[l])
         layer = oracle.Layer(shape, synth.layer_weights(shape, l, variant=case["variant"]), int4_weights=tier != 1)
         for row in (0, M - 1):
             cache, arrays = _export_cache(tod, torch, m, l, row, shape, s + 1)
-            r, rx, r32, k, v = refs(layer, cache, s, din[row:row + 1])
+            r, rx, r32, k, v, k32, v32 = refs(layer, cache, s, din[row:row + 1])
             st.add(f"layer {l} decode row {row}", dout[row:row + 1], rx, r, r32)
-            code_rates.append(_code_agreement(shape, arrays, k, v, [s]))
-            print(f"layer {l} decode row {row}: new-position K/V byte agreement {code_rates[-1]:.5f}", flush=True)
+            code_rates.append((_code_agreement(shape, arrays, k, v, [s]), _oracle_code_agreement(shape, k, v, k32, v32)))
+            print(f"layer {l} decode row {row}: new-position K/V byte agreement {code_rates[-1][0]:.5f} "
+                  f"(fp32-accumulating oracle {code_rates[-1][1]:.5f})", flush=True)
             if row == pseq:
                 parts = [refs(layer, cache, t, pin[t:t + 1]) for t in PREFILL_POSITIONS]
                 got = np.concatenate([pout[t:t + 1] for t in PREFILL_POSITIONS])
                 st.add(f"layer {l} prefill row {row} positions {PREFILL_POSITIONS}", got,
                        np.concatenate([x[1] for x in parts]), np.concatenate([x[0] for x in parts]),
                        np.concatenate([x[2] for x in parts]))
-                code_rates.append(_code_agreement(shape, arrays, np.concatenate([x[3] for x in parts]),
-                                                  np.concatenate([x[4] for x in parts]), PREFILL_POSITIONS))
-                print(f"layer {l} prefill row {row}: K/V byte agreement {code_rates[-1]:.5f}", flush=True)
+                k64, v64 = np.concatenate([x[3] for x in parts]), np.concatenate([x[4] for x in parts])
+                k32, v32 = np.concatenate([x[5] for x in parts]), np.concatenate([x[6] for x in parts])
+                code_rates.append((_code_agreement(shape, arrays, k64, v64, PREFILL_POSITIONS),
+                                   _oracle_code_agreement(shape, k64, v64, k32, v32)))
+                print(f"layer {l} prefill row {row}: K/V byte agreement {code_rates[-1][0]:.5f} "
+                      f"(fp32-accumulating oracle {code_rates[-1][1]:.5f})", flush=True)
             cache.close()
         layer.close()
     m.close()
     g, f = np.concatenate(st.gpu), np.concatenate(st.fp32)
     ga, fa = np.concatenate(st.gpu_abs), np.concatenate(st.fp32_abs)
     print(f"{name}: GPU max {g.max():.2f} row-ulp, mean-abs {ga.mean():.4g}; fp32 oracle max {f.max():.2f} "
-          f"row-ulp, mean-abs {fa.mean():.4g}; K/V agreement min {min(code_rates):.5f}", flush=True)
+          f"row-ulp, mean-abs {fa.mean():.4g}; K/V agreement min {min(c[0] for c in code_rates):.5f} "
+          f"(fp32-accumulating oracle min {min(c[1] for c in code_rates):.5f})", flush=True)
     assert g.max() <= ROW_ULP_MAX
     assert ga.mean() <= MEAN_ABS_FACTOR * fa.mean()
-    assert min(code_rates) >= 0.999
+    group_bytes = (32 + 4) / (2 * shape.hidden * (0.5 + 4 / 64))  # one group of K or V over a position's bytes
+    for gpu_rate, fp32_rate in code_rates:
+        assert gpu_rate >= max(0.99, min(0.999, fp32_rate) - group_bytes), (gpu_rate, fp32_rate)
