@@ -468,14 +468,30 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
         if (s_ < nst)
             issue(s_, g0 + s_);
 
-    for (int it = 0; it < nst; it++) {
-        wait_vm_loads<C::LPS, S>(min(S - 2, nst - 1 - it));
-        __builtin_amdgcn_s_barrier();
-        if (it + S - 1 < nst)
-            issue((it + S - 1) % S, g0 + it + S - 1);
-        const uint8_t *base = smem + (it % S) * STAGE;
-        uint4_t bw[NB];
-        half2_t s2[NB], z2[NB];
+    // One K-group is four K-steps of 16. In each step the A operands of the next
+    // step (LDS) and its B operands are produced before this step's MFMAs.
+    const uint8_t *base = smem;
+    uint4_t bw[NB];
+    half2_t s2[NB], z2[NB];
+    half8_t a_cur[MB], b_cur[NB];
+    auto a_frag = [&](int i, int t) -> half8_t {
+        const int row = wm * RB + i * 32 + (lane & 31);
+        return *reinterpret_cast<const half8_t *>(base + row * 128 + (a_pos(row, 2 * t + (lane >> 5)) << 4));
+    };
+    // B operand of column block j at K-step t: dequantized codes, or the fp16
+    // W-tile fragment read like an A fragment
+    auto b_frag = [&](int j, int t) -> half8_t {
+        if constexpr (F16) {
+            const int row = (wn * NB + j) * 32 + (lane & 31);
+            return *reinterpret_cast<const half8_t *>(base + A_BYTES + row * 128 +
+                                                      (a_pos(row, 2 * t + (lane >> 5)) << 4));
+        } else {
+            return dequant_word(bw[j][t], s2[j], z2[j]);
+        }
+    };
+    // K-group `it` of this split: its ring stage, its weight words and the operands of step 0
+    auto begin_group = [&](int it) {
+        base = smem + (it % S) * STAGE;
         if constexpr (!F16) {
 #pragma unroll
             for (int j = 0; j < NB; j++) {
@@ -487,47 +503,29 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
                 z2[j] = __builtin_bit_cast(half2_t, (bp >> 16) * 0x10001u);
             }
         }
-        // B operand of column block j at K-step t: dequantized codes, or the fp16
-        // W-tile fragment read like an A fragment
-        auto b_frag = [&](int j, int t) -> half8_t {
-            if constexpr (F16) {
-                const int row = (wn * NB + j) * 32 + (lane & 31);
-                return *reinterpret_cast<const half8_t *>(base + A_BYTES + row * 128 +
-                                                          (a_pos(row, 2 * t + (lane >> 5)) << 4));
-            } else {
-                return dequant_word(bw[j][t], s2[j], z2[j]);
-            }
-        };
-        // Four K-steps of 16: the A operands of step t+1 (LDS) and its B operands
-        // are produced before the MFMAs of step t; the other wave on the SIMD
-        // fills the gaps.
-        half8_t a_cur[MB], a_nxt[MB], b_cur[NB], b_nxt[NB];
 #pragma unroll
-        for (int i = 0; i < MB; i++) {
-            const int row = wm * RB + i * 32 + (lane & 31);
-            a_cur[i] = *reinterpret_cast<const half8_t *>(base + row * 128 + (a_pos(row, lane >> 5) << 4));
-        }
+        for (int i = 0; i < MB; i++)
+            a_cur[i] = a_frag(i, 0);
 #pragma unroll
         for (int j = 0; j < NB; j++)
             b_cur[j] = b_frag(j, 0);
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-            if (t < 3) {
-#pragma unroll
-                for (int i = 0; i < MB; i++) {
-                    const int row = wm * RB + i * 32 + (lane & 31);
-                    a_nxt[i] = *reinterpret_cast<const half8_t *>(base + row * 128 +
-                                                                  (a_pos(row, 2 * (t + 1) + (lane >> 5)) << 4));
-                }
-#pragma unroll
-                for (int j = 0; j < NB; j++)
-                    b_nxt[j] = b_frag(j, t + 1);
-            }
+    };
+    auto k_step = [&](int t) {
+        half8_t a_nxt[MB], b_nxt[NB];
+        if (t < 3) {
 #pragma unroll
             for (int i = 0; i < MB; i++)
+                a_nxt[i] = a_frag(i, t + 1);
 #pragma unroll
-                for (int j = 0; j < NB; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[i], b_cur[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < NB; j++)
+                b_nxt[j] = b_frag(j, t + 1);
+        }
+#pragma unroll
+        for (int i = 0; i < MB; i++)
+#pragma unroll
+            for (int j = 0; j < NB; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_cur[i], b_cur[j], acc[i][j], 0, 0, 0);
+        if (t < 3) {
 #pragma unroll
             for (int i = 0; i < MB; i++)
                 a_cur[i] = a_nxt[i];
@@ -535,6 +533,17 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
             for (int j = 0; j < NB; j++)
                 b_cur[j] = b_nxt[j];
         }
+    };
+
+    for (int it = 0; it < nst; it++) {
+        wait_vm_loads<C::LPS, S>(min(S - 2, nst - 1 - it));
+        __builtin_amdgcn_s_barrier();
+        if (it + S - 1 < nst)
+            issue((it + S - 1) % S, g0 + it + S - 1);
+        begin_group(it);
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+            k_step(t);
     }
 
     // Epilogue through LDS: each 32 x 32 accumulator block goes to a per-wave
