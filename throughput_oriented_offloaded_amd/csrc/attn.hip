@@ -17,6 +17,8 @@
 
 namespace {
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
 // Exact codes of bytes 0,1 (HI = false) or 2,3 (HI = true) of a word whose
 // bytes each hold one 4-bit code: the byte read as fp8 e4m3 is c * 2^-9.
 template <bool HI> __device__ __forceinline__ half2_t code_pair(uint32_t nibbles)
@@ -29,6 +31,19 @@ __device__ __forceinline__ half2_t splat_half(uint32_t bits)
 {
     const half_t h = __builtin_bit_cast(half_t, (uint16_t)bits);
     return (half2_t){h, h};
+}
+
+// The eight cache values fp16(c_e * scale + zero), rounded once, of a code word whose nibble e
+// holds dim e: exact code pairs (e0,e2) (e4,e6) from the low nibbles, (e1,e3) (e5,e7) from the
+// high ones, then one packed FMA per pair.
+__device__ __forceinline__ half8_t dequant8(uint32_t w, half2_t s2, half2_t z2)
+{
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    const half2_t x02 = __builtin_elementwise_fma(code_pair<false>(lo), s2, z2);
+    const half2_t x46 = __builtin_elementwise_fma(code_pair<true>(lo), s2, z2);
+    const half2_t x13 = __builtin_elementwise_fma(code_pair<false>(hi), s2, z2);
+    const half2_t x57 = __builtin_elementwise_fma(code_pair<true>(hi), s2, z2);
+    return (half8_t){x02[0], x13[0], x02[1], x13[1], x46[0], x57[0], x46[1], x57[1]};
 }
 
 // One chunk of 64 positions as seen by one lane: L = d/32 lanes share a
@@ -249,6 +264,9 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
     constexpr int DB = D / 16;      // 16-dim output blocks
     constexpr int KP = D + 8;       // K row pitch (halves)
     constexpr int VP = 64 + 8;      // V^T row pitch (halves)
+    constexpr int WPR = CB / 4;     // 32-bit code words per position
+    constexpr int PPT = 64 * WPR / 256; // positions per thread in the dequantization (4 at d = 128)
+    static_assert(PPT == 2 || PPT == 4, "d = 64 or 128");
     __shared__ __attribute__((aligned(16))) half_t sk[64 * KP];
     __shared__ __attribute__((aligned(16))) half_t svt[D * VP];
 
@@ -282,29 +300,35 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
     const int last_key = min(len, qt * 64 + 64);
     for (int k0 = 0; k0 < last_key; k0 += 64) {
         __syncthreads();
-        // dequantize keys k0..k0+63: each thread takes one 32-bit code word (8 dims) of K and of V
-        for (int i = tid; i < 64 * (CB / 4); i += 256) {
-            const int r = i / (CB / 4), wd = i % (CB / 4), pos = k0 + r;
-            half8_t kh = {}, vh = {};
-            if (pos < len) {
-                const size_t at = slab * kv.cap + pos;
-                const uint32_t kw = *reinterpret_cast<const uint32_t *>(kv.kc + at * CB + 4 * wd);
-                const uint32_t vw = *reinterpret_cast<const uint32_t *>(kv.vc + at * CB + 4 * wd);
-                const uint32_t kpw = kv.kp[at * G + wd / 8], vpw = kv.vp[at * G + wd / 8];
-                const half_t ks = __builtin_bit_cast(half_t, (uint16_t)(kpw & 0xffff));
-                const half_t kz = __builtin_bit_cast(half_t, (uint16_t)(kpw >> 16));
-                const half_t vs = __builtin_bit_cast(half_t, (uint16_t)(vpw & 0xffff));
-                const half_t vz = __builtin_bit_cast(half_t, (uint16_t)(vpw >> 16));
+        // dequantize keys k0..k0+63: thread (word wd, positions p0..p0+PPT-1) takes code word wd (dims
+        // 8wd..8wd+7) of PPT consecutive positions, of K and of V; K rows go to LDS as 16-byte runs
+        // and each dim of V^T as one run of PPT keys
+        {
+            const int wd = tid % WPR, p0 = (tid / WPR) * PPT;
+            half8_t vh[PPT];
 #pragma unroll
-                for (int e = 0; e < 8; e++) { // canonical: nibble e of the word is dim 8 * wd + e
-                    kh[e] = __builtin_fmaf16((half_t)(float)((kw >> (4 * e)) & 15u), ks, kz);
-                    vh[e] = __builtin_fmaf16((half_t)(float)((vw >> (4 * e)) & 15u), vs, vz);
+            for (int i = 0; i < PPT; i++) {
+                const int pos = k0 + p0 + i;
+                half8_t kh = {};
+                vh[i] = (half8_t){};
+                if (pos < len) {
+                    const size_t at = slab * kv.cap + pos;
+                    const uint32_t kw = *reinterpret_cast<const uint32_t *>(kv.kc + at * CB + 4 * wd);
+                    const uint32_t vw = *reinterpret_cast<const uint32_t *>(kv.vc + at * CB + 4 * wd);
+                    const uint32_t kpw = kv.kp[at * G + wd / 8], vpw = kv.vp[at * G + wd / 8];
+                    kh = dequant8(kw, splat_half(kpw & 0xffffu), splat_half(kpw >> 16));
+                    vh[i] = dequant8(vw, splat_half(vpw & 0xffffu), splat_half(vpw >> 16));
                 }
+                *reinterpret_cast<half8_t *>(&sk[(p0 + i) * KP + 8 * wd]) = kh;
             }
-            *reinterpret_cast<half8_t *>(&sk[r * KP + 8 * wd]) = kh;
 #pragma unroll
-            for (int e = 0; e < 8; e++)
-                svt[(8 * wd + e) * VP + r] = vh[e];
+            for (int e = 0; e < 8; e++) {
+                half_t *dst = &svt[(8 * wd + e) * VP + p0];
+                if constexpr (PPT == 4)
+                    *reinterpret_cast<half4_t *>(dst) = (half4_t){vh[0][e], vh[1][e], vh[2][e], vh[3][e]};
+                else
+                    *reinterpret_cast<half2_t *>(dst) = (half2_t){vh[0][e], vh[1][e]};
+            }
         }
         __syncthreads();
 
