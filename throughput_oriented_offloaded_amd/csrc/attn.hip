@@ -11,8 +11,10 @@
 // positions with its own online softmax (details at k_attn_decode); nothing
 // is shared between wavefronts, so there are no workgroup barriers. K and V
 // codes share the canonical per-position layout.
-// Prefill (causal, all prompt positions) uses a tiled MFMA variant: 64 queries
+// Prefill (causal, all prompt positions) uses a tiled MFMA variant: 128 queries
 // per workgroup, K/V tiles of 64 positions dequantized into LDS, online softmax.
+#include <cstdlib>
+
 #include "common.hpp"
 
 namespace {
@@ -238,11 +240,13 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: 64 queries of one (sequence, head) per workgroup, causal, on MFMA.
+// Prefill: QT tiles of 64 queries of one (sequence, head) per workgroup (two by
+// default), causal, on MFMA.
 //
-// Four wavefronts take 16 queries each. Per tile of 64 keys, K is dequantized
-// into LDS row-major and V transposed (fp16 values, each rounded once, as the
-// cache defines them). Scores are computed transposed, S^T = K . Q^T, with
+// Wavefronts take 16 queries each, four per query tile. Per tile of 64 keys, K
+// is dequantized once for the whole workgroup into LDS row-major and V
+// transposed (fp16 values, each rounded once, as the cache defines them); a
+// wavefront whose queries all precede the tile only joins its barriers. Scores are computed transposed, S^T = K . Q^T, with
 // v_mfma_f32_16x16x32_f16: lane l ends up with keys 4*(l/16)+i (i < 4) of
 // each 16-key block for query l % 16. Those registers are directly the B
 // operand of O^T += V^T . P^T once the reduction index (keys) is permuted the
@@ -254,10 +258,10 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
 // remainder, each through its own MFMA, so the weights keep fp32-level
 // precision; the scale comes off exactly at the end. Accumulation is fp32.
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict__ q, int64_t q_stride,
-                                                      uint16_t *__restrict__ out, int64_t out_stride, int seq0,
-                                                      int len, KvView kv)
+template <int D, int QT>
+__global__ void __launch_bounds__(256 * QT) k_attn_prefill(const uint16_t *__restrict__ q, int64_t q_stride,
+                                                           uint16_t *__restrict__ out, int64_t out_stride, int seq0,
+                                                           int len, KvView kv)
 {
     constexpr int CB = D / 2, G = D / 64;
     constexpr int KS = D / 32;      // 32-dim MFMA steps of the score product
@@ -265,19 +269,22 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
     constexpr int KP = D + 8;       // K row pitch (halves)
     constexpr int VP = 64 + 8;      // V^T row pitch (halves)
     constexpr int WPR = CB / 4;     // 32-bit code words per position
-    constexpr int PPT = 64 * WPR / 256; // positions per thread in the dequantization (4 at d = 128)
-    static_assert(PPT == 2 || PPT == 4, "d = 64 or 128");
+    constexpr int PPT = 64 * WPR / (256 * QT); // positions per thread in the dequantization
+    static_assert(PPT == 1 || PPT == 2 || PPT == 4, "d = 64 or 128, one or two query tiles");
     __shared__ __attribute__((aligned(16))) half_t sk[64 * KP];
     __shared__ __attribute__((aligned(16))) half_t svt[D * VP];
 
-    const int qtiles = (len + 63) / 64;
-    const int qt = blockIdx.x % qtiles;
-    const int sh = blockIdx.x / qtiles;
+    // workgroup: QT consecutive query tiles of one (sequence, head); wave w takes queries 16 (w % 4) ..
+    // of tile QT * (workgroup's tile pair) + w / 4 and all its waves share each dequantized key tile
+    const int qtiles = (len + 63) / 64, groups = (qtiles + QT - 1) / QT;
+    const int qg = blockIdx.x % groups;
+    const int sh = blockIdx.x / groups;
     const int head = sh % kv.heads, s = sh / kv.heads;
     const size_t slab = kv_slab(kv, seq0 + s, head);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, g = lane >> 4;
-    const int qpos = qt * 64 + wave * 16 + col; // this lane's query
+    const int qt = qg * QT + (wave >> 2);       // this wave's query tile (may be past the last one)
+    const int qpos = qt * 64 + (wave & 3) * 16 + col; // this lane's query
     const bool qlive = qpos < len;
 
     // Q^T fragments (B operand): dims 32k + 8g .. +8 of query qpos (zeros past len)
@@ -297,7 +304,8 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
         acc[e] = (float4_t){0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_part = 0.0f; // l_part: this lane's share of the query's sum
 
-    const int last_key = min(len, qt * 64 + 64);
+    const int last_key = min(len, (qg * QT + QT - 1) * 64 + 64); // the workgroup's last key
+    const int my_last = qt < qtiles ? min(len, qt * 64 + 64) : 0;  // this wave's last key
     for (int k0 = 0; k0 < last_key; k0 += 64) {
         __syncthreads();
         // dequantize keys k0..k0+63: thread (word wd, positions p0..p0+PPT-1) takes code word wd (dims
@@ -326,11 +334,15 @@ __global__ void __launch_bounds__(256) k_attn_prefill(const uint16_t *__restrict
                 half_t *dst = &svt[(8 * wd + e) * VP + p0];
                 if constexpr (PPT == 4)
                     *reinterpret_cast<half4_t *>(dst) = (half4_t){vh[0][e], vh[1][e], vh[2][e], vh[3][e]};
-                else
+                else if constexpr (PPT == 2)
                     *reinterpret_cast<half2_t *>(dst) = (half2_t){vh[0][e], vh[1][e]};
+                else
+                    *dst = vh[0][e];
             }
         }
         __syncthreads();
+        if (k0 >= my_last) // keys past this wave's queries (wave-uniform); the barriers above still run
+            continue;
 
         // S^T for the four 16-key blocks: lane holds keys k0 + 16b + 4g + i for query qpos
         float sc[4][4];
@@ -422,13 +434,21 @@ hipError_t launch_attn_prefill(const uint16_t *q, int64_t q_stride, uint16_t *ou
 {
     if (n_seq == 0 || len == 0)
         return hipSuccess;
-    const int qtiles = (len + 63) / 64;
-    const dim3 grid((unsigned)n_seq * kv.heads * qtiles), block(256);
-    if (kv.head_dim == 128)
-        hipLaunchKernelGGL(k_attn_prefill<128>, grid, block, 0, st, q, q_stride, out, out_stride, seq0, len, kv);
-    else if (kv.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_prefill<64>, grid, block, 0, st, q, q_stride, out, out_stride, seq0, len, kv);
-    else
+    static const int qt_per_wg = [] {
+        const char *t = getenv("TOD_PREFILL_QT"); // query tiles per workgroup: 1 or 2
+        return t && atoi(t) == 1 ? 1 : 2;
+    }();
+    if (kv.head_dim != 128 && kv.head_dim != 64)
         return hipErrorInvalidValue;
+    const int qtiles = (len + 63) / 64, groups = (qtiles + qt_per_wg - 1) / qt_per_wg;
+    const dim3 grid((unsigned)n_seq * kv.heads * groups), block(256 * qt_per_wg);
+    if (kv.head_dim == 128 && qt_per_wg == 2)
+        hipLaunchKernelGGL((k_attn_prefill<128, 2>), grid, block, 0, st, q, q_stride, out, out_stride, seq0, len, kv);
+    else if (kv.head_dim == 128)
+        hipLaunchKernelGGL((k_attn_prefill<128, 1>), grid, block, 0, st, q, q_stride, out, out_stride, seq0, len, kv);
+    else if (qt_per_wg == 2)
+        hipLaunchKernelGGL((k_attn_prefill<64, 2>), grid, block, 0, st, q, q_stride, out, out_stride, seq0, len, kv);
+    else
+        hipLaunchKernelGGL((k_attn_prefill<64, 1>), grid, block, 0, st, q, q_stride, out, out_stride, seq0, len, kv);
     return hipGetLastError();
 }
