@@ -691,12 +691,34 @@ __global__ void __launch_bounds__(256) k_splitk_reduce(GemmArgs g, int splits)
 // output is summed over the splits, bias and residual added and rounded
 // exactly as in k_splitk_reduce; the fp16 row stays in registers for
 // layernorm_row, the same code as the LayerNorm kernel.
-template <int K>
+// SPLITS > 0: the split count is fixed at compile time and every partial, bias and residual
+// word of the thread's chunks is loaded before the first add (a chunk past the row's end reads
+// the row's last chunk again and is not used); the sums run in the same split order either way.
+template <int K, int SPLITS = 0>
 __global__ void __launch_bounds__(256) k_splitk_reduce_ln(GemmArgs g, int splits)
 {
     __shared__ float red[8];
     const int row = blockIdx.x, nch = g.N >> 3;
     const int64_t mn = (int64_t)g.M * g.N;
+    const bool has_bias = g.bias && g.epi != EPI_NONE, has_res = g.epi == EPI_BIAS_RES;
+    constexpr int NS = SPLITS > 0 ? SPLITS : 1;
+    float4_t pa[K][NS], pb[K][NS];
+    uint4_t bw[K], rw[K];
+    if constexpr (SPLITS > 0) {
+#pragma unroll
+        for (int k = 0; k < K; k++) {
+            const int c = min((int)threadIdx.x + 256 * k, nch - 1);
+            const int64_t i0 = (int64_t)row * g.N + 8 * c;
+#pragma unroll
+            for (int sp = 0; sp < SPLITS; sp++) {
+                pa[k][sp] = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0);
+                pb[k][sp] = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0 + 4);
+            }
+            bw[k] = has_bias ? *reinterpret_cast<const uint4_t *>(g.bias + 8 * c) : (uint4_t){0u, 0u, 0u, 0u};
+            rw[k] = has_res ? *reinterpret_cast<const uint4_t *>(g.residual + (int64_t)row * g.ldc + 8 * c)
+                            : (uint4_t){0u, 0u, 0u, 0u};
+        }
+    }
     uint4_t v[K];
 #pragma unroll
     for (int k = 0; k < K; k++) {
@@ -709,28 +731,40 @@ __global__ void __launch_bounds__(256) k_splitk_reduce_ln(GemmArgs g, int splits
 #pragma unroll
         for (int e = 0; e < 8; e++)
             x[e] = 0.0f;
-        for (int sp = 0; sp < splits; sp++) {
-            const float4_t p0 = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0);
-            const float4_t p1 = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0 + 4);
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                x[e] += p0[e];
-                x[4 + e] += p1[e];
-            }
-        }
         half8_t bias = {}, res = {};
-        if (g.bias && g.epi != EPI_NONE)
-            bias = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g.bias + 8 * c));
-        if (g.epi == EPI_BIAS_RES)
-            res = __builtin_bit_cast(half8_t,
-                                     *reinterpret_cast<const uint4_t *>(g.residual + (int64_t)row * g.ldc + 8 * c));
+        if constexpr (SPLITS > 0) {
+#pragma unroll
+            for (int sp = 0; sp < SPLITS; sp++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    x[e] += pa[k][sp][e];
+                    x[4 + e] += pb[k][sp][e];
+                }
+            bias = __builtin_bit_cast(half8_t, bw[k]);
+            res = __builtin_bit_cast(half8_t, rw[k]);
+        } else {
+            for (int sp = 0; sp < splits; sp++) {
+                const float4_t p0 = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0);
+                const float4_t p1 = *reinterpret_cast<const float4_t *>(g.ws + sp * mn + i0 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    x[e] += p0[e];
+                    x[4 + e] += p1[e];
+                }
+            }
+            if (has_bias)
+                bias = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4_t *>(g.bias + 8 * c));
+            if (has_res)
+                res = __builtin_bit_cast(half8_t,
+                                         *reinterpret_cast<const uint4_t *>(g.residual + (int64_t)row * g.ldc + 8 * c));
+        }
         half8_t o;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             float t = x[e];
-            if (g.bias && g.epi != EPI_NONE)
+            if (has_bias)
                 t += (float)bias[e];
-            if (g.epi == EPI_BIAS_RES)
+            if (has_res)
                 t += (float)res[e];
             if (g.epi == EPI_BIAS_RELU)
                 t = fmaxf(t, 0.0f);
@@ -980,15 +1014,19 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         return g.ln_y ? launch_layernorm(g.y, g.M, g.N, g.ln_g, g.ln_b, g.ln_y, st) : hipSuccess;
     if (g.ln_y) {
         const dim3 grid((unsigned)g.M), block(256);
-        const int chunks = layernorm_chunks(g.N);
+        const int chunks = layernorm_chunks(g.N), sp = p.tm.splits;
         if (chunks <= 1)
-            hipLaunchKernelGGL(k_splitk_reduce_ln<1>, grid, block, 0, st, g, p.tm.splits);
+            hipLaunchKernelGGL(k_splitk_reduce_ln<1>, grid, block, 0, st, g, sp);
         else if (chunks <= 2)
-            hipLaunchKernelGGL(k_splitk_reduce_ln<2>, grid, block, 0, st, g, p.tm.splits);
+            hipLaunchKernelGGL(k_splitk_reduce_ln<2>, grid, block, 0, st, g, sp);
+        else if (chunks <= 4 && sp == 2)
+            hipLaunchKernelGGL((k_splitk_reduce_ln<4, 2>), grid, block, 0, st, g, sp);
+        else if (chunks <= 4 && sp == 4)
+            hipLaunchKernelGGL((k_splitk_reduce_ln<4, 4>), grid, block, 0, st, g, sp);
         else if (chunks <= 4)
-            hipLaunchKernelGGL(k_splitk_reduce_ln<4>, grid, block, 0, st, g, p.tm.splits);
+            hipLaunchKernelGGL(k_splitk_reduce_ln<4>, grid, block, 0, st, g, sp);
         else
-            hipLaunchKernelGGL(k_splitk_reduce_ln<8>, grid, block, 0, st, g, p.tm.splits);
+            hipLaunchKernelGGL(k_splitk_reduce_ln<8>, grid, block, 0, st, g, sp);
         return hipGetLastError();
     }
     const int64_t n = (int64_t)g.M * g.N;
