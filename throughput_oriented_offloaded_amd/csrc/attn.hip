@@ -93,16 +93,19 @@ struct SoftmaxState {
 //    added once at the end from the running sum of p * zero. So V enters as
 //    the exact value zero + c * scale (never rounded to fp16), and each
 //    accumulator carries only the code part of the weighted sum.
-template <int D>
+// R < L: only the first R rounds of PPI positions (the rest of the chunk lies past the context,
+// so those positions would contribute exact zeros).
+template <int D, int R = D / 32>
 __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, int slot, int ctx,
                                              const half2_t (&qa)[8], const half2_t (&qb)[8], SoftmaxState &st)
 {
     constexpr int L = D / 32, PPI = 64 / L;
+    static_assert(R >= 1 && R <= L, "rounds of a chunk");
     const float inv_sqrt_d = 1.0f / sqrtf((float)D);
-    float sc[L];
+    float sc[R];
     float mloc = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < L; j++) {
+    for (int j = 0; j < R; j++) {
         const half2_t s2 = splat_half(c.kp[j] & 0xffffu), z2 = splat_half(c.kp[j] >> 16);
         float da = 0.0f, db = 0.0f;
 #pragma unroll
@@ -133,7 +136,7 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
         st.m_run = mloc;
     }
 #pragma unroll
-    for (int j = 0; j < L; j++) {
+    for (int j = 0; j < R; j++) {
         const bool live = c0 + slot + PPI * j < ctx;
         const float p = __expf(sc[j] - st.m_run); // 0 past the context
         const float ps = live ? p * h2f((uint16_t)(c.vp[j] & 0xffffu)) : 0.0f;
@@ -204,20 +207,34 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
     st.m_run = -INFINITY;
     st.lsum = st.zsum = 0.0f;
 
-    // chunks in pairs through two register buffers; loads of a chunk index
-    // past the context are clamped to its last position (cache hits)
+    // chunks in pairs through two register buffers (loads of a position past
+    // the context are clamped to its last position: cache hits); the last
+    // chunk runs only its rounds that hold live positions
     KvChunk<L> ca, cb;
     const int nchunks = (ctx + 63) / 64;
-    int c0 = 0;
+    int c0 = 0, i = 0;
     load_chunk<D>(ca, 0, slot, pc, ctx, kc, vc, kp, vp);
-    for (int i = 0; i + 2 <= nchunks; i += 2, c0 += 128) {
+    for (; i + 2 < nchunks; i += 2, c0 += 128) {
         load_chunk<D>(cb, c0 + 64, slot, pc, ctx, kc, vc, kp, vp);
         attend_chunk<D>(ca, c0, slot, ctx, qa, qb, st);
         load_chunk<D>(ca, c0 + 128, slot, pc, ctx, kc, vc, kp, vp);
         attend_chunk<D>(cb, c0 + 64, slot, ctx, qa, qb, st);
     }
-    if (nchunks & 1)
+    if (nchunks - i == 2) {
+        load_chunk<D>(cb, c0 + 64, slot, pc, ctx, kc, vc, kp, vp);
         attend_chunk<D>(ca, c0, slot, ctx, qa, qb, st);
+        c0 += 64;
+        ca = cb;
+    }
+    const int rounds = (ctx - c0 + 64 / L - 1) / (64 / L); // 1 .. L, wave-uniform
+    if (rounds >= L)
+        attend_chunk<D, L>(ca, c0, slot, ctx, qa, qb, st);
+    else if (rounds == 1)
+        attend_chunk<D, 1>(ca, c0, slot, ctx, qa, qb, st);
+    else if (L > 2 && rounds == 2)
+        attend_chunk<D, (L > 2 ? 2 : 1)>(ca, c0, slot, ctx, qa, qb, st);
+    else
+        attend_chunk<D, (L > 3 ? 3 : 1)>(ca, c0, slot, ctx, qa, qb, st);
 
     // add the zero term, sum over the wave's positions
     const float den = reduce_slots<L>(st.lsum, OpAdd());
