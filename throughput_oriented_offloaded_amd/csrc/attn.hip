@@ -263,7 +263,8 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
 // Wavefronts take 16 queries each, four per query tile. Per tile of 64 keys, K
 // is dequantized once for the whole workgroup into LDS row-major and V
 // transposed (fp16 values, each rounded once, as the cache defines them); a
-// wavefront whose queries all precede the tile only joins its barriers. Scores are computed transposed, S^T = K . Q^T, with
+// wavefront whose queries all precede the tile only joins its barriers.
+// Scores are computed transposed, S^T = K . Q^T, with
 // v_mfma_f32_16x16x32_f16: lane l ends up with keys 4*(l/16)+i (i < 4) of
 // each 16-key block for query l % 16. Those registers are directly the B
 // operand of O^T += V^T . P^T once the reduction index (keys) is permuted the
@@ -438,9 +439,11 @@ hipError_t launch_attn_decode(const uint16_t *q, int64_t q_stride, uint16_t *out
         return hipSuccess;
     const dim3 grid((unsigned)(((int64_t)rows * kv.heads + 3) / 4)), block(256);
     if (kv.head_dim == 128)
-        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, dctx, kv);
+        hipLaunchKernelGGL(k_attn_decode<128>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx,
+                           dctx, kv);
     else if (kv.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx, dctx, kv);
+        hipLaunchKernelGGL(k_attn_decode<64>, grid, block, 0, st, q, q_stride, out, out_stride, rows, seq0, ctx,
+                           dctx, kv);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

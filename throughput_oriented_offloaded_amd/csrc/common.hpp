@@ -323,14 +323,16 @@ struct GemmArgs {
     // gamma ln_g, beta ln_b; fused into the split-K reduction when there is one
     const uint16_t *ln_g, *ln_b;
     uint16_t *ln_y;
-    // EPI_QKV_APPEND (one decode step; int4 weights on the pipelined kernel, K loop not
-    // split): output columns [kv_col0, kv_col0 + h) are K and the next h are V. Each row's
-    // K and V are quantized in groups of 64 and stored at position *kv_dpos (kv_pos0 when
-    // null) of sequence kv_seq0 + row in kv, and in kv_mirror too when its kc is set; only
-    // the columns before kv_col0 (the query) are written to y.
+    // EPI_QKV_APPEND (int4 weights on the pipelined kernel, K loop not split): output
+    // columns [kv_col0, kv_col0 + h) are K and the next h are V. Rows come in runs of
+    // kv_rows_per_seq consecutive positions of one sequence (1 in a decode step, the prompt
+    // length in prefill; 0 counts as 1): row r's K and V are quantized in groups of 64 and
+    // stored at position (*kv_dpos, or kv_pos0 when null) + r % kv_rows_per_seq of sequence
+    // kv_seq0 + r / kv_rows_per_seq in kv, and in kv_mirror too when its kc is set; only the
+    // columns before kv_col0 (the query) are written to y.
     KvView kv, kv_mirror;
     const int *kv_dpos;
-    int kv_pos0, kv_seq0, kv_col0;
+    int kv_pos0, kv_seq0, kv_col0, kv_rows_per_seq;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t st);
 size_t gemm_workspace_bytes(int M, int N, int K, bool int4);

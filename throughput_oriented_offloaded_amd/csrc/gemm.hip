@@ -291,7 +291,8 @@ template <int BM_, bool F16 = false, int S_ = 0> struct W4 {
     static constexpr int S = S_ ? S_ : F16 ? 2 : 3;     // ring stages
     static constexpr int AL = (BM / 8) / WAVES;         // 1 KiB A chunks (8 rows) loaded per wave per stage
     static constexpr int WL = F16 ? (BN / 8) / WAVES : 0; // fp16: 1 KiB W chunks per wave per stage
-    static constexpr int LPS = AL + (F16 ? WL : 2);     // loads per wave per stage: A chunks, W chunks or codes and params
+    // loads per wave per stage: A chunks, W chunks or codes and params
+    static constexpr int LPS = AL + (F16 ? WL : 2);
     static_assert(BM % 64 == 0 && (BM / 8) % WAVES == 0, "A chunks split evenly over the waves");
 };
 
@@ -329,7 +330,9 @@ __device__ __forceinline__ void wait_vm_loads(int younger)
 // and gb + 32 + c0 .. +15 (b) of one row, fp16 after the bias; its partner (lane ^ 1) holds
 // the other 32 columns of the 64-column group gb. Quantized exactly as the KV-append
 // kernel does (the same group_quant and code_of on the same fp16 values) and stored in the
-// cache's canonical layout.
+// cache's canonical layout. RUNS: rows come in runs of g.kv_rows_per_seq positions of one
+// sequence (prefill); otherwise each row is its own sequence (a decode step).
+template <bool RUNS>
 __device__ __forceinline__ void qkv_append(const GemmArgs &g, int grow, int gb, int c0, half8_t a0, half8_t a1,
                                            half8_t b0, half8_t b1)
 {
@@ -362,8 +365,9 @@ __device__ __forceinline__ void qkv_append(const GemmArgs &g, int grow, int gb, 
     const int d = g.kv.head_dim, h = g.kv.heads * d;
     const int rel = gb - g.kv_col0, isv = rel >= h ? 1 : 0, within = rel - isv * h;
     const int head = within / d, grp = (within % d) / 64;
-    const int pos = g.kv_dpos ? *g.kv_dpos : g.kv_pos0;
-    const size_t at = kv_slab(g.kv, g.kv_seq0 + grow, head) * g.kv.cap + pos;
+    const int seq = RUNS ? grow / g.kv_rows_per_seq : grow, off = RUNS ? grow - seq * g.kv_rows_per_seq : 0;
+    const int pos = (g.kv_dpos ? *g.kv_dpos : g.kv_pos0) + off;
+    const size_t at = kv_slab(g.kv, g.kv_seq0 + seq, head) * g.kv.cap + pos;
     const size_t cofs = at * (d / 2) + grp * 32 + c0 / 2, pofs = at * (d / 64) + grp;
     const uint32_t param = (uint32_t)q.scale | ((uint32_t)q.zero << 16);
     uint8_t *codes = isv ? g.kv.vc : g.kv.kc;
@@ -380,7 +384,7 @@ __device__ __forceinline__ void qkv_append(const GemmArgs &g, int grow, int gb, 
     }
 }
 
-template <int BM_, bool F16, int S_ = 0, bool APPEND = false>
+template <int BM_, bool F16, int S_ = 0, int APPEND = 0>
 __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &tm)
 {
     using C = W4<BM_, F16, S_>;
@@ -558,7 +562,7 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
     // APPEND: the wave's 64 columns are one quantization group of K or V (the QKV
     // output's K and V start at a multiple of 64); column block 0's values wait here
     static_assert(!APPEND || NB == 2, "one 64-column group per wave");
-    const bool kv_group = APPEND && n0 + wn * NB * 32 >= g.kv_col0;
+    const bool kv_group = APPEND != 0 && n0 + wn * NB * 32 >= g.kv_col0;
     half8_t hold[APPEND ? MB : 1][2];
 #pragma unroll
     for (int j = 0; j < NB; j++) {
@@ -631,7 +635,7 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
                     hold[i][0] = o0;
                     hold[i][1] = o1;
                 } else {
-                    qkv_append(g, grow, n0 + wn * NB * 32, c0, hold[i][0], hold[i][1], o0, o1);
+                    qkv_append<APPEND == 2>(g, grow, n0 + wn * NB * 32, c0, hold[i][0], hold[i][1], o0, o1);
                 }
                 continue;
             }
@@ -648,22 +652,39 @@ __global__ void __launch_bounds__(512, 1) k_gemm_f16_256(GemmArgs g, TileMap tm)
 // 128 rows or fewer: short tiles, two workgroups per CU where LDS and registers allow
 __global__ void __launch_bounds__(512, 2) k_gemm_w4_128(GemmArgs g, TileMap tm) { gemm_w4_body<128, false>(g, tm); }
 __global__ void __launch_bounds__(512, 2) k_gemm_w4_64(GemmArgs g, TileMap tm) { gemm_w4_body<64, false>(g, tm); }
-// the QKV GEMM of a decode step with the K/V append in its epilogue (EPI_QKV_APPEND)
+// the QKV GEMM with the K/V append in its epilogue (EPI_QKV_APPEND): a decode step (one
+// position per sequence), and prefill (rows in runs of one sequence's positions)
 __global__ void __launch_bounds__(512, 1) k_gemm_w4_256a(GemmArgs g, TileMap tm)
 {
-    gemm_w4_body<256, false, 0, true>(g, tm);
+    gemm_w4_body<256, false, 0, 1>(g, tm);
 }
 __global__ void __launch_bounds__(512, 1) k_gemm_w4_192a(GemmArgs g, TileMap tm)
 {
-    gemm_w4_body<192, false, 0, true>(g, tm);
+    gemm_w4_body<192, false, 0, 1>(g, tm);
 }
 __global__ void __launch_bounds__(512, 2) k_gemm_w4_128a(GemmArgs g, TileMap tm)
 {
-    gemm_w4_body<128, false, 0, true>(g, tm);
+    gemm_w4_body<128, false, 0, 1>(g, tm);
 }
 __global__ void __launch_bounds__(512, 2) k_gemm_w4_64a(GemmArgs g, TileMap tm)
 {
-    gemm_w4_body<64, false, 0, true>(g, tm);
+    gemm_w4_body<64, false, 0, 1>(g, tm);
+}
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_256r(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<256, false, 0, 2>(g, tm);
+}
+__global__ void __launch_bounds__(512, 1) k_gemm_w4_192r(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<192, false, 0, 2>(g, tm);
+}
+__global__ void __launch_bounds__(512, 2) k_gemm_w4_128r(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<128, false, 0, 2>(g, tm);
+}
+__global__ void __launch_bounds__(512, 2) k_gemm_w4_64r(GemmArgs g, TileMap tm)
+{
+    gemm_w4_body<64, false, 0, 2>(g, tm);
 }
 // fp16, 128 rows or fewer: bound by the weight stream, so a third stage in flight pays
 __global__ void __launch_bounds__(512, 1) k_gemm_f16_64(GemmArgs g, TileMap tm) { gemm_w4_body<64, true, 3>(g, tm); }
@@ -972,14 +993,15 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t st)
         // only where the caller checked the plan: int4 weights, pipelined, K loop not split
         if (!int4 || !p.pipelined || p.tm.splits != 1 || g.kv_col0 % 64 || g.kv.head_dim % 64)
             return hipErrorInvalidValue;
+        const bool runs = g.kv_rows_per_seq > 1;
         if (p.bm == 64)
-            hipLaunchKernelGGL(k_gemm_w4_64a, grid, wg8, 0, st, g, p.tm);
+            hipLaunchKernelGGL(runs ? k_gemm_w4_64r : k_gemm_w4_64a, grid, wg8, 0, st, g, p.tm);
         else if (p.bm == 128)
-            hipLaunchKernelGGL(k_gemm_w4_128a, grid, wg8, 0, st, g, p.tm);
+            hipLaunchKernelGGL(runs ? k_gemm_w4_128r : k_gemm_w4_128a, grid, wg8, 0, st, g, p.tm);
         else if (p.bm == 192)
-            hipLaunchKernelGGL(k_gemm_w4_192a, grid, wg8, 0, st, g, p.tm);
+            hipLaunchKernelGGL(runs ? k_gemm_w4_192r : k_gemm_w4_192a, grid, wg8, 0, st, g, p.tm);
         else
-            hipLaunchKernelGGL(k_gemm_w4_256a, grid, wg8, 0, st, g, p.tm);
+            hipLaunchKernelGGL(runs ? k_gemm_w4_256r : k_gemm_w4_256a, grid, wg8, 0, st, g, p.tm);
         return hipGetLastError();
     }
     if (p.pipelined && !int4 && p.bm == 64)

@@ -281,12 +281,13 @@ void weights_of(const tod_model *m, const LayerStore &L, int mat, const uint8_t 
 
 // ln_g/ln_b (nullable): also write LayerNorm(y) into m->act, fused into the
 // GEMM's split-K reduction when it has one.
-// kv (nullable, EPI_QKV_APPEND): the cache the QKV GEMM appends this step's K/V to, for
-// sequences seq0 + row at position *dpos (pos0 when null), with its host mirror.
+// kv (nullable, EPI_QKV_APPEND): the cache the QKV GEMM appends the rows' K/V to, with its
+// host mirror: rows in runs of per_seq positions (*dpos, or pos0 when null, onwards) of
+// sequences seq0, seq0 + 1, ...
 int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStore &L, const uint8_t *slot,
              uint16_t *y, int64_t ldc, int epi, hipStream_t st, const uint16_t *ln_g = nullptr,
              const uint16_t *ln_b = nullptr, const KvView *kv = nullptr, const KvView *kv_mirror = nullptr,
-             int seq0 = 0, int pos0 = 0, const int *dpos = nullptr)
+             int seq0 = 0, int pos0 = 0, const int *dpos = nullptr, int per_seq = 1)
 {
     GemmArgs g{};
     g.a = a;
@@ -315,10 +316,19 @@ int run_gemm(tod_model *m, const uint16_t *a, int rows, int mat, const LayerStor
         g.kv_pos0 = pos0;
         g.kv_seq0 = seq0;
         g.kv_col0 = m->cfg.hidden; // q, then k, then v
+        g.kv_rows_per_seq = per_seq;
     }
     ProfScope ps(m, TOD_K_GEMM_QKV + mat, st);
     HIPCHK(launch_gemm(g, st));
     return TOD_OK;
+}
+
+// The QKV GEMM over `rows` rows can append K/V in its epilogue: int4 weights on the
+// pipelined kernel with the K loop not split.
+bool qkv_append_plan(const tod_model *m, int rows)
+{
+    const GemmPlanInfo qp = gemm_plan_info(rows, m->n_out[MAT_QKV], m->n_in[MAT_QKV], m->int4);
+    return m->int4 && qp.pipelined && qp.splits == 1;
 }
 
 // One decoder layer for `rows` rows whose hidden states start at `h`.
@@ -338,10 +348,12 @@ int layer_pass(tod_model *m, int l, const KvView &kv, uint16_t *h, int rows, boo
         ProfScope ps(m, TOD_K_LAYERNORM, st);
         HIPCHK(launch_layernorm(h, rows, hd, L.ln1_g, L.ln1_b, m->act, st));
     }
-    const bool fused = !prefill_mode && m->qkv_append; // K/V appended by the QKV GEMM itself
+    // K/V appended by the QKV GEMM itself (prefill: where its plan for these rows allows)
+    const bool fused = m->qkv_append && (!prefill_mode || qkv_append_plan(m, rows));
     if (fused) {
         if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wslot, m->qkv, 3 * hd, EPI_QKV_APPEND, st, nullptr, nullptr,
-                           &kv, kv_mirror, seq0, pos, dpos)))
+                           &kv, kv_mirror, seq0, prefill_mode ? 0 : pos, prefill_mode ? nullptr : dpos,
+                           prefill_mode ? s : 1)))
             return rc;
     } else if ((rc = run_gemm(m, m->act, rows, MAT_QKV, L, wslot, m->qkv, 3 * hd, EPI_BIAS, st))) {
         return rc;
@@ -1361,8 +1373,8 @@ int export_kv(tod_model *m, int layer, int block, int row, int head, int t0, int
         if (layer < 0 || layer >= m->cfg.n_layers || block < 0 || block >= m->run.n_blocks || row < 0 || row >= m->M ||
             head < 0 || head >= m->cfg.n_heads || t0 < 0 || t1 > m->cap || t0 > t1)
             return fail(TOD_EINVAL, "export_kv index out of range");
-        HIPCHK(launch_kv_export(m->kv[(size_t)block * m->cfg.n_layers + layer], row, head, t0, t1, d_kc, d_ks, d_kz, d_vc,
-                                d_vs, d_vz, S(stream)));
+        HIPCHK(launch_kv_export(m->kv[(size_t)block * m->cfg.n_layers + layer], row, head, t0, t1, d_kc, d_ks, d_kz,
+                                d_vc, d_vs, d_vz, S(stream)));
         return TOD_OK;
     });
 }
@@ -1500,7 +1512,8 @@ int linear_w4(const uint16_t *d_a, int64_t rows, int in, int out, const uint8_t 
     return guard("linear_w4", [&]() -> int {
         if (!d_codes)
             return fail(TOD_EINVAL, "null codes");
-        return linear_common(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y, stream);
+        return linear_common(d_a, rows, in, out, d_codes, d_scale, d_zero, nullptr, d_bias, d_residual, relu, d_y,
+                             stream);
     });
 }
 
