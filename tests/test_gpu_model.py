@@ -342,12 +342,14 @@ def test_weights_on_disk_give_identical_bits(tier, tmp_path):
 
 @pytest.mark.parametrize("kv_host", [0, 1])
 def test_qkv_gemm_append_gives_identical_bits(kv_host):
-    """Decode steps quantize and append each step's K and V in the QKV GEMM's epilogue where its plan
+    """Decode steps and prefill quantize and append K and V in the QKV GEMM's epilogue where its plan
     allows (int4 weights on the pipelined kernel, K loop not split), instead of a separate append
-    kernel. The same fp16 values go through the same quantizer, so tokens, logits and the cache must
-    equal the separate kernel's bit for bit (TOD_QKV_APPEND=0 at init_model turns the fused path
-    off). OPT-30B width (192-row QKV tiles at 512 rows), 2 layers, 3 decode steps; with kv_host the
-    last layer's cache lives in pinned host memory and the epilogue writes through to it too."""
+    kernel; prefill rows come in runs of one sequence's positions. The same fp16 values go through
+    the same quantizer, so tokens, logits and the cache (prompt and generated positions) must equal
+    the separate kernel's bit for bit (TOD_QKV_APPEND=0 at init_model turns the fused path off).
+    OPT-30B width (192-row QKV tiles at 512 decode rows, 256-row tiles at 1024 prefill rows), 2
+    layers, 3 decode steps; with kv_host the last layer's cache lives in pinned host memory and the
+    epilogue writes through to it too."""
     torch = torch_cuda()
     import throughput_oriented_offloaded_amd as tod
     shape = synth.WORKLOADS["opt-30b"].shape.replace(n_layers=2)
@@ -387,7 +389,7 @@ def test_qkv_gemm_append_gives_identical_bits(kv_host):
         m.close()
     print(f"kv_host {kv_host}: append launches separate {out['separate'][3]}, fused {out['fused'][3]}; "
           f"QKV launches {out['separate'][4]} / {out['fused'][4]}", flush=True)
-    assert out["separate"][3] > 0 and out["fused"][3] < out["separate"][3]  # prefill keeps its append kernel
+    assert out["separate"][3] > 0 and out["fused"][3] == 0  # no append kernel on the fused path
     assert np.array_equal(out["separate"][0], out["fused"][0])
     assert np.array_equal(out["separate"][1], out["fused"][1])
     assert out["separate"][2] == out["fused"][2]
