@@ -18,6 +18,9 @@
 //    ring.
 //    At 128 rows or fewer the same bodies run on 128- or 64-row tiles (int4,
 //    two workgroups per CU) and 64-row tiles (fp16).
+//    The QKV GEMM can quantize and append the rows' K and V to the int4 KV
+//    cache in its epilogue instead of storing them (k_gemm_w4_*a for a decode
+//    step, k_gemm_w4_*r for prefill's runs of one sequence's positions).
 //  * k_gemm (small GEMMs of 128 rows or fewer that would give the pipelined
 //    kernel fewer than 128 workgroups; fp16 weights whose N is not a
 //    multiple of 32): 256-thread
