@@ -523,6 +523,10 @@ __device__ __forceinline__ void gemm_w4_body(const GemmArgs &g, const TileMap &t
 #pragma unroll
             for (int i = 0; i < MB; i++)
                 a_nxt[i] = a_frag(i, t + 1);
+            // one workgroup per CU (int4, 192 or 256 rows): keep the next step's A reads ahead of
+            // this step's MFMAs; left alone, the compiler sinks each next to its first use
+            if constexpr (!F16 && BM >= 192)
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < NB; j++)
                 b_nxt[j] = b_frag(j, t + 1);
