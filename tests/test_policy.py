@@ -117,14 +117,23 @@ def test_gemm_estimates_bracket_the_roofline():
 
 
 def _measurements():
+    """(fields, comment) of each record."""
     path = os.path.join(ROOT, "profiles", "cost_model_measurements.txt")
     rows = []
     with open(path) as f:
         for line in f:
-            line = line.split("#", 1)[0].strip()
-            if line:
-                rows.append(line.split())
+            body, _, comment = line.partition("#")
+            if body.strip():
+                rows.append((body.split(), comment.strip()))
     return rows
+
+
+def _append_s(shape, rows, hw):
+    """The step model's K/V-append term for one layer: at least one launch, else the append's bytes
+    (reads 4d, writes d + d/8 per row and head) at the streaming rate. A decode step's QKV GEMM does
+    the append in its epilogue, so its recorded time holds what the model prices as this term."""
+    d = shape.head_dim
+    return max(hw["launch_us"] * 1e-6, rows * shape.n_heads * (4 * d + d + d / 8) / (hw["mem_gbs"] * 1e9))
 
 
 def test_estimates_match_recorded_measurements():
@@ -133,13 +142,15 @@ def test_estimates_match_recorded_measurements():
     tod = _lib()
     hw = tod.default_hw()
     checked = 0
-    for rec in _measurements():
+    for rec, comment in _measurements():
         kind, workload = rec[0], rec[1]
         w = synth.WORKLOADS[workload]
         shape = w.shape
         if kind == "gemm":
             rows, n, k, int4, measured_us = int(rec[2]), int(rec[3]), int(rec[4]), int(rec[5]), float(rec[6])
             predicted_us = tod.estimate_gemm(rows, n, k, int4, hw) * 1e6
+            if "K/V append in its epilogue" in comment:
+                predicted_us += _append_s(shape, rows, hw) * 1e6
         else:  # step: the workload's own run configuration, with the recorded placement
             hbm_layers, host_layers, prompt_len, measured_us = int(rec[2]), int(rec[3]), int(rec[4]), float(rec[5])
             run = dict(gpu_batch=w.gpu_batch, batches_per_block=w.batches_per_block, prompt_len=prompt_len,

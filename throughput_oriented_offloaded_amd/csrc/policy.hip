@@ -233,14 +233,14 @@ void default_hw(tod_hw *hw)
     hw->attn_gbs = 6100.0;    // decode attention, int4 cache, OPT-30B shape
     hw->mem_gbs = 7100.0;     // streaming reads with nontemporal 16-byte loads
     hw->link_gbs = 57.2;      // one pinned -> HBM copy of a layer image
-    hw->int4_tflops = 1280.0; // pipelined int4 GEMMs, steady rate with every CU busy (fitted)
-    hw->fp16_tflops = 1325.0; // pipelined fp16-weight GEMMs (LM head), steady rate (fitted)
+    hw->int4_tflops = 1260.0; // pipelined int4 GEMMs, steady rate with every CU busy (fitted)
+    hw->fp16_tflops = 1300.0; // pipelined fp16-weight GEMMs (LM head), steady rate (fitted)
     hw->launch_us = 4.0;      // per kernel inside a replayed decode graph
     hw->hbm_bytes = 280e9;    // device memory a model may use
     hw->host_bytes = 270e9;   // pinned host memory a process may hold
     hw->disk_gbs = 7.4;       // reads of the weight file (one image per read)
     hw->disk_bytes = 80e9;    // free space for the weight file
-    hw->gemm_wg_us = 19.0;    // fixed cost per wave of pipelined GEMM workgroups (fitted)
+    hw->gemm_wg_us = 20.0;    // fixed cost per wave of pipelined GEMM workgroups (fitted)
     hw->staged_tflops = 1700.0; // register-staged GEMM (<= 128 rows): flops, fitted
     hw->staged_gbs = 3230.0;   // register-staged GEMM: weight bytes, fitted
     hw->staged_us = 10.0;      // register-staged GEMM: fixed time (OPT-125m GEMMs at 8 rows)
