@@ -166,7 +166,8 @@ __device__ __forceinline__ void attend_chunk(const KvChunk<D / 32> &c, int c0, i
 // 64/L consecutive positions of K (or V) as one contiguous line. The next
 // chunk's loads are issued before the current chunk's arithmetic (two
 // register buffers), the softmax maximum and sums use DPP/swizzle reductions
-// within the wave, and the final cross-lane sum runs once per (sequence, head).
+// within the wave, and the final cross-lane sum runs once per (sequence, head)
+// as a reduce-scatter: each lane ends with its share of the output dims.
 template <int D>
 __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict__ q, int64_t q_stride,
                                                      uint16_t *__restrict__ out, int64_t out_stride, int rows,
@@ -236,24 +237,37 @@ __global__ void __launch_bounds__(256) k_attn_decode(const uint16_t *__restrict_
     else
         attend_chunk<D, (L > 3 ? 3 : 1)>(ca, c0, slot, ctx, qa, qb, st);
 
-    // add the zero term, sum over the wave's positions
+    // add the zero term, sum over the wave's positions: the denominator on every lane; the 32
+    // dims of each lane group as a butterfly reduce-scatter over the 64/L slots (slot bit k: the
+    // lanes L << k apart; each step keeps the half of the dims that bit selects), so each lane ends
+    // with 32 / (64/L) consecutive dims of its block, summed slot pair by slot pair
     const float den = reduce_slots<L>(st.lsum, OpAdd());
-    float o[32];
+    constexpr int NSLOT = 64 / L, KEEP = 32 / NSLOT, STEPS = L == 4 ? 4 : 5; // log2(NSLOT)
+    typedef float f32x32_t __attribute__((ext_vector_type(32))); // a vector: the selects below pick values
+    f32x32_t o;
 #pragma unroll
     for (int e = 0; e < 32; e++)
-        o[e] = reduce_slots<L>(st.acc[e] + st.zsum, OpAdd());
-    const float inv = 1.0f / den;
-    if (slot == 0) {
-        uint16_t *op = out + (int64_t)row * out_stride + (int64_t)head * D + pc * 32;
+        o[e] = st.acc[e] + st.zsum;
+    int e0 = 0;
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
-            uint4_t pk;
+    for (int k = 0; k < STEPS; k++) {
+        const int half = 16 >> k;
+        const bool hi = (slot >> k) & 1;
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                pk[i] = (uint32_t)f2h(o[8 * w + 2 * i] * inv) | ((uint32_t)f2h(o[8 * w + 2 * i + 1] * inv) << 16);
-            *reinterpret_cast<uint4_t *>(op + 8 * w) = pk;
+        for (int i = 0; i < half; i++) {
+            const float lo_v = o[i], hi_v = o[i + half];
+            const float send = hi ? lo_v : hi_v;
+            const float keep = hi ? hi_v : lo_v;
+            o[i] = keep + __shfl_xor(send, L << k, 64);
         }
+        e0 += hi ? half : 0;
     }
+    const float inv = 1.0f / den;
+    uint16_t *op = out + (int64_t)row * out_stride + (int64_t)head * D + pc * 32 + e0;
+    if constexpr (KEEP == 2)
+        *reinterpret_cast<uint32_t *>(op) = (uint32_t)f2h(o[0] * inv) | ((uint32_t)f2h(o[1] * inv) << 16);
+    else
+        *op = f2h(o[0] * inv);
 }
 
 // ---------------------------------------------------------------------------
